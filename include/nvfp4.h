@@ -1,0 +1,199 @@
+/*
+ * nvfp4.h -- C ABI of libnvfp4.so: the batched T-token NVFP4 W4A4 MLP on
+ * AMD Instinct MI355X (gfx950).
+ *
+ * Sources for the operations (web pages, cited by title and section):
+ *  [vllm]  vllm.cpp issue "tp>1 prefill is host-bound: per-token fp4 GEMM +
+ *          per-layer H2D activation staging" -- sections "Problem" and
+ *          "Fix directions" (1: one launch set per batch with a grid that
+ *          scales with T; 2: activations stay on the device across fp4
+ *          layers; 3: activation packing done on the device).
+ *  [llama] llama.cpp discussion "CUDA: NVFP4 prefill on Blackwell leaves
+ *          ~1.45x performance on the table" -- section "What the patch does"
+ *          (gate and up share one quantised activation; the GLU output is
+ *          quantised straight into the next GEMM's activation format;
+ *          aligned, pipelined tile loads) and "Verified" (MUL_MAT,
+ *          MUL_MAT_ID).
+ *  [dsv4]  nvfp4-megamoe-kernel "PERFORMANCE -- verified hot-path audit and
+ *          prioritized fixes" -- section P0 (activation global scale
+ *          amax / (6*448), amax clamped at 1e-8, kept on the device instead
+ *          of being read back with .item()) and P8 item 5 (MoE runner with
+ *          pre-allocated buffers, no host syncs, no dynamic shapes).
+ *
+ * NVFP4 layout (all calls).  A matrix [rows][cols] is
+ *   codes  : rows * cols/2 bytes, row-major, row r at codes + r*cols/2;
+ *            byte j of a row holds element 2j in bits 3:0 and element 2j+1
+ *            in bits 7:4; each 4-bit code is E2M1 (sign, 2 exponent bits,
+ *            1 mantissa bit; magnitudes 0 0.5 1 1.5 2 3 4 6);
+ *   scales : rows * cols/16 bytes, row-major; byte b of a row is the E4M3
+ *            (OCP "FN", max 448) scale of elements [16b, 16b+16);
+ *   gscale : one float32 global scale (one per expert for expert stacks),
+ *            device-resident; value = code * scale * gscale.
+ *
+ * Conventions (all calls).
+ *  - Every pointer is a device pointer unless its comment says host.
+ *  - Calls are asynchronous on `stream` (a hipStream_t; NULL = the default
+ *    stream).  The library never synchronises, never copies between host
+ *    and device, never allocates, and never reads device memory on the
+ *    host: global scales are produced and consumed on the device only.
+ *  - The caller owns every buffer.  The library keeps no pointer after a
+ *    call returns; its only state is a process-wide launch counter.
+ *  - Workspace: ws == NULL with ws_bytes != NULL is a size query: the
+ *    required size is stored in *ws_bytes and NVFP4_OK returned without
+ *    launching anything.  Otherwise *ws_bytes is the size of ws (ws_bytes ==
+ *    NULL means no workspace, size 0) and must be at least the required
+ *    size.  The workspace needs no initialisation; its contents after a call
+ *    are documented per call.
+ *  - Errors are returned before any work is enqueued, from host-side
+ *    validation: NULL pointers, shapes, alignment, workspace size, unknown
+ *    enum values; NVFP4_ERR_DEVICE when no gfx950 device is current.
+ *    NVFP4_ERR_LAUNCH reports a failed kernel launch.  Faults inside a
+ *    kernel (for instance an out-of-range row index in a_rows, or buffers
+ *    shorter than the stated shapes) are undefined behaviour.
+ *  - Inputs must be finite; NaN or Inf inputs give unspecified outputs.
+ *  - A zero-row call (T == 0, rows == 0, M == 0) is a successful no-op and
+ *    writes nothing, not even a global scale.
+ *  - Alignment: codes and scales base pointers 16-byte aligned, gscale
+ *    4-byte aligned, float/bf16 inputs and outputs 16-byte aligned with row
+ *    strides that keep every row 16-byte aligned.
+ */
+#ifndef NVFP4_H
+#define NVFP4_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct nvfp4_tensor {
+  uint8_t *codes;   /* packed E2M1 codes, see the layout above          */
+  uint8_t *scales;  /* E4M3 block scales, one per 16 elements of a row  */
+  float   *gscale;  /* device float32 global scale(s)                   */
+} nvfp4_tensor;
+
+enum nvfp4_status {
+  NVFP4_OK = 0,
+  NVFP4_ERR_NULL = 1,       /* a required pointer is NULL                       */
+  NVFP4_ERR_SHAPE = 2,      /* negative size, or a size not a required multiple */
+  NVFP4_ERR_ALIGN = 3,      /* pointer or row stride misaligned                 */
+  NVFP4_ERR_WORKSPACE = 4,  /* workspace smaller than required                  */
+  NVFP4_ERR_ARG = 5,        /* unknown enum value or inconsistent argument      */
+  NVFP4_ERR_DEVICE = 6,     /* no usable gfx950 device is current               */
+  NVFP4_ERR_LAUNCH = 7      /* a kernel launch failed                           */
+};
+
+enum nvfp4_dtype { NVFP4_F32 = 0, NVFP4_BF16 = 1 };
+
+enum nvfp4_gs_mode {
+  NVFP4_GS_COMPUTE = 0,  /* amax over the whole input on the device; writes *gscale */
+  NVFP4_GS_GIVEN = 1     /* use the float32 already stored at *gscale            */
+};
+
+enum nvfp4_epilogue {
+  NVFP4_EPI_STORE = 0,             /* out = A~ . W~^T scaled, float32 or bf16         */
+  NVFP4_EPI_SILU_MUL_REQUANT = 1   /* out_q = NVFP4(SiLU(A~ . Wg~^T) * (A~ . Wu~^T))  */
+};
+
+/*
+ * nvfp4_quantize_act -- NVFP4-quantise x [rows][cols] on the device.
+ * [dsv4] P0: gscale = RN32(max(max|x|, 1e-8) / (6*448)), computed on the
+ * device over the whole tensor of this call and written to *out.gscale
+ * (NVFP4_GS_COMPUTE), or read from *out.gscale (NVFP4_GS_GIVEN).  Then per
+ * 16-element block: scale = E4M3 round-to-nearest-even of blockmax / (6 *
+ * gscale), saturating at 448; codes = E2M1 round-to-nearest-even of x /
+ * (scale * gscale), saturating at 6, sign bit = sign bit of x, magnitude 0
+ * in a block whose scale is 0.  All rounding decisions are exact (ties to
+ * even).  [vllm] Fix directions 3 (packing on the device); the same call
+ * quantises weights (rows = output features) in a cold setup step.
+ *   x       : float32 (x_dtype NVFP4_F32) or bf16 (NVFP4_BF16), row stride
+ *             ld_x elements (ld_x >= cols)
+ *   cols    : multiple of 16
+ *   ws      : NVFP4_GS_COMPUTE needs a small workspace (block partial
+ *             maxima, at most 4 KiB); NVFP4_GS_GIVEN needs none
+ * Two kernel launches (COMPUTE) or one (GIVEN), independent of rows.
+ */
+int nvfp4_quantize_act(const void *x, int x_dtype, int64_t rows, int64_t cols, int64_t ld_x,
+                       nvfp4_tensor out, int gs_mode, void *ws, size_t *ws_bytes, void *stream);
+
+/*
+ * nvfp4_gemm -- C[M][N] = (A~ . B~^T) * gscale_a * gscale_b.
+ * One NVFP4 x NVFP4 contraction, K-contiguous operands as a linear layer
+ * stores them ([llama] "Verified", MUL_MAT).  One launch per call whatever
+ * M is ([vllm] Fix directions 1).  Accumulation in float32 on the matrix
+ * cores, products exact.
+ *   a : [M][K] NVFP4, b : [N][K] NVFP4 (one gscale each)
+ *   K : multiple of 128
+ *   c : float32 or bf16 (c_dtype), row stride ldc >= N elements
+ */
+int nvfp4_gemm(nvfp4_tensor a, nvfp4_tensor b, int64_t M, int64_t N, int64_t K,
+               void *c, int c_dtype, int64_t ldc, void *ws, size_t *ws_bytes, void *stream);
+
+/*
+ * nvfp4_mlp_gu_act -- gate/up projections, SiLU(gate) * up, requantisation.
+ * [llama] "What the patch does": gate and up read one shared quantised
+ * activation x~; the GLU output H = SiLU(x~ . Wg~^T) * (x~ . Wu~^T)
+ * (SiLU(g) = g / (1 + e^-g), float32) is quantised directly into the down
+ * projection's NVFP4 input h_out, with a global scale computed on the device
+ * over the whole [T][I] tensor of this call and written to *h_out.gscale.
+ *   x      : [T][K] NVFP4;  w_gate, w_up : [I][K] NVFP4
+ *   h_out  : [T][I] NVFP4 (codes, scales, gscale written)
+ *   K, I   : multiples of 128
+ *   ws     : on return its first T*I*4 bytes hold H in float32, row-major
+ *            [T][I] (the value that was quantised)
+ * Launch count is fixed (independent of T).
+ */
+int nvfp4_mlp_gu_act(nvfp4_tensor x, nvfp4_tensor w_gate, nvfp4_tensor w_up,
+                     int64_t T, int64_t K, int64_t I, nvfp4_tensor h_out,
+                     void *ws, size_t *ws_bytes, void *stream);
+
+/*
+ * nvfp4_mlp_down -- Y[T][K] = (H~ . Wd~^T) * gscale_h * gscale_wd.
+ * The down projection of the MLP ([vllm] "Problem": MlpDownFp4, here once
+ * per batch).  y is float32 (parity) or bf16 (the next layer's activation,
+ * kept on the device: [vllm] Fix directions 2).
+ *   h : [T][I] NVFP4;  w_down : [K][I] NVFP4;  I multiple of 128
+ *   y : row stride ldy >= K elements
+ */
+int nvfp4_mlp_down(nvfp4_tensor h, nvfp4_tensor w_down, int64_t T, int64_t I, int64_t K,
+                   void *y, int y_dtype, int64_t ldy, void *ws, size_t *ws_bytes, void *stream);
+
+/*
+ * nvfp4_grouped_gemm -- expert-grouped NVFP4 GEMM in one launch per GEMM
+ * ([llama] "Verified", MUL_MAT_ID; [dsv4] P8 item 5: no host syncs, no
+ * dynamic shapes).  Slot s (0 <= s < M) reads activation row a_rows[s] of a
+ * (row s when a_rows is NULL); slots [group_offsets[e], group_offsets[e+1])
+ * belong to expert e.  a_rows and group_offsets stay on the device; the host
+ * only knows the static slot count M, and group_offsets[E] must equal M.
+ *   a             : [rows_a][K] NVFP4 (rows_a is implied by a_rows)
+ *   w0            : [E][N][K] NVFP4 expert stack, gscale[E] (gate weights in
+ *                   the GLU epilogue)
+ *   w1            : [E][N][K] up weights (GLU epilogue only; else ignored)
+ *   epilogue      : NVFP4_EPI_STORE -> out [M][N] float32/bf16, row stride
+ *                   ld_out, scaled by gscale_a * w0.gscale[e];
+ *                   NVFP4_EPI_SILU_MUL_REQUANT -> out_q [M][N] NVFP4 of
+ *                   SiLU(gate) * up with one global scale over all M slots
+ *                   (written to *out_q.gscale)
+ *   K, N          : multiples of 128;  E >= 1
+ *   ws            : GLU epilogue: its first M*N*4 bytes hold the float32 GLU
+ *                   output [M][N] on return
+ */
+int nvfp4_grouped_gemm(nvfp4_tensor a, const int32_t *a_rows, const int32_t *group_offsets,
+                       int E, int64_t M, nvfp4_tensor w0, nvfp4_tensor w1, int64_t N, int64_t K,
+                       int epilogue, void *out, int out_dtype, int64_t ld_out, nvfp4_tensor out_q,
+                       void *ws, size_t *ws_bytes, void *stream);
+
+/* Static message for a status code (host string, never NULL). */
+const char *nvfp4_strerror(int status);
+
+/* Number of kernel launches this library has enqueued in this process
+ * (a host counter; lets a caller check that the launch count of a call does
+ * not depend on T -- [vllm] "Problem": identical per-token launches). */
+uint64_t nvfp4_launch_count(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* NVFP4_H */

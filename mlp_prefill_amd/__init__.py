@@ -1,0 +1,228 @@
+"""Python binding of libnvfp4.so: the batched T-token NVFP4 W4A4 MLP on MI355X.
+
+Argument marshalling only.  Every step of the path runs in the library's HIP
+kernels; torch provides device memory and the current stream.  The functions
+carry the C entry points' names (see include/nvfp4.h for the contract).
+
+Importing this module loads the built library and fails loudly when it is
+missing; there is no fallback implementation.
+"""
+import ctypes
+import os
+from dataclasses import dataclass
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libnvfp4.so")
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError(f"{LIB_PATH} is not built (python -m mlp_prefill_amd.build)")
+
+_lib = ctypes.CDLL(LIB_PATH)
+
+# ---- C types -------------------------------------------------------------------
+_vp = ctypes.c_void_p
+_i64 = ctypes.c_int64
+
+
+class nvfp4_tensor(ctypes.Structure):
+    _fields_ = [("codes", _vp), ("scales", _vp), ("gscale", _vp)]
+
+
+OK, ERR_NULL, ERR_SHAPE, ERR_ALIGN, ERR_WORKSPACE, ERR_ARG, ERR_DEVICE, ERR_LAUNCH = range(8)
+F32, BF16 = 0, 1
+GS_COMPUTE, GS_GIVEN = 0, 1
+EPI_STORE, EPI_SILU_MUL_REQUANT = 0, 1
+
+_sig = {
+    "nvfp4_quantize_act": [_vp, ctypes.c_int, _i64, _i64, _i64, nvfp4_tensor, ctypes.c_int, _vp,
+                           ctypes.POINTER(ctypes.c_size_t), _vp],
+    "nvfp4_gemm": [nvfp4_tensor, nvfp4_tensor, _i64, _i64, _i64, _vp, ctypes.c_int, _i64, _vp,
+                   ctypes.POINTER(ctypes.c_size_t), _vp],
+    "nvfp4_mlp_gu_act": [nvfp4_tensor, nvfp4_tensor, nvfp4_tensor, _i64, _i64, _i64, nvfp4_tensor, _vp,
+                         ctypes.POINTER(ctypes.c_size_t), _vp],
+    "nvfp4_mlp_down": [nvfp4_tensor, nvfp4_tensor, _i64, _i64, _i64, _vp, ctypes.c_int, _i64, _vp,
+                       ctypes.POINTER(ctypes.c_size_t), _vp],
+    "nvfp4_grouped_gemm": [nvfp4_tensor, _vp, _vp, ctypes.c_int, _i64, nvfp4_tensor, nvfp4_tensor, _i64, _i64,
+                           ctypes.c_int, _vp, ctypes.c_int, _i64, nvfp4_tensor, _vp,
+                           ctypes.POINTER(ctypes.c_size_t), _vp],
+}
+for _name, _args in _sig.items():
+    _f = getattr(_lib, _name)
+    _f.argtypes = _args
+    _f.restype = ctypes.c_int
+_lib.nvfp4_strerror.argtypes = [ctypes.c_int]
+_lib.nvfp4_strerror.restype = ctypes.c_char_p
+_lib.nvfp4_launch_count.argtypes = []
+_lib.nvfp4_launch_count.restype = ctypes.c_uint64
+
+lib = _lib
+
+
+class Nvfp4Error(RuntimeError):
+    def __init__(self, status, where):
+        super().__init__(f"{where}: {_lib.nvfp4_strerror(status).decode()} (status {status})")
+        self.status = status
+
+
+def _check(status, where):
+    if status != OK:
+        raise Nvfp4Error(status, where)
+
+
+def launch_count():
+    """Kernel launches this library has enqueued in this process."""
+    return int(_lib.nvfp4_launch_count())
+
+
+def _stream(stream=None):
+    if stream is not None:
+        return _vp(stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream))
+    return _vp(torch.cuda.current_stream().cuda_stream)
+
+
+def _ptr(t):
+    return _vp(t.data_ptr()) if t is not None else _vp(0)
+
+
+# ---- device NVFP4 matrices --------------------------------------------------------
+@dataclass
+class NVFP4:
+    """Device NVFP4 matrix [rows][cols] (or an expert stack [experts][rows][cols])."""
+    codes: torch.Tensor     # uint8 [..., rows, cols // 2]
+    scales: torch.Tensor    # uint8 [..., rows, cols // 16]
+    gscale: torch.Tensor    # float32 [1] or [experts]
+    rows: int
+    cols: int
+
+    @staticmethod
+    def empty(rows, cols, device="cuda", experts=None):
+        lead = () if experts is None else (experts,)
+        return NVFP4(torch.empty(lead + (rows, cols // 2), dtype=torch.uint8, device=device),
+                     torch.empty(lead + (rows, cols // 16), dtype=torch.uint8, device=device),
+                     torch.empty((experts or 1,), dtype=torch.float32, device=device),
+                     rows, cols)
+
+    @staticmethod
+    def stack(mats):
+        """Stack per-expert matrices into one [experts][rows][cols] operand."""
+        return NVFP4(torch.stack([m.codes for m in mats]), torch.stack([m.scales for m in mats]),
+                     torch.cat([m.gscale for m in mats]), mats[0].rows, mats[0].cols)
+
+    def c(self):
+        return nvfp4_tensor(self.codes.data_ptr(), self.scales.data_ptr(), self.gscale.data_ptr())
+
+
+def _null_tensor():
+    return nvfp4_tensor(0, 0, 0)
+
+
+def _dtype_code(t):
+    if t.dtype == torch.bfloat16:
+        return BF16
+    if t.dtype == torch.float32:
+        return F32
+    raise TypeError(f"unsupported dtype {t.dtype}")
+
+
+def _workspace(query, ws, device):
+    """Query the required size, allocate (or check) a byte workspace."""
+    size = ctypes.c_size_t(0)
+    _check(query(_vp(0), ctypes.byref(size)), "workspace query")
+    need = size.value
+    if ws is None:
+        ws = torch.empty(max(need, 256), dtype=torch.uint8, device=device)
+    return ws, ctypes.c_size_t(ws.numel())
+
+
+# ---- entry points ----------------------------------------------------------------
+def nvfp4_quantize_act(x, out, gs_mode=GS_COMPUTE, ws=None, stream=None):
+    """Quantise x [rows, cols] (bf16 or float32, device) into `out` (NVFP4)."""
+    rows, cols = x.shape
+    ld = x.stride(0)
+    if x.stride(1) != 1:
+        raise ValueError("x must be row-major")
+    dt = _dtype_code(x)
+
+    def q(wsp, szp):
+        return _lib.nvfp4_quantize_act(_vp(0), dt, rows, cols, ld, _null_tensor(), gs_mode, wsp, szp, _vp(0))
+    ws, sz = _workspace(q, ws, x.device)
+    _check(_lib.nvfp4_quantize_act(_ptr(x), dt, rows, cols, ld, out.c(), gs_mode, _ptr(ws), ctypes.byref(sz),
+                                   _stream(stream)), "nvfp4_quantize_act")
+    return out
+
+
+def nvfp4_gemm(a, b, c, stream=None):
+    """c [M, N] (float32 or bf16) = A~ . B~^T * gs_a * gs_b."""
+    m, n = c.shape
+    _check(_lib.nvfp4_gemm(a.c(), b.c(), m, n, a.cols, _ptr(c), _dtype_code(c), c.stride(0), _vp(0),
+                           None, _stream(stream)), "nvfp4_gemm")
+    return c
+
+
+def mlp_gu_act_ws_bytes(t, k, i):
+    size = ctypes.c_size_t(0)
+    _check(_lib.nvfp4_mlp_gu_act(_null_tensor(), _null_tensor(), _null_tensor(), t, k, i, _null_tensor(),
+                                 _vp(0), ctypes.byref(size), _vp(0)), "workspace query")
+    return size.value
+
+
+def nvfp4_mlp_gu_act(x, w_gate, w_up, h_out, ws=None, stream=None):
+    """h_out (NVFP4 [T, I]) = requant(SiLU(x~ . Wg~^T) * (x~ . Wu~^T)); ws keeps float32 H."""
+    t, k, i = x.rows, x.cols, w_gate.rows
+    need = mlp_gu_act_ws_bytes(t, k, i)
+    if ws is None:
+        ws = torch.empty(max(need, 256), dtype=torch.uint8, device=x.codes.device)
+    sz = ctypes.c_size_t(ws.numel())
+    _check(_lib.nvfp4_mlp_gu_act(x.c(), w_gate.c(), w_up.c(), t, k, i, h_out.c(), _ptr(ws), ctypes.byref(sz),
+                                 _stream(stream)), "nvfp4_mlp_gu_act")
+    return ws
+
+
+def nvfp4_mlp_down(h, w_down, y, stream=None):
+    """y [T, K] (float32 or bf16) = H~ . Wd~^T * gs_h * gs_wd."""
+    t, kk = y.shape
+    _check(_lib.nvfp4_mlp_down(h.c(), w_down.c(), t, h.cols, kk, _ptr(y), _dtype_code(y), y.stride(0), _vp(0),
+                               None, _stream(stream)), "nvfp4_mlp_down")
+    return y
+
+
+def grouped_ws_bytes(m, n, k, e, epilogue):
+    size = ctypes.c_size_t(0)
+    _check(_lib.nvfp4_grouped_gemm(_null_tensor(), _vp(0), _vp(0), e, m, _null_tensor(), _null_tensor(), n, k,
+                                   epilogue, _vp(0), F32, n, _null_tensor(), _vp(0), ctypes.byref(size), _vp(0)),
+           "workspace query")
+    return size.value
+
+
+def nvfp4_grouped_gemm(a, a_rows, group_offsets, w0, w1=None, out=None, out_q=None,
+                       epilogue=EPI_STORE, m=None, ws=None, stream=None):
+    """Expert-grouped GEMM; see include/nvfp4.h.  Returns the workspace used (GLU epilogue)."""
+    e = w0.gscale.numel()
+    n, k = w0.rows, w0.cols
+    if m is None:
+        m = out.shape[0] if out is not None else out_q.rows
+    need = grouped_ws_bytes(m, n, k, e, epilogue)
+    if need and ws is None:
+        ws = torch.empty(need, dtype=torch.uint8, device=w0.codes.device)
+    sz = ctypes.c_size_t(ws.numel() if ws is not None else 0)
+    out_dt = _dtype_code(out) if out is not None else F32
+    ld = out.stride(0) if out is not None else n
+    _check(_lib.nvfp4_grouped_gemm(a.c(), _ptr(a_rows), _ptr(group_offsets), e, m, w0.c(),
+                                   w1.c() if w1 is not None else _null_tensor(), n, k, epilogue, _ptr(out), out_dt,
+                                   ld, out_q.c() if out_q is not None else _null_tensor(), _ptr(ws),
+                                   ctypes.byref(sz), _stream(stream)), "nvfp4_grouped_gemm")
+    return ws
+
+
+# ---- convenience: host <-> device NVFP4 (test and setup plumbing) -------------------
+def to_device(q_codes, q_scales, gs, rows, cols, device="cuda"):
+    """NVFP4 from host arrays (numpy uint8 codes/scales, float32 gs)."""
+    return NVFP4(torch.from_numpy(q_codes).to(device), torch.from_numpy(q_scales).to(device),
+                 torch.tensor([float(gs)], dtype=torch.float32, device=device), rows, cols)
+
+
+def bf16_from_bits(bits_u16, device="cuda"):
+    """bf16 device tensor from a numpy uint16 array of bf16 bit patterns."""
+    return torch.from_numpy(bits_u16.view("int16")).to(device).view(torch.bfloat16)

@@ -1,0 +1,212 @@
+// C ABI of libnvfp4.so: host-side validation, workspace sizing and dispatch.
+// Every check happens before anything is enqueued; the calls never
+// synchronise, copy, allocate or read device memory on the host.
+#include "nvfp4.h"
+
+#include <atomic>
+#include <cstring>
+
+#include "internal.h"
+
+namespace nvfp4 {
+
+static std::atomic<uint64_t> g_launches{0};
+void count_launch() { g_launches.fetch_add(1, std::memory_order_relaxed); }
+
+}  // namespace nvfp4
+
+namespace {
+
+using nvfp4::Operand;
+
+constexpr int kMaxDevices = 64;
+std::atomic<int> g_dev_state[kMaxDevices];  // 0 unknown, 1 gfx950, 2 unusable
+
+// The current device must be a gfx950.  The first call per device reads its
+// properties; later calls only ask which device is current.
+int check_device() {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) {
+    (void)hipGetLastError();
+    return NVFP4_ERR_DEVICE;
+  }
+  int st = g_dev_state[dev].load(std::memory_order_acquire);
+  if (st == 0) {
+    hipDeviceProp_t prop;
+    if (hipGetDeviceProperties(&prop, dev) != hipSuccess) {
+      (void)hipGetLastError();
+      return NVFP4_ERR_DEVICE;
+    }
+    st = (std::strncmp(prop.gcnArchName, "gfx950", 6) == 0) ? 1 : 2;
+    g_dev_state[dev].store(st, std::memory_order_release);
+  }
+  return st == 1 ? NVFP4_OK : NVFP4_ERR_DEVICE;
+}
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
+int check_tensor(const nvfp4_tensor& t) {
+  if (!t.codes || !t.scales || !t.gscale) return NVFP4_ERR_NULL;
+  if (!aligned(t.codes, 16) || !aligned(t.scales, 16) || !aligned(t.gscale, 4)) return NVFP4_ERR_ALIGN;
+  return NVFP4_OK;
+}
+
+Operand op(const nvfp4_tensor& t) { return Operand{t.codes, t.scales, t.gscale}; }
+
+size_t round_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
+
+// Workspace bookkeeping: returns NVFP4_OK and sets *is_query when the call is
+// a size query; NVFP4_ERR_WORKSPACE when the given workspace is too small.
+int workspace(void* ws, size_t* ws_bytes, size_t need, bool* is_query) {
+  *is_query = false;
+  if (ws == nullptr && ws_bytes != nullptr) {
+    *ws_bytes = need;
+    *is_query = true;
+    return NVFP4_OK;
+  }
+  const size_t have = ws_bytes ? *ws_bytes : 0;
+  if (need > 0 && (ws == nullptr || have < need)) return NVFP4_ERR_WORKSPACE;
+  if (need > 0 && !aligned(ws, 256)) return NVFP4_ERR_ALIGN;
+  return NVFP4_OK;
+}
+
+int elem_size(int dtype) { return dtype == NVFP4_BF16 ? 2 : 4; }
+bool dtype_ok(int dtype) { return dtype == NVFP4_F32 || dtype == NVFP4_BF16; }
+
+// Float32 GLU output [rows][cols] followed by the partial maxima.
+size_t glu_ws(int64_t rows, int64_t cols, size_t npart) {
+  return round_up((size_t)rows * (size_t)cols * sizeof(float), 256) + round_up(npart * sizeof(float), 256);
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* nvfp4_strerror(int status) {
+  switch (status) {
+    case NVFP4_OK: return "ok";
+    case NVFP4_ERR_NULL: return "a required pointer is NULL";
+    case NVFP4_ERR_SHAPE: return "invalid shape";
+    case NVFP4_ERR_ALIGN: return "misaligned pointer or row stride";
+    case NVFP4_ERR_WORKSPACE: return "workspace too small";
+    case NVFP4_ERR_ARG: return "invalid argument";
+    case NVFP4_ERR_DEVICE: return "no usable gfx950 device";
+    case NVFP4_ERR_LAUNCH: return "kernel launch failed";
+    default: return "unknown status";
+  }
+}
+
+uint64_t nvfp4_launch_count(void) { return nvfp4::g_launches.load(std::memory_order_relaxed); }
+
+int nvfp4_quantize_act(const void* x, int x_dtype, int64_t rows, int64_t cols, int64_t ld_x, nvfp4_tensor out,
+                       int gs_mode, void* ws, size_t* ws_bytes, void* stream) {
+  if (!dtype_ok(x_dtype) || (gs_mode != NVFP4_GS_COMPUTE && gs_mode != NVFP4_GS_GIVEN)) return NVFP4_ERR_ARG;
+  if (rows < 0 || cols < 0 || cols % 16 != 0 || ld_x < cols) return NVFP4_ERR_SHAPE;
+  if (rows * (cols / 16) >= ((int64_t)1 << 31)) return NVFP4_ERR_SHAPE;
+  bool query;
+  int rc = workspace(ws, ws_bytes, nvfp4::quantize_ws_bytes(rows, cols, gs_mode), &query);
+  if (rc != NVFP4_OK || query) return rc;
+  if (rows == 0 || cols == 0) return NVFP4_OK;
+  if (!x) return NVFP4_ERR_NULL;
+  if ((rc = check_tensor(out)) != NVFP4_OK) return rc;
+  if (!aligned(x, 16) || (ld_x * elem_size(x_dtype)) % 16 != 0) return NVFP4_ERR_ALIGN;
+  if ((rc = check_device()) != NVFP4_OK) return rc;
+  return nvfp4::quantize_launch(x, x_dtype, rows, cols, ld_x, out.codes, out.scales, out.gscale, gs_mode, ws,
+                                reinterpret_cast<hipStream_t>(stream));
+}
+
+int nvfp4_gemm(nvfp4_tensor a, nvfp4_tensor b, int64_t M, int64_t N, int64_t K, void* c, int c_dtype,
+               int64_t ldc, void* ws, size_t* ws_bytes, void* stream) {
+  if (!dtype_ok(c_dtype)) return NVFP4_ERR_ARG;
+  if (M < 0 || N < 0 || K <= 0 || K % 128 != 0 || ldc < N) return NVFP4_ERR_SHAPE;
+  bool query;
+  int rc = workspace(ws, ws_bytes, 0, &query);
+  if (rc != NVFP4_OK || query) return rc;
+  if (M == 0 || N == 0) return NVFP4_OK;
+  if ((rc = check_tensor(a)) != NVFP4_OK || (rc = check_tensor(b)) != NVFP4_OK) return rc;
+  if (!c) return NVFP4_ERR_NULL;
+  if (!aligned(c, 16) || (ldc * elem_size(c_dtype)) % 16 != 0) return NVFP4_ERR_ALIGN;
+  if ((rc = check_device()) != NVFP4_OK) return rc;
+  return nvfp4::gemm_launch(op(a), op(b), M, N, K, c, c_dtype == NVFP4_BF16, ldc,
+                            reinterpret_cast<hipStream_t>(stream));
+}
+
+int nvfp4_mlp_gu_act(nvfp4_tensor x, nvfp4_tensor w_gate, nvfp4_tensor w_up, int64_t T, int64_t K, int64_t I,
+                     nvfp4_tensor h_out, void* ws, size_t* ws_bytes, void* stream) {
+  if (T < 0 || K <= 0 || I <= 0 || K % 128 != 0 || I % 128 != 0) return NVFP4_ERR_SHAPE;
+  if (T * (I / 16) >= ((int64_t)1 << 31)) return NVFP4_ERR_SHAPE;
+  const size_t npart = nvfp4::glu_partials_needed(T, I);
+  bool query;
+  int rc = workspace(ws, ws_bytes, T > 0 ? glu_ws(T, I, npart) : 0, &query);
+  if (rc != NVFP4_OK || query) return rc;
+  if (T == 0) return NVFP4_OK;
+  if ((rc = check_tensor(x)) != NVFP4_OK || (rc = check_tensor(w_gate)) != NVFP4_OK ||
+      (rc = check_tensor(w_up)) != NVFP4_OK || (rc = check_tensor(h_out)) != NVFP4_OK)
+    return rc;
+  if ((rc = check_device()) != NVFP4_OK) return rc;
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  float* h = reinterpret_cast<float*>(ws);
+  float* partials = reinterpret_cast<float*>(reinterpret_cast<char*>(ws) +
+                                             round_up((size_t)T * (size_t)I * sizeof(float), 256));
+  uint32_t np = 0;
+  rc = nvfp4::gemm_glu_launch(op(x), op(w_gate), op(w_up), T, I, K, h, partials, &np, st);
+  if (rc != NVFP4_OK) return rc;
+  return nvfp4::requant_f32_launch(h, T, I, h_out.codes, h_out.scales, h_out.gscale, partials, np, st);
+}
+
+int nvfp4_mlp_down(nvfp4_tensor h, nvfp4_tensor w_down, int64_t T, int64_t I, int64_t K, void* y, int y_dtype,
+                   int64_t ldy, void* ws, size_t* ws_bytes, void* stream) {
+  if (!dtype_ok(y_dtype)) return NVFP4_ERR_ARG;
+  if (T < 0 || I <= 0 || K <= 0 || I % 128 != 0 || ldy < K) return NVFP4_ERR_SHAPE;
+  bool query;
+  int rc = workspace(ws, ws_bytes, 0, &query);
+  if (rc != NVFP4_OK || query) return rc;
+  if (T == 0) return NVFP4_OK;
+  if ((rc = check_tensor(h)) != NVFP4_OK || (rc = check_tensor(w_down)) != NVFP4_OK) return rc;
+  if (!y) return NVFP4_ERR_NULL;
+  if (!aligned(y, 16) || (ldy * elem_size(y_dtype)) % 16 != 0) return NVFP4_ERR_ALIGN;
+  if ((rc = check_device()) != NVFP4_OK) return rc;
+  return nvfp4::gemm_launch(op(h), op(w_down), T, K, I, y, y_dtype == NVFP4_BF16, ldy,
+                            reinterpret_cast<hipStream_t>(stream));
+}
+
+int nvfp4_grouped_gemm(nvfp4_tensor a, const int32_t* a_rows, const int32_t* group_offsets, int E, int64_t M,
+                       nvfp4_tensor w0, nvfp4_tensor w1, int64_t N, int64_t K, int epilogue, void* out,
+                       int out_dtype, int64_t ld_out, nvfp4_tensor out_q, void* ws, size_t* ws_bytes,
+                       void* stream) {
+  const bool glu = (epilogue == NVFP4_EPI_SILU_MUL_REQUANT);
+  if (epilogue != NVFP4_EPI_STORE && !glu) return NVFP4_ERR_ARG;
+  if (!glu && !dtype_ok(out_dtype)) return NVFP4_ERR_ARG;
+  if (E < 1 || E > 4096) return NVFP4_ERR_ARG;
+  if (M < 0 || N <= 0 || K <= 0 || N % 128 != 0 || K % 128 != 0) return NVFP4_ERR_SHAPE;
+  if (!glu && ld_out < N) return NVFP4_ERR_SHAPE;
+  if (M * (N / 16) >= ((int64_t)1 << 31)) return NVFP4_ERR_SHAPE;
+  const size_t npart = glu ? nvfp4::grouped_glu_partials_needed(M, N, E) : 0;
+  bool query;
+  int rc = workspace(ws, ws_bytes, (glu && M > 0) ? glu_ws(M, N, npart) : 0, &query);
+  if (rc != NVFP4_OK || query) return rc;
+  if (M == 0) return NVFP4_OK;
+  if (!group_offsets) return NVFP4_ERR_NULL;
+  if ((rc = check_tensor(a)) != NVFP4_OK || (rc = check_tensor(w0)) != NVFP4_OK) return rc;
+  if (glu) {
+    if ((rc = check_tensor(w1)) != NVFP4_OK || (rc = check_tensor(out_q)) != NVFP4_OK) return rc;
+  } else {
+    if (!out) return NVFP4_ERR_NULL;
+    if (!aligned(out, 16) || (ld_out * elem_size(out_dtype)) % 16 != 0) return NVFP4_ERR_ALIGN;
+  }
+  if (!aligned(group_offsets, 4) || (a_rows && !aligned(a_rows, 4))) return NVFP4_ERR_ALIGN;
+  if ((rc = check_device()) != NVFP4_OK) return rc;
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  if (!glu)
+    return nvfp4::grouped_gemm_launch(op(a), a_rows, group_offsets, E, M, op(w0), N, K, out,
+                                      out_dtype == NVFP4_BF16, ld_out, st);
+  float* h = reinterpret_cast<float*>(ws);
+  float* partials = reinterpret_cast<float*>(reinterpret_cast<char*>(ws) +
+                                             round_up((size_t)M * (size_t)N * sizeof(float), 256));
+  uint32_t np = 0;
+  rc = nvfp4::grouped_glu_launch(op(a), a_rows, group_offsets, E, M, op(w0), op(w1), N, K, h, partials, &np, st);
+  if (rc != NVFP4_OK) return rc;
+  return nvfp4::requant_f32_launch(h, M, N, out_q.codes, out_q.scales, out_q.gscale, partials, np, st);
+}
+
+}  // extern "C"

@@ -1,0 +1,167 @@
+// NVFP4 activation quantisation on the device: tensor amax, global scale,
+// E4M3 block scales and packed E2M1 codes.
+//
+// The activation global scale amax/(6*448), clamped at 1e-8, is the runtime
+// scale of the DSV4 audit page (section P0); here it is produced and consumed
+// on the device and never read back to the host.  Packing happens on the
+// device (vllm.cpp issue, "Fix directions" 3).
+//
+// Two kernels: amax_partials writes one partial maximum per work-group;
+// quantize reduces those partials again in every work-group (a few KiB from
+// L2, no atomics, no zero-initialised state), forms the global scale, and
+// quantises one 16-element block per thread.  Both are HBM-bound: the
+// quantiser reads 2 (bf16) or 4 (float32) bytes per element and writes
+// 0.5 + 1/16 bytes.
+#include "device_common.h"
+#include "internal.h"
+
+namespace nvfp4 {
+
+template <typename T>
+struct Load16;
+
+// 16 bf16 values (32 B, 16-B aligned) -> float32
+template <>
+struct Load16<uint16_t> {
+  __device__ __forceinline__ static void run(const uint16_t* p, float v[16]) {
+    const uint4 a = *reinterpret_cast<const uint4*>(p);
+    const uint4 b = *reinterpret_cast<const uint4*>(p + 8);
+    const uint32_t w[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      v[2 * i] = __uint_as_float(w[i] << 16);
+      v[2 * i + 1] = __uint_as_float(w[i] & 0xFFFF0000u);
+    }
+  }
+};
+
+// 16 float32 values (64 B, 16-B aligned)
+template <>
+struct Load16<float> {
+  __device__ __forceinline__ static void run(const float* p, float v[16]) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float4 q = *reinterpret_cast<const float4*>(p + 4 * i);
+      v[4 * i] = q.x; v[4 * i + 1] = q.y; v[4 * i + 2] = q.z; v[4 * i + 3] = q.w;
+    }
+  }
+};
+
+template <typename T>
+__global__ void __launch_bounds__(256) amax_partials_kernel(const T* __restrict__ x, uint32_t nbc,
+                                                            uint32_t nblocks, int64_t ld,
+                                                            float* __restrict__ partials) {
+  __shared__ float red[4];
+  float m = 0.f;
+  for (uint32_t b = blockIdx.x * 256u + threadIdx.x; b < nblocks; b += gridDim.x * 256u) {
+    const uint32_t row = b / nbc, cb = b - row * nbc;
+    float v[16];
+    Load16<T>::run(x + (int64_t)row * ld + (int64_t)cb * kBlock, v);
+#pragma unroll
+    for (int i = 0; i < 16; ++i) m = fmaxf(m, fabsf(v[i]));
+  }
+  m = block_max(m, red);
+  if (threadIdx.x == 0) partials[blockIdx.x] = m;
+}
+
+// mode 0: gs from the partial maxima (written to gs_ptr by work-group 0);
+// mode 1: gs read from gs_ptr.
+template <typename T>
+__global__ void __launch_bounds__(256) quantize_kernel(const T* __restrict__ x, uint32_t nbc,
+                                                       uint32_t nblocks, int64_t ld,
+                                                       const float* __restrict__ partials,
+                                                       uint32_t npart, float* gs_ptr, int mode,
+                                                       uint8_t* __restrict__ codes,
+                                                       uint8_t* __restrict__ scales) {
+  __shared__ float red[4];
+  float gs;
+  if (mode == 0) {
+    float m = 0.f;
+    for (uint32_t i = threadIdx.x; i < npart; i += 256u) m = fmaxf(m, partials[i]);
+    m = block_max(m, red);
+    gs = global_scale_from_amax(m);
+    if (blockIdx.x == 0 && threadIdx.x == 0) *gs_ptr = gs;
+  } else {
+    gs = *gs_ptr;
+  }
+  for (uint32_t b = blockIdx.x * 256u + threadIdx.x; b < nblocks; b += gridDim.x * 256u) {
+    const uint32_t row = b / nbc, cb = b - row * nbc;
+    float v[16];
+    Load16<T>::run(x + (int64_t)row * ld + (int64_t)cb * kBlock, v);
+    float amax_b = 0.f;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) amax_b = fmaxf(amax_b, fabsf(v[i]));
+    const uint32_t s = e4m3_block_scale(amax_b, gs);
+    float thr[7];
+    e2m1_thresholds(e4m3_value(s) * (double)gs, thr);
+    uint32_t w0 = 0, w1 = 0;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      w0 |= e2m1_code(v[i], thr) << (4 * i);
+      w1 |= e2m1_code(v[8 + i], thr) << (4 * i);
+    }
+    const int64_t boff = (int64_t)row * nbc + cb;
+    *reinterpret_cast<uint2*>(codes + boff * 8) = make_uint2(w0, w1);
+    scales[boff] = (uint8_t)s;
+  }
+}
+
+// Work-groups of the quantiser: enough to fill the chip, few enough that the
+// per-work-group re-reduction of the partial maxima stays cheap.
+constexpr uint32_t kQuantGrid = 2048;
+
+static uint32_t amax_grid(uint32_t nblocks) {
+  uint32_t g = (nblocks + 1023u) / 1024u;   // ~4 blocks of 16 per thread
+  if (g < 1) g = 1;
+  if (g > kMaxPartials) g = kMaxPartials;
+  return g;
+}
+
+size_t quantize_ws_bytes(int64_t rows, int64_t cols, int gs_mode) {
+  if (gs_mode != 0) return 0;
+  (void)rows; (void)cols;
+  return kMaxPartials * sizeof(float);
+}
+
+template <typename T>
+static int quantize_launch_t(const T* x, int64_t rows, int64_t cols, int64_t ld, uint8_t* codes,
+                             uint8_t* scales, float* gs, int gs_mode, float* partials,
+                             const float* ext_partials, uint32_t ext_npart, hipStream_t st) {
+  const uint32_t nbc = (uint32_t)(cols / kBlock);
+  const uint32_t nblocks = (uint32_t)rows * nbc;
+  uint32_t qgrid = (nblocks + 255u) / 256u;
+  if (qgrid > kQuantGrid) qgrid = kQuantGrid;
+  if (qgrid < 1) qgrid = 1;
+  if (gs_mode == 0 && ext_partials == nullptr) {
+    const uint32_t g = amax_grid(nblocks);
+    hipLaunchKernelGGL(amax_partials_kernel<T>, dim3(g), dim3(256), 0, st, x, nbc, nblocks, ld, partials);
+    count_launch();
+    hipLaunchKernelGGL(quantize_kernel<T>, dim3(qgrid), dim3(256), 0, st, x, nbc, nblocks, ld,
+                       (const float*)partials, g, gs, 0, codes, scales);
+  } else if (gs_mode == 0) {
+    hipLaunchKernelGGL(quantize_kernel<T>, dim3(qgrid), dim3(256), 0, st, x, nbc, nblocks, ld,
+                       ext_partials, ext_npart, gs, 0, codes, scales);
+  } else {
+    hipLaunchKernelGGL(quantize_kernel<T>, dim3(qgrid), dim3(256), 0, st, x, nbc, nblocks, ld,
+                       (const float*)nullptr, 0u, gs, 1, codes, scales);
+  }
+  count_launch();
+  return hipGetLastError() == hipSuccess ? 0 : 7;
+}
+
+int quantize_launch(const void* x, int x_dtype, int64_t rows, int64_t cols, int64_t ld, uint8_t* codes,
+                    uint8_t* scales, float* gs, int gs_mode, void* ws, hipStream_t st) {
+  float* partials = reinterpret_cast<float*>(ws);
+  if (x_dtype == 1)
+    return quantize_launch_t(reinterpret_cast<const uint16_t*>(x), rows, cols, ld, codes, scales, gs,
+                             gs_mode, partials, nullptr, 0, st);
+  return quantize_launch_t(reinterpret_cast<const float*>(x), rows, cols, ld, codes, scales, gs, gs_mode,
+                           partials, nullptr, 0, st);
+}
+
+int requant_f32_launch(const float* h, int64_t rows, int64_t cols, uint8_t* codes, uint8_t* scales,
+                       float* gs, const float* partials, uint32_t npart, hipStream_t st) {
+  return quantize_launch_t(h, rows, cols, cols, codes, scales, gs, 0, nullptr, partials, npart, st);
+}
+
+}  // namespace nvfp4

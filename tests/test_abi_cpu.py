@@ -1,0 +1,141 @@
+"""The C ABI on a host without a GPU: exports, validation, workspace sizing.
+
+Every call here fails validation (or the device check) before anything is
+enqueued, so no pointer is ever dereferenced.  Tests that rely on the device
+check failing are skipped where a GPU is present.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+import torch
+
+import mlp_prefill_amd as m
+from mlp_prefill_amd import nvfp4_tensor
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "nvfp4.h")
+no_gpu = pytest.mark.skipif(torch.cuda.device_count() > 0, reason="needs a host without a GPU")
+
+FAKE = 0x100000          # aligned, never dereferenced
+
+
+def _t(c=FAKE, s=FAKE, g=FAKE):
+    return nvfp4_tensor(c, s, g)
+
+
+def _size():
+    return ctypes.c_size_t(0)
+
+
+def test_library_exports_every_declared_function():
+    text = open(HEADER).read()
+    names = set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(nvfp4_\w+)\s*\(", text, re.M))
+    assert {"nvfp4_quantize_act", "nvfp4_gemm", "nvfp4_mlp_gu_act", "nvfp4_mlp_down",
+            "nvfp4_grouped_gemm", "nvfp4_strerror", "nvfp4_launch_count"} <= names
+    lib = ctypes.CDLL(m.LIB_PATH)
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_strerror_covers_all_codes():
+    for code in range(8):
+        assert m.lib.nvfp4_strerror(code)
+    assert m.lib.nvfp4_strerror(99) == b"unknown status"
+
+
+def test_quantize_validation():
+    q = m.lib.nvfp4_quantize_act
+    sz = ctypes.c_size_t(1 << 20)
+    assert q(FAKE, 7, 4, 32, 32, _t(), 0, FAKE, ctypes.byref(sz), None) == m.ERR_ARG        # dtype
+    assert q(FAKE, m.BF16, 4, 32, 32, _t(), 9, FAKE, ctypes.byref(sz), None) == m.ERR_ARG   # gs mode
+    assert q(FAKE, m.BF16, 4, 24, 24, _t(), 0, FAKE, ctypes.byref(sz), None) == m.ERR_SHAPE  # cols % 16
+    assert q(FAKE, m.BF16, 4, 32, 16, _t(), 0, FAKE, ctypes.byref(sz), None) == m.ERR_SHAPE  # ld < cols
+    assert q(FAKE, m.BF16, -1, 32, 32, _t(), 0, FAKE, ctypes.byref(sz), None) == m.ERR_SHAPE
+    assert q(None, m.BF16, 4, 32, 32, _t(), 0, FAKE, ctypes.byref(sz), None) == m.ERR_NULL
+    assert q(FAKE, m.BF16, 4, 32, 32, _t(g=0), 0, FAKE, ctypes.byref(sz), None) == m.ERR_NULL
+    assert q(FAKE + 2, m.BF16, 4, 32, 32, _t(), 0, FAKE, ctypes.byref(sz), None) == m.ERR_ALIGN
+    assert q(FAKE, m.BF16, 4, 32, 36, _t(), 0, FAKE, ctypes.byref(sz), None) == m.ERR_ALIGN   # row stride
+    assert q(FAKE, m.BF16, 4, 32, 32, _t(c=FAKE + 8), 0, FAKE, ctypes.byref(sz), None) == m.ERR_ALIGN
+    small = ctypes.c_size_t(16)
+    assert q(FAKE, m.BF16, 4, 32, 32, _t(), 0, FAKE, ctypes.byref(small), None) == m.ERR_WORKSPACE
+    assert q(FAKE, m.BF16, 4, 32, 32, _t(), 0, FAKE, None, None) == m.ERR_WORKSPACE
+    # zero rows: a successful no-op even with NULL data pointers
+    assert q(None, m.BF16, 0, 32, 32, nvfp4_tensor(0, 0, 0), 0, FAKE, ctypes.byref(sz), None) == m.OK
+
+
+def test_quantize_workspace_query():
+    q = m.lib.nvfp4_quantize_act
+    s = _size()
+    assert q(None, m.BF16, 1024, 5120, 5120, nvfp4_tensor(0, 0, 0), m.GS_COMPUTE, None, ctypes.byref(s), None) == m.OK
+    assert 0 < s.value <= 16384
+    s = _size()
+    assert q(None, m.BF16, 1024, 5120, 5120, nvfp4_tensor(0, 0, 0), m.GS_GIVEN, None, ctypes.byref(s), None) == m.OK
+    assert s.value == 0
+
+
+def test_gemm_and_down_validation():
+    g = m.lib.nvfp4_gemm
+    assert g(_t(), _t(), 4, 8, 100, FAKE, m.F32, 8, None, None, None) == m.ERR_SHAPE        # K % 128
+    assert g(_t(), _t(), 4, 8, 128, FAKE, 5, 8, None, None, None) == m.ERR_ARG
+    assert g(_t(), _t(), 4, 8, 128, FAKE, m.F32, 4, None, None, None) == m.ERR_SHAPE        # ldc < N
+    assert g(_t(), _t(), 4, 8, 128, None, m.F32, 8, None, None, None) == m.ERR_NULL
+    assert g(_t(), _t(), 4, 6, 128, FAKE, m.F32, 6, None, None, None) == m.ERR_ALIGN        # row stride 24 B
+    assert g(_t(), _t(s=FAKE + 4), 4, 8, 128, FAKE, m.F32, 8, None, None, None) == m.ERR_ALIGN
+    assert g(_t(), _t(), 0, 8, 128, None, m.F32, 8, None, None, None) == m.OK               # empty
+    d = m.lib.nvfp4_mlp_down
+    assert d(_t(), _t(), 4, 100, 64, FAKE, m.F32, 64, None, None, None) == m.ERR_SHAPE      # I % 128
+    assert d(_t(), _t(), 4, 128, 64, FAKE, m.BF16, 60, None, None, None) == m.ERR_SHAPE     # ldy < K
+
+
+def test_gu_act_validation_and_workspace():
+    f = m.lib.nvfp4_mlp_gu_act
+    z = nvfp4_tensor(0, 0, 0)
+    s = _size()
+    assert f(z, z, z, 1024, 5120, 17408, z, None, ctypes.byref(s), None) == m.OK
+    assert s.value >= 1024 * 17408 * 4
+    assert f(z, z, z, 4, 5120, 17400, z, None, ctypes.byref(s), None) == m.ERR_SHAPE
+    small = ctypes.c_size_t(1024)
+    assert f(_t(), _t(), _t(), 4, 128, 128, _t(), FAKE, ctypes.byref(small), None) == m.ERR_WORKSPACE
+    big = ctypes.c_size_t(1 << 24)
+    assert f(_t(), _t(), _t(), 4, 128, 128, _t(), FAKE + 64, ctypes.byref(big), None) == m.ERR_ALIGN
+    assert f(_t(), _t(c=0), _t(), 4, 128, 128, _t(), FAKE, ctypes.byref(big), None) == m.ERR_NULL
+    assert f(z, z, z, 0, 128, 128, z, FAKE, ctypes.byref(big), None) == m.OK
+
+
+def test_grouped_validation():
+    f = m.lib.nvfp4_grouped_gemm
+    sz = ctypes.c_size_t(1 << 30)
+    args = lambda **kw: dict(dict(a=_t(), rows=FAKE, off=FAKE, E=4, M=64, w0=_t(), w1=_t(), N=128, K=128,
+                                  epi=m.EPI_STORE, out=FAKE, dt=m.F32, ld=128, oq=_t()), **kw)
+
+    def call(**kw):
+        a = args(**kw)
+        return f(a["a"], a["rows"], a["off"], a["E"], a["M"], a["w0"], a["w1"], a["N"], a["K"], a["epi"],
+                 a["out"], a["dt"], a["ld"], a["oq"], FAKE, ctypes.byref(sz), None)
+    assert call(E=0) == m.ERR_ARG
+    assert call(epi=5) == m.ERR_ARG
+    assert call(N=100) == m.ERR_SHAPE
+    assert call(off=None) == m.ERR_NULL
+    assert call(out=None) == m.ERR_NULL
+    assert call(epi=m.EPI_SILU_MUL_REQUANT, w1=nvfp4_tensor(0, 0, 0)) == m.ERR_NULL
+    assert call(rows=FAKE + 2) == m.ERR_ALIGN
+    assert call(M=0) == m.OK
+    s = _size()
+    z = nvfp4_tensor(0, 0, 0)
+    assert f(z, None, None, 64, 32768, z, z, 2048, 4096, m.EPI_SILU_MUL_REQUANT, None, m.F32, 2048, z, None,
+             ctypes.byref(s), None) == m.OK
+    assert s.value >= 32768 * 2048 * 4
+
+
+@no_gpu
+def test_valid_calls_report_missing_device_and_launch_nothing():
+    before = m.lib.nvfp4_launch_count()
+    sz = ctypes.c_size_t(1 << 20)
+    assert m.lib.nvfp4_quantize_act(FAKE, m.BF16, 4, 32, 32, _t(), 0, FAKE, ctypes.byref(sz), None) == m.ERR_DEVICE
+    assert m.lib.nvfp4_gemm(_t(), _t(), 4, 8, 128, FAKE, m.F32, 8, None, None, None) == m.ERR_DEVICE
+    big = ctypes.c_size_t(1 << 24)
+    assert m.lib.nvfp4_mlp_gu_act(_t(), _t(), _t(), 4, 128, 128, _t(), FAKE, ctypes.byref(big), None) == m.ERR_DEVICE
+    assert m.lib.nvfp4_mlp_down(_t(), _t(), 4, 128, 64, FAKE, m.F32, 64, None, None, None) == m.ERR_DEVICE
+    assert m.lib.nvfp4_launch_count() == before

@@ -1,0 +1,131 @@
+"""Device MLP (quantise -> gate/up + SiLU*up + requant -> down) vs the oracle.
+
+Stages compared (all against the oracle's own end-to-end run):
+  S1  x~ bit-exact;
+  S2  the float32 GLU output H the device quantised vs the oracle's H;
+  S3  H~: every code or scale that differs from the oracle's must be a
+      rounding decision the oracle takes within 2^-14 (relative) of a
+      boundary -- the device's float32 accumulation moves H by ~1e-6, so
+      such decisions can legitimately go either way;
+  S4  Y vs the oracle's Y after accounting for those boundary flips
+      (the oracle's down projection of the difference of the two H~), gate
+      2e-3 max-normalised; the raw end-to-end error is reported.
+"""
+import numpy as np
+import pytest
+import torch
+
+from oracle import gemm as ogemm
+from oracle import mlp as omlp
+from oracle import quant
+from synthetic import WORKLOADS, bf16_bits_to_f32, bf16_normal, outlier_channels
+from tests.gpu_util import (TOL, announce, assert_nvfp4_equal, dev_bf16, dev_quantize, legit_requant_flips,
+                            max_norm_err, require_gpu, to_host)
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(autouse=True, scope="module")
+def _gpu():
+    require_gpu()
+
+
+def _weights(k, i, seeds, sigma=0.02):
+    gb = bf16_normal(seeds[0], (i, k), sigma=sigma)
+    ub = bf16_normal(seeds[1], (i, k), sigma=sigma)
+    db = bf16_normal(seeds[2], (k, i), sigma=sigma)
+    dev = [dev_quantize(b) for b in (gb, ub, db)]
+    ref = [quant.quantize(bf16_bits_to_f32(b)) for b in (gb, ub, db)]
+    return dev, ref
+
+
+def run_device_mlp(xbits, wdev, y_dtype=torch.float32):
+    """quantize_act -> mlp_gu_act -> mlp_down on the device; returns (x~, H, H~, Y)."""
+    import mlp_prefill_amd as m
+    t, k = xbits.shape
+    i = wdev[0].rows
+    x = dev_bf16(xbits)
+    xq = m.NVFP4.empty(t, k)
+    m.nvfp4_quantize_act(x, xq)
+    hq = m.NVFP4.empty(t, i)
+    ws = m.nvfp4_mlp_gu_act(xq, wdev[0], wdev[1], hq)
+    y = torch.empty((t, k), dtype=y_dtype, device="cuda")
+    m.nvfp4_mlp_down(hq, wdev[2], y)
+    torch.cuda.synchronize()
+    h = ws[: t * i * 4].view(torch.float32).view(t, i).cpu().numpy()
+    return xq, h, hq, y
+
+
+def check_mlp(xbits, wdev, wref, label):
+    t, k = xbits.shape
+    x = bf16_bits_to_f32(xbits)
+    xq, h, hq, y = run_device_mlp(xbits, wdev)
+    ref = omlp.mlp(x, *wref)
+    assert_nvfp4_equal(to_host(xq), ref["xq"], f"{label} x~")                       # S1
+    eh = max_norm_err(h, ref["h"])                                                  # S2
+    hq_dev = to_host(hq)
+    nflip, nsflip = legit_requant_flips(ref["h"].astype(np.float32), hq_dev, ref["hq"])  # S3
+    y = y.cpu().numpy()
+    e2e = max_norm_err(y, ref["y"])
+    corr = ref["y"] + ogemm.gemm(hq_dev, wref[2]) - ogemm.gemm(ref["hq"], wref[2])
+    ecorr = max_norm_err(y, corr)                                                   # S4
+    print(f"{label}: H err {eh:.2e}  requant flips {nflip} codes / {nsflip} scales  "
+          f"Y err e2e {e2e:.2e}  flip-corrected {ecorr:.2e}  gs_h dev {hq_dev.gs!r} ref {ref['hq'].gs!r}")
+    assert eh <= 1e-4
+    # gs_h = amax(H)/2688 moves with the device's H (float32 accumulation)
+    assert abs(float(hq_dev.gs) / float(ref["hq"].gs) - 1.0) <= 2.0 ** -16
+    assert ecorr <= TOL
+    return e2e
+
+
+SMALL = [(1, 256, 384), (37, 256, 384), (64, 512, 256), (129, 384, 640)]
+
+
+@pytest.mark.parametrize("t,k,i", SMALL, ids=[f"T{t}_K{k}_I{i}" for t, k, i in SMALL])
+def test_mlp_small_shapes(t, k, i):
+    announce(f"mlp T={t} K={k} I={i}")
+    wdev, wref = _weights(k, i, (100 + t, 200 + t, 300 + t))
+    check_mlp(bf16_normal(400 + t, (t, k)), wdev, wref, f"T{t}")
+
+
+@pytest.fixture(scope="module")
+def decode_weights():
+    p = WORKLOADS["mlp_decode_5120x17408"].params
+    return _weights(p["K"], p["I"], (p["wg_seed"], p["wu_seed"], p["wd_seed"]))
+
+
+def test_mlp_decode_T1_T5(decode_weights):
+    import mlp_prefill_amd as m
+    p = WORKLOADS["mlp_decode_5120x17408"].params
+    wdev, wref = decode_weights
+    launches = {}
+    for t in p["Ts"]:
+        announce(f"decode mlp T={t}")
+        xbits = bf16_normal(p["x_seed"], (t, p["K"]))
+        before = m.launch_count()
+        run_device_mlp(xbits, wdev)
+        launches[t] = m.launch_count() - before
+        check_mlp(xbits, wdev, wref, f"decode T{t}")
+    # one launch set per batch: the number of launches does not depend on T
+    assert len(set(launches.values())) == 1, launches
+
+
+def test_mlp_prefill_1024_outliers():
+    p = WORKLOADS["mlp_prefill_1024x5120x17408"].params
+    announce("prefill mlp T=1024 (full size)")
+    wdev, wref = _weights(p["K"], p["I"], (p["wg_seed"], p["wu_seed"], p["wd_seed"]))
+    xbits = bf16_normal(p["x_seed"], (p["T"], p["K"]), outliers=outlier_channels(p["outlier_seed"], p["K"]))
+    check_mlp(xbits, wdev, wref, "prefill T1024")
+
+
+def test_launch_count_independent_of_T():
+    import mlp_prefill_amd as m
+    wdev, _ = _weights(256, 384, (1, 2, 3))
+    counts = []
+    for t in (1, 5, 64, 1024):
+        announce(f"launch count T={t}")
+        before = m.launch_count()
+        run_device_mlp(bf16_normal(9, (t, 256)), wdev)
+        counts.append(m.launch_count() - before)
+    assert len(set(counts)) == 1, counts
+    assert counts[0] <= 5
