@@ -1,0 +1,262 @@
+"""Benchmark of the batched NVFP4 W4A4 MLP on one MI355X.
+
+Default workload: a 16384-token prefill processed as 16 ubatches of 1024
+tokens through 4 stacked MLP layers (hidden 5120, intermediate 17408), bf16
+activations kept on the device between layers.  One step = the whole pass
+(64 MLP calls: quantise x, gate/up + SiLU*up + requantise, down -> bf16).
+Inputs are seeded synthetic draws (N(0,1) activations, N(0,0.02) weights),
+resident in HBM before the timed region; weights are quantised on the device
+beforehand (cold path).
+
+Prints one JSON line.  Extra fields: the 1024-token MLP, the decode-shaped
+T=1 / T=5 MLP (weight-streaming GB/s, cold and hot MALL), the roofline of the
+dominant kernel and the CPU oracle timed on a bounded sample.
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+import torch
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "NVFP4 MLP effective TFLOPS & tokens/s at T=1024/16384; % MFMA peak; T=1 HBM GB/s"
+PEAK_F16_TFLOPS = 2500.0          # MI355X dense f16 MFMA
+PEAK_HBM_GBS = 8000.0             # MI355X HBM3E
+K_HID, I_INT = 5120, 17408
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def mlp_flops(t, k=K_HID, i=I_INT):
+    return 6.0 * t * k * i
+
+
+class Layer:
+    """Quantised weights of one MLP layer on the device."""
+
+    def __init__(self, m, seeds, k=K_HID, i=I_INT):
+        from synthetic import bf16_normal
+        self.w = []
+        for seed, shp in zip(seeds, [(i, k), (i, k), (k, i)]):
+            bits = bf16_normal(seed, shp, sigma=0.02)
+            x = m.bf16_from_bits(bits)
+            q = m.NVFP4.empty(*shp)
+            m.nvfp4_quantize_act(x, q)
+            del x
+            self.w.append(q)
+
+
+class MlpRunner:
+    """Preallocated buffers for one MLP call shape (T tokens)."""
+
+    def __init__(self, m, t, k=K_HID, i=I_INT):
+        self.m, self.t, self.k, self.i = m, t, k, i
+        self.xq = m.NVFP4.empty(t, k)
+        self.hq = m.NVFP4.empty(t, i)
+        self.ws_q = torch.empty(m.ws_bytes_quantize(t, k), dtype=torch.uint8, device="cuda")
+        self.ws_gu = torch.empty(max(m.mlp_gu_act_ws_bytes(t, k, i), 256), dtype=torch.uint8, device="cuda")
+
+    def __call__(self, x, layer, y):
+        m = self.m
+        m.nvfp4_quantize_act(x, self.xq, ws=self.ws_q)
+        m.nvfp4_mlp_gu_act(self.xq, layer.w[0], layer.w[1], self.hq, ws=self.ws_gu)
+        m.nvfp4_mlp_down(self.hq, layer.w[2], y)
+
+
+def time_events(fn, reps, warm=2, scrub=None):
+    """Per-repetition device durations (ms) with HIP events on the current stream."""
+    for _ in range(warm):
+        fn()
+    out = []
+    for _ in range(reps):
+        if scrub is not None:
+            scrub()
+        s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        s.record()
+        fn()
+        e.record()
+        e.synchronize()
+        out.append(s.elapsed_time(e))
+    return out
+
+
+def cpu_baseline(n_ubatch):
+    """The oracle on the first `n_ubatch` 1024-token ubatches of the stacked workload through layer 0."""
+    from threadpoolctl import threadpool_info
+
+    from oracle import mlp as omlp
+    from oracle import quant
+    from synthetic import WORKLOADS, bf16_bits_to_f32, bf16_normal, layer_seeds
+    p = WORKLOADS["mlp_long_prefill_16x1024_4layers"].params
+    ub = p["ubatch"]
+    x = bf16_bits_to_f32(bf16_normal(p["x_seed"], (p["T"], p["K"])))[:n_ubatch * ub]
+    log("cpu baseline: quantising layer-0 weights with the oracle (cold, untimed)")
+    w = [quant.quantize(bf16_bits_to_f32(bf16_normal(s, shp, sigma=p["w_sigma"])))
+         for s, shp in zip(layer_seeds(p["layer_seed0"], 0), [(p["I"], p["K"]), (p["I"], p["K"]), (p["K"], p["I"])])]
+    log(f"cpu baseline: oracle MLP on {n_ubatch} ubatches of {ub} tokens (timed)")
+    t0 = time.perf_counter()
+    for u in range(n_ubatch):
+        omlp.mlp(x[u * ub:(u + 1) * ub], *w)
+    dt = time.perf_counter() - t0
+    t_sample = n_ubatch * ub
+    threads = max([d.get("num_threads", 1) for d in threadpool_info()] or [1])
+    return {"value": mlp_flops(t_sample) / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"the first {n_ubatch} ubatches ({t_sample} tokens) of the long-prefill input through "
+                      f"layer 0 (quantise x, gate/up, SiLU*up, requantise, down; float64 numpy); {dt:.2f} s, "
+                      f"{t_sample / dt:.1f} tokens/s; weight quantisation excluded",
+            "seconds": dt}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=5)
+    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-extra", action="store_true", help="skip the 1024-token and decode lines")
+    ap.add_argument("--cpu-ubatches", type=int, default=4, help="ubatches the CPU oracle runs (about 10 s)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported (the path is built and measured "
+              f"on a single MI355X)", file=sys.stderr)
+        return 2
+
+    import mlp_prefill_amd as m
+    from synthetic import WORKLOADS, bf16_normal, layer_seeds
+    torch.cuda.set_device(0)
+    p = WORKLOADS["mlp_long_prefill_16x1024_4layers"].params
+    T, UB, L = p["T"], p["ubatch"], p["layers"]
+
+    log("generating inputs and quantising weights on the device")
+    x_all = m.bf16_from_bits(bf16_normal(p["x_seed"], (T, K_HID)))
+    layers = [Layer(m, layer_seeds(p["layer_seed0"], li)) for li in range(L)]
+    run = MlpRunner(m, UB)
+    y_buf = [torch.empty((UB, K_HID), dtype=torch.bfloat16, device="cuda") for _ in range(2)]
+    out = torch.empty((T, K_HID), dtype=torch.bfloat16, device="cuda")
+    torch.cuda.synchronize()
+
+    def step():
+        for u in range(T // UB):
+            cur = x_all[u * UB:(u + 1) * UB]
+            for li, layer in enumerate(layers):
+                dst = out[u * UB:(u + 1) * UB] if li == L - 1 else y_buf[li % 2]
+                run(cur, layer, dst)
+                cur = dst
+
+    log(f"warmup {args.warmup} steps")
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    log(f"timing {args.steps} steps")
+    s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    s.record()
+    for _ in range(args.steps):
+        step()
+    e.record()
+    torch.cuda.synchronize()
+    ms = s.elapsed_time(e) / args.steps
+    flops = mlp_flops(T) * L
+    tflops = flops / (ms * 1e-3) / 1e12
+    tokens_s = T / (ms * 1e-3)
+    log(f"{ms:.3f} ms/step, {tflops:.1f} TFLOP/s, {tokens_s:.0f} tokens/s")
+
+    # ---- dominant kernel: the gate/up GEMM with the SiLU*up epilogue ------------------
+    # nvfp4_mlp_gu_act = [gate/up GEMM + GLU] then [requantise H].  The requantise
+    # kernel's work is timed alone as a given-scale quantisation of the same
+    # float32 H; the GEMM kernel's duration is the difference.
+    x0 = x_all[:UB]
+    m.nvfp4_quantize_act(x0, run.xq, ws=run.ws_q)
+    h32 = run.ws_gu[: UB * I_INT * 4].view(torch.float32).view(UB, I_INT)
+    hq_tmp = m.NVFP4.empty(UB, I_INT)
+    hq_tmp.gscale.fill_(1.0)
+    t_gu = time_events(lambda: m.nvfp4_mlp_gu_act(run.xq, layers[0].w[0], layers[0].w[1], run.hq, ws=run.ws_gu), 20)
+    t_rq = time_events(lambda: m.nvfp4_quantize_act(h32, hq_tmp, gs_mode=m.GS_GIVEN), 20)
+    gemm_ms = float(np.mean(t_gu) - np.mean(t_rq))
+    gemm_flops = 4.0 * UB * K_HID * I_INT
+    achieved = gemm_flops / (gemm_ms * 1e-3) / 1e12
+    roofline = {"bound": "mfma", "achieved": achieved, "peak": PEAK_F16_TFLOPS, "unit": "TFLOP/s",
+                "frac": achieved / PEAK_F16_TFLOPS, "traffic": None,
+                "kernel": "gemm_kernel<2,2,2,2,dual,dense,glu> (gate/up + SiLU*up, T=1024 ubatch)",
+                "flops_per_launch": gemm_flops, "avg_launch_ms": gemm_ms,
+                "gu_act_call_ms": float(np.mean(t_gu)), "requant_ms": float(np.mean(t_rq)),
+                "peak_fp4_tflops_for_reference": 10100.0,
+                "frac_of_fp4_peak": achieved / 10100.0}
+    log(f"dominant kernel {gemm_ms:.3f} ms -> {achieved:.1f} TFLOP/s ({100 * achieved / PEAK_F16_TFLOPS:.1f}% of f16 peak)")
+
+    extra = {}
+    if not args.no_extra:
+        extra = extra_lines(m)
+
+    result = {
+        "metric": METRIC, "value": tflops, "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "f16", "data": "synthetic",
+        "config": {"workload": "mlp_long_prefill_16x1024_4layers", "tokens": T, "ubatch": UB, "layers": L,
+                   "hidden": K_HID, "intermediate": I_INT, "storage": "nvfp4 (e2m1 codes, e4m3 block-16 scales, "
+                   "fp32 global scale)", "accumulate": "fp32"},
+        "tokens_per_s": tokens_s, "flops_per_step": flops,
+        "roofline": roofline,
+    }
+    result.update(extra)
+    if not args.no_cpu_baseline:
+        cb = cpu_baseline(args.cpu_ubatches)
+        result["cpu_baseline"] = cb
+        log(f"cpu baseline {cb['value'] * 1e3:.2f} GFLOP/s on {cb['cores']} threads")
+    print(json.dumps(result), flush=True)
+    return 0
+
+
+def extra_lines(m):
+    """1024-token MLP and decode-shaped T=1/T=5 MLP (separate weights, as their workloads define)."""
+    from synthetic import WORKLOADS, bf16_normal, outlier_channels
+    out = {}
+    p3 = WORKLOADS["mlp_prefill_1024x5120x17408"].params
+    log("extra: 1024-token MLP")
+    lay = Layer(m, (p3["wg_seed"], p3["wu_seed"], p3["wd_seed"]))
+    x = m.bf16_from_bits(bf16_normal(p3["x_seed"], (p3["T"], K_HID),
+                                     outliers=outlier_channels(p3["outlier_seed"], K_HID)))
+    run = MlpRunner(m, p3["T"])
+    y = torch.empty((p3["T"], K_HID), dtype=torch.float32, device="cuda")
+    t = time_events(lambda: run(x, lay, y), 20)
+    ms = float(np.median(t))
+    out["prefill_1024"] = {"workload": "mlp_prefill_1024x5120x17408", "ms": ms,
+                           "tflops": mlp_flops(p3["T"]) / (ms * 1e-3) / 1e12,
+                           "tokens_per_s": p3["T"] / (ms * 1e-3),
+                           "frac_f16_peak": mlp_flops(p3["T"]) / (ms * 1e-3) / 1e12 / PEAK_F16_TFLOPS}
+    del lay, run, x, y
+    p2 = WORKLOADS["mlp_decode_5120x17408"].params
+    log("extra: decode-shaped MLP T=1, T=5")
+    lay = Layer(m, (p2["wg_seed"], p2["wu_seed"], p2["wd_seed"]))
+    wbytes = sum(w.codes.numel() + w.scales.numel() + 4 for w in lay.w)
+    scrub_buf = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+    dec = {"workload": "mlp_decode_5120x17408", "weight_bytes": wbytes}
+    launches = {}
+    for tt in p2["Ts"]:
+        x = m.bf16_from_bits(bf16_normal(p2["x_seed"], (tt, K_HID)))
+        run = MlpRunner(m, tt)
+        y = torch.empty((tt, K_HID), dtype=torch.float32, device="cuda")
+        before = m.launch_count()
+        run(x, lay, y)
+        launches[tt] = m.launch_count() - before
+        hot = float(np.median(time_events(lambda: run(x, lay, y), 50)))
+        cold = float(np.median(time_events(lambda: run(x, lay, y), 20, scrub=lambda: scrub_buf.fill_(tt))))
+        dec[f"T{tt}"] = {"ms_hot": hot, "ms_cold": cold, "hbm_gbs_cold": wbytes / (cold * 1e-3) / 1e9,
+                         "hbm_gbs_hot": wbytes / (hot * 1e-3) / 1e9,
+                         "frac_hbm_peak_cold": wbytes / (cold * 1e-3) / 1e9 / PEAK_HBM_GBS}
+    dec["launches_per_call"] = launches
+    dec["t5_over_t1_cold"] = dec["T5"]["ms_cold"] / dec["T1"]["ms_cold"]
+    out["decode"] = dec
+    return out
+
+
+if __name__ == "__main__":
+    sys.exit(main())

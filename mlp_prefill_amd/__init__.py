@@ -161,6 +161,14 @@ def nvfp4_gemm(a, b, c, stream=None):
     return c
 
 
+def ws_bytes_quantize(rows, cols, gs_mode=GS_COMPUTE):
+    """Workspace bytes nvfp4_quantize_act needs (at least 256 so a buffer can always be allocated)."""
+    size = ctypes.c_size_t(0)
+    _check(_lib.nvfp4_quantize_act(_vp(0), BF16, rows, cols, cols, _null_tensor(), gs_mode, _vp(0),
+                                   ctypes.byref(size), _vp(0)), "workspace query")
+    return max(size.value, 256)
+
+
 def mlp_gu_act_ws_bytes(t, k, i):
     size = ctypes.c_size_t(0)
     _check(_lib.nvfp4_mlp_gu_act(_null_tensor(), _null_tensor(), _null_tensor(), t, k, i, _null_tensor(),
