@@ -63,12 +63,13 @@ class MlpRunner:
         self.hq = m.NVFP4.empty(t, i)
         self.ws_q = torch.empty(m.ws_bytes_quantize(t, k), dtype=torch.uint8, device="cuda")
         self.ws_gu = torch.empty(max(m.mlp_gu_act_ws_bytes(t, k, i), 256), dtype=torch.uint8, device="cuda")
+        self.ws_dn = torch.empty(max(m.mlp_down_ws_bytes(t, i, k), 256), dtype=torch.uint8, device="cuda")
 
     def __call__(self, x, layer, y):
         m = self.m
         m.nvfp4_quantize_act(x, self.xq, ws=self.ws_q)
         m.nvfp4_mlp_gu_act(self.xq, layer.w[0], layer.w[1], self.hq, ws=self.ws_gu)
-        m.nvfp4_mlp_down(self.hq, layer.w[2], y)
+        m.nvfp4_mlp_down(self.hq, layer.w[2], y, ws=self.ws_dn)
 
 
 def time_events(fn, reps, warm=2, scrub=None):

@@ -153,11 +153,23 @@ def nvfp4_quantize_act(x, out, gs_mode=GS_COMPUTE, ws=None, stream=None):
     return out
 
 
-def nvfp4_gemm(a, b, c, stream=None):
+def gemm_ws_bytes(m, n, k):
+    """Workspace bytes nvfp4_gemm needs for C [m, n] with K = k."""
+    size = ctypes.c_size_t(0)
+    _check(_lib.nvfp4_gemm(_null_tensor(), _null_tensor(), m, n, k, _vp(0), F32, max(n, 1), _vp(0),
+                           ctypes.byref(size), _vp(0)), "workspace query")
+    return size.value
+
+
+def nvfp4_gemm(a, b, c, ws=None, stream=None):
     """c [M, N] (float32 or bf16) = A~ . B~^T * gs_a * gs_b."""
     m, n = c.shape
-    _check(_lib.nvfp4_gemm(a.c(), b.c(), m, n, a.cols, _ptr(c), _dtype_code(c), c.stride(0), _vp(0),
-                           None, _stream(stream)), "nvfp4_gemm")
+    need = gemm_ws_bytes(m, n, a.cols)
+    if ws is None:
+        ws = torch.empty(max(need, 256), dtype=torch.uint8, device=c.device)
+    sz = ctypes.c_size_t(ws.numel())
+    _check(_lib.nvfp4_gemm(a.c(), b.c(), m, n, a.cols, _ptr(c), _dtype_code(c), c.stride(0), _ptr(ws),
+                           ctypes.byref(sz), _stream(stream)), "nvfp4_gemm")
     return c
 
 
@@ -188,11 +200,23 @@ def nvfp4_mlp_gu_act(x, w_gate, w_up, h_out, ws=None, stream=None):
     return ws
 
 
-def nvfp4_mlp_down(h, w_down, y, stream=None):
+def mlp_down_ws_bytes(t, i, k):
+    """Workspace bytes nvfp4_mlp_down needs for T tokens, intermediate i, hidden k."""
+    size = ctypes.c_size_t(0)
+    _check(_lib.nvfp4_mlp_down(_null_tensor(), _null_tensor(), t, i, k, _vp(0), F32, k, _vp(0),
+                               ctypes.byref(size), _vp(0)), "workspace query")
+    return size.value
+
+
+def nvfp4_mlp_down(h, w_down, y, ws=None, stream=None):
     """y [T, K] (float32 or bf16) = H~ . Wd~^T * gs_h * gs_wd."""
     t, kk = y.shape
-    _check(_lib.nvfp4_mlp_down(h.c(), w_down.c(), t, h.cols, kk, _ptr(y), _dtype_code(y), y.stride(0), _vp(0),
-                               None, _stream(stream)), "nvfp4_mlp_down")
+    need = mlp_down_ws_bytes(t, h.cols, kk)
+    if ws is None:
+        ws = torch.empty(max(need, 256), dtype=torch.uint8, device=y.device)
+    sz = ctypes.c_size_t(ws.numel())
+    _check(_lib.nvfp4_mlp_down(h.c(), w_down.c(), t, h.cols, kk, _ptr(y), _dtype_code(y), y.stride(0), _ptr(ws),
+                               ctypes.byref(sz), _stream(stream)), "nvfp4_mlp_down")
     return y
 
 

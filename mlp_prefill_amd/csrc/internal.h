@@ -30,24 +30,20 @@ struct Operand {
   const float* gscale;
 };
 
-// C[M][N] = A . B^T * gs_a * gs_b, float32 (c_bf16 = 0) or bf16 output.
-int gemm_launch(Operand a, Operand b, int64_t M, int64_t N, int64_t K, void* c, int c_bf16, int64_t ldc,
-                hipStream_t st);
+// Store-epilogue contraction C[M][N] = A . W^T * gs_a * gs_w (float32 or bf16),
+// dense (off == nullptr) or expert-grouped (slot s reads activation row
+// rows[s] or s; slots [off[e], off[e+1]) use expert e's weights, stride N*K).
+// Workspace: f16-expanded activations, then split-K partial sums.
+size_t store_ws_bytes(int64_t M, int64_t N, int64_t K, int E, bool grouped);
+int store_launch(Operand a, const int32_t* rows, const int32_t* off, int E, int64_t M, Operand w, int64_t N,
+                 int64_t K, void* c, int c_bf16, int64_t ldc, void* ws, hipStream_t st);
 
-// H[M][N] = SiLU(A . G^T * gs_a*gs_g) * (A . U^T * gs_a*gs_u) into h (float32,
-// row-major, ld N) with one partial |H| max per work-group in `partials`;
-// returns the number of partials through *npart.
-size_t glu_partials_needed(int64_t M, int64_t N);
-int gemm_glu_launch(Operand a, Operand g, Operand u, int64_t M, int64_t N, int64_t K, float* h,
-                    float* partials, uint32_t* npart, hipStream_t st);
-
-// Grouped (expert) variants; slot s reads row a_rows[s] (or s), slots
-// [off[e], off[e+1]) use expert e's weights (stride N*K per expert).
-size_t grouped_glu_partials_needed(int64_t M, int64_t N, int E);
-int grouped_gemm_launch(Operand a, const int32_t* a_rows, const int32_t* off, int E, int64_t M, Operand w,
-                        int64_t N, int64_t K, void* c, int c_bf16, int64_t ldc, hipStream_t st);
-int grouped_glu_launch(Operand a, const int32_t* a_rows, const int32_t* off, int E, int64_t M, Operand g,
-                       Operand u, int64_t N, int64_t K, float* h, float* partials, uint32_t* npart,
-                       hipStream_t st);
+// H = SiLU(A . G^T * gs_a*gs_g) * (A . U^T * gs_a*gs_u) (float32, row-major
+// [M][N], at the start of the workspace), then its NVFP4 requantisation with a
+// global scale over all M rows.  Dense or grouped as above.
+size_t glu_ws_bytes(int64_t M, int64_t N, int64_t K, int E, bool grouped);
+int glu_launch(Operand a, const int32_t* a_rows, const int32_t* off, int E, int64_t M, Operand gt, Operand up,
+               int64_t N, int64_t K, uint8_t* hq_codes, uint8_t* hq_scales, float* hq_gs, void* ws,
+               hipStream_t st);
 
 }  // namespace nvfp4

@@ -53,8 +53,6 @@ int check_tensor(const nvfp4_tensor& t) {
 
 Operand op(const nvfp4_tensor& t) { return Operand{t.codes, t.scales, t.gscale}; }
 
-size_t round_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
-
 // Workspace bookkeeping: returns NVFP4_OK and sets *is_query when the call is
 // a size query; NVFP4_ERR_WORKSPACE when the given workspace is too small.
 int workspace(void* ws, size_t* ws_bytes, size_t need, bool* is_query) {
@@ -72,11 +70,6 @@ int workspace(void* ws, size_t* ws_bytes, size_t need, bool* is_query) {
 
 int elem_size(int dtype) { return dtype == NVFP4_BF16 ? 2 : 4; }
 bool dtype_ok(int dtype) { return dtype == NVFP4_F32 || dtype == NVFP4_BF16; }
-
-// Float32 GLU output [rows][cols] followed by the partial maxima.
-size_t glu_ws(int64_t rows, int64_t cols, size_t npart) {
-  return round_up((size_t)rows * (size_t)cols * sizeof(float), 256) + round_up(npart * sizeof(float), 256);
-}
 
 }  // namespace
 
@@ -119,55 +112,50 @@ int nvfp4_gemm(nvfp4_tensor a, nvfp4_tensor b, int64_t M, int64_t N, int64_t K, 
                int64_t ldc, void* ws, size_t* ws_bytes, void* stream) {
   if (!dtype_ok(c_dtype)) return NVFP4_ERR_ARG;
   if (M < 0 || N < 0 || K <= 0 || K % 128 != 0 || ldc < N) return NVFP4_ERR_SHAPE;
+  if (M * (K / 16) >= ((int64_t)1 << 31)) return NVFP4_ERR_SHAPE;
   bool query;
-  int rc = workspace(ws, ws_bytes, 0, &query);
+  int rc = workspace(ws, ws_bytes, (M > 0 && N > 0) ? nvfp4::store_ws_bytes(M, N, K, 1, false) : 0, &query);
   if (rc != NVFP4_OK || query) return rc;
   if (M == 0 || N == 0) return NVFP4_OK;
   if ((rc = check_tensor(a)) != NVFP4_OK || (rc = check_tensor(b)) != NVFP4_OK) return rc;
   if (!c) return NVFP4_ERR_NULL;
   if (!aligned(c, 16) || (ldc * elem_size(c_dtype)) % 16 != 0) return NVFP4_ERR_ALIGN;
   if ((rc = check_device()) != NVFP4_OK) return rc;
-  return nvfp4::gemm_launch(op(a), op(b), M, N, K, c, c_dtype == NVFP4_BF16, ldc,
-                            reinterpret_cast<hipStream_t>(stream));
+  return nvfp4::store_launch(op(a), nullptr, nullptr, 1, M, op(b), N, K, c, c_dtype == NVFP4_BF16, ldc, ws,
+                             reinterpret_cast<hipStream_t>(stream));
 }
 
 int nvfp4_mlp_gu_act(nvfp4_tensor x, nvfp4_tensor w_gate, nvfp4_tensor w_up, int64_t T, int64_t K, int64_t I,
                      nvfp4_tensor h_out, void* ws, size_t* ws_bytes, void* stream) {
   if (T < 0 || K <= 0 || I <= 0 || K % 128 != 0 || I % 128 != 0) return NVFP4_ERR_SHAPE;
   if (T * (I / 16) >= ((int64_t)1 << 31)) return NVFP4_ERR_SHAPE;
-  const size_t npart = nvfp4::glu_partials_needed(T, I);
   bool query;
-  int rc = workspace(ws, ws_bytes, T > 0 ? glu_ws(T, I, npart) : 0, &query);
+  int rc = workspace(ws, ws_bytes, T > 0 ? nvfp4::glu_ws_bytes(T, I, K, 1, false) : 0, &query);
   if (rc != NVFP4_OK || query) return rc;
   if (T == 0) return NVFP4_OK;
   if ((rc = check_tensor(x)) != NVFP4_OK || (rc = check_tensor(w_gate)) != NVFP4_OK ||
       (rc = check_tensor(w_up)) != NVFP4_OK || (rc = check_tensor(h_out)) != NVFP4_OK)
     return rc;
   if ((rc = check_device()) != NVFP4_OK) return rc;
-  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
-  float* h = reinterpret_cast<float*>(ws);
-  float* partials = reinterpret_cast<float*>(reinterpret_cast<char*>(ws) +
-                                             round_up((size_t)T * (size_t)I * sizeof(float), 256));
-  uint32_t np = 0;
-  rc = nvfp4::gemm_glu_launch(op(x), op(w_gate), op(w_up), T, I, K, h, partials, &np, st);
-  if (rc != NVFP4_OK) return rc;
-  return nvfp4::requant_f32_launch(h, T, I, h_out.codes, h_out.scales, h_out.gscale, partials, np, st);
+  return nvfp4::glu_launch(op(x), nullptr, nullptr, 1, T, op(w_gate), op(w_up), I, K, h_out.codes, h_out.scales,
+                           h_out.gscale, ws, reinterpret_cast<hipStream_t>(stream));
 }
 
 int nvfp4_mlp_down(nvfp4_tensor h, nvfp4_tensor w_down, int64_t T, int64_t I, int64_t K, void* y, int y_dtype,
                    int64_t ldy, void* ws, size_t* ws_bytes, void* stream) {
   if (!dtype_ok(y_dtype)) return NVFP4_ERR_ARG;
   if (T < 0 || I <= 0 || K <= 0 || I % 128 != 0 || ldy < K) return NVFP4_ERR_SHAPE;
+  if (T * (I / 16) >= ((int64_t)1 << 31)) return NVFP4_ERR_SHAPE;
   bool query;
-  int rc = workspace(ws, ws_bytes, 0, &query);
+  int rc = workspace(ws, ws_bytes, T > 0 ? nvfp4::store_ws_bytes(T, K, I, 1, false) : 0, &query);
   if (rc != NVFP4_OK || query) return rc;
   if (T == 0) return NVFP4_OK;
   if ((rc = check_tensor(h)) != NVFP4_OK || (rc = check_tensor(w_down)) != NVFP4_OK) return rc;
   if (!y) return NVFP4_ERR_NULL;
   if (!aligned(y, 16) || (ldy * elem_size(y_dtype)) % 16 != 0) return NVFP4_ERR_ALIGN;
   if ((rc = check_device()) != NVFP4_OK) return rc;
-  return nvfp4::gemm_launch(op(h), op(w_down), T, K, I, y, y_dtype == NVFP4_BF16, ldy,
-                            reinterpret_cast<hipStream_t>(stream));
+  return nvfp4::store_launch(op(h), nullptr, nullptr, 1, T, op(w_down), K, I, y, y_dtype == NVFP4_BF16, ldy, ws,
+                             reinterpret_cast<hipStream_t>(stream));
 }
 
 int nvfp4_grouped_gemm(nvfp4_tensor a, const int32_t* a_rows, const int32_t* group_offsets, int E, int64_t M,
@@ -181,9 +169,10 @@ int nvfp4_grouped_gemm(nvfp4_tensor a, const int32_t* a_rows, const int32_t* gro
   if (M < 0 || N <= 0 || K <= 0 || N % 128 != 0 || K % 128 != 0) return NVFP4_ERR_SHAPE;
   if (!glu && ld_out < N) return NVFP4_ERR_SHAPE;
   if (M * (N / 16) >= ((int64_t)1 << 31)) return NVFP4_ERR_SHAPE;
-  const size_t npart = glu ? nvfp4::grouped_glu_partials_needed(M, N, E) : 0;
+  if (M * (K / 16) >= ((int64_t)1 << 31)) return NVFP4_ERR_SHAPE;
   bool query;
-  int rc = workspace(ws, ws_bytes, (glu && M > 0) ? glu_ws(M, N, npart) : 0, &query);
+  const size_t need = M == 0 ? 0 : (glu ? nvfp4::glu_ws_bytes(M, N, K, E, true) : nvfp4::store_ws_bytes(M, N, K, E, true));
+  int rc = workspace(ws, ws_bytes, need, &query);
   if (rc != NVFP4_OK || query) return rc;
   if (M == 0) return NVFP4_OK;
   if (!group_offsets) return NVFP4_ERR_NULL;
@@ -198,15 +187,10 @@ int nvfp4_grouped_gemm(nvfp4_tensor a, const int32_t* a_rows, const int32_t* gro
   if ((rc = check_device()) != NVFP4_OK) return rc;
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
   if (!glu)
-    return nvfp4::grouped_gemm_launch(op(a), a_rows, group_offsets, E, M, op(w0), N, K, out,
-                                      out_dtype == NVFP4_BF16, ld_out, st);
-  float* h = reinterpret_cast<float*>(ws);
-  float* partials = reinterpret_cast<float*>(reinterpret_cast<char*>(ws) +
-                                             round_up((size_t)M * (size_t)N * sizeof(float), 256));
-  uint32_t np = 0;
-  rc = nvfp4::grouped_glu_launch(op(a), a_rows, group_offsets, E, M, op(w0), op(w1), N, K, h, partials, &np, st);
-  if (rc != NVFP4_OK) return rc;
-  return nvfp4::requant_f32_launch(h, M, N, out_q.codes, out_q.scales, out_q.gscale, partials, np, st);
+    return nvfp4::store_launch(op(a), a_rows, group_offsets, E, M, op(w0), N, K, out, out_dtype == NVFP4_BF16,
+                               ld_out, ws, st);
+  return nvfp4::glu_launch(op(a), a_rows, group_offsets, E, M, op(w0), op(w1), N, K, out_q.codes, out_q.scales,
+                           out_q.gscale, ws, st);
 }
 
 }  // extern "C"

@@ -77,16 +77,24 @@ def test_quantize_workspace_query():
 
 def test_gemm_and_down_validation():
     g = m.lib.nvfp4_gemm
-    assert g(_t(), _t(), 4, 8, 100, FAKE, m.F32, 8, None, None, None) == m.ERR_SHAPE        # K % 128
-    assert g(_t(), _t(), 4, 8, 128, FAKE, 5, 8, None, None, None) == m.ERR_ARG
-    assert g(_t(), _t(), 4, 8, 128, FAKE, m.F32, 4, None, None, None) == m.ERR_SHAPE        # ldc < N
-    assert g(_t(), _t(), 4, 8, 128, None, m.F32, 8, None, None, None) == m.ERR_NULL
-    assert g(_t(), _t(), 4, 6, 128, FAKE, m.F32, 6, None, None, None) == m.ERR_ALIGN        # row stride 24 B
-    assert g(_t(), _t(s=FAKE + 4), 4, 8, 128, FAKE, m.F32, 8, None, None, None) == m.ERR_ALIGN
-    assert g(_t(), _t(), 0, 8, 128, None, m.F32, 8, None, None, None) == m.OK               # empty
+    big = ctypes.c_size_t(1 << 30)
+    ws = (FAKE, ctypes.byref(big), None)
+    assert g(_t(), _t(), 4, 8, 100, FAKE, m.F32, 8, *ws) == m.ERR_SHAPE        # K % 128
+    assert g(_t(), _t(), 4, 8, 128, FAKE, 5, 8, *ws) == m.ERR_ARG
+    assert g(_t(), _t(), 4, 8, 128, FAKE, m.F32, 4, *ws) == m.ERR_SHAPE        # ldc < N
+    assert g(_t(), _t(), 4, 8, 128, None, m.F32, 8, *ws) == m.ERR_NULL
+    assert g(_t(), _t(), 4, 6, 128, FAKE, m.F32, 6, *ws) == m.ERR_ALIGN        # row stride 24 B
+    assert g(_t(), _t(s=FAKE + 4), 4, 8, 128, FAKE, m.F32, 8, *ws) == m.ERR_ALIGN
+    assert g(_t(), _t(), 4, 8, 128, FAKE, m.F32, 8, None, None, None) == m.ERR_WORKSPACE
+    assert g(_t(), _t(), 0, 8, 128, None, m.F32, 8, None, None, None) == m.OK   # empty
+    s = _size()
+    assert g(nvfp4_tensor(0, 0, 0), nvfp4_tensor(0, 0, 0), 1024, 5120, 17408, None, m.F32, 5120, None,
+             ctypes.byref(s), None) == m.OK
+    assert s.value >= 1024 * 17408 * 2                                        # f16 activation copy
     d = m.lib.nvfp4_mlp_down
-    assert d(_t(), _t(), 4, 100, 64, FAKE, m.F32, 64, None, None, None) == m.ERR_SHAPE      # I % 128
-    assert d(_t(), _t(), 4, 128, 64, FAKE, m.BF16, 60, None, None, None) == m.ERR_SHAPE     # ldy < K
+    assert d(_t(), _t(), 4, 100, 64, FAKE, m.F32, 64, *ws) == m.ERR_SHAPE      # I % 128
+    assert d(_t(), _t(), 4, 128, 64, FAKE, m.BF16, 60, *ws) == m.ERR_SHAPE     # ldy < K
+    assert d(_t(), _t(), 4, 128, 64, None, m.F32, 64, *ws) == m.ERR_NULL
 
 
 def test_gu_act_validation_and_workspace():
@@ -134,8 +142,8 @@ def test_valid_calls_report_missing_device_and_launch_nothing():
     before = m.lib.nvfp4_launch_count()
     sz = ctypes.c_size_t(1 << 20)
     assert m.lib.nvfp4_quantize_act(FAKE, m.BF16, 4, 32, 32, _t(), 0, FAKE, ctypes.byref(sz), None) == m.ERR_DEVICE
-    assert m.lib.nvfp4_gemm(_t(), _t(), 4, 8, 128, FAKE, m.F32, 8, None, None, None) == m.ERR_DEVICE
     big = ctypes.c_size_t(1 << 24)
+    assert m.lib.nvfp4_gemm(_t(), _t(), 4, 8, 128, FAKE, m.F32, 8, FAKE, ctypes.byref(big), None) == m.ERR_DEVICE
     assert m.lib.nvfp4_mlp_gu_act(_t(), _t(), _t(), 4, 128, 128, _t(), FAKE, ctypes.byref(big), None) == m.ERR_DEVICE
-    assert m.lib.nvfp4_mlp_down(_t(), _t(), 4, 128, 64, FAKE, m.F32, 64, None, None, None) == m.ERR_DEVICE
+    assert m.lib.nvfp4_mlp_down(_t(), _t(), 4, 128, 64, FAKE, m.F32, 64, FAKE, ctypes.byref(big), None) == m.ERR_DEVICE
     assert m.lib.nvfp4_launch_count() == before

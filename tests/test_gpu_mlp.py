@@ -128,4 +128,4 @@ def test_launch_count_independent_of_T():
         run_device_mlp(bf16_normal(9, (t, 256)), wdev)
         counts.append(m.launch_count() - before)
     assert len(set(counts)) == 1, counts
-    assert counts[0] <= 5
+    assert counts[0] <= 8        # quantise 2, gate/up 3, down 3
