@@ -70,38 +70,41 @@ def global_scale(x):
     return np.float32(np.float64(amax) / GS_DIVISOR)
 
 
-def _round_by_midpoints(values, thresholds):
-    """Round-to-nearest-even onto a grid given its midpoint thresholds.
-
-    `thresholds` ([..., n]) are the exact midpoints between grid points
-    0..n (increasing along the last axis); `values` ([...] broadcastable with
-    thresholds[..., 0]) are non-negative.  Returns the grid index: the number of
-    midpoints strictly below the value, plus one if the value sits exactly on
-    midpoint i with i odd (between grid points i and i+1 the even one wins).
-    Values above the last midpoint get index n, i.e. saturate.
-    """
-    v = values[..., None]
-    above = (v > thresholds).sum(axis=-1)
-    odd = (np.arange(thresholds.shape[-1]) % 2 == 1)
-    tie_up = ((v == thresholds) & odd).sum(axis=-1)
-    return (above + tie_up).astype(np.int64)
-
-
 def block_scale_codes(block_amax, gs):
-    """E4M3 code of each block scale: RNE_E4M3(block_amax / (6*gs)), saturating at 448."""
+    """E4M3 code of each block scale: RNE_E4M3(block_amax / (6*gs)), saturating at 448.
+
+    thr[c] = 6 * mid_c * gs is the exact decision threshold between codes c
+    and c+1 (increasing in c).  The code is the number of thresholds strictly
+    below the value, plus one when the value sits exactly on thr[c] with c
+    odd (between c and c+1 the even code wins).  Values above the last
+    threshold get code 0x7E (448): saturation.
+    """
     thr = (6.0 * formats.E4M3_MIDS) * np.float64(gs)          # exact, <= 31 significant bits
     a = np.asarray(block_amax, dtype=np.float64)
-    return _round_by_midpoints(a, thr).astype(np.uint8)
+    below = np.searchsorted(thr, a, side="left")             # number of thresholds < a
+    on = below < len(thr)
+    tie = np.zeros(a.shape, dtype=bool)
+    tie[on] = thr[below[on]] == a[on]
+    code = below + (tie & (below % 2 == 1))
+    return code.astype(np.uint8)
 
 
 def element_codes(x_blocks, scale_codes, gs):
-    """E2M1 codes of x_blocks [..., nb, 16] given each block's E4M3 scale code [..., nb]."""
+    """E2M1 codes of x_blocks [..., nb, 16] given each block's E4M3 scale code [..., nb].
+
+    The decision threshold between magnitudes i and i+1 is mid_i * d * gs
+    (exact).  On an exact tie the even index wins: at even i the value must
+    exceed the threshold to round up, at odd i it rounds up when equal too.
+    """
     d = formats.E4M3_TABLE[scale_codes.astype(np.int64)]    # exact decoded block scale
-    thr = (formats.E2M1_MIDS * d[..., None]) * np.float64(gs)  # [..., nb, 7], exact
+    dgs = (d * np.float64(gs))[..., None]                    # [..., nb, 1], exact
     mag = np.abs(x_blocks.astype(np.float64))
-    idx = _round_by_midpoints(mag, thr[..., None, :])       # [..., nb, 16]
-    idx = np.where((d == 0.0)[..., None], 0, idx)           # zero scale: magnitude 0
-    sign = np.signbit(x_blocks).astype(np.int64)
+    idx = np.zeros(mag.shape, dtype=np.int8)
+    for i, mid in enumerate(formats.E2M1_MIDS):
+        thr = mid * dgs                                      # exact, <= 31 significant bits
+        idx += (mag > thr) if i % 2 == 0 else (mag >= thr)
+    idx = np.where((d == 0.0)[..., None], 0, idx)            # zero scale: magnitude 0
+    sign = np.signbit(x_blocks).astype(np.int8)
     return (sign * 8 + idx).astype(np.uint8)
 
 
@@ -134,7 +137,7 @@ def quantize(x, gs=None):
     rows, cols = x.shape
     gs = global_scale(x) if gs is None else np.float32(gs)
     nb = cols // BLOCK
-    row_chunk = max(1, (1 << 21) // max(cols, 1))         # bounds the temporaries
+    row_chunk = max(1, (1 << 23) // max(cols, 1))         # bounds the temporaries
     codes = np.empty((rows, cols // 2), dtype=np.uint8)
     scales = np.empty((rows, nb), dtype=np.uint8)
     if rows == 0 or cols == 0:
