@@ -28,7 +28,35 @@ if ROOT not in sys.path:
 METRIC = "NVFP4 MLP effective TFLOPS & tokens/s at T=1024/16384; % MFMA peak; T=1 HBM GB/s"
 PEAK_F16_TFLOPS = 2500.0          # MI355X dense f16 MFMA
 PEAK_HBM_GBS = 8000.0             # MI355X HBM3E
+PEAK_FP4_TFLOPS = 10100.0         # MI355X dense fp4 MFMA (not the arithmetic used here)
 K_HID, I_INT = 5120, 17408
+COPY_BYTES = 256 << 20            # elementwise pass used to calibrate byte counters
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gate_up_gemm_traffic.json")
+KERNEL_SOURCES = [os.path.join(ROOT, "mlp_prefill_amd", "csrc", f) for f in ("gemm.hip", "device_common.h")]
+
+
+def kernel_source_hash():
+    """SHA-256 of the dominant kernel's sources with // comments and blank lines removed."""
+    import hashlib
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        for line in open(f, encoding="utf-8"):
+            code = line.split("//", 1)[0].strip()
+            if code:
+                h.update(code.encode() + b"\n")
+    return h.hexdigest()
+
+
+def traffic_bytes():
+    """HBM bytes per launch of the dominant kernel from the committed counter
+    summary, or None when the kernel sources changed since it was taken."""
+    try:
+        rec = json.load(open(TRAFFIC_FILE))
+    except (OSError, ValueError):
+        return None
+    if rec.get("source_sha256") != kernel_source_hash():
+        return None
+    return rec.get("hbm_bytes_per_launch")
 
 
 def log(msg):
@@ -122,8 +150,8 @@ def main():
     ap.add_argument("--steps", type=int, default=5)
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--no-extra", action="store_true", help="skip the 1024-token and decode lines")
-    ap.add_argument("--cpu-ubatches", type=int, default=4, help="ubatches the CPU oracle runs (about 10 s)")
+    ap.add_argument("--no-extra", action="store_true", help="skip the 1024-token, decode and expert-grouped lines")
+    ap.add_argument("--cpu-ubatches", type=int, default=8, help="ubatches the CPU oracle runs (about 10-15 s)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported (the path is built and measured "
@@ -157,6 +185,10 @@ def main():
         step()
     torch.cuda.synchronize()
     log(f"timing {args.steps} steps")
+    n_calls = (T // UB) * L
+    # The dominant kernel (gate/up contraction) is bracketed by HIP events on
+    # its own stream inside the library, throughout the timed region.
+    m.nvfp4_timing_begin(m.KC_GEMM_GLU, n_calls * args.steps)
     s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     s.record()
@@ -165,33 +197,44 @@ def main():
     e.record()
     torch.cuda.synchronize()
     ms = s.elapsed_time(e) / args.steps
+    n_gemm, dropped, gemm_total_ms = m.nvfp4_timing_end()
+    assert n_gemm == n_calls * args.steps and dropped == 0, (n_gemm, dropped)
     flops = mlp_flops(T) * L
     tflops = flops / (ms * 1e-3) / 1e12
     tokens_s = T / (ms * 1e-3)
     log(f"{ms:.3f} ms/step, {tflops:.1f} TFLOP/s, {tokens_s:.0f} tokens/s")
 
-    # ---- dominant kernel: the gate/up GEMM with the SiLU*up epilogue ------------------
-    # nvfp4_mlp_gu_act = [gate/up GEMM + GLU] then [requantise H].  The requantise
-    # kernel's work is timed alone as a given-scale quantisation of the same
-    # float32 H; the GEMM kernel's duration is the difference.
-    x0 = x_all[:UB]
-    m.nvfp4_quantize_act(x0, run.xq, ws=run.ws_q)
-    h32 = run.ws_gu[: UB * I_INT * 4].view(torch.float32).view(UB, I_INT)
-    hq_tmp = m.NVFP4.empty(UB, I_INT)
-    hq_tmp.gscale.fill_(1.0)
-    t_gu = time_events(lambda: m.nvfp4_mlp_gu_act(run.xq, layers[0].w[0], layers[0].w[1], run.hq, ws=run.ws_gu), 20)
-    t_rq = time_events(lambda: m.nvfp4_quantize_act(h32, hq_tmp, gs_mode=m.GS_GIVEN), 20)
-    gemm_ms = float(np.mean(t_gu) - np.mean(t_rq))
+    # ---- dominant kernel: the gate/up contraction with the SiLU*up epilogue ------------
+    gemm_ms = gemm_total_ms / n_gemm
     gemm_flops = 4.0 * UB * K_HID * I_INT
     achieved = gemm_flops / (gemm_ms * 1e-3) / 1e12
     roofline = {"bound": "mfma", "achieved": achieved, "peak": PEAK_F16_TFLOPS, "unit": "TFLOP/s",
-                "frac": achieved / PEAK_F16_TFLOPS, "traffic": None,
-                "kernel": "gemm_kernel<2,2,2,2,dual,dense,glu> (gate/up + SiLU*up, T=1024 ubatch)",
-                "flops_per_launch": gemm_flops, "avg_launch_ms": gemm_ms,
-                "gu_act_call_ms": float(np.mean(t_gu)), "requant_ms": float(np.mean(t_rq)),
-                "peak_fp4_tflops_for_reference": 10100.0,
-                "frac_of_fp4_peak": achieved / 10100.0}
+                "frac": achieved / PEAK_F16_TFLOPS, "traffic": traffic_bytes(),
+                "kernel": "nvfp4::gemm_kernel<4, 2, 1, true, false, 1> (gate/up contraction, SiLU*up epilogue, "
+                          "1024-token ubatch)",
+                "flops_per_launch": gemm_flops, "avg_launch_ms": gemm_ms, "launches_timed": n_gemm,
+                "arith": "f16 MFMA 32x32x16, fp32 accumulate (NVFP4 operands expanded exactly)",
+                "frac_of_fp4_dense_peak": achieved / PEAK_FP4_TFLOPS}
     log(f"dominant kernel {gemm_ms:.3f} ms -> {achieved:.1f} TFLOP/s ({100 * achieved / PEAK_F16_TFLOPS:.1f}% of f16 peak)")
+
+    # Per-class breakdown of one further step (each class timed in its own window).
+    breakdown = {}
+    for name, kc in (("quantize", m.KC_QUANTIZE), ("expand", m.KC_EXPAND), ("gemm_glu", m.KC_GEMM_GLU),
+                     ("gemm_store", m.KC_GEMM_STORE), ("reduce", m.KC_REDUCE)):
+        m.nvfp4_timing_begin(kc, 8 * n_calls)
+        step()
+        n_k, _, tot = m.nvfp4_timing_end()
+        breakdown[name] = {"launches_per_step": n_k, "ms_per_step": tot}
+    roofline["breakdown_one_step"] = breakdown
+
+    # A plain elementwise kernel of known traffic (reads and writes COPY_BYTES),
+    # so that profiler byte counters taken on this same command can be
+    # calibrated against it.
+    src = torch.zeros(COPY_BYTES // 4, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    torch.neg(src, out=dst)
+    torch.cuda.synchronize()
+    del src, dst
 
     extra = {}
     if not args.no_extra:
@@ -256,7 +299,52 @@ def extra_lines(m):
     dec["launches_per_call"] = launches
     dec["t5_over_t1_cold"] = dec["T5"]["ms_cold"] / dec["T1"]["ms_cold"]
     out["decode"] = dec
+    del lay, scrub_buf
+    out["moe"] = moe_line(m)
     return out
+
+
+def moe_line(m):
+    """Expert-grouped MLP: 4096 tokens routed top-8 over 64 experts (hidden 4096, expert width 2048)."""
+    from synthetic import WORKLOADS, bf16_normal, expert_seeds, moe_routing
+    p = WORKLOADS["moe_4096_top8_of_64"].params
+    t, e, top, k, i = p["T"], p["E"], p["topk"], p["K"], p["I"]
+    log("extra: expert-grouped MLP (64 experts, top-8)")
+    r = moe_routing(p["router_seed"], t, e, top)
+    mats = [[], [], []]
+    for x in range(e):
+        for j, (sd, shp) in enumerate(zip(expert_seeds(p["expert_seed0"], x), [(i, k), (i, k), (k, i)])):
+            w = m.bf16_from_bits(bf16_normal(sd, shp, sigma=0.02))
+            q = m.NVFP4.empty(*shp)
+            m.nvfp4_quantize_act(w, q)
+            mats[j].append(q)
+    wg, wu, wd = (m.NVFP4.stack(v) for v in mats)
+    del mats
+    x = m.bf16_from_bits(bf16_normal(p["x_seed"], (t, k)))
+    rows = torch.from_numpy(np.ascontiguousarray(r.a_rows, dtype=np.int32)).cuda()
+    offs = torch.from_numpy(np.ascontiguousarray(r.group_offsets, dtype=np.int32)).cuda()
+    slots = t * top
+    xq = m.NVFP4.empty(t, k)
+    hq = m.NVFP4.empty(slots, i)
+    y = torch.empty((slots, k), dtype=torch.bfloat16, device="cuda")
+    ws_q = torch.empty(m.ws_bytes_quantize(t, k), dtype=torch.uint8, device="cuda")
+    ws_g = torch.empty(max(m.grouped_ws_bytes(slots, i, k, e, m.EPI_SILU_MUL_REQUANT), 256), dtype=torch.uint8,
+                       device="cuda")
+    ws_d = torch.empty(max(m.grouped_ws_bytes(slots, k, i, e, m.EPI_STORE), 256), dtype=torch.uint8, device="cuda")
+
+    def call():
+        m.nvfp4_quantize_act(x, xq, ws=ws_q)
+        m.nvfp4_grouped_gemm(xq, rows, offs, wg, wu, out_q=hq, epilogue=m.EPI_SILU_MUL_REQUANT, m=slots, ws=ws_g)
+        m.nvfp4_grouped_gemm(hq, None, offs, wd, out=y, epilogue=m.EPI_STORE, ws=ws_d)
+
+    before = m.launch_count()
+    call()
+    launches = m.launch_count() - before
+    ms = float(np.median(time_events(call, 10)))
+    flops = mlp_flops(slots, k, i)
+    tf = flops / (ms * 1e-3) / 1e12
+    return {"workload": "moe_4096_top8_of_64", "ms": ms, "tflops": tf, "frac_f16_peak": tf / PEAK_F16_TFLOPS,
+            "tokens_per_s": t / (ms * 1e-3), "slots": slots, "launches_per_call": launches}
 
 
 if __name__ == "__main__":

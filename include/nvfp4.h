@@ -37,7 +37,9 @@
  *    and device, never allocates, and never reads device memory on the
  *    host: global scales are produced and consumed on the device only.
  *  - The caller owns every buffer.  The library keeps no pointer after a
- *    call returns; its only state is a process-wide launch counter.
+ *    call returns; its only state is a process-wide launch counter, a
+ *    per-device record of the device check, and the optional timing window
+ *    (nvfp4_timing_begin / nvfp4_timing_end).
  *  - Workspace: ws == NULL with ws_bytes != NULL is a size query: the
  *    required size is stored in *ws_bytes and NVFP4_OK returned without
  *    launching anything.  Otherwise *ws_bytes is the size of ws (ws_bytes ==
@@ -120,12 +122,16 @@ int nvfp4_quantize_act(const void *x, int x_dtype, int64_t rows, int64_t cols, i
 /*
  * nvfp4_gemm -- C[M][N] = (A~ . B~^T) * gscale_a * gscale_b.
  * One NVFP4 x NVFP4 contraction, K-contiguous operands as a linear layer
- * stores them ([llama] "Verified", MUL_MAT).  One launch per call whatever
- * M is ([vllm] Fix directions 1).  Accumulation in float32 on the matrix
- * cores, products exact.
- *   a : [M][K] NVFP4, b : [N][K] NVFP4 (one gscale each)
- *   K : multiple of 128
- *   c : float32 or bf16 (c_dtype), row stride ldc >= N elements
+ * stores them ([llama] "Verified", MUL_MAT).  Three launches per call
+ * whatever M is ([vllm] Fix directions 1): expansion of a~ to f16 (exact),
+ * the contraction, and a fixed-order split-K reduction (over zero rows when
+ * K is not split).  Accumulation in float32 on the matrix cores, every
+ * product exact.
+ *   a  : [M][K] NVFP4, b : [N][K] NVFP4 (one gscale each)
+ *   K  : multiple of 128
+ *   c  : float32 or bf16 (c_dtype), row stride ldc >= N elements
+ *   ws : required: the f16 copy of a~ (M*K*2 bytes) and, when K is split,
+ *        the float32 partial sums; contents unspecified on return
  */
 int nvfp4_gemm(nvfp4_tensor a, nvfp4_tensor b, int64_t M, int64_t N, int64_t K,
                void *c, int c_dtype, int64_t ldc, void *ws, size_t *ws_bytes, void *stream);
@@ -140,9 +146,11 @@ int nvfp4_gemm(nvfp4_tensor a, nvfp4_tensor b, int64_t M, int64_t N, int64_t K,
  *   x      : [T][K] NVFP4;  w_gate, w_up : [I][K] NVFP4
  *   h_out  : [T][I] NVFP4 (codes, scales, gscale written)
  *   K, I   : multiples of 128
- *   ws     : on return its first T*I*4 bytes hold H in float32, row-major
- *            [T][I] (the value that was quantised)
- * Launch count is fixed (independent of T).
+ *   ws     : required; on return its first T*I*4 bytes hold H in float32,
+ *            row-major [T][I] (the value that was quantised); then the f16
+ *            copy of x~ and the per-tile maxima of |H|
+ * Three launches per call (expansion, contraction with the SiLU*up epilogue
+ * and the |H| tile maxima, requantisation), independent of T.
  */
 int nvfp4_mlp_gu_act(nvfp4_tensor x, nvfp4_tensor w_gate, nvfp4_tensor w_up,
                      int64_t T, int64_t K, int64_t I, nvfp4_tensor h_out,
@@ -153,8 +161,10 @@ int nvfp4_mlp_gu_act(nvfp4_tensor x, nvfp4_tensor w_gate, nvfp4_tensor w_up,
  * The down projection of the MLP ([vllm] "Problem": MlpDownFp4, here once
  * per batch).  y is float32 (parity) or bf16 (the next layer's activation,
  * kept on the device: [vllm] Fix directions 2).
- *   h : [T][I] NVFP4;  w_down : [K][I] NVFP4;  I multiple of 128
- *   y : row stride ldy >= K elements
+ *   h  : [T][I] NVFP4;  w_down : [K][I] NVFP4;  I multiple of 128
+ *   y  : row stride ldy >= K elements
+ *   ws : required, as for nvfp4_gemm (f16 copy of h~, split-K partials)
+ * Three launches per call, independent of T.
  */
 int nvfp4_mlp_down(nvfp4_tensor h, nvfp4_tensor w_down, int64_t T, int64_t I, int64_t K,
                    void *y, int y_dtype, int64_t ldy, void *ws, size_t *ws_bytes, void *stream);
@@ -191,6 +201,44 @@ const char *nvfp4_strerror(int status);
  * (a host counter; lets a caller check that the launch count of a call does
  * not depend on T -- [vllm] "Problem": identical per-token launches). */
 uint64_t nvfp4_launch_count(void);
+
+/*
+ * Kernel timing (instrumentation; nothing is timed unless a window is open).
+ * Kernel classes: every launch of the library belongs to exactly one.
+ */
+enum nvfp4_kernel_class {
+  NVFP4_KC_QUANTIZE = 0,     /* amax partials and quantise kernels (also the requantisation of H) */
+  NVFP4_KC_EXPAND = 1,       /* NVFP4 -> f16 activation expansion ahead of a contraction          */
+  NVFP4_KC_GEMM_GLU = 2,     /* contraction with the SiLU*up epilogue (gate/up projection)         */
+  NVFP4_KC_GEMM_STORE = 3,   /* contraction with the store epilogue (down projection, nvfp4_gemm)  */
+  NVFP4_KC_REDUCE = 4        /* split-K reduction and output scaling                               */
+};
+
+#define NVFP4_TIMING_MAX_LAUNCHES 1048576
+
+/*
+ * nvfp4_timing_begin -- open a timing window for one kernel class.  Until
+ * nvfp4_timing_end, every launch of that class (on any stream, from any
+ * thread) is bracketed by two HIP events recorded on the launch's own
+ * stream, so the measured span is that kernel alone.  Creates
+ * 2 * max_launches HIP events (host-side objects, no device memory);
+ * launches beyond max_launches are counted as dropped and not timed.
+ * Errors: NVFP4_ERR_ARG for an unknown class, max_launches outside
+ * [1, NVFP4_TIMING_MAX_LAUNCHES] or a window already open;
+ * NVFP4_ERR_LAUNCH when the events cannot be created.
+ */
+int nvfp4_timing_begin(int kernel_class, int64_t max_launches);
+
+/*
+ * nvfp4_timing_end -- close the window: waits on the host for the last
+ * recorded event (the one call of the library that synchronises), then
+ * writes to host memory the number of launches timed, the number dropped and
+ * the sum of their durations in milliseconds, and destroys the events.
+ * Errors: NVFP4_ERR_NULL for a NULL output; NVFP4_ERR_ARG when no window is
+ * open; NVFP4_ERR_LAUNCH when an event record or query failed (the window is
+ * closed either way).
+ */
+int nvfp4_timing_end(int64_t *launches, int64_t *dropped, double *total_ms);
 
 #ifdef __cplusplus
 }

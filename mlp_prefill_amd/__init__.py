@@ -34,6 +34,7 @@ OK, ERR_NULL, ERR_SHAPE, ERR_ALIGN, ERR_WORKSPACE, ERR_ARG, ERR_DEVICE, ERR_LAUN
 F32, BF16 = 0, 1
 GS_COMPUTE, GS_GIVEN = 0, 1
 EPI_STORE, EPI_SILU_MUL_REQUANT = 0, 1
+KC_QUANTIZE, KC_EXPAND, KC_GEMM_GLU, KC_GEMM_STORE, KC_REDUCE = range(5)
 
 _sig = {
     "nvfp4_quantize_act": [_vp, ctypes.c_int, _i64, _i64, _i64, nvfp4_tensor, ctypes.c_int, _vp,
@@ -56,6 +57,10 @@ _lib.nvfp4_strerror.argtypes = [ctypes.c_int]
 _lib.nvfp4_strerror.restype = ctypes.c_char_p
 _lib.nvfp4_launch_count.argtypes = []
 _lib.nvfp4_launch_count.restype = ctypes.c_uint64
+_lib.nvfp4_timing_begin.argtypes = [ctypes.c_int, _i64]
+_lib.nvfp4_timing_begin.restype = ctypes.c_int
+_lib.nvfp4_timing_end.argtypes = [ctypes.POINTER(_i64), ctypes.POINTER(_i64), ctypes.POINTER(ctypes.c_double)]
+_lib.nvfp4_timing_end.restype = ctypes.c_int
 
 lib = _lib
 
@@ -74,6 +79,18 @@ def _check(status, where):
 def launch_count():
     """Kernel launches this library has enqueued in this process."""
     return int(_lib.nvfp4_launch_count())
+
+
+def nvfp4_timing_begin(kernel_class, max_launches):
+    """Open a timing window for one kernel class (see include/nvfp4.h)."""
+    _check(_lib.nvfp4_timing_begin(kernel_class, max_launches), "nvfp4_timing_begin")
+
+
+def nvfp4_timing_end():
+    """Close the timing window: (launches timed, launches dropped, summed milliseconds)."""
+    n, d, ms = _i64(0), _i64(0), ctypes.c_double(0.0)
+    _check(_lib.nvfp4_timing_end(ctypes.byref(n), ctypes.byref(d), ctypes.byref(ms)), "nvfp4_timing_end")
+    return n.value, d.value, ms.value
 
 
 def _stream(stream=None):

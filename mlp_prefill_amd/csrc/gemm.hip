@@ -21,14 +21,18 @@
 // chunk, lane half h of a weight fragment reads 32 code bytes (64 elements)
 // and the 4 scale bytes covering them, and feeds elements 64h + 8s .. +7 to
 // MFMA step s (s = 0..7); the activation fragment for step s is the 16 bytes
-// of f16 at the same K positions.  Weight fragments are expanded in
-// registers (hardware E2M1 -> f16 convert and an exact f16 multiply by the
-// E4M3 scale) one step ahead of the MFMAs that consume them, so the vector
-// ALU work co-issues with the matrix core; packed weights are prefetched one
-// chunk ahead and activation fragments two steps ahead.
+// of f16 at the same K positions.
 //
-// The waves of a work-group sit side by side along N and share activation
-// rows (L1/L2 hits); each expands only its own weight columns, so no
+// Each 128-wide K chunk of the work-group's activation tile (f16) and weight
+// tile (packed codes and scales) is copied from global memory straight into
+// LDS by the LDS DMA path, double-buffered: the copy of chunk c+1 is in
+// flight while chunk c is consumed.  Weight fragments are read from LDS
+// packed and expanded in registers (hardware E2M1 -> f16 convert and an
+// exact f16 multiply by the E4M3 scale) one step ahead of the MFMAs that
+// consume them, so the vector ALU work co-issues with the matrix core.
+//
+// The waves of a work-group sit side by side along N and share the staged
+// activation rows; each expands only its own weight columns, so no
 // expansion is duplicated.  Work-group tiles are remapped so that the tiles
 // of one XCD share weight columns in its L2.
 //
@@ -502,8 +506,9 @@ static Plan plan_store(int64_t M, int64_t N, int64_t K, int E, bool grouped) {
 template <int WN, int TM, int TN, bool DUAL, bool GROUPED, int EPI>
 static void launch_cfg(const GemmArgs& g, hipStream_t st) {
   const uint32_t grid = g.m_tiles * g.n_tiles * g.splits;
+  const int slot = launch_begin(EPI == EPI_GLU ? KC_GEMM_GLU : KC_GEMM_STORE, st);
   hipLaunchKernelGGL((gemm_kernel<WN, TM, TN, DUAL, GROUPED, EPI>), dim3(grid), dim3(WN * 64), 0, st, g);
-  count_launch();
+  launch_end(slot, st);
 }
 
 static void launch_expand(const uint8_t* codes, const uint8_t* scales, const int32_t* rows, int64_t nrows,
@@ -513,8 +518,9 @@ static void launch_expand(const uint8_t* codes, const uint8_t* scales, const int
   uint32_t grid = (nblocks + 255u) / 256u;
   if (grid > 4096u) grid = 4096u;
   if (grid < 1u) grid = 1u;
+  const int slot = launch_begin(KC_EXPAND, st);
   hipLaunchKernelGGL(expand_kernel, dim3(grid), dim3(256), 0, st, codes, scales, rows, nbc, nblocks, out);
-  count_launch();
+  launch_end(slot, st);
 }
 
 static void launch_reduce(const float* part, uint32_t splits, int64_t M, int64_t N, const float* a_gs,
@@ -523,9 +529,10 @@ static void launch_reduce(const float* part, uint32_t splits, int64_t M, int64_t
   int64_t blocks = (M * N + 255) / 256;
   if (blocks > 8192) blocks = 8192;
   if (blocks < 1) blocks = 1;
+  const int slot = launch_begin(KC_REDUCE, st);
   hipLaunchKernelGGL(splitk_reduce_kernel, dim3((uint32_t)blocks), dim3(256), 0, st, part, splits, M, N, a_gs,
                      b_gs, off, E, out, bf16, ldo);
-  count_launch();
+  launch_end(slot, st);
 }
 
 static size_t align256(size_t v) { return (v + 255) / 256 * 256; }

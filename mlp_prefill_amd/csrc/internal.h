@@ -12,7 +12,14 @@ namespace nvfp4 {
 // Largest number of partial maxima any amax reduction produces.
 constexpr uint32_t kMaxPartials = 4096;
 
-void count_launch();
+// Kernel classes of the timing window (same values as the public enum).
+enum KernelClass { KC_QUANTIZE = 0, KC_EXPAND = 1, KC_GEMM_GLU = 2, KC_GEMM_STORE = 3, KC_REDUCE = 4, KC_COUNT = 5 };
+
+// Every launch is bracketed by these two calls: launch_begin records the
+// start event when a timing window for `kc` is open (returns its slot, else
+// -1); launch_end records the matching end event and counts the launch.
+int launch_begin(int kc, hipStream_t st);
+void launch_end(int slot, hipStream_t st);
 
 // ---- quantisation -----------------------------------------------------------
 size_t quantize_ws_bytes(int64_t rows, int64_t cols, int gs_mode);

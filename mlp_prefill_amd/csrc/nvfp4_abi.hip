@@ -5,13 +5,45 @@
 
 #include <atomic>
 #include <cstring>
+#include <mutex>
+#include <vector>
 
 #include "internal.h"
 
 namespace nvfp4 {
 
 static std::atomic<uint64_t> g_launches{0};
-void count_launch() { g_launches.fetch_add(1, std::memory_order_relaxed); }
+
+// Timing window: at most one open at a time.  `active` is read on every
+// launch without the lock; the event pool only changes under the lock.
+struct Timing {
+  std::mutex mu;
+  std::atomic<int> active{-1};
+  std::vector<hipEvent_t> ev;  // [start, end] per slot
+  int64_t used = 0, dropped = 0, cap = 0;
+  bool record_failed = false;
+};
+static Timing g_timing;
+
+int launch_begin(int kc, hipStream_t st) {
+  if (g_timing.active.load(std::memory_order_acquire) != kc) return -1;
+  std::lock_guard<std::mutex> lk(g_timing.mu);
+  if (g_timing.active.load(std::memory_order_relaxed) != kc) return -1;
+  if (g_timing.used >= g_timing.cap) {
+    ++g_timing.dropped;
+    return -1;
+  }
+  const int slot = (int)g_timing.used++;
+  if (hipEventRecord(g_timing.ev[2 * slot], st) != hipSuccess) g_timing.record_failed = true;
+  return slot;
+}
+
+void launch_end(int slot, hipStream_t st) {
+  g_launches.fetch_add(1, std::memory_order_relaxed);
+  if (slot < 0) return;
+  std::lock_guard<std::mutex> lk(g_timing.mu);
+  if (hipEventRecord(g_timing.ev[2 * slot + 1], st) != hipSuccess) g_timing.record_failed = true;
+}
 
 }  // namespace nvfp4
 
@@ -90,6 +122,55 @@ const char* nvfp4_strerror(int status) {
 }
 
 uint64_t nvfp4_launch_count(void) { return nvfp4::g_launches.load(std::memory_order_relaxed); }
+
+int nvfp4_timing_begin(int kernel_class, int64_t max_launches) {
+  using nvfp4::g_timing;
+  if (kernel_class < 0 || kernel_class >= nvfp4::KC_COUNT) return NVFP4_ERR_ARG;
+  if (max_launches <= 0 || max_launches > NVFP4_TIMING_MAX_LAUNCHES) return NVFP4_ERR_ARG;
+  std::lock_guard<std::mutex> lk(g_timing.mu);
+  if (g_timing.active.load(std::memory_order_relaxed) >= 0) return NVFP4_ERR_ARG;
+  g_timing.ev.assign((size_t)(2 * max_launches), nullptr);
+  for (auto& e : g_timing.ev) {
+    if (hipEventCreate(&e) != hipSuccess) {
+      (void)hipGetLastError();
+      for (auto& d : g_timing.ev)
+        if (d) (void)hipEventDestroy(d);
+      g_timing.ev.clear();
+      return NVFP4_ERR_LAUNCH;
+    }
+  }
+  g_timing.used = g_timing.dropped = 0;
+  g_timing.cap = max_launches;
+  g_timing.record_failed = false;
+  g_timing.active.store(kernel_class, std::memory_order_release);
+  return NVFP4_OK;
+}
+
+int nvfp4_timing_end(int64_t* launches, int64_t* dropped, double* total_ms) {
+  using nvfp4::g_timing;
+  if (!launches || !dropped || !total_ms) return NVFP4_ERR_NULL;
+  std::lock_guard<std::mutex> lk(g_timing.mu);
+  if (g_timing.active.load(std::memory_order_relaxed) < 0) return NVFP4_ERR_ARG;
+  g_timing.active.store(-1, std::memory_order_release);
+  int status = g_timing.record_failed ? NVFP4_ERR_LAUNCH : NVFP4_OK;
+  double sum = 0.0;
+  for (int64_t i = 0; i < g_timing.used && status == NVFP4_OK; ++i) {
+    float ms = 0.f;
+    if (hipEventSynchronize(g_timing.ev[2 * i + 1]) != hipSuccess ||
+        hipEventElapsedTime(&ms, g_timing.ev[2 * i], g_timing.ev[2 * i + 1]) != hipSuccess) {
+      (void)hipGetLastError();
+      status = NVFP4_ERR_LAUNCH;
+    }
+    sum += ms;
+  }
+  for (auto& e : g_timing.ev) (void)hipEventDestroy(e);
+  g_timing.ev.clear();
+  *launches = g_timing.used;
+  *dropped = g_timing.dropped;
+  *total_ms = sum;
+  g_timing.used = g_timing.dropped = g_timing.cap = 0;
+  return status;
+}
 
 int nvfp4_quantize_act(const void* x, int x_dtype, int64_t rows, int64_t cols, int64_t ld_x, nvfp4_tensor out,
                        int gs_mode, void* ws, size_t* ws_bytes, void* stream) {

@@ -9,7 +9,8 @@
 // Two kernels: amax_partials writes one partial maximum per work-group;
 // quantize reduces those partials again in every work-group (a few KiB from
 // L2, no atomics, no zero-initialised state), forms the global scale, and
-// quantises one 16-element block per thread.  Both are HBM-bound: the
+// quantises 16-element blocks in a grid-stride loop (one block per thread per
+// iteration, at most 2048 work-groups).  Both are HBM-bound: the
 // quantiser reads 2 (bf16) or 4 (float32) bytes per element and writes
 // 0.5 + 1/16 bytes.
 #include "device_common.h"
@@ -134,18 +135,23 @@ static int quantize_launch_t(const T* x, int64_t rows, int64_t cols, int64_t ld,
   if (qgrid < 1) qgrid = 1;
   if (gs_mode == 0 && ext_partials == nullptr) {
     const uint32_t g = amax_grid(nblocks);
+    const int s0 = launch_begin(KC_QUANTIZE, st);
     hipLaunchKernelGGL(amax_partials_kernel<T>, dim3(g), dim3(256), 0, st, x, nbc, nblocks, ld, partials);
-    count_launch();
+    launch_end(s0, st);
+    const int s1 = launch_begin(KC_QUANTIZE, st);
     hipLaunchKernelGGL(quantize_kernel<T>, dim3(qgrid), dim3(256), 0, st, x, nbc, nblocks, ld,
                        (const float*)partials, g, gs, 0, codes, scales);
-  } else if (gs_mode == 0) {
-    hipLaunchKernelGGL(quantize_kernel<T>, dim3(qgrid), dim3(256), 0, st, x, nbc, nblocks, ld,
-                       ext_partials, ext_npart, gs, 0, codes, scales);
+    launch_end(s1, st);
   } else {
-    hipLaunchKernelGGL(quantize_kernel<T>, dim3(qgrid), dim3(256), 0, st, x, nbc, nblocks, ld,
-                       (const float*)nullptr, 0u, gs, 1, codes, scales);
+    const int s1 = launch_begin(KC_QUANTIZE, st);
+    if (gs_mode == 0)
+      hipLaunchKernelGGL(quantize_kernel<T>, dim3(qgrid), dim3(256), 0, st, x, nbc, nblocks, ld,
+                         ext_partials, ext_npart, gs, 0, codes, scales);
+    else
+      hipLaunchKernelGGL(quantize_kernel<T>, dim3(qgrid), dim3(256), 0, st, x, nbc, nblocks, ld,
+                         (const float*)nullptr, 0u, gs, 1, codes, scales);
+    launch_end(s1, st);
   }
-  count_launch();
   return hipGetLastError() == hipSuccess ? 0 : 7;
 }
 

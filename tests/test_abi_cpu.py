@@ -147,3 +147,23 @@ def test_valid_calls_report_missing_device_and_launch_nothing():
     assert m.lib.nvfp4_mlp_gu_act(_t(), _t(), _t(), 4, 128, 128, _t(), FAKE, ctypes.byref(big), None) == m.ERR_DEVICE
     assert m.lib.nvfp4_mlp_down(_t(), _t(), 4, 128, 64, FAKE, m.F32, 64, FAKE, ctypes.byref(big), None) == m.ERR_DEVICE
     assert m.lib.nvfp4_launch_count() == before
+
+
+def test_timing_window_validation():
+    lib = m.lib
+    n, d, ms = ctypes.c_int64(), ctypes.c_int64(), ctypes.c_double()
+    out = (ctypes.byref(n), ctypes.byref(d), ctypes.byref(ms))
+    assert lib.nvfp4_timing_begin(-1, 8) == m.ERR_ARG
+    assert lib.nvfp4_timing_begin(5, 8) == m.ERR_ARG
+    assert lib.nvfp4_timing_begin(m.KC_GEMM_GLU, 0) == m.ERR_ARG
+    assert lib.nvfp4_timing_begin(m.KC_GEMM_GLU, (1 << 20) + 1) == m.ERR_ARG
+    assert lib.nvfp4_timing_end(*out) == m.ERR_ARG                      # no window open
+    assert lib.nvfp4_timing_end(None, out[1], out[2]) == m.ERR_NULL
+    st = lib.nvfp4_timing_begin(m.KC_GEMM_GLU, 4)
+    if st == m.OK:                                                       # events available
+        assert lib.nvfp4_timing_begin(m.KC_EXPAND, 4) == m.ERR_ARG      # one window at a time
+        assert lib.nvfp4_timing_end(*out) == m.OK
+        assert (n.value, d.value, ms.value) == (0, 0, 0.0)
+    else:                                                                # no device: events cannot be made
+        assert st == m.ERR_LAUNCH
+        assert lib.nvfp4_timing_end(*out) == m.ERR_ARG
