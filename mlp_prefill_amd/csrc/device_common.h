@@ -159,9 +159,13 @@ __device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
   return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
 }
 
-// SiLU(g) * u in float32.
+// SiLU(g) * u in float32, SiLU(g) = g / (1 + e^-g), with the hardware
+// exp2 and reciprocal (each within about one ulp; the result is within a few
+// ulp of the correctly rounded value).  Large |g| saturate correctly: e^-g
+// overflows to +inf for g << 0 (SiLU -> -0) and underflows to 0 for g >> 0.
 __device__ __forceinline__ float silu_mul(float g, float u) {
-  return g / (1.0f + expf(-g)) * u;
+  const float e = __builtin_amdgcn_exp2f(g * -1.4426950408889634f);
+  return g * __builtin_amdgcn_rcpf(1.0f + e) * u;
 }
 
 // Work-group index remapped so that each XCD (work-groups are dealt

@@ -48,6 +48,7 @@
 namespace nvfp4 {
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
 
 struct GemmArgs {
   const _Float16* a;      // expanded activations, f16 [rows][K] (slot order when grouped)
@@ -153,10 +154,14 @@ struct Cfg {
 template <int WN, int TM, int TN, bool DUAL>
 struct Ctx {
   using C = Cfg<WN, TM, TN, DUAL>;
-  const _Float16* a_src[C::SA];  // global source of each staged 16-B unit (chunk 0 of this split)
-  const uint8_t* b_src[C::SB];
-  const uint8_t* s_src[C::SD];
-  f16x8 ring[2][TM];             // activation fragments of the current and next step
+  // Staging sources: buffer descriptors (wave-uniform, based at this tile's
+  // first row and this split's first chunk) and each lane's byte offset of
+  // every staged unit; a chunk adds a scalar offset.
+  i32x4 ra, rb, ru, rsb, rsu;
+  uint32_t a_off[C::SA];
+  uint32_t b_off[C::SB];
+  uint32_t s_off[C::SD];
+  f16x8 ring[4][TM];             // activation fragments, slot = step % 4
   int lds_row[TM];               // LDS unit index of this lane's activation rows (row * 16)
   int lds_swz;                   // row % 16 of this lane's activation rows
   f32x16 acc[TM][TN];
@@ -170,26 +175,86 @@ struct Lds {
 };
 
 // Copy one K chunk of the work-group's activation and weight tiles straight
-// from global memory into LDS buffer `l` (LDS DMA: no registers, no LDS store
-// instructions).  Lane l of a wave writes the 16 (or 4) bytes at LDS unit
-// base + l, so each unit's global source is chosen to realise the swizzled
-// layout described above.
+// from global memory into one LDS buffer (LDS DMA: no registers, no LDS
+// store instructions).  Lane l of a wave writes the 16 (or 4) bytes at LDS
+// unit base + l, so each unit's global source is chosen to realise the
+// swizzled layout described above.
+//
+// The copies are buffer loads with the LDS bit, issued from inline assembly:
+// lane offsets are fixed, the chunk offset is a scalar operand and M0 (the
+// wave's LDS destination) a scalar, so a chunk costs no vector ALU work.  The
+// compiler does not see these copies, so it neither waits for them nor moves
+// LDS reads across the explicit waits (vmcnt + barrier, below) that order
+// them.  Nothing else in these kernels uses M0 (gfx950 LDS instructions do not
+// read it and no register is indexed dynamically), so clobbering it is safe.
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(size_t)(const __attribute__((address_space(3))) char*)p;
+}
+
+// Raw buffer descriptor over `bytes` bytes at p (gfx9 family: dword3
+// 0x00020000, stride 0), made wave-uniform.
+__device__ __forceinline__ i32x4 buf_desc(const void* p, int64_t bytes) {
+  const uint64_t a = (uint64_t)(size_t)p;
+  const int32_t n = bytes > 0x7FFFFFFF ? 0x7FFFFFFF : (bytes < 0 ? 0 : (int32_t)bytes);
+  i32x4 d;
+  d[0] = __builtin_amdgcn_readfirstlane((int32_t)(uint32_t)a);
+  d[1] = __builtin_amdgcn_readfirstlane((int32_t)((uint32_t)(a >> 32) & 0xFFFFu));
+  d[2] = __builtin_amdgcn_readfirstlane(n);
+  d[3] = 0x00020000;
+  return d;
+}
+
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+// (soff and lds are wave-uniform and made scalar here; the offset goes
+// through a scratch SGPR because a constant would otherwise be printed as a
+// literal, which the instruction does not accept.)
+__device__ __forceinline__ void dma_b128(const i32x4& r, uint32_t voff, uint32_t soff, uint32_t lds) {
+  soff = __builtin_amdgcn_readfirstlane(soff);
+  lds = __builtin_amdgcn_readfirstlane(lds);
+  uint32_t t;
+  asm volatile("s_mov_b32 m0, %[l]\n\ts_mov_b32 %[t], %[so]\n\ts_nop 0\n\tbuffer_load_dwordx4 %[vo], %[r], %[t] offen lds"
+               : [t] "=&s"(t) : [vo] "v"(voff), [r] "s"(r), [so] "s"(soff), [l] "s"(lds) : "memory", "m0");
+}
+__device__ __forceinline__ void dma_b32(const i32x4& r, uint32_t voff, uint32_t soff, uint32_t lds) {
+  soff = __builtin_amdgcn_readfirstlane(soff);
+  lds = __builtin_amdgcn_readfirstlane(lds);
+  uint32_t t;
+  asm volatile("s_mov_b32 m0, %[l]\n\ts_mov_b32 %[t], %[so]\n\ts_nop 0\n\tbuffer_load_dword %[vo], %[r], %[t] offen lds"
+               : [t] "=&s"(t) : [vo] "v"(voff), [r] "s"(r), [so] "s"(soff), [l] "s"(lds) : "memory", "m0");
+}
+#pragma clang diagnostic pop
+
+// la / lb / ls: this wave's LDS byte address in the buffer's activation,
+// weight-code and scale arrays.
 template <int WN, int TM, int TN, bool DUAL>
-__device__ __forceinline__ void stage_dma(const Ctx<WN, TM, TN, DUAL>& x, const Lds& l, int64_t chunk) {
+__device__ __forceinline__ void stage_dma(const Ctx<WN, TM, TN, DUAL>& x, uint32_t la, uint32_t lb, uint32_t ls,
+                                          int64_t chunk) {
   using C = Cfg<WN, TM, TN, DUAL>;
-#if defined(__HIP_DEVICE_COMPILE__)   // the LDS DMA builtin exists only in the device pass
-  const int wbase = (threadIdx.x >> 6) * 64;
+  const uint32_t ca = (uint32_t)chunk * 256u, cb = (uint32_t)chunk * 64u, cs = (uint32_t)chunk * 8u;
 #pragma unroll
-  for (int u = 0; u < C::SA; ++u)
-    __builtin_amdgcn_global_load_lds(x.a_src[u] + chunk * 128, l.a + u * C::NT + wbase, 16, 0, 0);
+  for (int u = 0; u < C::SA; ++u) dma_b128(x.ra, x.a_off[u], ca, la + u * C::NT * 16);
 #pragma unroll
-  for (int u = 0; u < C::SB; ++u)
-    __builtin_amdgcn_global_load_lds(x.b_src[u] + chunk * 64, l.b + u * C::NT + wbase, 16, 0, 0);
+  for (int u = 0; u < C::SB; ++u)   // units 0 .. 2TN-1 hold gate rows, the rest up rows
+    dma_b128((DUAL && u >= 2 * TN) ? x.ru : x.rb, x.b_off[u], cb, lb + u * C::NT * 16);
 #pragma unroll
-  for (int u = 0; u < C::SD; ++u)
-    __builtin_amdgcn_global_load_lds(x.s_src[u] + chunk * 8, reinterpret_cast<uint32_t*>(l.s) + u * C::NT + wbase,
-                                     4, 0, 0);
-#endif
+  for (int u = 0; u < C::SD; ++u)   // units 0 .. TN-1 hold gate rows
+    dma_b32((DUAL && u >= TN) ? x.rsu : x.rsb, x.s_off[u], cs, ls + u * C::NT * 4);
+}
+
+// Wait until at most `later` chunks' copies of this wave are in flight (all
+// older ones have landed in LDS), then synchronise the work-group: after it,
+// every wave's share of those chunks is visible and every wave has finished
+// reading the buffer the next copy overwrites.
+template <int PER, int MAXLATER>
+__device__ __forceinline__ void ring_wait(int64_t later) {
+  if (MAXLATER >= 2 && later >= 2)
+    asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" : : "n"(2 * PER) : "memory");
+  else if (MAXLATER >= 1 && later >= 1)
+    asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" : : "n"(PER) : "memory");
+  else
+    asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" : : : "memory");
+  __builtin_amdgcn_sched_barrier(0);
 }
 
 // Packed weight fragment of LDS row `row` for this lane's K half.
@@ -247,16 +312,16 @@ __device__ __forceinline__ void pipe_step(Ctx<WN, TM, TN, DUAL>& x, const Lds& l
   constexpr int NMFMA = TM * TN * (DUAL ? 2 : 1);
   constexpr int NVALU = TN * (DUAL ? 2 : 1) * 9;
   if constexpr (S < 7) {
-    read_a<S + 1, (S + 1) & 1>(x, l);
+    read_a<S + 1, (S + 1) % 4>(x, l);
     expand_b<TN, DUAL, S + 1>(f, e_nxt);
   }
 #pragma unroll
   for (int i = 0; i < TM; ++i)
 #pragma unroll
     for (int j = 0; j < TN; ++j) {
-      x.acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(x.ring[S & 1][i], e_cur.b[j], x.acc[i][j], 0, 0, 0);
+      x.acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(x.ring[S % 4][i], e_cur.b[j], x.acc[i][j], 0, 0, 0);
       if constexpr (DUAL)
-        x.accu[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(x.ring[S & 1][i], e_cur.u[j], x.accu[i][j], 0, 0, 0);
+        x.accu[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(x.ring[S % 4][i], e_cur.u[j], x.accu[i][j], 0, 0, 0);
     }
   interleave_hint<(S < 7 ? TM : 0), NMFMA, (S < 7 ? (NVALU + NMFMA - 1) / NMFMA : 0)>();
 }
@@ -278,6 +343,61 @@ __device__ __forceinline__ void run_chunk(Ctx<WN, TM, TN, DUAL>& x, const Lds& l
   pipe_step<7>(x, l, f, e1, e0);
 }
 
+// ---- the cross-chunk pipeline (two LDS buffers) ---------------------------------------
+// Step S of chunk c (buffer lc; chunk c+1 lives in ln): the MFMAs of step S
+// use activation slot S%4 and the expanded weights e_cur, while the
+// activations of step S+2 are read (from ln for S >= 6) and the weights of
+// step S+1 are expanded (chunk c+1's first step for S = 7).  At S = 6 the
+// work-group synchronises once: chunk c+1's copy has landed (vmcnt) and
+// every wave has finished reading lc (lgkmcnt: the reads for steps 6 and 7
+// were issued at steps 4 and 5), so the copy of chunk c+2 goes into lc and
+// chunk c+1's packed weights are read from ln.  No step waits on a chunk
+// boundary.  Reads of ln past the last chunk fetch stale data that is never
+// used.
+template <int S, int WN, int TM, int TN, bool DUAL>
+__device__ __forceinline__ void xstep(Ctx<WN, TM, TN, DUAL>& x, const Lds& lc, const Lds& ln,
+                                      const BPack<TN, DUAL>& fc, BPack<TN, DUAL>& fn, BExp<TN, DUAL>& e_cur,
+                                      BExp<TN, DUAL>& e_nxt, bool refill, int64_t chunk2, uint32_t da, uint32_t db,
+                                      uint32_t ds) {
+  constexpr int NMFMA = TM * TN * (DUAL ? 2 : 1);
+  constexpr int NVALU = TN * (DUAL ? 2 : 1) * 9;
+  constexpr int NDS = TM + (S == 6 ? 3 * TN * (DUAL ? 2 : 1) : 0);
+  if constexpr (S == 6) {
+    asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" : : : "memory");
+    __builtin_amdgcn_sched_barrier(0);
+    if (refill) stage_dma(x, da, db, ds, chunk2);
+    read_b<WN, TM, TN, DUAL>(ln, fn);
+  }
+  if constexpr (S + 2 < 8) read_a<S + 2, (S + 2) % 4>(x, lc);
+  else read_a<S - 6, (S + 2) % 4>(x, ln);
+  if constexpr (S + 1 < 8) expand_b<TN, DUAL, S + 1>(fc, e_nxt);
+  else expand_b<TN, DUAL, 0>(fn, e_nxt);
+#pragma unroll
+  for (int i = 0; i < TM; ++i)
+#pragma unroll
+    for (int j = 0; j < TN; ++j) {
+      x.acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(x.ring[S % 4][i], e_cur.b[j], x.acc[i][j], 0, 0, 0);
+      if constexpr (DUAL)
+        x.accu[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(x.ring[S % 4][i], e_cur.u[j], x.accu[i][j], 0, 0, 0);
+    }
+  interleave_hint<NDS, NMFMA, (NVALU + NMFMA - 1) / NMFMA>();
+}
+
+template <int WN, int TM, int TN, bool DUAL>
+__device__ __forceinline__ void xchunk(Ctx<WN, TM, TN, DUAL>& x, const Lds& lc, const Lds& ln,
+                                       const BPack<TN, DUAL>& fc, BPack<TN, DUAL>& fn, BExp<TN, DUAL>& e0,
+                                       BExp<TN, DUAL>& e1, bool refill, int64_t chunk2, uint32_t da, uint32_t db,
+                                       uint32_t ds) {
+  xstep<0>(x, lc, ln, fc, fn, e0, e1, refill, chunk2, da, db, ds);
+  xstep<1>(x, lc, ln, fc, fn, e1, e0, refill, chunk2, da, db, ds);
+  xstep<2>(x, lc, ln, fc, fn, e0, e1, refill, chunk2, da, db, ds);
+  xstep<3>(x, lc, ln, fc, fn, e1, e0, refill, chunk2, da, db, ds);
+  xstep<4>(x, lc, ln, fc, fn, e0, e1, refill, chunk2, da, db, ds);
+  xstep<5>(x, lc, ln, fc, fn, e1, e0, refill, chunk2, da, db, ds);
+  xstep<6>(x, lc, ln, fc, fn, e0, e1, refill, chunk2, da, db, ds);
+  xstep<7>(x, lc, ln, fc, fn, e1, e0, refill, chunk2, da, db, ds);
+}
+
 // Tile shape of the large-batch kernels (rows per wave) and the number of
 // work-groups the register budget must leave room for on one CU.
 #ifndef NVFP4_GLU_TM
@@ -289,19 +409,40 @@ __device__ __forceinline__ void run_chunk(Ctx<WN, TM, TN, DUAL>& x, const Lds& l
 #ifndef NVFP4_MIN_WG_PER_CU
 #define NVFP4_MIN_WG_PER_CU 2
 #endif
+// Work-groups the split-K plan of the store epilogue aims for.
+#ifndef NVFP4_SPLIT_TARGET
+#define NVFP4_SPLIT_TARGET 768
+#endif
+// Waves per work-group of the large-batch kernels (side by side in N).
+#ifndef NVFP4_GLU_WN
+#define NVFP4_GLU_WN 4
+#endif
+#ifndef NVFP4_STORE_WN
+#define NVFP4_STORE_WN 4
+#endif
+// LDS buffers of the chunk ring (2 to 4).
+#ifndef NVFP4_GLU_STAGES
+#define NVFP4_GLU_STAGES 2
+#endif
+#ifndef NVFP4_STORE_STAGES
+#define NVFP4_STORE_STAGES 2
+#endif
+#ifndef NVFP4_GLU_MINWG
+#define NVFP4_GLU_MINWG NVFP4_MIN_WG_PER_CU
+#endif
+#ifndef NVFP4_STORE_MINWG
+#define NVFP4_STORE_MINWG NVFP4_MIN_WG_PER_CU
+#endif
 
-template <int WN, int TM, int TN, bool DUAL, bool GROUPED, int EPI>
-__global__ void __launch_bounds__(WN * 64, NVFP4_MIN_WG_PER_CU) gemm_kernel(GemmArgs p) {
+template <int WN, int TM, int TN, bool DUAL, bool GROUPED, int EPI, int NS, int MINWG>
+__global__ void __launch_bounds__(WN * 64, MINWG) gemm_kernel(GemmArgs p) {
   using C = Cfg<WN, TM, TN, DUAL>;
   constexpr int BM = C::BM;
   constexpr int BN = C::BN;
   __shared__ float red[WN];
-  __shared__ f16x8 lds_a0[C::LDS_A];
-  __shared__ f16x8 lds_a1[C::LDS_A];
-  __shared__ u32x4 lds_b0[C::LDS_B];
-  __shared__ u32x4 lds_b1[C::LDS_B];
-  __shared__ uint2 lds_s0[C::NB];
-  __shared__ uint2 lds_s1[C::NB];
+  __shared__ f16x8 lds_a[NS][C::LDS_A];
+  __shared__ u32x4 lds_b[NS][C::LDS_B];
+  __shared__ uint2 lds_s[NS][C::NB];
   const int lane = threadIdx.x & 63;
   const int wn = threadIdx.x >> 6;
   const int r32 = lane & 31, hh = lane >> 5;
@@ -353,35 +494,43 @@ __global__ void __launch_bounds__(WN * 64, NVFP4_MIN_WG_PER_CU) gemm_kernel(Gemm
 
   // ---- staging sources (rows past the end are clamped; never stored) ----------
   Ctx<WN, TM, TN, DUAL> x;
+  {
+    const int64_t a_rows = (m_end < m0 + BM ? m_end : m0 + BM) - m0;
+    const int64_t b_rows = (p.N < n0 + BN ? p.N : n0 + BN) - n0;
+    x.ra = buf_desc(p.a + m0 * K + c_begin * 128, a_rows * K * 2 - c_begin * 256);
+    x.rb = buf_desc(p.b_codes + wstride_c + n0 * kb + c_begin * 64, b_rows * kb - c_begin * 64);
+    x.rsb = buf_desc(p.b_scales + wstride_s + n0 * ks + c_begin * 8, b_rows * ks - c_begin * 8);
+    if constexpr (DUAL) {
+      x.ru = buf_desc(p.u_codes + wstride_c + n0 * kb + c_begin * 64, b_rows * kb - c_begin * 64);
+      x.rsu = buf_desc(p.u_scales + wstride_s + n0 * ks + c_begin * 8, b_rows * ks - c_begin * 8);
+    } else {
+      x.ru = x.rb;
+      x.rsu = x.rsb;
+    }
+  }
 #pragma unroll
   for (int u = 0; u < C::SA; ++u) {
     const int pu = u * C::NT + threadIdx.x;
     const int row = pu >> 4, slot = pu & 15;
     int64_t m = m0 + row;
     if (m > m_end - 1) m = m_end - 1;
-    x.a_src[u] = p.a + m * K + c_begin * 128 + ((slot ^ (row & 15)) << 3);
+    x.a_off[u] = (uint32_t)(((m - m0) * K + ((slot ^ (row & 15)) << 3)) * 2);
   }
-  auto wrow = [&](int rho, const uint8_t*& codes, const uint8_t*& scales) {
-    const bool up = DUAL && rho >= BN;
-    int64_t n = n0 + (up ? rho - BN : rho);
+  auto wrow = [&](int rho) -> int64_t {          // row of this tile's gate (or up) matrix, clamped
+    int64_t n = n0 + ((DUAL && rho >= BN) ? rho - BN : rho);
     if (n > p.N - 1) n = p.N - 1;
-    codes = (up ? p.u_codes : p.b_codes) + wstride_c + n * kb + c_begin * 64;
-    scales = (up ? p.u_scales : p.b_scales) + wstride_s + n * ks + c_begin * 8;
+    return n - n0;
   };
 #pragma unroll
   for (int u = 0; u < C::SB; ++u) {
     const int pu = u * C::NT + threadIdx.x;      // LDS unit: row pu/4, slot pu%4
     const int row = pu >> 2, slot = pu & 3;
-    const uint8_t *cd, *sc;
-    wrow(row, cd, sc);
-    x.b_src[u] = cd + ((slot ^ ((row >> 2) & 3)) << 4);
+    x.b_off[u] = (uint32_t)(wrow(row) * kb + ((slot ^ ((row >> 2) & 3)) << 4));
   }
 #pragma unroll
   for (int u = 0; u < C::SD; ++u) {
     const int pu = u * C::NT + threadIdx.x;      // LDS dword: row pu/2, half pu%2
-    const uint8_t *cd, *sc;
-    wrow(pu >> 1, cd, sc);
-    x.s_src[u] = sc + ((pu & 1) << 2);
+    x.s_off[u] = (uint32_t)(wrow(pu >> 1) * ks + ((pu & 1) << 2));
   }
 #pragma unroll
   for (int i = 0; i < TM; ++i) x.lds_row[i] = (i * 32 + r32) * 16;
@@ -396,22 +545,48 @@ __global__ void __launch_bounds__(WN * 64, NVFP4_MIN_WG_PER_CU) gemm_kernel(Gemm
         if constexpr (DUAL) x.accu[i][j][r] = 0.f;
       }
 
-  // ---- main loop: chunk c+1 streams into the other LDS buffer (DMA) while
-  // chunk c runs; one barrier per chunk -----------------------------------------
-  const Lds l0{lds_a0, lds_b0, lds_s0}, l1{lds_a1, lds_b1, lds_s1};
-  stage_dma(x, l0, 0);
-  __builtin_amdgcn_s_waitcnt(0);     // vmcnt(0): this wave's copies have landed
-  __builtin_amdgcn_s_barrier();
-  for (int64_t c = 0; c < nch; c += 2) {
-    if (c + 1 < nch) stage_dma(x, l1, c + 1);
-    run_chunk(x, l0);
-    __builtin_amdgcn_s_waitcnt(0);
-    __builtin_amdgcn_s_barrier();
-    if (c + 1 >= nch) break;
-    if (c + 2 < nch) stage_dma(x, l0, c + 2);
-    run_chunk(x, l1);
-    __builtin_amdgcn_s_waitcnt(0);
-    __builtin_amdgcn_s_barrier();
+  // ---- main loop ------------------------------------------------------------------
+  const uint32_t wb = (uint32_t)__builtin_amdgcn_readfirstlane(threadIdx.x >> 6) * 64u;
+  auto la = [&](int st) { return lds_addr(lds_a[st]) + wb * 16u; };
+  auto lb = [&](int st) { return lds_addr(lds_b[st]) + wb * 16u; };
+  auto ls = [&](int st) { return lds_addr(lds_s[st]) + wb * 4u; };
+  if constexpr (NS == 2) {
+    // Two buffers, pipelined across chunk boundaries (xstep above).
+    const Lds l0{lds_a[0], lds_b[0], lds_s[0]}, l1{lds_a[1], lds_b[1], lds_s[1]};
+    BPack<TN, DUAL> f0, f1;
+    BExp<TN, DUAL> e0, e1;
+    stage_dma(x, la(0), lb(0), ls(0), 0);
+    asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" : : : "memory");
+    __builtin_amdgcn_sched_barrier(0);
+    if (nch > 1) stage_dma(x, la(1), lb(1), ls(1), 1);
+    read_b<WN, TM, TN, DUAL>(l0, f0);
+    read_a<0, 0>(x, l0);
+    read_a<1, 1>(x, l0);
+    expand_b<TN, DUAL, 0>(f0, e0);
+    for (int64_t c = 0; c < nch; c += 2) {
+      xchunk(x, l0, l1, f0, f1, e0, e1, c + 2 < nch, c + 2, la(0), lb(0), ls(0));
+      if (c + 1 >= nch) break;
+      xchunk(x, l1, l0, f1, f0, e0, e1, c + 3 < nch, c + 3, la(1), lb(1), ls(1));
+    }
+  } else {
+    // NS-buffer ring: the copies of chunks c+1 .. c+NS-2 stay in flight while
+    // chunk c is consumed; the buffer of chunk c-1 is refilled with chunk
+    // c+NS-1 right after the barrier that ends its last reads.
+    static_assert(NS >= 3 && NS <= 4, "ring of 3 or 4 buffers");
+    constexpr int PER = C::SA + C::SB + C::SD;      // copies per wave per chunk
+    static_assert((NS - 2) * PER <= 63, "vmcnt range");
+#pragma unroll
+    for (int st = 0; st < NS - 1; ++st)
+      if (st < nch) stage_dma(x, la(st), lb(st), ls(st), st);
+    int sc = 0;                                      // buffer of chunk c
+    for (int64_t c = 0; c < nch; ++c) {
+      const int64_t later = (nch - 1 - c) < (NS - 2) ? (nch - 1 - c) : (NS - 2);
+      ring_wait<PER, NS - 2>(later);
+      const int sf = sc == 0 ? NS - 1 : sc - 1;      // buffer of chunk c-1
+      if (c + NS - 1 < nch) stage_dma(x, la(sf), lb(sf), ls(sf), c + NS - 1);
+      run_chunk(x, Lds{lds_a[sc], lds_b[sc], lds_s[sc]});
+      sc = sc == NS - 1 ? 0 : sc + 1;
+    }
   }
 
   // ---- epilogue ---------------------------------------------------------------------
@@ -452,6 +627,176 @@ __global__ void __launch_bounds__(WN * 64, NVFP4_MIN_WG_PER_CU) gemm_kernel(Gemm
   }
 }
 
+// ---- small batches (M <= 32): the contraction is a weight stream -------------------
+// A work-group is kSkWaves waves on the same 32 weight rows (x2 with the
+// gate/up pair); each wave takes its own slice of the work-group's K range and
+// the slices' sums are added through LDS in wave order (deterministic).
+// Packed weights and the f16 activation fragments go from global memory
+// straight into registers kSkDepth chunks ahead of their MFMAs -- no LDS
+// staging and no barrier in the main loop -- so each wave keeps several KiB of
+// loads in flight, which is what a weight stream needs to approach the HBM
+// bandwidth.  The MFMA tile is 32 rows, so any M <= 32 costs the same.
+constexpr int kSkWaves = 4;
+constexpr int kSkDepth = 2;
+
+template <bool DUAL>
+struct SkSlot {
+  Frag b, u;
+  f16x8 a[8];
+};
+
+// Raw buffer resource over `bytes` bytes at p (gfx9 family: dword3 0x00020000).
+// Reads past the range return zero.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* p, int64_t bytes) {
+  const int32_t n = bytes > 0x7FFFFFFF ? 0x7FFFFFFF : (bytes < 0 ? 0 : (int32_t)bytes);
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), 0, n, 0x00020000);
+}
+
+__device__ __forceinline__ f16x8 frag_expand_rt(const Frag& f, int s) {
+  const uint32_t w = (s < 4) ? f.c0[s & 3] : f.c1[s & 3];
+  return expand8(w, (f.s >> (8 * (s >> 1))) & 0xFFu);
+}
+
+template <bool DUAL, int EPI>
+__global__ void __launch_bounds__(kSkWaves * 64) skinny_kernel(GemmArgs p) {
+  constexpr int NM = DUAL ? 2 : 1;
+  __shared__ float red[kSkWaves * NM * 16 * 64];
+  __shared__ float redmax[kSkWaves];
+  const int lane = threadIdx.x & 63;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave-uniform: keeps the loop scalar
+  const int r32 = lane & 31, hh = lane >> 5;
+  const uint32_t n_tile = blockIdx.x % p.n_tiles;
+  const uint32_t split = blockIdx.x / p.n_tiles;
+  const int64_t n0 = (int64_t)n_tile * 32;
+  const int64_t K = p.K, kb = K >> 1, ks = K >> 4;
+  const int64_t total = K >> 7;
+  const int64_t cs0 = (int64_t)split * p.chunks_per_split;
+  int64_t cs1 = cs0 + p.chunks_per_split;
+  if (cs1 > total) cs1 = total;
+  const int64_t len = cs1 > cs0 ? cs1 - cs0 : 0;
+  const int64_t c0 = cs0 + (len * w) / kSkWaves;
+  const int64_t n = cs0 + (len * (w + 1)) / kSkWaves - c0;   // chunks of this wave (wave-uniform, may be 0)
+
+  // Buffer loads (one wave-uniform resource per operand, based at this tile's
+  // first row): 32-bit lane offsets, the chunk offset in the scalar operand.
+  // They are intrinsic calls, which the compiler keeps where they are written,
+  // so the register ring below stays a software pipeline.
+  const int64_t nrow = (p.N - n0) < 32 ? (p.N - n0) : 32;
+  const int32_t wr = r32 < nrow ? r32 : (int32_t)nrow - 1;
+  const int32_t arow = r32 < p.M ? r32 : (int32_t)p.M - 1;   // rows past M: finite, never stored
+  const int64_t cbase = n0 * kb + c0 * 64, sbase = n0 * ks + c0 * 8;
+  const __amdgpu_buffer_rsrc_t rb = make_rsrc(p.b_codes + cbase, nrow * kb - c0 * 64);
+  const __amdgpu_buffer_rsrc_t rbs = make_rsrc(p.b_scales + sbase, nrow * ks - c0 * 8);
+  __amdgpu_buffer_rsrc_t ru = rb, rus = rbs;
+  if constexpr (DUAL) {
+    ru = make_rsrc(p.u_codes + cbase, nrow * kb - c0 * 64);
+    rus = make_rsrc(p.u_scales + sbase, nrow * ks - c0 * 8);
+  }
+  const __amdgpu_buffer_rsrc_t ra = make_rsrc(p.a + c0 * 128, (int64_t)p.M * K * 2 - c0 * 256);
+  const int32_t vo_c = wr * (int32_t)kb + hh * 32;
+  const int32_t vo_s = wr * (int32_t)ks + hh * 4;
+  const int32_t vo_a = arow * (int32_t)K * 2 + hh * 128;
+
+  auto load = [&](int64_t c, SkSlot<DUAL>& sl) {
+    const int32_t cc = (int32_t)c * 64, csc = (int32_t)c * 8, ca = (int32_t)c * 256;
+    sl.b.c0 = __builtin_amdgcn_raw_buffer_load_b128(rb, vo_c, cc, 0);
+    sl.b.c1 = __builtin_amdgcn_raw_buffer_load_b128(rb, vo_c + 16, cc, 0);
+    sl.b.s = __builtin_amdgcn_raw_buffer_load_b32(rbs, vo_s, csc, 0);
+    if constexpr (DUAL) {
+      sl.u.c0 = __builtin_amdgcn_raw_buffer_load_b128(ru, vo_c, cc, 0);
+      sl.u.c1 = __builtin_amdgcn_raw_buffer_load_b128(ru, vo_c + 16, cc, 0);
+      sl.u.s = __builtin_amdgcn_raw_buffer_load_b32(rus, vo_s, csc, 0);
+    }
+#pragma unroll
+    for (int s = 0; s < 8; ++s) {
+      const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(ra, vo_a + 16 * s, ca, 0);
+      sl.a[s] = __builtin_bit_cast(f16x8, v);
+    }
+  };
+
+  f32x16 acc, accu;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    acc[r] = 0.f;
+    accu[r] = 0.f;
+  }
+  auto compute = [&](const SkSlot<DUAL>& sl) {
+#pragma unroll
+    for (int s = 0; s < 8; ++s) {
+      acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(sl.a[s], frag_expand_rt(sl.b, s), acc, 0, 0, 0);
+      if constexpr (DUAL)
+        accu = __builtin_amdgcn_mfma_f32_32x32x16_f16(sl.a[s], frag_expand_rt(sl.u, s), accu, 0, 0, 0);
+    }
+  };
+
+  // Every load is unconditional (chunk indices clamped to the wave's last
+  // chunk: the tail re-reads it from L2) so that the loads stay in issue order
+  // and each MFMA waits only for the loads of its own chunk.
+  if (n > 0) {
+    const int64_t last = n - 1;
+    SkSlot<DUAL> ring[kSkDepth];
+#pragma unroll
+    for (int d = 0; d < kSkDepth; ++d) {
+      load(d < last ? d : last, ring[d]);
+      __builtin_amdgcn_sched_barrier(0);   // slots issue in order: slot 0 is the oldest
+    }
+    for (int64_t c = 0; c < n; c += kSkDepth) {
+#pragma unroll
+      for (int d = 0; d < kSkDepth; ++d) {
+        if (c + d < n) compute(ring[d]);
+        __builtin_amdgcn_sched_barrier(0);   // keep the refill after the MFMAs that read the slot
+        const int64_t nx = c + d + kSkDepth;
+        load(nx < last ? nx : last, ring[d]);
+        __builtin_amdgcn_sched_barrier(0);   // and before the next slot's MFMAs
+      }
+    }
+  }
+
+  // ---- add the waves' partial tiles (wave order), then the epilogue ----------------
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    red[((w * NM) * 16 + r) * 64 + lane] = acc[r];
+    if constexpr (DUAL) red[((w * NM + 1) * 16 + r) * 64 + lane] = accu[r];
+  }
+  __syncthreads();
+  const float alpha = p.a_gs[0] * p.b_gs[0];
+  float alpha_u = 0.f;
+  if constexpr (DUAL) alpha_u = p.a_gs[0] * p.u_gs[0];
+  float hmax = 0.f;
+#pragma unroll
+  for (int i = 0; i < 1024 / (kSkWaves * 64); ++i) {
+    const int e = (int)threadIdx.x + i * kSkWaves * 64;
+    const int r = e >> 6, l = e & 63;
+    float g = 0.f, u = 0.f;
+#pragma unroll
+    for (int w2 = 0; w2 < kSkWaves; ++w2) {
+      g += red[((w2 * NM) * 16 + r) * 64 + l];
+      if constexpr (DUAL) u += red[((w2 * NM + 1) * 16 + r) * 64 + l];
+    }
+    const int64_t row = 8 * (r >> 2) + 4 * (l >> 5) + (r & 3);
+    const int64_t col = n0 + (l & 31);
+    if (row < p.M && col < p.N) {
+      if constexpr (EPI == EPI_GLU) {
+        const float hv = silu_mul(g * alpha, u * alpha_u);
+        p.h[row * p.N + col] = hv;
+        hmax = fmaxf(hmax, fabsf(hv));
+      } else if (p.splits > 1) {
+        p.split_out[((int64_t)split * p.M + row) * p.N + col] = g;
+      } else {
+        const float v = g * alpha;
+        if (p.c_bf16)
+          reinterpret_cast<uint16_t*>(p.c)[row * p.ldc + col] = (uint16_t)f32_to_bf16_bits(v);
+        else
+          reinterpret_cast<float*>(p.c)[row * p.ldc + col] = v;
+      }
+    }
+  }
+  if constexpr (EPI == EPI_GLU) {
+    hmax = block_max(hmax, redmax);
+    if (threadIdx.x == 0) p.partials[blockIdx.x] = hmax;
+  }
+}
+
 // out[m][n] = (sum over splits, in split order) * gs_a * gs_b[expert of slot m].
 __global__ void __launch_bounds__(256) splitk_reduce_kernel(const float* __restrict__ part, uint32_t splits,
                                                             int64_t M, int64_t N, const float* a_gs,
@@ -476,9 +821,10 @@ __global__ void __launch_bounds__(256) splitk_reduce_kernel(const float* __restr
 }
 
 // ---- launch configurations ----------------------------------------------------------
-// Large batches: four waves side by side in N, each 128 rows x 32 columns
-// (x2 with the gate/up pair).  Small batches (M <= 32): 32-row tiles, two
-// waves per work-group to spread the weight stream over more work-groups.
+// Large batches: four waves side by side in N, each 32 * TM rows x 32 columns
+// (x2 with the gate/up pair).  Small batches (M <= 32): the weight-stream
+// kernel, 32 weight rows per work-group, K split over its waves (and, for the
+// store epilogue, over work-groups too).
 struct Plan {
   bool small;
   uint32_t m_tiles, n_tiles, splits, chunks_per_split;
@@ -489,25 +835,41 @@ static uint32_t cdiv(int64_t a, int64_t b) { return (uint32_t)((a + b - 1) / b);
 static Plan plan_store(int64_t M, int64_t N, int64_t K, int E, bool grouped) {
   Plan pl{};
   pl.small = !grouped && M <= 32;
-  const int64_t bm = pl.small ? 32 : 32 * NVFP4_STORE_TM;
-  const int64_t bn = pl.small ? 64 : 128;
-  pl.m_tiles = grouped ? cdiv(M, 32 * NVFP4_STORE_TM) + (uint32_t)E : cdiv(M, bm);
-  pl.n_tiles = cdiv(N, bn);
   const uint32_t chunks = (uint32_t)(K / 128);
-  // Split K until there are >= ~3 work-groups per CU, keeping >= 8 chunks per split.
-  const uint32_t tiles = pl.m_tiles * pl.n_tiles;
   uint32_t s = 1;
-  while (s < 8 && tiles * s < 768 && chunks / (s + 1) >= 8) ++s;
+  if (pl.small) {
+    // Weight stream: split K until there are >= 512 work-groups (>= 2 waves
+    // per SIMD), keeping >= 4 chunks per wave.
+    pl.m_tiles = 1;
+    pl.n_tiles = cdiv(N, 32);
+    while (s < 16 && pl.n_tiles * s < 512 && chunks / (s + 1) >= 4u * kSkWaves) ++s;
+  } else {
+    pl.m_tiles = grouped ? cdiv(M, 32 * NVFP4_STORE_TM) + (uint32_t)E : cdiv(M, 32 * NVFP4_STORE_TM);
+    pl.n_tiles = cdiv(N, 32 * NVFP4_STORE_WN);
+    // Split K until there are enough work-groups, keeping >= 8 chunks per split.
+    const uint32_t tiles = pl.m_tiles * pl.n_tiles;
+    while (s < 8 && tiles * s < NVFP4_SPLIT_TARGET && chunks / (s + 1) >= 8) ++s;
+  }
   pl.chunks_per_split = cdiv(chunks, s);
   pl.splits = cdiv(chunks, pl.chunks_per_split);
   return pl;
+}
+
+template <bool DUAL, int EPI>
+static void launch_skinny(const GemmArgs& g, hipStream_t st) {
+  const uint32_t grid = g.n_tiles * g.splits;
+  const int slot = launch_begin(EPI == EPI_GLU ? KC_GEMM_GLU : KC_GEMM_STORE, st);
+  hipLaunchKernelGGL((skinny_kernel<DUAL, EPI>), dim3(grid), dim3(kSkWaves * 64), 0, st, g);
+  launch_end(slot, st);
 }
 
 template <int WN, int TM, int TN, bool DUAL, bool GROUPED, int EPI>
 static void launch_cfg(const GemmArgs& g, hipStream_t st) {
   const uint32_t grid = g.m_tiles * g.n_tiles * g.splits;
   const int slot = launch_begin(EPI == EPI_GLU ? KC_GEMM_GLU : KC_GEMM_STORE, st);
-  hipLaunchKernelGGL((gemm_kernel<WN, TM, TN, DUAL, GROUPED, EPI>), dim3(grid), dim3(WN * 64), 0, st, g);
+  constexpr int NS = EPI == EPI_GLU ? NVFP4_GLU_STAGES : NVFP4_STORE_STAGES;
+  constexpr int MW = EPI == EPI_GLU ? NVFP4_GLU_MINWG : NVFP4_STORE_MINWG;
+  hipLaunchKernelGGL((gemm_kernel<WN, TM, TN, DUAL, GROUPED, EPI, NS, MW>), dim3(grid), dim3(WN * 64), 0, st, g);
   launch_end(slot, st);
 }
 
@@ -575,9 +937,9 @@ int store_launch(Operand a, const int32_t* rows, const int32_t* off, int E, int6
   g.E = E;
   g.m_tiles = pl.m_tiles;
   g.n_tiles = pl.n_tiles;
-  if (grouped) launch_cfg<4, NVFP4_STORE_TM, 1, false, true, EPI_STORE>(g, st);
-  else if (pl.small) launch_cfg<2, 1, 1, false, false, EPI_STORE>(g, st);
-  else launch_cfg<4, NVFP4_STORE_TM, 1, false, false, EPI_STORE>(g, st);
+  if (grouped) launch_cfg<NVFP4_STORE_WN, NVFP4_STORE_TM, 1, false, true, EPI_STORE>(g, st);
+  else if (pl.small) launch_skinny<false, EPI_STORE>(g, st);
+  else launch_cfg<NVFP4_STORE_WN, NVFP4_STORE_TM, 1, false, false, EPI_STORE>(g, st);
   // The reduction always runs (over zero rows when K was not split), so the
   // number of launches never depends on the shape.
   launch_reduce(part, pl.splits, pl.splits > 1 ? M : 0, N, a.gscale, w.gscale, off, E, c, c_bf16, ldc, st);
@@ -586,9 +948,9 @@ int store_launch(Operand a, const int32_t* rows, const int32_t* off, int E, int6
 
 // GLU GEMM.  Workspace: [H float32 M x N][A f16 M x K][partials].
 static uint32_t glu_parts(int64_t M, int64_t N, int E, bool grouped) {
-  if (grouped) return (cdiv(M, 32 * NVFP4_GLU_TM) + (uint32_t)E) * cdiv(N, 128);
-  if (M <= 32) return cdiv(M, 32) * cdiv(N, 64);
-  return cdiv(M, 32 * NVFP4_GLU_TM) * cdiv(N, 128);
+  if (grouped) return (cdiv(M, 32 * NVFP4_GLU_TM) + (uint32_t)E) * cdiv(N, 32 * NVFP4_GLU_WN);
+  if (M <= 32) return cdiv(N, 32);
+  return cdiv(M, 32 * NVFP4_GLU_TM) * cdiv(N, 32 * NVFP4_GLU_WN);
 }
 
 size_t glu_ws_bytes(int64_t M, int64_t N, int64_t K, int E, bool grouped) {
@@ -614,16 +976,16 @@ int glu_launch(Operand a, const int32_t* a_rows, const int32_t* off, int E, int6
   g.chunks_per_split = (uint32_t)(K / 128);
   if (grouped) {
     g.m_tiles = cdiv(M, 32 * NVFP4_GLU_TM) + (uint32_t)E;
-    g.n_tiles = cdiv(N, 128);
-    launch_cfg<4, NVFP4_GLU_TM, 1, true, true, EPI_GLU>(g, st);
+    g.n_tiles = cdiv(N, 32 * NVFP4_GLU_WN);
+    launch_cfg<NVFP4_GLU_WN, NVFP4_GLU_TM, 1, true, true, EPI_GLU>(g, st);
   } else if (M <= 32) {
-    g.m_tiles = cdiv(M, 32);
-    g.n_tiles = cdiv(N, 64);
-    launch_cfg<2, 1, 1, true, false, EPI_GLU>(g, st);
+    g.m_tiles = 1;
+    g.n_tiles = cdiv(N, 32);
+    launch_skinny<true, EPI_GLU>(g, st);
   } else {
     g.m_tiles = cdiv(M, 32 * NVFP4_GLU_TM);
-    g.n_tiles = cdiv(N, 128);
-    launch_cfg<4, NVFP4_GLU_TM, 1, true, false, EPI_GLU>(g, st);
+    g.n_tiles = cdiv(N, 32 * NVFP4_GLU_WN);
+    launch_cfg<NVFP4_GLU_WN, NVFP4_GLU_TM, 1, true, false, EPI_GLU>(g, st);
   }
   if (hipGetLastError() != hipSuccess) return 7;
   return requant_f32_launch(h, M, N, hq_codes, hq_scales, hq_gs, partials, glu_parts(M, N, E, grouped), st);

@@ -48,7 +48,7 @@ def test_gemm_16x256x512_workload():
 
 
 SHAPES = [(1, 64, 128), (5, 320, 384), (31, 128, 256), (33, 512, 256), (200, 384, 640), (130, 1000, 1024),
-          (64, 8, 128)]
+          (64, 8, 128), (7, 100, 256), (32, 1000, 384), (3, 40, 1152), (2, 96, 8192)]
 
 
 @pytest.mark.parametrize("m,n,k", SHAPES, ids=[f"{m}x{n}x{k}" for m, n, k in SHAPES])
