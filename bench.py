@@ -9,8 +9,9 @@ resident in HBM before the timed region; weights are quantised on the device
 beforehand (cold path).
 
 Prints one JSON line.  Extra fields: the 1024-token MLP, the decode-shaped
-T=1 / T=5 MLP (weight-streaming GB/s, cold and hot MALL), the roofline of the
-dominant kernel and the CPU oracle timed on a bounded sample.
+T=1 / T=5 MLP (weight-streaming GB/s, cold and hot MALL), the 4-layer decode
+stack eager and replayed from a HIP graph, the expert-grouped MLP, the
+roofline of the dominant kernel and the CPU oracle timed on a bounded sample.
 """
 import argparse
 import json
@@ -239,6 +240,7 @@ def main():
     extra = {}
     if not args.no_extra:
         extra = extra_lines(m)
+        extra["decode_stack"] = decode_stack_line(m, layers)
 
     result = {
         "metric": METRIC, "value": tflops, "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
@@ -304,6 +306,42 @@ def extra_lines(m):
     out["decode"] = dec
     del lay, scrub_buf
     out["moe"] = moe_line(m)
+    return out
+
+
+def decode_stack_line(m, layers):
+    """One token (T = 1) and five (T = 5) through the 4 stacked full-size layers,
+    eager and replayed from a HIP graph.  The 601.6 MB of weights exceed the
+    256 MB MALL, so every pass streams them from HBM."""
+    log("extra: 4-layer decode stack, eager and HIP graph")
+    wbytes = sum(w.codes.numel() + w.scales.numel() + 4 for lay in layers for w in lay.w)
+    out = {"workload": "mlp_long_prefill_16x1024_4layers weights, T = 1 and T = 5 per pass", "weight_bytes": wbytes}
+    for t in (1, 5):
+        from synthetic import bf16_normal
+        x = m.bf16_from_bits(bf16_normal(99, (t, K_HID)))
+        run = MlpRunner(m, t)
+        ys = [torch.empty((t, K_HID), dtype=torch.bfloat16, device="cuda") for _ in range(2)]
+
+        def stack():
+            cur = x
+            for li, lay in enumerate(layers):
+                run(cur, lay, ys[li % 2])
+                cur = ys[li % 2]
+        eager = float(np.median(time_events(stack, 20)))
+        s = torch.cuda.Stream()
+        s.wait_stream(torch.cuda.current_stream())
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.stream(s):
+            with torch.cuda.graph(g, stream=s):
+                stack()
+        torch.cuda.current_stream().wait_stream(s)
+        torch.cuda.synchronize()
+        graph = float(np.median(time_events(g.replay, 20)))
+        out[f"T{t}"] = {"ms_eager": eager, "ms_graph": graph, "ms_per_layer_graph": graph / len(layers),
+                        "hbm_gbs_graph": wbytes / (graph * 1e-3) / 1e9,
+                        "frac_hbm_peak_graph": wbytes / (graph * 1e-3) / 1e9 / PEAK_HBM_GBS,
+                        "launches_per_pass": 8 * len(layers)}
+        del g
     return out
 
 
