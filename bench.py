@@ -346,6 +346,152 @@ def decode_stack_line(m, layers):
 
 
 def moe_line(m):
+    """Expert-grouped MoE layer on the device: 4096 tokens routed top-8 over 64
+    experts (hidden 4096, expert width 2048): route, quantise, grouped gate/up +
+    SiLU*up + requantise, grouped down, combine."""
+    from synthetic import WORKLOADS, bf16_normal, expert_seeds, router_logits
+    p = WORKLOADS["moe_4096_top8_of_64"].params
+    t, e, top, k, i = p["T"], p["E"], p["topk"], p["K"], p["I"]
+    log("extra: expert-grouped MoE layer (64 experts, top-8), device routing and combine")
+    mats = [[], [], []]
+    for x in range(e):
+        for j, (sd, shp) in enumerate(zip(expert_seeds(p["expert_seed0"], x), [(i, k), (i, k), (k, i)])):
+            w = m.bf16_from_bits(bf16_normal(sd, shp, sigma=0.02))
+            q = m.NVFP4.empty(*shp)
+            m.nvfp4_quantize_act(w, q)
+            mats[j].append(q)
+    wg, wu, wd = (m.NVFP4.stack(v) for v in mats)
+    del mats
+    x = m.bf16_from_bits(bf16_normal(p["x_seed"], (t, k)))
+    logits = torch.from_numpy(router_logits(p["router_seed"], t, e)).cuda()
+    slots = t * top
+    offs = torch.empty(e + 1, dtype=torch.int32, device="cuda")
+    rows = torch.empty(slots, dtype=torch.int32, device="cuda")
+    slot_of = torch.empty((t, top), dtype=torch.int32, device="cuda")
+    cw = torch.empty((t, top), dtype=torch.float32, device="cuda")
+    ws_r = torch.empty(max(m.moe_route_ws_bytes(t, e, top), 256), dtype=torch.uint8, device="cuda")
+    xq = m.NVFP4.empty(t, k)
+    hq = m.NVFP4.empty(slots, i)
+    ys = torch.empty((slots, k), dtype=torch.bfloat16, device="cuda")
+    y = torch.empty((t, k), dtype=torch.bfloat16, device="cuda")
+    ws_q = torch.empty(m.ws_bytes_quantize(t, k), dtype=torch.uint8, device="cuda")
+    ws_g = torch.empty(max(m.grouped_ws_bytes(slots, i, k, e, m.EPI_SILU_MUL_REQUANT), 256), dtype=torch.uint8,
+                       device="cuda")
+    ws_d = torch.empty(max(m.grouped_ws_bytes(slots, k, i, e, m.EPI_STORE), 256), dtype=torch.uint8, device="cuda")
+
+    def layer():
+        m.nvfp4_moe_route(logits, top, offs, rows, slot_of, cw, ws=ws_r)
+        m.nvfp4_quantize_act(x, xq, ws=ws_q)
+        m.nvfp4_grouped_gemm(xq, rows, offs, wg, wu, out_q=hq, epilogue=m.EPI_SILU_MUL_REQUANT, m=slots, ws=ws_g)
+        m.nvfp4_grouped_gemm(hq, None, offs, wd, out=ys, epilogue=m.EPI_STORE, ws=ws_d)
+        m.nvfp4_moe_combine(ys, slot_of, cw, y)
+
+    before = m.launch_count()
+    layer()
+    launches = m.launch_count() - before
+    ms = float(np.median(time_events(layer, 10)))
+    parts = {}
+    for name, kc in (("route", m.KC_ROUTE), ("combine", m.KC_COMBINE)):
+        m.nvfp4_timing_begin(kc, 64)
+        for _ in range(5):
+            layer()
+        n, _, tot = m.nvfp4_timing_end()
+        parts[f"{name}_ms"] = tot / 5
+    flops = mlp_flops(slots, k, i)
+    tf = flops / (ms * 1e-3) / 1e12
+    comb_bytes = slots * k * 2 + t * k * 2 + t * top * 8
+    return {"workload": "moe_4096_top8_of_64", "ms": ms, "tflops": tf, "frac_f16_peak": tf / PEAK_F16_TFLOPS,
+            "tokens_per_s": t / (ms * 1e-3), "slots": slots, "launches_per_call": launches, **parts,
+            "combine_gbs": comb_bytes / (parts["combine_ms"] * 1e-3) / 1e9,
+            "note": "ms covers routing, quantisation, both grouped GEMMs and the combine; TFLOP/s counts the "
+                    "6*slots*K*I of the expert MLPs"}
+
+
+def extra_lines(m):
+    """1024-token MLP and decode-shaped T=1/T=5 MLP (separate weights, as their workloads define)."""
+    from synthetic import WORKLOADS, bf16_normal, outlier_channels
+    out = {}
+    p3 = WORKLOADS["mlp_prefill_1024x5120x17408"].params
+    log("extra: 1024-token MLP")
+    lay = Layer(m, (p3["wg_seed"], p3["wu_seed"], p3["wd_seed"]))
+    x = m.bf16_from_bits(bf16_normal(p3["x_seed"], (p3["T"], K_HID),
+                                     outliers=outlier_channels(p3["outlier_seed"], K_HID)))
+    run = MlpRunner(m, p3["T"])
+    y = torch.empty((p3["T"], K_HID), dtype=torch.float32, device="cuda")
+    t = time_events(lambda: run(x, lay, y), 20)
+    ms = float(np.median(t))
+    out["prefill_1024"] = {"workload": "mlp_prefill_1024x5120x17408", "ms": ms,
+                           "tflops": mlp_flops(p3["T"]) / (ms * 1e-3) / 1e12,
+                           "tokens_per_s": p3["T"] / (ms * 1e-3),
+                           "frac_f16_peak": mlp_flops(p3["T"]) / (ms * 1e-3) / 1e12 / PEAK_F16_TFLOPS}
+    del lay, run, x, y
+    p2 = WORKLOADS["mlp_decode_5120x17408"].params
+    log("extra: decode-shaped MLP T=1, T=5")
+    lay = Layer(m, (p2["wg_seed"], p2["wu_seed"], p2["wd_seed"]))
+    wbytes = sum(w.codes.numel() + w.scales.numel() + 4 for w in lay.w)
+    scrub_buf = torch.ones(1 << 27, dtype=torch.int64, device="cuda")
+    dec = {"workload": "mlp_decode_5120x17408", "weight_bytes": wbytes}
+    launches = {}
+    for tt in p2["Ts"]:
+        x = m.bf16_from_bits(bf16_normal(p2["x_seed"], (tt, K_HID)))
+        run = MlpRunner(m, tt)
+        y = torch.empty((tt, K_HID), dtype=torch.float32, device="cuda")
+        before = m.launch_count()
+        run(x, lay, y)
+        launches[tt] = m.launch_count() - before
+        hot = float(np.median(time_events(lambda: run(x, lay, y), 50)))
+        # cold: reading a 1 GiB buffer between reps evicts the 150 MB of weights
+        # from the 256 MB MALL and the L2s (a read leaves no dirty lines whose
+        # write-back would compete with the timed call)
+        cold = float(np.median(time_events(lambda: run(x, lay, y), 20, scrub=lambda: scrub_buf.sum())))
+        dec[f"T{tt}"] = {"ms_hot": hot, "ms_cold": cold, "hbm_gbs_cold": wbytes / (cold * 1e-3) / 1e9,
+                         "hbm_gbs_hot": wbytes / (hot * 1e-3) / 1e9,
+                         "frac_hbm_peak_cold": wbytes / (cold * 1e-3) / 1e9 / PEAK_HBM_GBS}
+    dec["launches_per_call"] = launches
+    dec["t5_over_t1_cold"] = dec["T5"]["ms_cold"] / dec["T1"]["ms_cold"]
+    out["decode"] = dec
+    del lay, scrub_buf
+    out["moe"] = moe_line(m)
+    return out
+
+
+def decode_stack_line(m, layers):
+    """One token (T = 1) and five (T = 5) through the 4 stacked full-size layers,
+    eager and replayed from a HIP graph.  The 601.6 MB of weights exceed the
+    256 MB MALL, so every pass streams them from HBM."""
+    log("extra: 4-layer decode stack, eager and HIP graph")
+    wbytes = sum(w.codes.numel() + w.scales.numel() + 4 for lay in layers for w in lay.w)
+    out = {"workload": "mlp_long_prefill_16x1024_4layers weights, T = 1 and T = 5 per pass", "weight_bytes": wbytes}
+    for t in (1, 5):
+        from synthetic import bf16_normal
+        x = m.bf16_from_bits(bf16_normal(99, (t, K_HID)))
+        run = MlpRunner(m, t)
+        ys = [torch.empty((t, K_HID), dtype=torch.bfloat16, device="cuda") for _ in range(2)]
+
+        def stack():
+            cur = x
+            for li, lay in enumerate(layers):
+                run(cur, lay, ys[li % 2])
+                cur = ys[li % 2]
+        eager = float(np.median(time_events(stack, 20)))
+        s = torch.cuda.Stream()
+        s.wait_stream(torch.cuda.current_stream())
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.stream(s):
+            with torch.cuda.graph(g, stream=s):
+                stack()
+        torch.cuda.current_stream().wait_stream(s)
+        torch.cuda.synchronize()
+        graph = float(np.median(time_events(g.replay, 20)))
+        out[f"T{t}"] = {"ms_eager": eager, "ms_graph": graph, "ms_per_layer_graph": graph / len(layers),
+                        "hbm_gbs_graph": wbytes / (graph * 1e-3) / 1e9,
+                        "frac_hbm_peak_graph": wbytes / (graph * 1e-3) / 1e9 / PEAK_HBM_GBS,
+                        "launches_per_pass": 8 * len(layers)}
+        del g
+    return out
+
+
+def moe_line(m):
     """Expert-grouped MLP: 4096 tokens routed top-8 over 64 experts (hidden 4096, expert width 2048)."""
     from synthetic import WORKLOADS, bf16_normal, expert_seeds, moe_routing
     p = WORKLOADS["moe_4096_top8_of_64"].params

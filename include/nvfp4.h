@@ -194,6 +194,44 @@ int nvfp4_grouped_gemm(nvfp4_tensor a, const int32_t *a_rows, const int32_t *gro
                        int epilogue, void *out, int out_dtype, int64_t ld_out, nvfp4_tensor out_q,
                        void *ws, size_t *ws_bytes, void *stream);
 
+/*
+ * nvfp4_moe_route -- top-k routing of T tokens over E experts into the slot
+ * layout nvfp4_grouped_gemm takes, on the device (no host read of expert ids:
+ * [dsv4] P8 item 5; grouped MUL_MAT_ID slots: [llama] "Verified").  Each
+ * token takes the k experts with the largest logits, ties to the lower
+ * expert id; its weights are the softmax over those k logits,
+ * w_j = exp(l_j - l_max) / sum over the k chosen of exp(l_i - l_max) (float32).
+ * Slots are the (token, choice) pairs sorted by (expert, token).
+ *   logits        : float32 [T][E], row stride ld >= E elements
+ *   E, k          : 1 <= E <= 4096, 1 <= k <= min(E, 16)
+ *   group_offsets : int32 [E+1] out: first slot of each expert; [E] = T*k
+ *   a_rows        : int32 [T*k] out: token of each slot
+ *   slot_of       : int32 [T][k] out: slot of token t's j-th choice (choices
+ *                   by decreasing logit)
+ *   weights       : float32 [T][k] out: the combine weights, same order
+ *   ws            : required (per-token choices and ranks, per-block counts)
+ * Three launches, independent of T; the slot order does not depend on
+ * scheduling (no atomics).  Logits must be finite.
+ */
+int nvfp4_moe_route(const float *logits, int64_t T, int E, int k, int64_t ld, int32_t *group_offsets,
+                    int32_t *a_rows, int32_t *slot_of, float *weights, void *ws, size_t *ws_bytes,
+                    void *stream);
+
+/*
+ * nvfp4_moe_combine -- y[t][n] = sum over j of weights[t][j] *
+ * y_slots[slot_of[t][j]][n]: the weighted sum of each token's expert outputs
+ * (float32 accumulation, choices in order j = 0 .. k-1).
+ *   y_slots : float32 or bf16 (slots_dtype) [M][N], row stride ld_slots
+ *   slot_of, weights : [T][k] as written by nvfp4_moe_route; every slot index
+ *             must be a row of y_slots (undefined behaviour otherwise)
+ *   y       : float32 or bf16 (y_dtype) [T][N], row stride ldy
+ *   N       : multiple of 8; rows of y_slots and y 16-byte aligned
+ * One launch.
+ */
+int nvfp4_moe_combine(const void *y_slots, int slots_dtype, int64_t ld_slots, const int32_t *slot_of,
+                      const float *weights, int64_t T, int k, int64_t N, void *y, int y_dtype, int64_t ldy,
+                      void *stream);
+
 /* Static message for a status code (host string, never NULL). */
 const char *nvfp4_strerror(int status);
 
@@ -211,7 +249,9 @@ enum nvfp4_kernel_class {
   NVFP4_KC_EXPAND = 1,       /* NVFP4 -> f16 activation expansion ahead of a contraction          */
   NVFP4_KC_GEMM_GLU = 2,     /* contraction with the SiLU*up epilogue (gate/up projection)         */
   NVFP4_KC_GEMM_STORE = 3,   /* contraction with the store epilogue (down projection, nvfp4_gemm)  */
-  NVFP4_KC_REDUCE = 4        /* split-K reduction and output scaling                               */
+  NVFP4_KC_REDUCE = 4,       /* split-K reduction and output scaling                               */
+  NVFP4_KC_ROUTE = 5,        /* expert routing kernels (nvfp4_moe_route)                           */
+  NVFP4_KC_COMBINE = 6       /* weighted combine of expert outputs (nvfp4_moe_combine)             */
 };
 
 #define NVFP4_TIMING_MAX_LAUNCHES 1048576

@@ -34,7 +34,7 @@ OK, ERR_NULL, ERR_SHAPE, ERR_ALIGN, ERR_WORKSPACE, ERR_ARG, ERR_DEVICE, ERR_LAUN
 F32, BF16 = 0, 1
 GS_COMPUTE, GS_GIVEN = 0, 1
 EPI_STORE, EPI_SILU_MUL_REQUANT = 0, 1
-KC_QUANTIZE, KC_EXPAND, KC_GEMM_GLU, KC_GEMM_STORE, KC_REDUCE = range(5)
+KC_QUANTIZE, KC_EXPAND, KC_GEMM_GLU, KC_GEMM_STORE, KC_REDUCE, KC_ROUTE, KC_COMBINE = range(7)
 
 _sig = {
     "nvfp4_quantize_act": [_vp, ctypes.c_int, _i64, _i64, _i64, nvfp4_tensor, ctypes.c_int, _vp,
@@ -48,6 +48,10 @@ _sig = {
     "nvfp4_grouped_gemm": [nvfp4_tensor, _vp, _vp, ctypes.c_int, _i64, nvfp4_tensor, nvfp4_tensor, _i64, _i64,
                            ctypes.c_int, _vp, ctypes.c_int, _i64, nvfp4_tensor, _vp,
                            ctypes.POINTER(ctypes.c_size_t), _vp],
+    "nvfp4_moe_route": [_vp, _i64, ctypes.c_int, ctypes.c_int, _i64, _vp, _vp, _vp, _vp, _vp,
+                        ctypes.POINTER(ctypes.c_size_t), _vp],
+    "nvfp4_moe_combine": [_vp, ctypes.c_int, _i64, _vp, _vp, _i64, ctypes.c_int, _i64, _vp, ctypes.c_int, _i64,
+                          _vp],
 }
 for _name, _args in _sig.items():
     _f = getattr(_lib, _name)
@@ -263,6 +267,35 @@ def nvfp4_grouped_gemm(a, a_rows, group_offsets, w0, w1=None, out=None, out_q=No
                                    ld, out_q.c() if out_q is not None else _null_tensor(), _ptr(ws),
                                    ctypes.byref(sz), _stream(stream)), "nvfp4_grouped_gemm")
     return ws
+
+
+def moe_route_ws_bytes(t, e, k):
+    size = ctypes.c_size_t(0)
+    _check(_lib.nvfp4_moe_route(_vp(0), t, e, k, e, _vp(0), _vp(0), _vp(0), _vp(0), _vp(0), ctypes.byref(size),
+                                _vp(0)), "workspace query")
+    return size.value
+
+
+def nvfp4_moe_route(logits, k, group_offsets, a_rows, slot_of, weights, ws=None, stream=None):
+    """Top-k routing on the device; see include/nvfp4.h.  logits: float32 [T][E] device tensor."""
+    t, e = logits.shape
+    need = moe_route_ws_bytes(t, e, k)
+    if ws is None:
+        ws = torch.empty(max(need, 256), dtype=torch.uint8, device=logits.device)
+    sz = ctypes.c_size_t(ws.numel())
+    _check(_lib.nvfp4_moe_route(_ptr(logits), t, e, k, logits.stride(0), _ptr(group_offsets), _ptr(a_rows),
+                                _ptr(slot_of), _ptr(weights), _ptr(ws), ctypes.byref(sz), _stream(stream)),
+           "nvfp4_moe_route")
+    return ws
+
+
+def nvfp4_moe_combine(y_slots, slot_of, weights, y, stream=None):
+    """y[t] = sum_j weights[t, j] * y_slots[slot_of[t, j]] on the device; see include/nvfp4.h."""
+    t, k = slot_of.shape
+    n = y.shape[1]
+    _check(_lib.nvfp4_moe_combine(_ptr(y_slots), _dtype_code(y_slots), y_slots.stride(0), _ptr(slot_of),
+                                  _ptr(weights), t, k, n, _ptr(y), _dtype_code(y), y.stride(0), _stream(stream)),
+           "nvfp4_moe_combine")
 
 
 # ---- convenience: host <-> device NVFP4 (test and setup plumbing) -------------------

@@ -11,7 +11,7 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libnvfp4.so")
 
-SOURCES = ["nvfp4_abi.hip", "quant.hip", "gemm.hip"]
+SOURCES = ["nvfp4_abi.hip", "quant.hip", "gemm.hip", "moe.hip"]
 
 FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",

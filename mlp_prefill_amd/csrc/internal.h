@@ -13,7 +13,14 @@ namespace nvfp4 {
 constexpr uint32_t kMaxPartials = 4096;
 
 // Kernel classes of the timing window (same values as the public enum).
-enum KernelClass { KC_QUANTIZE = 0, KC_EXPAND = 1, KC_GEMM_GLU = 2, KC_GEMM_STORE = 3, KC_REDUCE = 4, KC_COUNT = 5 };
+enum KernelClass {
+  KC_QUANTIZE = 0, KC_EXPAND = 1, KC_GEMM_GLU = 2, KC_GEMM_STORE = 3, KC_REDUCE = 4, KC_ROUTE = 5, KC_COMBINE = 6,
+  KC_COUNT = 7
+};
+
+// Limits of the expert routing.
+constexpr int kMaxTopK = 16;
+constexpr int kMaxExperts = 4096;
 
 // Every launch is bracketed by these two calls: launch_begin records the
 // start event when a timing window for `kc` is open (returns its slot, else
@@ -52,5 +59,12 @@ size_t glu_ws_bytes(int64_t M, int64_t N, int64_t K, int E, bool grouped);
 int glu_launch(Operand a, const int32_t* a_rows, const int32_t* off, int E, int64_t M, Operand gt, Operand up,
                int64_t N, int64_t K, uint8_t* hq_codes, uint8_t* hq_scales, float* hq_gs, void* ws,
                hipStream_t st);
+
+// ---- expert routing and combine ----------------------------------------------
+size_t route_ws_bytes(int64_t T, int E, int k);
+int route_launch(const float* logits, int64_t T, int E, int k, int64_t ld, int32_t* group_offsets, int32_t* a_rows,
+                 int32_t* slot_of, float* weights, void* ws, hipStream_t st);
+int combine_launch(const void* ys, int ys_bf16, int64_t ld_s, const int32_t* slot_of, const float* weights, int64_t T,
+                   int k, int64_t N, void* y, int y_bf16, int64_t ldy, hipStream_t st);
 
 }  // namespace nvfp4

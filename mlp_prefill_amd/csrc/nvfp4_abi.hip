@@ -239,6 +239,40 @@ int nvfp4_mlp_down(nvfp4_tensor h, nvfp4_tensor w_down, int64_t T, int64_t I, in
                              reinterpret_cast<hipStream_t>(stream));
 }
 
+int nvfp4_moe_route(const float* logits, int64_t T, int E, int k, int64_t ld, int32_t* group_offsets,
+                    int32_t* a_rows, int32_t* slot_of, float* weights, void* ws, size_t* ws_bytes, void* stream) {
+  if (E < 1 || E > nvfp4::kMaxExperts || k < 1 || k > nvfp4::kMaxTopK || k > E) return NVFP4_ERR_ARG;
+  if (T < 0 || ld < E) return NVFP4_ERR_SHAPE;
+  if (T * k >= ((int64_t)1 << 31) || T * ld >= ((int64_t)1 << 40)) return NVFP4_ERR_SHAPE;
+  bool query;
+  int rc = workspace(ws, ws_bytes, T > 0 ? nvfp4::route_ws_bytes(T, E, k) : 0, &query);
+  if (rc != NVFP4_OK || query) return rc;
+  if (T == 0) return NVFP4_OK;
+  if (!logits || !group_offsets || !a_rows || !slot_of || !weights) return NVFP4_ERR_NULL;
+  if (!aligned(logits, 4) || !aligned(group_offsets, 4) || !aligned(a_rows, 4) || !aligned(slot_of, 4) ||
+      !aligned(weights, 4))
+    return NVFP4_ERR_ALIGN;
+  if ((rc = check_device()) != NVFP4_OK) return rc;
+  return nvfp4::route_launch(logits, T, E, k, ld, group_offsets, a_rows, slot_of, weights, ws,
+                             reinterpret_cast<hipStream_t>(stream));
+}
+
+int nvfp4_moe_combine(const void* y_slots, int slots_dtype, int64_t ld_slots, const int32_t* slot_of,
+                      const float* weights, int64_t T, int k, int64_t N, void* y, int y_dtype, int64_t ldy,
+                      void* stream) {
+  if (!dtype_ok(slots_dtype) || !dtype_ok(y_dtype) || k < 1 || k > nvfp4::kMaxTopK) return NVFP4_ERR_ARG;
+  if (T < 0 || N < 0 || N % 8 != 0 || ld_slots < N || ldy < N) return NVFP4_ERR_SHAPE;
+  if (T == 0 || N == 0) return NVFP4_OK;
+  if (!y_slots || !slot_of || !weights || !y) return NVFP4_ERR_NULL;
+  if (!aligned(y_slots, 16) || !aligned(y, 16) || (ld_slots * elem_size(slots_dtype)) % 16 != 0 ||
+      (ldy * elem_size(y_dtype)) % 16 != 0 || !aligned(slot_of, 4) || !aligned(weights, 4))
+    return NVFP4_ERR_ALIGN;
+  int rc;
+  if ((rc = check_device()) != NVFP4_OK) return rc;
+  return nvfp4::combine_launch(y_slots, slots_dtype == NVFP4_BF16, ld_slots, slot_of, weights, T, k, N, y,
+                               y_dtype == NVFP4_BF16, ldy, reinterpret_cast<hipStream_t>(stream));
+}
+
 int nvfp4_grouped_gemm(nvfp4_tensor a, const int32_t* a_rows, const int32_t* group_offsets, int E, int64_t M,
                        nvfp4_tensor w0, nvfp4_tensor w1, int64_t N, int64_t K, int epilogue, void* out,
                        int out_dtype, int64_t ld_out, nvfp4_tensor out_q, void* ws, size_t* ws_bytes,

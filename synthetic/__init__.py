@@ -14,7 +14,7 @@ weights ~ N(0, 0.02) in bf16.
 
 bf16 values are carried on the host as uint16 bit patterns (numpy has no bf16).
 """
-from dataclasses import dataclass, field
+from dataclasses import dataclass
 
 import numpy as np
 
@@ -53,32 +53,9 @@ def bf16_normal(seed, shape, sigma=1.0, outliers=None, outlier_gain=50.0):
     return _round_f32_to_bf16_bits(x)
 
 
-@dataclass
-class Routing:
-    """Top-k routing of T tokens over E experts, as slots grouped by expert."""
-    topk: np.ndarray            # int32 [T, k], expert ids per token, by decreasing logit
-    a_rows: np.ndarray          # int32 [T*k], token of each slot, slots sorted by (expert, token)
-    group_offsets: np.ndarray   # int32 [E+1], first slot of each expert
-    logits: np.ndarray = field(repr=False, default=None)   # float32 [T, E]
-
-
-def moe_routing(seed, t, e, k):
-    """Router logits ~ N(0,1) (PCG64 `seed`); each token picks its k largest (ties: lower id).
-
-    Softmax is monotone, so the top-k of the probabilities is the top-k of the
-    logits.  Slots are ordered by expert, then by token.
-    """
-    rng = np.random.default_rng(seed)
-    logits = rng.standard_normal((t, e), dtype=np.float32)
-    order = np.argsort(-logits, axis=1, kind="stable")[:, :k]
-    experts = order.reshape(-1)
-    tokens = np.repeat(np.arange(t), k)
-    slot_order = np.lexsort((tokens, experts))
-    a_rows = tokens[slot_order].astype(np.int32)
-    counts = np.bincount(experts, minlength=e)
-    offsets = np.zeros(e + 1, dtype=np.int32)
-    offsets[1:] = np.cumsum(counts)
-    return Routing(order.astype(np.int32), a_rows, offsets, logits)
+def router_logits(seed, t, e):
+    """Router logits ~ N(0, 1), float32 [t, e] (PCG64 `seed`)."""
+    return np.random.default_rng(seed).standard_normal((t, e), dtype=np.float32)
 
 
 @dataclass

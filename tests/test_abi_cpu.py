@@ -154,7 +154,7 @@ def test_timing_window_validation():
     n, d, ms = ctypes.c_int64(), ctypes.c_int64(), ctypes.c_double()
     out = (ctypes.byref(n), ctypes.byref(d), ctypes.byref(ms))
     assert lib.nvfp4_timing_begin(-1, 8) == m.ERR_ARG
-    assert lib.nvfp4_timing_begin(5, 8) == m.ERR_ARG
+    assert lib.nvfp4_timing_begin(7, 8) == m.ERR_ARG                  # one past the last class
     assert lib.nvfp4_timing_begin(m.KC_GEMM_GLU, 0) == m.ERR_ARG
     assert lib.nvfp4_timing_begin(m.KC_GEMM_GLU, (1 << 20) + 1) == m.ERR_ARG
     assert lib.nvfp4_timing_end(*out) == m.ERR_ARG                      # no window open
@@ -167,3 +167,33 @@ def test_timing_window_validation():
     else:                                                                # no device: events cannot be made
         assert st == m.ERR_LAUNCH
         assert lib.nvfp4_timing_end(*out) == m.ERR_ARG
+
+
+def test_moe_route_and_combine_validation():
+    lib = m.lib
+    sz = ctypes.c_size_t(1 << 20)
+    r = lib.nvfp4_moe_route
+    assert r(FAKE, 16, 0, 1, 8, FAKE, FAKE, FAKE, FAKE, FAKE, ctypes.byref(sz), None) == m.ERR_ARG      # E < 1
+    assert r(FAKE, 16, 8, 9, 8, FAKE, FAKE, FAKE, FAKE, FAKE, ctypes.byref(sz), None) == m.ERR_ARG      # k > E
+    assert r(FAKE, 16, 64, 17, 64, FAKE, FAKE, FAKE, FAKE, FAKE, ctypes.byref(sz), None) == m.ERR_ARG   # k > 16
+    assert r(FAKE, 16, 5000, 2, 5000, FAKE, FAKE, FAKE, FAKE, FAKE, ctypes.byref(sz), None) == m.ERR_ARG
+    assert r(FAKE, 16, 8, 2, 4, FAKE, FAKE, FAKE, FAKE, FAKE, ctypes.byref(sz), None) == m.ERR_SHAPE    # ld < E
+    assert r(FAKE, -1, 8, 2, 8, FAKE, FAKE, FAKE, FAKE, FAKE, ctypes.byref(sz), None) == m.ERR_SHAPE
+    q = ctypes.c_size_t(0)
+    assert r(None, 4096, 64, 8, 64, None, None, None, None, None, ctypes.byref(q), None) == m.OK
+    assert q.value >= 2 * 4096 * 8 * 4 + 64 * 64 * 4                                                    # ids, ranks, counts
+    small = ctypes.c_size_t(q.value - 1)
+    assert r(FAKE, 4096, 64, 8, 64, FAKE, FAKE, FAKE, FAKE, FAKE, ctypes.byref(small), None) == m.ERR_WORKSPACE
+    z = ctypes.c_size_t(1 << 20)
+    assert r(FAKE, 0, 64, 8, 64, None, None, None, None, FAKE, ctypes.byref(z), None) == m.OK           # T = 0
+    big = lambda: ctypes.byref(ctypes.c_size_t(1 << 20))                                               # noqa: E731
+    assert r(None, 16, 8, 2, 8, FAKE, FAKE, FAKE, FAKE, FAKE, big(), None) == m.ERR_NULL
+    assert r(FAKE + 2, 16, 8, 2, 8, FAKE, FAKE, FAKE, FAKE, FAKE, big(), None) == m.ERR_ALIGN
+    c = lib.nvfp4_moe_combine
+    assert c(FAKE, 7, 64, FAKE, FAKE, 16, 2, 64, FAKE, m.F32, 64, None) == m.ERR_ARG                   # dtype
+    assert c(FAKE, m.BF16, 64, FAKE, FAKE, 16, 0, 64, FAKE, m.F32, 64, None) == m.ERR_ARG              # k
+    assert c(FAKE, m.BF16, 64, FAKE, FAKE, 16, 2, 60, FAKE, m.F32, 64, None) == m.ERR_SHAPE            # N % 8
+    assert c(FAKE, m.BF16, 32, FAKE, FAKE, 16, 2, 64, FAKE, m.F32, 64, None) == m.ERR_SHAPE            # ld < N
+    assert c(FAKE, m.BF16, 64, FAKE, FAKE, 0, 2, 64, FAKE, m.F32, 64, None) == m.OK                    # T = 0
+    assert c(None, m.BF16, 64, FAKE, FAKE, 16, 2, 64, FAKE, m.F32, 64, None) == m.ERR_NULL
+    assert c(FAKE, m.BF16, 68, FAKE, FAKE, 16, 2, 64, FAKE, m.F32, 64, None) == m.ERR_ALIGN            # row stride

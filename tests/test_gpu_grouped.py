@@ -5,8 +5,9 @@ import torch
 
 from oracle import gemm as ogemm
 from oracle import mlp as omlp
+from oracle import moe as omoe
 from oracle import quant
-from synthetic import WORKLOADS, bf16_bits_to_f32, bf16_normal, expert_seeds, moe_routing
+from synthetic import WORKLOADS, bf16_bits_to_f32, bf16_normal, expert_seeds, router_logits
 from tests.gpu_util import (TOL, announce, assert_nvfp4_equal, dev_quantize, legit_requant_flips, max_norm_err,
                             require_gpu, to_host)
 
@@ -66,7 +67,7 @@ def _check_small(t, e, k, i, a_rows, offsets, seed):
 
 def test_grouped_mlp_routed_top2():
     announce("grouped mlp: 96 tokens, top-2 of 8 experts")
-    r = moe_routing(55, 96, 8, 2)
+    r = omoe.route(router_logits(55, 96, 8), 2)
     _check_small(96, 8, 256, 384, r.a_rows, r.group_offsets, 56)
 
 
@@ -111,7 +112,7 @@ def test_grouped_mlp_moe_workload_full_size_sampled():
     p = WORKLOADS["moe_4096_top8_of_64"].params
     t, e, top, k, i = p["T"], p["E"], p["topk"], p["K"], p["I"]
     announce("grouped mlp: MoE workload full size (sampled experts)")
-    r = moe_routing(p["router_seed"], t, e, top)
+    r = omoe.route(router_logits(p["router_seed"], t, e), top)
     xb = bf16_normal(p["x_seed"], (t, k))
     xq = dev_quantize(xb)
     wdev, _ = _experts(e, k, i, p["expert_seed0"], with_ref=False)
