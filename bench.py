@@ -241,6 +241,7 @@ def main():
     if not args.no_extra:
         extra = extra_lines(m)
         extra["decode_stack"] = decode_stack_line(m, layers)
+        extra["quantize"] = quantize_line(m)
 
     result = {
         "metric": METRIC, "value": tflops, "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
@@ -304,8 +305,51 @@ def extra_lines(m):
     dec["launches_per_call"] = launches
     dec["t5_over_t1_cold"] = dec["T5"]["ms_cold"] / dec["T1"]["ms_cold"]
     out["decode"] = dec
+    del lay
+    # the tensor-parallel (tp = 2) shard on one GPU: intermediate 8704
+    log("extra: tp=2 shard MLP (5120 -> 2 x 8704 -> 5120), T = 1024 and T = 1")
+    ih = I_INT // 2
+    lay = Layer(m, (6001, 6002, 6003), i=ih)
+    shard = {"workload": "mlp_prefill_1024x5120x17408 tp=2 shard (intermediate 8704)"}
+    for tt in (1024, 1):
+        x = m.bf16_from_bits(bf16_normal(6004, (tt, K_HID)))
+        run = MlpRunner(m, tt, i=ih)
+        y = torch.empty((tt, K_HID), dtype=torch.bfloat16, device="cuda")
+        if tt == 1:
+            ms = float(np.median(time_events(lambda: run(x, lay, y), 20, scrub=lambda: scrub_buf.sum())))
+            wb = sum(w.codes.numel() + w.scales.numel() + 4 for w in lay.w)
+            shard["T1"] = {"ms_cold": ms, "hbm_gbs_cold": wb / (ms * 1e-3) / 1e9}
+        else:
+            ms = float(np.median(time_events(lambda: run(x, lay, y), 20)))
+            tf = mlp_flops(tt, i=ih) / (ms * 1e-3) / 1e12
+            shard["T1024"] = {"ms": ms, "tflops": tf, "frac_f16_peak": tf / PEAK_F16_TFLOPS,
+                              "tokens_per_s": tt / (ms * 1e-3)}
+    out["tp2_shard"] = shard
     del lay, scrub_buf
     out["moe"] = moe_line(m)
+    return out
+
+
+def quantize_line(m):
+    """Activation quantisation (A1+A2, two launches) and the fused RMSNorm variant
+    (N2), bf16 input: GB/s of the algorithmic traffic, 2 B read + 0.5625 B
+    written per element, at the 1024-token shape and on a 65536 x 5120 probe."""
+    from synthetic import bf16_normal
+    log("extra: quantisation kernels (plain and RMSNorm-fused)")
+    out = {"unit_bytes_per_element": 2.5625}
+    g = torch.ones(K_HID, dtype=torch.float32, device="cuda")
+    for rows in (1024, 65536):
+        x = m.bf16_from_bits(bf16_normal(777, (1024, K_HID))).repeat(rows // 1024, 1)
+        q = m.NVFP4.empty(rows, K_HID)
+        ws = torch.empty(max(m.ws_bytes_quantize(rows, K_HID), m.rmsnorm_quantize_ws_bytes(rows, K_HID)),
+                         dtype=torch.uint8, device="cuda")
+        nbytes = rows * K_HID * 2.5625
+        tq = float(np.median(time_events(lambda: m.nvfp4_quantize_act(x, q, ws=ws), 20)))
+        tn = float(np.median(time_events(lambda: m.nvfp4_rmsnorm_quantize_act(x, g, 1e-6, q, ws=ws), 20)))
+        out[f"rows{rows}"] = {"quantize_ms": tq, "quantize_gbs": nbytes / (tq * 1e-3) / 1e9,
+                              "quantize_frac_hbm": nbytes / (tq * 1e-3) / 1e9 / PEAK_HBM_GBS,
+                              "rmsnorm_quantize_ms": tn, "rmsnorm_quantize_gbs": nbytes / (tn * 1e-3) / 1e9}
+        del x, q, ws
     return out
 
 
@@ -405,133 +449,6 @@ def moe_line(m):
             "combine_gbs": comb_bytes / (parts["combine_ms"] * 1e-3) / 1e9,
             "note": "ms covers routing, quantisation, both grouped GEMMs and the combine; TFLOP/s counts the "
                     "6*slots*K*I of the expert MLPs"}
-
-
-def extra_lines(m):
-    """1024-token MLP and decode-shaped T=1/T=5 MLP (separate weights, as their workloads define)."""
-    from synthetic import WORKLOADS, bf16_normal, outlier_channels
-    out = {}
-    p3 = WORKLOADS["mlp_prefill_1024x5120x17408"].params
-    log("extra: 1024-token MLP")
-    lay = Layer(m, (p3["wg_seed"], p3["wu_seed"], p3["wd_seed"]))
-    x = m.bf16_from_bits(bf16_normal(p3["x_seed"], (p3["T"], K_HID),
-                                     outliers=outlier_channels(p3["outlier_seed"], K_HID)))
-    run = MlpRunner(m, p3["T"])
-    y = torch.empty((p3["T"], K_HID), dtype=torch.float32, device="cuda")
-    t = time_events(lambda: run(x, lay, y), 20)
-    ms = float(np.median(t))
-    out["prefill_1024"] = {"workload": "mlp_prefill_1024x5120x17408", "ms": ms,
-                           "tflops": mlp_flops(p3["T"]) / (ms * 1e-3) / 1e12,
-                           "tokens_per_s": p3["T"] / (ms * 1e-3),
-                           "frac_f16_peak": mlp_flops(p3["T"]) / (ms * 1e-3) / 1e12 / PEAK_F16_TFLOPS}
-    del lay, run, x, y
-    p2 = WORKLOADS["mlp_decode_5120x17408"].params
-    log("extra: decode-shaped MLP T=1, T=5")
-    lay = Layer(m, (p2["wg_seed"], p2["wu_seed"], p2["wd_seed"]))
-    wbytes = sum(w.codes.numel() + w.scales.numel() + 4 for w in lay.w)
-    scrub_buf = torch.ones(1 << 27, dtype=torch.int64, device="cuda")
-    dec = {"workload": "mlp_decode_5120x17408", "weight_bytes": wbytes}
-    launches = {}
-    for tt in p2["Ts"]:
-        x = m.bf16_from_bits(bf16_normal(p2["x_seed"], (tt, K_HID)))
-        run = MlpRunner(m, tt)
-        y = torch.empty((tt, K_HID), dtype=torch.float32, device="cuda")
-        before = m.launch_count()
-        run(x, lay, y)
-        launches[tt] = m.launch_count() - before
-        hot = float(np.median(time_events(lambda: run(x, lay, y), 50)))
-        # cold: reading a 1 GiB buffer between reps evicts the 150 MB of weights
-        # from the 256 MB MALL and the L2s (a read leaves no dirty lines whose
-        # write-back would compete with the timed call)
-        cold = float(np.median(time_events(lambda: run(x, lay, y), 20, scrub=lambda: scrub_buf.sum())))
-        dec[f"T{tt}"] = {"ms_hot": hot, "ms_cold": cold, "hbm_gbs_cold": wbytes / (cold * 1e-3) / 1e9,
-                         "hbm_gbs_hot": wbytes / (hot * 1e-3) / 1e9,
-                         "frac_hbm_peak_cold": wbytes / (cold * 1e-3) / 1e9 / PEAK_HBM_GBS}
-    dec["launches_per_call"] = launches
-    dec["t5_over_t1_cold"] = dec["T5"]["ms_cold"] / dec["T1"]["ms_cold"]
-    out["decode"] = dec
-    del lay, scrub_buf
-    out["moe"] = moe_line(m)
-    return out
-
-
-def decode_stack_line(m, layers):
-    """One token (T = 1) and five (T = 5) through the 4 stacked full-size layers,
-    eager and replayed from a HIP graph.  The 601.6 MB of weights exceed the
-    256 MB MALL, so every pass streams them from HBM."""
-    log("extra: 4-layer decode stack, eager and HIP graph")
-    wbytes = sum(w.codes.numel() + w.scales.numel() + 4 for lay in layers for w in lay.w)
-    out = {"workload": "mlp_long_prefill_16x1024_4layers weights, T = 1 and T = 5 per pass", "weight_bytes": wbytes}
-    for t in (1, 5):
-        from synthetic import bf16_normal
-        x = m.bf16_from_bits(bf16_normal(99, (t, K_HID)))
-        run = MlpRunner(m, t)
-        ys = [torch.empty((t, K_HID), dtype=torch.bfloat16, device="cuda") for _ in range(2)]
-
-        def stack():
-            cur = x
-            for li, lay in enumerate(layers):
-                run(cur, lay, ys[li % 2])
-                cur = ys[li % 2]
-        eager = float(np.median(time_events(stack, 20)))
-        s = torch.cuda.Stream()
-        s.wait_stream(torch.cuda.current_stream())
-        g = torch.cuda.CUDAGraph()
-        with torch.cuda.stream(s):
-            with torch.cuda.graph(g, stream=s):
-                stack()
-        torch.cuda.current_stream().wait_stream(s)
-        torch.cuda.synchronize()
-        graph = float(np.median(time_events(g.replay, 20)))
-        out[f"T{t}"] = {"ms_eager": eager, "ms_graph": graph, "ms_per_layer_graph": graph / len(layers),
-                        "hbm_gbs_graph": wbytes / (graph * 1e-3) / 1e9,
-                        "frac_hbm_peak_graph": wbytes / (graph * 1e-3) / 1e9 / PEAK_HBM_GBS,
-                        "launches_per_pass": 8 * len(layers)}
-        del g
-    return out
-
-
-def moe_line(m):
-    """Expert-grouped MLP: 4096 tokens routed top-8 over 64 experts (hidden 4096, expert width 2048)."""
-    from synthetic import WORKLOADS, bf16_normal, expert_seeds, moe_routing
-    p = WORKLOADS["moe_4096_top8_of_64"].params
-    t, e, top, k, i = p["T"], p["E"], p["topk"], p["K"], p["I"]
-    log("extra: expert-grouped MLP (64 experts, top-8)")
-    r = moe_routing(p["router_seed"], t, e, top)
-    mats = [[], [], []]
-    for x in range(e):
-        for j, (sd, shp) in enumerate(zip(expert_seeds(p["expert_seed0"], x), [(i, k), (i, k), (k, i)])):
-            w = m.bf16_from_bits(bf16_normal(sd, shp, sigma=0.02))
-            q = m.NVFP4.empty(*shp)
-            m.nvfp4_quantize_act(w, q)
-            mats[j].append(q)
-    wg, wu, wd = (m.NVFP4.stack(v) for v in mats)
-    del mats
-    x = m.bf16_from_bits(bf16_normal(p["x_seed"], (t, k)))
-    rows = torch.from_numpy(np.ascontiguousarray(r.a_rows, dtype=np.int32)).cuda()
-    offs = torch.from_numpy(np.ascontiguousarray(r.group_offsets, dtype=np.int32)).cuda()
-    slots = t * top
-    xq = m.NVFP4.empty(t, k)
-    hq = m.NVFP4.empty(slots, i)
-    y = torch.empty((slots, k), dtype=torch.bfloat16, device="cuda")
-    ws_q = torch.empty(m.ws_bytes_quantize(t, k), dtype=torch.uint8, device="cuda")
-    ws_g = torch.empty(max(m.grouped_ws_bytes(slots, i, k, e, m.EPI_SILU_MUL_REQUANT), 256), dtype=torch.uint8,
-                       device="cuda")
-    ws_d = torch.empty(max(m.grouped_ws_bytes(slots, k, i, e, m.EPI_STORE), 256), dtype=torch.uint8, device="cuda")
-
-    def call():
-        m.nvfp4_quantize_act(x, xq, ws=ws_q)
-        m.nvfp4_grouped_gemm(xq, rows, offs, wg, wu, out_q=hq, epilogue=m.EPI_SILU_MUL_REQUANT, m=slots, ws=ws_g)
-        m.nvfp4_grouped_gemm(hq, None, offs, wd, out=y, epilogue=m.EPI_STORE, ws=ws_d)
-
-    before = m.launch_count()
-    call()
-    launches = m.launch_count() - before
-    ms = float(np.median(time_events(call, 10)))
-    flops = mlp_flops(slots, k, i)
-    tf = flops / (ms * 1e-3) / 1e12
-    return {"workload": "moe_4096_top8_of_64", "ms": ms, "tflops": tf, "frac_f16_peak": tf / PEAK_F16_TFLOPS,
-            "tokens_per_s": t / (ms * 1e-3), "slots": slots, "launches_per_call": launches}
 
 
 if __name__ == "__main__":

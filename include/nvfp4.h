@@ -69,6 +69,9 @@
 extern "C" {
 #endif
 
+/* The library is built with hidden visibility; exactly these declarations are exported. */
+#pragma GCC visibility push(default)
+
 typedef struct nvfp4_tensor {
   uint8_t *codes;   /* packed E2M1 codes, see the layout above          */
   uint8_t *scales;  /* E4M3 block scales, one per 16 elements of a row  */
@@ -118,6 +121,24 @@ enum nvfp4_epilogue {
  */
 int nvfp4_quantize_act(const void *x, int x_dtype, int64_t rows, int64_t cols, int64_t ld_x,
                        nvfp4_tensor out, int gs_mode, void *ws, size_t *ws_bytes, void *stream);
+
+/*
+ * nvfp4_rmsnorm_quantize_act -- NVFP4 quantisation of RMSNorm(x), fused:
+ * y[r][c] = (x[r][c] * rinv[r]) * gamma[c] with rinv[r] = 1 / sqrt(mean over
+ * the row of x^2 + eps), formed in float32 and never written; then exactly as
+ * nvfp4_quantize_act (NVFP4_GS_COMPUTE) applied to y.  [dsv4] P8 item 2 (fold
+ * the RMSNorm into the next NVFP4 linear's activation quantisation);
+ * [llama] "What the patch does" (batched-row rms_norm).
+ *   x     : float32 or bf16 (x_dtype) [rows][cols], row stride ld_x
+ *   gamma : float32 [cols], device, 16-byte aligned
+ *   eps   : finite, >= 0
+ *   ws    : required; on return its first rows*4 bytes hold rinv (float32)
+ * Two launches (row statistics and max|y|, then quantisation), independent
+ * of rows.
+ */
+int nvfp4_rmsnorm_quantize_act(const void *x, int x_dtype, int64_t rows, int64_t cols, int64_t ld_x,
+                               const float *gamma, float eps, nvfp4_tensor out, void *ws, size_t *ws_bytes,
+                               void *stream);
 
 /*
  * nvfp4_gemm -- C[M][N] = (A~ . B~^T) * gscale_a * gscale_b.
@@ -279,6 +300,8 @@ int nvfp4_timing_begin(int kernel_class, int64_t max_launches);
  * closed either way).
  */
 int nvfp4_timing_end(int64_t *launches, int64_t *dropped, double *total_ms);
+
+#pragma GCC visibility pop
 
 #ifdef __cplusplus
 }

@@ -48,6 +48,8 @@ _sig = {
     "nvfp4_grouped_gemm": [nvfp4_tensor, _vp, _vp, ctypes.c_int, _i64, nvfp4_tensor, nvfp4_tensor, _i64, _i64,
                            ctypes.c_int, _vp, ctypes.c_int, _i64, nvfp4_tensor, _vp,
                            ctypes.POINTER(ctypes.c_size_t), _vp],
+    "nvfp4_rmsnorm_quantize_act": [_vp, ctypes.c_int, _i64, _i64, _i64, _vp, ctypes.c_float, nvfp4_tensor, _vp,
+                                   ctypes.POINTER(ctypes.c_size_t), _vp],
     "nvfp4_moe_route": [_vp, _i64, ctypes.c_int, ctypes.c_int, _i64, _vp, _vp, _vp, _vp, _vp,
                         ctypes.POINTER(ctypes.c_size_t), _vp],
     "nvfp4_moe_combine": [_vp, ctypes.c_int, _i64, _vp, _vp, _i64, ctypes.c_int, _i64, _vp, ctypes.c_int, _i64,
@@ -266,6 +268,27 @@ def nvfp4_grouped_gemm(a, a_rows, group_offsets, w0, w1=None, out=None, out_q=No
                                    w1.c() if w1 is not None else _null_tensor(), n, k, epilogue, _ptr(out), out_dt,
                                    ld, out_q.c() if out_q is not None else _null_tensor(), _ptr(ws),
                                    ctypes.byref(sz), _stream(stream)), "nvfp4_grouped_gemm")
+    return ws
+
+
+def rmsnorm_quantize_ws_bytes(rows, cols):
+    size = ctypes.c_size_t(0)
+    _check(_lib.nvfp4_rmsnorm_quantize_act(_vp(0), BF16, rows, cols, cols, _vp(0), 1e-6, _null_tensor(), _vp(0),
+                                           ctypes.byref(size), _vp(0)), "workspace query")
+    return size.value
+
+
+def nvfp4_rmsnorm_quantize_act(x, gamma, eps, out, ws=None, stream=None):
+    """NVFP4 of RMSNorm(x) = x * gamma / sqrt(mean(x^2) + eps), fused; see include/nvfp4.h.
+    Returns the workspace (its first rows floats hold 1/rms)."""
+    rows, cols = x.shape
+    need = rmsnorm_quantize_ws_bytes(rows, cols)
+    if ws is None:
+        ws = torch.empty(max(need, 256), dtype=torch.uint8, device=x.device)
+    sz = ctypes.c_size_t(ws.numel())
+    _check(_lib.nvfp4_rmsnorm_quantize_act(_ptr(x), _dtype_code(x), rows, cols, x.stride(0), _ptr(gamma), float(eps),
+                                           out.c(), _ptr(ws), ctypes.byref(sz), _stream(stream)),
+           "nvfp4_rmsnorm_quantize_act")
     return ws
 
 

@@ -18,6 +18,8 @@ FLAGS = [
     # packed float32 instructions stay off for all device code
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-Wall", "-Wno-unused-function",
+    # only the C ABI declared in include/nvfp4.h is exported
+    "-fvisibility=hidden",
 ]
 
 

@@ -38,6 +38,13 @@ __device__ __forceinline__ float wave_max(float v) {
   return v;
 }
 
+// Wave sum in a fixed butterfly order (the same on every run).
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, kWave);
+  return v;
+}
+
 // Block-wide max; `lds` holds at least blockDim.x / 64 floats.  All threads
 // get the result.
 __device__ __forceinline__ float block_max(float v, float* lds) {

@@ -37,6 +37,12 @@ int quantize_launch(const void* x, int x_dtype, int64_t rows, int64_t cols, int6
 int requant_f32_launch(const float* h, int64_t rows, int64_t cols, uint8_t* codes, uint8_t* scales,
                        float* gs, const float* partials, uint32_t npart, hipStream_t st);
 
+// RMSNorm fused into the quantiser: workspace = inverse rms per row, then the
+// partial maxima.
+size_t rmsnorm_quantize_ws_bytes(int64_t rows);
+int rmsnorm_quantize_launch(const void* x, int x_dtype, int64_t rows, int64_t cols, int64_t ld, const float* gamma,
+                            float eps, uint8_t* codes, uint8_t* scales, float* gs, void* ws, hipStream_t st);
+
 // ---- contractions -----------------------------------------------------------
 struct Operand {
   const uint8_t* codes;

@@ -189,6 +189,25 @@ int nvfp4_quantize_act(const void* x, int x_dtype, int64_t rows, int64_t cols, i
                                 reinterpret_cast<hipStream_t>(stream));
 }
 
+int nvfp4_rmsnorm_quantize_act(const void* x, int x_dtype, int64_t rows, int64_t cols, int64_t ld_x,
+                               const float* gamma, float eps, nvfp4_tensor out, void* ws, size_t* ws_bytes,
+                               void* stream) {
+  if (!dtype_ok(x_dtype)) return NVFP4_ERR_ARG;
+  if (!(eps >= 0.0f) || !(eps <= 3.0e38f)) return NVFP4_ERR_ARG;   // finite and non-negative (NaN fails)
+  if (rows < 0 || cols < 0 || cols % 16 != 0 || ld_x < cols) return NVFP4_ERR_SHAPE;
+  if (rows * (cols / 16) >= ((int64_t)1 << 31)) return NVFP4_ERR_SHAPE;
+  bool query;
+  int rc = workspace(ws, ws_bytes, rows > 0 && cols > 0 ? nvfp4::rmsnorm_quantize_ws_bytes(rows) : 0, &query);
+  if (rc != NVFP4_OK || query) return rc;
+  if (rows == 0 || cols == 0) return NVFP4_OK;
+  if (!x || !gamma) return NVFP4_ERR_NULL;
+  if ((rc = check_tensor(out)) != NVFP4_OK) return rc;
+  if (!aligned(x, 16) || (ld_x * elem_size(x_dtype)) % 16 != 0 || !aligned(gamma, 16)) return NVFP4_ERR_ALIGN;
+  if ((rc = check_device()) != NVFP4_OK) return rc;
+  return nvfp4::rmsnorm_quantize_launch(x, x_dtype, rows, cols, ld_x, gamma, eps, out.codes, out.scales, out.gscale,
+                                        ws, reinterpret_cast<hipStream_t>(stream));
+}
+
 int nvfp4_gemm(nvfp4_tensor a, nvfp4_tensor b, int64_t M, int64_t N, int64_t K, void* c, int c_dtype,
                int64_t ldc, void* ws, size_t* ws_bytes, void* stream) {
   if (!dtype_ok(c_dtype)) return NVFP4_ERR_ARG;

@@ -67,13 +67,17 @@ __global__ void __launch_bounds__(256) amax_partials_kernel(const T* __restrict_
 
 // mode 0: gs from the partial maxima (written to gs_ptr by work-group 0);
 // mode 1: gs read from gs_ptr.
-template <typename T>
+// NORM: quantise y = (x * rinv[row]) * gamma[col] (float32, the RMSNorm
+// output) instead of x.
+template <typename T, bool NORM = false>
 __global__ void __launch_bounds__(256) quantize_kernel(const T* __restrict__ x, uint32_t nbc,
                                                        uint32_t nblocks, int64_t ld,
                                                        const float* __restrict__ partials,
                                                        uint32_t npart, float* gs_ptr, int mode,
                                                        uint8_t* __restrict__ codes,
-                                                       uint8_t* __restrict__ scales) {
+                                                       uint8_t* __restrict__ scales,
+                                                       const float* __restrict__ rinv = nullptr,
+                                                       const float* __restrict__ gamma = nullptr) {
   __shared__ float red[4];
   float gs;
   if (mode == 0) {
@@ -89,6 +93,13 @@ __global__ void __launch_bounds__(256) quantize_kernel(const T* __restrict__ x, 
     const uint32_t row = b / nbc, cb = b - row * nbc;
     float v[16];
     Load16<T>::run(x + (int64_t)row * ld + (int64_t)cb * kBlock, v);
+    if constexpr (NORM) {
+      const float r = rinv[row];
+      float g[16];
+      Load16<float>::run(gamma + (int64_t)cb * kBlock, g);
+#pragma unroll
+      for (int i = 0; i < 16; ++i) v[i] = (v[i] * r) * g[i];
+    }
     float amax_b = 0.f;
 #pragma unroll
     for (int i = 0; i < 16; ++i) amax_b = fmaxf(amax_b, fabsf(v[i]));
@@ -105,6 +116,42 @@ __global__ void __launch_bounds__(256) quantize_kernel(const T* __restrict__ x, 
     *reinterpret_cast<uint2*>(codes + boff * 8) = make_uint2(w0, w1);
     scales[boff] = (uint8_t)s;
   }
+}
+
+// RMSNorm fused into the quantiser, first pass: one wave per row (grid-stride)
+// forms r = 1 / sqrt(mean(x^2) + eps) (float32 sum in a fixed order, IEEE
+// sqrt and division) and stores it in rinv[row]; the work-group's max of
+// |(x * r) * gamma| goes to partials[blockIdx.x].  The second pass is
+// quantize_kernel<T, true>, which forms the same float32 products.
+template <typename T>
+__global__ void __launch_bounds__(256) rms_amax_kernel(const T* __restrict__ x, int64_t rows, uint32_t nbc,
+                                                       int64_t ld, const float* __restrict__ gamma, float eps,
+                                                       float* __restrict__ rinv, float* __restrict__ partials) {
+  __shared__ float red[4];
+  const int lane = threadIdx.x & 63;
+  float m = 0.f;
+  for (int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6); row < rows; row += (int64_t)gridDim.x * 4) {
+    const T* xr = x + row * ld;
+    float ss = 0.f;
+    for (uint32_t cb = lane; cb < nbc; cb += 64) {
+      float v[16];
+      Load16<T>::run(xr + (int64_t)cb * kBlock, v);
+#pragma unroll
+      for (int i = 0; i < 16; ++i) ss = fmaf(v[i], v[i], ss);
+    }
+    ss = wave_sum(ss);
+    const float r = 1.0f / sqrtf(ss / (float)(nbc * kBlock) + eps);
+    if (lane == 0) rinv[row] = r;
+    for (uint32_t cb = lane; cb < nbc; cb += 64) {
+      float v[16], g[16];
+      Load16<T>::run(xr + (int64_t)cb * kBlock, v);
+      Load16<float>::run(gamma + (int64_t)cb * kBlock, g);
+#pragma unroll
+      for (int i = 0; i < 16; ++i) m = fmaxf(m, fabsf((v[i] * r) * g[i]));
+    }
+  }
+  m = block_max(m, red);
+  if (threadIdx.x == 0) partials[blockIdx.x] = m;
 }
 
 // Work-groups of the quantiser: enough to fill the chip, few enough that the
@@ -163,6 +210,42 @@ int quantize_launch(const void* x, int x_dtype, int64_t rows, int64_t cols, int6
                              gs_mode, partials, nullptr, 0, st);
   return quantize_launch_t(reinterpret_cast<const float*>(x), rows, cols, ld, codes, scales, gs, gs_mode,
                            partials, nullptr, 0, st);
+}
+
+size_t rmsnorm_quantize_ws_bytes(int64_t rows) {
+  return ((size_t)rows * 4 + 255) / 256 * 256 + kMaxPartials * sizeof(float);
+}
+
+template <typename T>
+static int rmsnorm_quantize_t(const T* x, int64_t rows, int64_t cols, int64_t ld, const float* gamma, float eps,
+                              uint8_t* codes, uint8_t* scales, float* gs, void* ws, hipStream_t st) {
+  float* rinv = reinterpret_cast<float*>(ws);
+  float* partials = reinterpret_cast<float*>(reinterpret_cast<char*>(ws) + ((size_t)rows * 4 + 255) / 256 * 256);
+  const uint32_t nbc = (uint32_t)(cols / kBlock);
+  const uint32_t nblocks = (uint32_t)rows * nbc;
+  int64_t g = (rows + 3) / 4;
+  if (g > kMaxPartials) g = kMaxPartials;
+  uint32_t qgrid = (nblocks + 255u) / 256u;
+  if (qgrid > kQuantGrid) qgrid = kQuantGrid;
+  if (qgrid < 1) qgrid = 1;
+  const int s0 = launch_begin(KC_QUANTIZE, st);
+  hipLaunchKernelGGL(rms_amax_kernel<T>, dim3((uint32_t)g), dim3(256), 0, st, x, rows, nbc, ld, gamma, eps, rinv,
+                     partials);
+  launch_end(s0, st);
+  const int s1 = launch_begin(KC_QUANTIZE, st);
+  hipLaunchKernelGGL((quantize_kernel<T, true>), dim3(qgrid), dim3(256), 0, st, x, nbc, nblocks, ld,
+                     (const float*)partials, (uint32_t)g, gs, 0, codes, scales, (const float*)rinv, gamma);
+  launch_end(s1, st);
+  return hipGetLastError() == hipSuccess ? 0 : 7;
+}
+
+int rmsnorm_quantize_launch(const void* x, int x_dtype, int64_t rows, int64_t cols, int64_t ld, const float* gamma,
+                            float eps, uint8_t* codes, uint8_t* scales, float* gs, void* ws, hipStream_t st) {
+  if (x_dtype == 1)
+    return rmsnorm_quantize_t(reinterpret_cast<const uint16_t*>(x), rows, cols, ld, gamma, eps, codes, scales, gs,
+                              ws, st);
+  return rmsnorm_quantize_t(reinterpret_cast<const float*>(x), rows, cols, ld, gamma, eps, codes, scales, gs, ws,
+                            st);
 }
 
 int requant_f32_launch(const float* h, int64_t rows, int64_t cols, uint8_t* codes, uint8_t* scales,

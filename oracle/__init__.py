@@ -24,8 +24,9 @@ It computes, slowly and in float64 numpy, exactly what the pages describe:
                    "Fix directions" 1-2) and the expert-grouped variant.
 * ``moe``       -- top-k routing into expert-grouped slots and the weighted
                    combine of the per-slot outputs (readings in its docstring).
+* ``norm``      -- RMSNorm fused into the activation quantisation.
 
 Every rounding decision is taken in exact arithmetic (float64 products that are
 provably exact); see each function's docstring for the reading it follows.
 """
-from . import formats, quant, gemm, mlp, moe  # noqa: F401
+from . import formats, quant, gemm, mlp, moe, norm  # noqa: F401

@@ -37,6 +37,12 @@ def test_library_exports_every_declared_function():
     lib = ctypes.CDLL(m.LIB_PATH)
     for n in names:
         assert hasattr(lib, n), n
+    # and nothing else: the library is built with hidden visibility
+    import subprocess
+    nm = subprocess.run(["nm", "-D", "--defined-only", m.LIB_PATH], capture_output=True, text=True)
+    if nm.returncode == 0:
+        exported = {ln.split()[-1] for ln in nm.stdout.splitlines() if " T " in ln}
+        assert exported == names, sorted(exported ^ names)
 
 
 def test_strerror_covers_all_codes():
@@ -197,3 +203,19 @@ def test_moe_route_and_combine_validation():
     assert c(FAKE, m.BF16, 64, FAKE, FAKE, 0, 2, 64, FAKE, m.F32, 64, None) == m.OK                    # T = 0
     assert c(None, m.BF16, 64, FAKE, FAKE, 16, 2, 64, FAKE, m.F32, 64, None) == m.ERR_NULL
     assert c(FAKE, m.BF16, 68, FAKE, FAKE, 16, 2, 64, FAKE, m.F32, 64, None) == m.ERR_ALIGN            # row stride
+
+
+def test_rmsnorm_quantize_validation():
+    f = m.lib.nvfp4_rmsnorm_quantize_act
+    big = lambda: ctypes.byref(ctypes.c_size_t(1 << 24))                                               # noqa: E731
+    assert f(FAKE, 7, 4, 32, 32, FAKE, 1e-6, _t(), FAKE, big(), None) == m.ERR_ARG                     # dtype
+    assert f(FAKE, m.BF16, 4, 32, 32, FAKE, -1.0, _t(), FAKE, big(), None) == m.ERR_ARG                # eps < 0
+    assert f(FAKE, m.BF16, 4, 32, 32, FAKE, float("nan"), _t(), FAKE, big(), None) == m.ERR_ARG        # eps NaN
+    assert f(FAKE, m.BF16, 4, 24, 24, FAKE, 1e-6, _t(), FAKE, big(), None) == m.ERR_SHAPE              # cols % 16
+    assert f(FAKE, m.BF16, 4, 32, 16, FAKE, 1e-6, _t(), FAKE, big(), None) == m.ERR_SHAPE              # ld < cols
+    q = ctypes.c_size_t(0)
+    assert f(None, m.BF16, 1000, 5120, 5120, None, 1e-6, _t(0, 0, 0), None, ctypes.byref(q), None) == m.OK
+    assert q.value >= 1000 * 4 + 4096 * 4
+    assert f(FAKE, m.BF16, 0, 32, 32, None, 1e-6, _t(0, 0, 0), FAKE, big(), None) == m.OK              # rows = 0
+    assert f(FAKE, m.BF16, 4, 32, 32, None, 1e-6, _t(), FAKE, big(), None) == m.ERR_NULL                # gamma
+    assert f(FAKE, m.BF16, 4, 32, 32, FAKE + 4, 1e-6, _t(), FAKE, big(), None) == m.ERR_ALIGN          # gamma align

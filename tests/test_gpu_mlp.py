@@ -118,6 +118,19 @@ def test_mlp_prefill_1024_outliers():
     check_mlp(xbits, wdev, wref, "prefill T1024")
 
 
+@pytest.mark.parametrize("t", [256, 1])
+def test_mlp_tp2_shard_shapes(t):
+    """The tensor-parallel (tp = 2) shard of the MLP on one GPU: gate/up
+    [5120 -> 2 x 8704], down [8704 -> 5120] (8704 is the per-shard width of the
+    vllm.cpp issue's trace, "Problem")."""
+    announce(f"mlp tp=2 shard T={t}")
+    p = WORKLOADS["mlp_prefill_1024x5120x17408"].params
+    k, i = p["K"], p["I"] // 2
+    wdev, wref = _weights(k, i, (6001, 6002, 6003))
+    xb = bf16_normal(6004 + t, (t, k), outliers=outlier_channels(p["outlier_seed"], k))
+    check_mlp(xb, wdev, wref, f"tp2 shard T={t}")
+
+
 def test_launch_count_independent_of_T():
     import mlp_prefill_amd as m
     wdev, _ = _weights(256, 384, (1, 2, 3))
