@@ -26,6 +26,18 @@ bf16(RN32(Y)), round-to-nearest-even.  No residual and no norm sit between the
 layers -- the pages do not describe any around the MLP.  Each call (one ubatch
 through one layer) computes its own activation global scales.
 
+Static global scales (DSV4 audit page, section P0, fix 1): the activation
+global scales are measured once, by a warm-up forward pass, kept on the
+device, and used as given by every later call.  With the scale of H known in
+advance, the GLU output can be quantised by the producer itself, and the down
+projection can emit the next layer's NVFP4 input directly (same page, section
+P8, item 1: quantise in the producer's epilogue instead of writing a
+wide-precision tensor for the consumer to re-read).  Reading taken: the
+warm-up scales are the ones the dynamic path computes on the warm-up batch,
+unchanged (no margin); later inputs beyond 6 * 448 * gs saturate (block scale
+448, codes +-6); the down output that is quantised is RN32 of Y (float32, no
+bf16 step in between).
+
 Grouped (expert) variant: slots are token rows gathered by `a_rows`, grouped by
 expert through `group_offsets`; each expert applies its own weights (with their
 own global scales) to its slots; the GLU output of all slots shares one global
@@ -69,6 +81,32 @@ def mlp(x, w_gate, w_up, w_down):
     """One MLP call on float32 activations x [T, K]; returns every stage."""
     xq = quant.quantize(x)
     h, hq = mlp_gu_act(xq, w_gate, w_up)
+    y = mlp_down(hq, w_down)
+    return {"xq": xq, "h": h, "hq": hq, "y": y}
+
+
+def warmup_scales(x_warm, w_gate, w_up):
+    """Global scales (gs_x, gs_h) that the dynamic path computes on a warm-up batch."""
+    xq = quant.quantize(np.asarray(x_warm, dtype=np.float32))
+    _, hq = mlp_gu_act(xq, w_gate, w_up)
+    return np.float32(xq.gs), np.float32(hq.gs)
+
+
+def mlp_gu_act_static(xq, w_gate, w_up, gs_h):
+    """Gate/up with the given global scale for H~; returns H (float64) and H~."""
+    h = glu(gemm(xq, w_gate), gemm(xq, w_up))
+    return h, quant.quantize(h.astype(np.float32), gs=gs_h)
+
+
+def mlp_down_quant(hq, w_down, gs_y):
+    """Down projection emitting NVFP4 with the given global scale: NVFP4(RN32(Y))."""
+    return quant.quantize(gemm(hq, w_down).astype(np.float32), gs=gs_y)
+
+
+def mlp_static(x, w_gate, w_up, w_down, gs_x, gs_h):
+    """One MLP call with static global scales for x~ and H~; returns every stage."""
+    xq = quant.quantize(np.asarray(x, dtype=np.float32), gs=gs_x)
+    h, hq = mlp_gu_act_static(xq, w_gate, w_up, gs_h)
     y = mlp_down(hq, w_down)
     return {"xq": xq, "h": h, "hq": hq, "y": y}
 

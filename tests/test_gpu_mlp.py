@@ -142,3 +142,25 @@ def test_launch_count_independent_of_T():
         counts.append(m.launch_count() - before)
     assert len(set(counts)) == 1, counts
     assert counts[0] <= 8        # quantise 2, gate/up 3, down 3
+
+
+@pytest.mark.parametrize("t,k,i", [(1000, 384, 1024), (1024, 5120, 17408)], ids=["T1000_K384_I1024", "T1024_K5120_I17408"])
+def test_gate_up_deterministic_any_workspace(t, k, i):
+    """Gate/up output (float32 H and H~) is bit-identical across calls
+    whatever the workspace holds beforehand: no workspace word is read before
+    the call writes it, and every reduction runs in a fixed order."""
+    import mlp_prefill_amd as m
+    announce(f"gate/up determinism T={t} K={k} I={i}")
+    wdev, _ = _weights(k, i, (7001, 7002, 7003))
+    xq = dev_quantize(bf16_normal(7004, (t, k)))
+    need = m.mlp_gu_act_ws_bytes(t, k, i)
+    outs = []
+    for fill in (0x00, 0xFF, 0x5A):
+        ws = torch.full((need,), fill, dtype=torch.uint8, device="cuda")
+        hq = m.NVFP4.empty(t, i)
+        m.nvfp4_mlp_gu_act(xq, wdev[0], wdev[1], hq, ws=ws)
+        torch.cuda.synchronize()
+        outs.append((ws[: t * i * 4].clone().cpu().numpy(), to_host(hq)))
+    for h, hq in outs[1:]:
+        assert np.array_equal(h, outs[0][0])
+        assert_nvfp4_equal(hq, outs[0][1], "H~ across workspaces")
