@@ -191,6 +191,41 @@ int nvfp4_mlp_down(nvfp4_tensor h, nvfp4_tensor w_down, int64_t T, int64_t I, in
                    void *y, int y_dtype, int64_t ldy, void *ws, size_t *ws_bytes, void *stream);
 
 /*
+ * nvfp4_mlp_gu_act_static -- nvfp4_mlp_gu_act with a static global scale
+ * for H~.  [dsv4] P0, fix 1: the activation global scales are measured once
+ * by a warm-up pass (for instance the scale nvfp4_mlp_gu_act wrote to its
+ * h_out.gscale) and kept on the device; [dsv4] P8, item 1: with the scale
+ * known in advance the producer quantises its own output.  *h_out.gscale is
+ * READ on the device (never written); the GLU output is quantised in the
+ * contraction's epilogue (values above 6 * 448 * gscale saturate to block
+ * scale 448 and codes +-6), so no float32 H is written and no amax or
+ * requantisation pass runs.
+ *   x, w_gate, w_up, K, I : as nvfp4_mlp_gu_act
+ *   h_out : [T][I] NVFP4; codes and scales written, gscale read
+ *   ws    : required (the f16 copy of x~)
+ * Two launches per call (expansion, contraction), independent of T.
+ */
+int nvfp4_mlp_gu_act_static(nvfp4_tensor x, nvfp4_tensor w_gate, nvfp4_tensor w_up,
+                            int64_t T, int64_t K, int64_t I, nvfp4_tensor h_out,
+                            void *ws, size_t *ws_bytes, void *stream);
+
+/*
+ * nvfp4_mlp_down_quant -- the down projection emitting NVFP4 directly:
+ * y_out = NVFP4(Y) with Y = (H~ . Wd~^T) * gscale_h * gscale_wd in float32
+ * (the values nvfp4_mlp_down stores as float32) and the global scale
+ * *y_out.gscale READ on the device -- the next layer's static input scale
+ * ([dsv4] P8, item 1: no wide-precision output for the consumer to
+ * re-quantise; P0, fix 1: scale from a warm-up pass).
+ *   h : [T][I] NVFP4;  w_down : [K][I] NVFP4;  I multiple of 128,
+ *   K multiple of 16;  y_out : [T][K] NVFP4 (codes, scales written)
+ *   ws : required, as nvfp4_mlp_down
+ * Three launches per call (expansion, contraction, quantising split
+ * reduction), independent of T.
+ */
+int nvfp4_mlp_down_quant(nvfp4_tensor h, nvfp4_tensor w_down, int64_t T, int64_t I, int64_t K,
+                         nvfp4_tensor y_out, void *ws, size_t *ws_bytes, void *stream);
+
+/*
  * nvfp4_grouped_gemm -- expert-grouped NVFP4 GEMM in one launch per GEMM
  * ([llama] "Verified", MUL_MAT_ID; [dsv4] P8 item 5: no host syncs, no
  * dynamic shapes).  Slot s (0 <= s < M) reads activation row a_rows[s] of a

@@ -45,6 +45,10 @@ _sig = {
                          ctypes.POINTER(ctypes.c_size_t), _vp],
     "nvfp4_mlp_down": [nvfp4_tensor, nvfp4_tensor, _i64, _i64, _i64, _vp, ctypes.c_int, _i64, _vp,
                        ctypes.POINTER(ctypes.c_size_t), _vp],
+    "nvfp4_mlp_gu_act_static": [nvfp4_tensor, nvfp4_tensor, nvfp4_tensor, _i64, _i64, _i64, nvfp4_tensor, _vp,
+                                ctypes.POINTER(ctypes.c_size_t), _vp],
+    "nvfp4_mlp_down_quant": [nvfp4_tensor, nvfp4_tensor, _i64, _i64, _i64, nvfp4_tensor, _vp,
+                             ctypes.POINTER(ctypes.c_size_t), _vp],
     "nvfp4_grouped_gemm": [nvfp4_tensor, _vp, _vp, ctypes.c_int, _i64, nvfp4_tensor, nvfp4_tensor, _i64, _i64,
                            ctypes.c_int, _vp, ctypes.c_int, _i64, nvfp4_tensor, _vp,
                            ctypes.POINTER(ctypes.c_size_t), _vp],
@@ -221,6 +225,48 @@ def nvfp4_mlp_gu_act(x, w_gate, w_up, h_out, ws=None, stream=None):
     _check(_lib.nvfp4_mlp_gu_act(x.c(), w_gate.c(), w_up.c(), t, k, i, h_out.c(), _ptr(ws), ctypes.byref(sz),
                                  _stream(stream)), "nvfp4_mlp_gu_act")
     return ws
+
+
+def mlp_gu_act_static_ws_bytes(t, k, i):
+    """Workspace bytes nvfp4_mlp_gu_act_static needs."""
+    size = ctypes.c_size_t(0)
+    _check(_lib.nvfp4_mlp_gu_act_static(_null_tensor(), _null_tensor(), _null_tensor(), t, k, i, _null_tensor(),
+                                        _vp(0), ctypes.byref(size), _vp(0)), "workspace query")
+    return size.value
+
+
+def nvfp4_mlp_gu_act_static(x, w_gate, w_up, h_out, ws=None, stream=None):
+    """h_out (NVFP4 [T, I]) = NVFP4(SiLU(x~ . Wg~^T) * (x~ . Wu~^T)) with the global
+    scale already stored in h_out.gscale (read on the device)."""
+    t, k, i = x.rows, x.cols, w_gate.rows
+    need = mlp_gu_act_static_ws_bytes(t, k, i)
+    if ws is None:
+        ws = torch.empty(max(need, 256), dtype=torch.uint8, device=x.codes.device)
+    sz = ctypes.c_size_t(ws.numel())
+    _check(_lib.nvfp4_mlp_gu_act_static(x.c(), w_gate.c(), w_up.c(), t, k, i, h_out.c(), _ptr(ws),
+                                        ctypes.byref(sz), _stream(stream)), "nvfp4_mlp_gu_act_static")
+    return h_out
+
+
+def mlp_down_quant_ws_bytes(t, i, k):
+    """Workspace bytes nvfp4_mlp_down_quant needs."""
+    size = ctypes.c_size_t(0)
+    _check(_lib.nvfp4_mlp_down_quant(_null_tensor(), _null_tensor(), t, i, k, _null_tensor(), _vp(0),
+                                     ctypes.byref(size), _vp(0)), "workspace query")
+    return size.value
+
+
+def nvfp4_mlp_down_quant(h, w_down, y_out, ws=None, stream=None):
+    """y_out (NVFP4 [T, K]) = NVFP4(H~ . Wd~^T * gs_h * gs_wd) with the global scale
+    already stored in y_out.gscale (read on the device)."""
+    t, i, kk = h.rows, h.cols, w_down.rows
+    need = mlp_down_quant_ws_bytes(t, i, kk)
+    if ws is None:
+        ws = torch.empty(max(need, 256), dtype=torch.uint8, device=h.codes.device)
+    sz = ctypes.c_size_t(ws.numel())
+    _check(_lib.nvfp4_mlp_down_quant(h.c(), w_down.c(), t, i, kk, y_out.c(), _ptr(ws), ctypes.byref(sz),
+                                     _stream(stream)), "nvfp4_mlp_down_quant")
+    return y_out
 
 
 def mlp_down_ws_bytes(t, i, k):

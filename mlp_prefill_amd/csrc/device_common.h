@@ -138,6 +138,26 @@ __device__ __forceinline__ uint32_t e2m1_code(float x, const float T[7]) {
   return ((__float_as_uint(x) >> 31) << 3) | idx;
 }
 
+// One 16-element block with global scale gs -> its E4M3 scale code (the
+// return value) and its sixteen E2M1 codes packed low nibble first (w0:
+// elements 0..7, w1: elements 8..15).  Both roundings are decided exactly.
+__device__ __forceinline__ uint32_t quantize_block16(const float v[16], float gs, uint32_t& w0, uint32_t& w1) {
+  float amax_b = 0.f;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) amax_b = fmaxf(amax_b, fabsf(v[i]));
+  const uint32_t s = e4m3_block_scale(amax_b, gs);
+  float thr[7];
+  e2m1_thresholds(e4m3_value(s) * (double)gs, thr);
+  w0 = 0;
+  w1 = 0;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    w0 |= e2m1_code(v[i], thr) << (4 * i);
+    w1 |= e2m1_code(v[8 + i], thr) << (4 * i);
+  }
+  return s;
+}
+
 // ---- NVFP4 -> f16 expansion for the matrix cores ---------------------------
 // Eight packed E2M1 codes (one dword, element j in bits 4j+3:4j) and their
 // E4M3 scale code s -> eight f16 values code_j * dec(s), exactly.  The

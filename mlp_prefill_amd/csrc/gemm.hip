@@ -72,6 +72,10 @@ struct GemmArgs {
   uint32_t n_tiles;
   uint32_t splits;
   uint32_t chunks_per_split;
+  int force_split;        // store epilogue: write split_out even when splits == 1
+  uint8_t* q_codes;       // EPI_GLUQ output [M][N] NVFP4 and its given global scale
+  uint8_t* q_scales;
+  const float* q_gs;
 };
 
 // ---- expansion of the activation operand ------------------------------------------
@@ -125,7 +129,9 @@ __device__ __forceinline__ void expand_b(const BPack<TN, DUAL>& f, BExp<TN, DUAL
   }
 }
 
-enum { EPI_STORE = 0, EPI_GLU = 1 };
+// EPI_GLUQ: the GLU output quantised in the epilogue with a given global
+// scale (no float32 H, no requantisation launch).
+enum { EPI_STORE = 0, EPI_GLU = 1, EPI_GLUQ = 2 };
 
 // Per-chunk LDS staging (one 128-wide K chunk):
 //   activations: BM rows x 16 slots of 16 B (f16); row r keeps K segment g
@@ -590,6 +596,49 @@ __global__ void __launch_bounds__(WN * 64, MINWG) gemm_kernel(GemmArgs p) {
   }
 
   // ---- epilogue ---------------------------------------------------------------------
+  if constexpr (EPI == EPI_GLUQ) {
+    // SiLU(gate) * up of the whole tile goes to LDS (the stage buffers are
+    // free once every wave is past the main loop), then each thread quantises
+    // whole 16-column blocks of it with the given global scale.  Columns are
+    // XOR-swizzled in units of four floats by the row, so the two row halves
+    // of an MFMA fragment store to different banks.
+    static_assert(DUAL && !GROUPED, "quantising GLU epilogue: dense gate/up pair");
+    static_assert(BM * C::BN * 4 <= (int)sizeof(lds_b), "GLU tile must fit the stage buffers");
+    float* tile = reinterpret_cast<float*>(&lds_b[0][0]);
+    const float alpha = p.a_gs[0] * p.b_gs[0];
+    const float alpha_u = p.a_gs[0] * p.u_gs[0];
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+      for (int j = 0; j < TN; ++j) {
+        const int col = (wn * TN + j) * 32 + r32;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int row = i * 32 + 8 * (r >> 2) + 4 * hh + (r & 3);
+          tile[row * C::BN + (col ^ ((row & 7) << 2))] = silu_mul(x.acc[i][j][r] * alpha, x.accu[i][j][r] * alpha_u);
+        }
+      }
+    __syncthreads();
+    const float gs = p.q_gs[0];
+    constexpr int NBC = C::BN / 16;
+    for (int q = threadIdx.x; q < BM * NBC; q += C::NT) {
+      const int row = q / NBC, cb = q - row * NBC;
+      const int64_t grow = m0 + row, gcol = n0 + cb * 16;
+      if (grow >= m_end || gcol >= p.N) continue;
+      float v[16];
+#pragma unroll
+      for (int g4 = 0; g4 < 4; ++g4) {
+        const float4 t4 = *reinterpret_cast<const float4*>(tile + row * C::BN + ((cb * 16 + 4 * g4) ^ ((row & 7) << 2)));
+        v[4 * g4] = t4.x; v[4 * g4 + 1] = t4.y; v[4 * g4 + 2] = t4.z; v[4 * g4 + 3] = t4.w;
+      }
+      uint32_t w0, w1;
+      const uint32_t sc = quantize_block16(v, gs, w0, w1);
+      *reinterpret_cast<uint2*>(p.q_codes + grow * (p.N / 2) + gcol / 2) = make_uint2(w0, w1);
+      p.q_scales[grow * (p.N / 16) + gcol / 16] = (uint8_t)sc;
+    }
+    return;
+  }
   const float alpha = p.a_gs[0] * p.b_gs[GROUPED ? e : 0];
   float alpha_u = 0.f;
   if constexpr (DUAL) alpha_u = p.a_gs[0] * p.u_gs[GROUPED ? e : 0];
@@ -608,7 +657,7 @@ __global__ void __launch_bounds__(WN * 64, MINWG) gemm_kernel(GemmArgs p) {
             p.h[row * p.N + col] = hv;
             hmax = fmaxf(hmax, fabsf(hv));
           } else {
-            if (p.splits > 1) {
+            if (p.splits > 1 || p.force_split) {
               p.split_out[((int64_t)split * p.M + row) * p.N + col] = x.acc[i][j][r];
             } else {
               const float v = x.acc[i][j][r] * alpha;
@@ -662,6 +711,7 @@ __global__ void __launch_bounds__(kSkWaves * 64) skinny_kernel(GemmArgs p) {
   constexpr int NM = DUAL ? 2 : 1;
   __shared__ float red[kSkWaves * NM * 16 * 64];
   __shared__ float redmax[kSkWaves];
+  __shared__ float tq[EPI == EPI_GLUQ ? 32 * 33 : 1];
   const int lane = threadIdx.x & 63;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave-uniform: keeps the loop scalar
   const int r32 = lane & 31, hh = lane >> 5;
@@ -775,12 +825,16 @@ __global__ void __launch_bounds__(kSkWaves * 64) skinny_kernel(GemmArgs p) {
     }
     const int64_t row = 8 * (r >> 2) + 4 * (l >> 5) + (r & 3);
     const int64_t col = n0 + (l & 31);
+    if constexpr (EPI == EPI_GLUQ) {
+      tq[row * 33 + (l & 31)] = silu_mul(g * alpha, u * alpha_u);
+      continue;
+    }
     if (row < p.M && col < p.N) {
       if constexpr (EPI == EPI_GLU) {
         const float hv = silu_mul(g * alpha, u * alpha_u);
         p.h[row * p.N + col] = hv;
         hmax = fmaxf(hmax, fabsf(hv));
-      } else if (p.splits > 1) {
+      } else if (p.splits > 1 || p.force_split) {
         p.split_out[((int64_t)split * p.M + row) * p.N + col] = g;
       } else {
         const float v = g * alpha;
@@ -794,6 +848,22 @@ __global__ void __launch_bounds__(kSkWaves * 64) skinny_kernel(GemmArgs p) {
   if constexpr (EPI == EPI_GLU) {
     hmax = block_max(hmax, redmax);
     if (threadIdx.x == 0) p.partials[blockIdx.x] = hmax;
+  }
+  if constexpr (EPI == EPI_GLUQ) {
+    // the 32 x 32 tile (rows past M are computed, never stored): threads
+    // 0..63 quantise its two 16-column blocks per row
+    __syncthreads();
+    const int row = (int)threadIdx.x >> 1, half = (int)threadIdx.x & 1;
+    const int64_t gcol = n0 + 16 * half;
+    if (threadIdx.x < 64 && row < p.M && gcol < p.N) {
+      float v[16];
+#pragma unroll
+      for (int c = 0; c < 16; ++c) v[c] = tq[row * 33 + 16 * half + c];
+      uint32_t w0, w1;
+      const uint32_t sc = quantize_block16(v, p.q_gs[0], w0, w1);
+      *reinterpret_cast<uint2*>(p.q_codes + row * (p.N / 2) + gcol / 2) = make_uint2(w0, w1);
+      p.q_scales[row * (p.N / 16) + gcol / 16] = (uint8_t)sc;
+    }
   }
 }
 
@@ -817,6 +887,43 @@ __global__ void __launch_bounds__(256) splitk_reduce_kernel(const float* __restr
       reinterpret_cast<uint16_t*>(out)[m * ldo + n] = (uint16_t)f32_to_bf16_bits(v);
     else
       reinterpret_cast<float*>(out)[m * ldo + n] = v;
+  }
+}
+
+// The same reduction, quantised: each thread takes whole 16-column blocks,
+// adds the splits in split order, scales by gs_a * gs_b (the float32 values
+// splitk_reduce_kernel would store) and quantises them with the given global
+// scale.
+__global__ void __launch_bounds__(256) splitk_reduce_quant_kernel(const float* __restrict__ part, uint32_t splits,
+                                                                  int64_t M, int64_t N, const float* a_gs,
+                                                                  const float* b_gs, const float* q_gs,
+                                                                  uint8_t* __restrict__ codes,
+                                                                  uint8_t* __restrict__ scales) {
+  const int64_t nbc = N / 16, total = M * nbc, plane = M * N;
+  const float alpha = a_gs[0] * b_gs[0];
+  const float gs = q_gs[0];
+  for (int64_t b = (int64_t)blockIdx.x * 256 + threadIdx.x; b < total; b += (int64_t)gridDim.x * 256) {
+    const int64_t m = b / nbc, cb = b - m * nbc;
+    const float* src = part + m * N + cb * 16;
+    float v[16];
+#pragma unroll
+    for (int c = 0; c < 16; ++c) v[c] = 0.f;
+    for (uint32_t sp = 0; sp < splits; ++sp) {
+#pragma unroll
+      for (int g4 = 0; g4 < 4; ++g4) {
+        const float4 t4 = *reinterpret_cast<const float4*>(src + (int64_t)sp * plane + 4 * g4);
+        v[4 * g4] += t4.x;
+        v[4 * g4 + 1] += t4.y;
+        v[4 * g4 + 2] += t4.z;
+        v[4 * g4 + 3] += t4.w;
+      }
+    }
+#pragma unroll
+    for (int c = 0; c < 16; ++c) v[c] *= alpha;
+    uint32_t w0, w1;
+    const uint32_t sc = quantize_block16(v, gs, w0, w1);
+    *reinterpret_cast<uint2*>(codes + b * 8) = make_uint2(w0, w1);
+    scales[b] = (uint8_t)sc;
   }
 }
 
@@ -858,7 +965,7 @@ static Plan plan_store(int64_t M, int64_t N, int64_t K, int E, bool grouped) {
 template <bool DUAL, int EPI>
 static void launch_skinny(const GemmArgs& g, hipStream_t st) {
   const uint32_t grid = g.n_tiles * g.splits;
-  const int slot = launch_begin(EPI == EPI_GLU ? KC_GEMM_GLU : KC_GEMM_STORE, st);
+  const int slot = launch_begin(EPI != EPI_STORE ? KC_GEMM_GLU : KC_GEMM_STORE, st);
   hipLaunchKernelGGL((skinny_kernel<DUAL, EPI>), dim3(grid), dim3(kSkWaves * 64), 0, st, g);
   launch_end(slot, st);
 }
@@ -866,9 +973,9 @@ static void launch_skinny(const GemmArgs& g, hipStream_t st) {
 template <int WN, int TM, int TN, bool DUAL, bool GROUPED, int EPI>
 static void launch_cfg(const GemmArgs& g, hipStream_t st) {
   const uint32_t grid = g.m_tiles * g.n_tiles * g.splits;
-  const int slot = launch_begin(EPI == EPI_GLU ? KC_GEMM_GLU : KC_GEMM_STORE, st);
-  constexpr int NS = EPI == EPI_GLU ? NVFP4_GLU_STAGES : NVFP4_STORE_STAGES;
-  constexpr int MW = EPI == EPI_GLU ? NVFP4_GLU_MINWG : NVFP4_STORE_MINWG;
+  const int slot = launch_begin(EPI != EPI_STORE ? KC_GEMM_GLU : KC_GEMM_STORE, st);
+  constexpr int NS = EPI != EPI_STORE ? NVFP4_GLU_STAGES : NVFP4_STORE_STAGES;
+  constexpr int MW = EPI != EPI_STORE ? NVFP4_GLU_MINWG : NVFP4_STORE_MINWG;
   hipLaunchKernelGGL((gemm_kernel<WN, TM, TN, DUAL, GROUPED, EPI, NS, MW>), dim3(grid), dim3(WN * 64), 0, st, g);
   launch_end(slot, st);
 }
@@ -989,6 +1096,57 @@ int glu_launch(Operand a, const int32_t* a_rows, const int32_t* off, int E, int6
   }
   if (hipGetLastError() != hipSuccess) return 7;
   return requant_f32_launch(h, M, N, hq_codes, hq_scales, hq_gs, partials, glu_parts(M, N, E, grouped), st);
+}
+
+size_t glu_static_ws_bytes(int64_t M, int64_t K) { return align256((size_t)M * K * 2); }
+
+int glu_static_launch(Operand a, int64_t M, Operand gt, Operand up, int64_t N, int64_t K, uint8_t* hq_codes,
+                      uint8_t* hq_scales, const float* hq_gs, void* ws, hipStream_t st) {
+  _Float16* a16 = reinterpret_cast<_Float16*>(ws);
+  launch_expand(a.codes, a.scales, nullptr, M, K, a16, st);
+  GemmArgs g = base_args(a16, a.gscale, gt, M, N, K);
+  g.u_codes = up.codes;
+  g.u_scales = up.scales;
+  g.u_gs = up.gscale;
+  g.q_codes = hq_codes;
+  g.q_scales = hq_scales;
+  g.q_gs = hq_gs;
+  g.chunks_per_split = (uint32_t)(K / 128);
+  if (M <= 32) {
+    g.m_tiles = 1;
+    g.n_tiles = cdiv(N, 32);
+    launch_skinny<true, EPI_GLUQ>(g, st);
+  } else {
+    g.m_tiles = cdiv(M, 32 * NVFP4_GLU_TM);
+    g.n_tiles = cdiv(N, 32 * NVFP4_GLU_WN);
+    launch_cfg<NVFP4_GLU_WN, NVFP4_GLU_TM, 1, true, false, EPI_GLUQ>(g, st);
+  }
+  return hipGetLastError() == hipSuccess ? 0 : 7;
+}
+
+int store_quant_launch(Operand a, int64_t M, Operand w, int64_t N, int64_t K, uint8_t* yq_codes, uint8_t* yq_scales,
+                       const float* yq_gs, void* ws, hipStream_t st) {
+  _Float16* a16 = reinterpret_cast<_Float16*>(ws);
+  float* part = reinterpret_cast<float*>(reinterpret_cast<char*>(ws) + align256((size_t)M * K * 2));
+  launch_expand(a.codes, a.scales, nullptr, M, K, a16, st);
+  const Plan pl = plan_store(M, N, K, 1, false);
+  GemmArgs g = base_args(a16, a.gscale, w, M, N, K);
+  g.splits = pl.splits;
+  g.chunks_per_split = pl.chunks_per_split;
+  g.split_out = part;
+  g.force_split = 1;
+  g.m_tiles = pl.m_tiles;
+  g.n_tiles = pl.n_tiles;
+  if (pl.small) launch_skinny<false, EPI_STORE>(g, st);
+  else launch_cfg<NVFP4_STORE_WN, NVFP4_STORE_TM, 1, false, false, EPI_STORE>(g, st);
+  int64_t blocks = (M * (N / 16) + 255) / 256;
+  if (blocks > 8192) blocks = 8192;
+  if (blocks < 1) blocks = 1;
+  const int slot = launch_begin(KC_REDUCE, st);
+  hipLaunchKernelGGL(splitk_reduce_quant_kernel, dim3((uint32_t)blocks), dim3(256), 0, st, part, pl.splits, M, N,
+                     a.gscale, w.gscale, yq_gs, yq_codes, yq_scales);
+  launch_end(slot, st);
+  return hipGetLastError() == hipSuccess ? 0 : 7;
 }
 
 }  // namespace nvfp4

@@ -258,6 +258,38 @@ int nvfp4_mlp_down(nvfp4_tensor h, nvfp4_tensor w_down, int64_t T, int64_t I, in
                              reinterpret_cast<hipStream_t>(stream));
 }
 
+int nvfp4_mlp_gu_act_static(nvfp4_tensor x, nvfp4_tensor w_gate, nvfp4_tensor w_up, int64_t T, int64_t K, int64_t I,
+                            nvfp4_tensor h_out, void* ws, size_t* ws_bytes, void* stream) {
+  if (T < 0 || K <= 0 || I <= 0 || K % 128 != 0 || I % 128 != 0) return NVFP4_ERR_SHAPE;
+  if (T * (I / 16) >= ((int64_t)1 << 31) || T * (K / 16) >= ((int64_t)1 << 31)) return NVFP4_ERR_SHAPE;
+  bool query;
+  int rc = workspace(ws, ws_bytes, T > 0 ? nvfp4::glu_static_ws_bytes(T, K) : 0, &query);
+  if (rc != NVFP4_OK || query) return rc;
+  if (T == 0) return NVFP4_OK;
+  if ((rc = check_tensor(x)) != NVFP4_OK || (rc = check_tensor(w_gate)) != NVFP4_OK ||
+      (rc = check_tensor(w_up)) != NVFP4_OK || (rc = check_tensor(h_out)) != NVFP4_OK)
+    return rc;
+  if ((rc = check_device()) != NVFP4_OK) return rc;
+  return nvfp4::glu_static_launch(op(x), T, op(w_gate), op(w_up), I, K, h_out.codes, h_out.scales, h_out.gscale, ws,
+                                  reinterpret_cast<hipStream_t>(stream));
+}
+
+int nvfp4_mlp_down_quant(nvfp4_tensor h, nvfp4_tensor w_down, int64_t T, int64_t I, int64_t K, nvfp4_tensor y_out,
+                         void* ws, size_t* ws_bytes, void* stream) {
+  if (T < 0 || I <= 0 || K <= 0 || I % 128 != 0 || K % 16 != 0) return NVFP4_ERR_SHAPE;
+  if (T * (I / 16) >= ((int64_t)1 << 31) || T * (K / 16) >= ((int64_t)1 << 31)) return NVFP4_ERR_SHAPE;
+  bool query;
+  int rc = workspace(ws, ws_bytes, T > 0 ? nvfp4::store_ws_bytes(T, K, I, 1, false) : 0, &query);
+  if (rc != NVFP4_OK || query) return rc;
+  if (T == 0) return NVFP4_OK;
+  if ((rc = check_tensor(h)) != NVFP4_OK || (rc = check_tensor(w_down)) != NVFP4_OK ||
+      (rc = check_tensor(y_out)) != NVFP4_OK)
+    return rc;
+  if ((rc = check_device()) != NVFP4_OK) return rc;
+  return nvfp4::store_quant_launch(op(h), T, op(w_down), K, I, y_out.codes, y_out.scales, y_out.gscale, ws,
+                                   reinterpret_cast<hipStream_t>(stream));
+}
+
 int nvfp4_moe_route(const float* logits, int64_t T, int E, int k, int64_t ld, int32_t* group_offsets,
                     int32_t* a_rows, int32_t* slot_of, float* weights, void* ws, size_t* ws_bytes, void* stream) {
   if (E < 1 || E > nvfp4::kMaxExperts || k < 1 || k > nvfp4::kMaxTopK || k > E) return NVFP4_ERR_ARG;

@@ -100,18 +100,8 @@ __global__ void __launch_bounds__(256) quantize_kernel(const T* __restrict__ x, 
 #pragma unroll
       for (int i = 0; i < 16; ++i) v[i] = (v[i] * r) * g[i];
     }
-    float amax_b = 0.f;
-#pragma unroll
-    for (int i = 0; i < 16; ++i) amax_b = fmaxf(amax_b, fabsf(v[i]));
-    const uint32_t s = e4m3_block_scale(amax_b, gs);
-    float thr[7];
-    e2m1_thresholds(e4m3_value(s) * (double)gs, thr);
-    uint32_t w0 = 0, w1 = 0;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      w0 |= e2m1_code(v[i], thr) << (4 * i);
-      w1 |= e2m1_code(v[8 + i], thr) << (4 * i);
-    }
+    uint32_t w0, w1;
+    const uint32_t s = quantize_block16(v, gs, w0, w1);
     const int64_t boff = (int64_t)row * nbc + cb;
     *reinterpret_cast<uint2*>(codes + boff * 8) = make_uint2(w0, w1);
     scales[boff] = (uint8_t)s;

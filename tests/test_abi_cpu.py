@@ -118,6 +118,30 @@ def test_gu_act_validation_and_workspace():
     assert f(z, z, z, 0, 128, 128, z, FAKE, ctypes.byref(big), None) == m.OK
 
 
+def test_static_scale_entry_points_validation_and_workspace():
+    f = m.lib.nvfp4_mlp_gu_act_static
+    z = nvfp4_tensor(0, 0, 0)
+    s = _size()
+    assert f(z, z, z, 1024, 5120, 17408, z, None, ctypes.byref(s), None) == m.OK
+    assert s.value == 1024 * 5120 * 2                     # only the f16 copy of x~: no float32 H
+    assert f(z, z, z, 4, 5120, 17400, z, None, ctypes.byref(s), None) == m.ERR_SHAPE
+    small = ctypes.c_size_t(1024)
+    assert f(_t(), _t(), _t(), 64, 128, 128, _t(), FAKE, ctypes.byref(small), None) == m.ERR_WORKSPACE
+    big = ctypes.c_size_t(1 << 24)
+    assert f(_t(), _t(), _t(), 4, 128, 128, _t(g=0), FAKE, ctypes.byref(big), None) == m.ERR_NULL   # gscale read
+    assert f(_t(), _t(), _t(), 4, 128, 128, _t(s=FAKE + 4), FAKE, ctypes.byref(big), None) == m.ERR_ALIGN
+    assert f(z, z, z, 0, 128, 128, z, FAKE, ctypes.byref(big), None) == m.OK
+    d = m.lib.nvfp4_mlp_down_quant
+    assert d(z, z, 1024, 17408, 5120, z, None, ctypes.byref(s), None) == m.OK
+    s2 = _size()
+    assert m.lib.nvfp4_mlp_down(z, z, 1024, 17408, 5120, None, m.F32, 5120, None, ctypes.byref(s2), None) == m.OK
+    assert s.value == s2.value                            # same split plan as the float32 down projection
+    assert d(_t(), _t(), 4, 100, 64, _t(), FAKE, ctypes.byref(big), None) == m.ERR_SHAPE      # I % 128
+    assert d(_t(), _t(), 4, 128, 40, _t(), FAKE, ctypes.byref(big), None) == m.ERR_SHAPE      # K % 16
+    assert d(_t(), _t(), 4, 128, 64, _t(c=0), FAKE, ctypes.byref(big), None) == m.ERR_NULL
+    assert d(_t(), _t(), 0, 128, 64, z, FAKE, ctypes.byref(big), None) == m.OK
+
+
 def test_grouped_validation():
     f = m.lib.nvfp4_grouped_gemm
     sz = ctypes.c_size_t(1 << 30)
@@ -152,6 +176,9 @@ def test_valid_calls_report_missing_device_and_launch_nothing():
     assert m.lib.nvfp4_gemm(_t(), _t(), 4, 8, 128, FAKE, m.F32, 8, FAKE, ctypes.byref(big), None) == m.ERR_DEVICE
     assert m.lib.nvfp4_mlp_gu_act(_t(), _t(), _t(), 4, 128, 128, _t(), FAKE, ctypes.byref(big), None) == m.ERR_DEVICE
     assert m.lib.nvfp4_mlp_down(_t(), _t(), 4, 128, 64, FAKE, m.F32, 64, FAKE, ctypes.byref(big), None) == m.ERR_DEVICE
+    assert m.lib.nvfp4_mlp_gu_act_static(_t(), _t(), _t(), 4, 128, 128, _t(), FAKE, ctypes.byref(big),
+                                         None) == m.ERR_DEVICE
+    assert m.lib.nvfp4_mlp_down_quant(_t(), _t(), 4, 128, 64, _t(), FAKE, ctypes.byref(big), None) == m.ERR_DEVICE
     assert m.lib.nvfp4_launch_count() == before
 
 
