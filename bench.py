@@ -240,6 +240,8 @@ def main():
     extra = {}
     if not args.no_extra:
         extra = extra_lines(m)
+        log("extra: long prefill with static global scales")
+        extra["static_gs"] = static_line(m, layers, x_all, args.steps)
         extra["decode_stack"] = decode_stack_line(m, layers)
         extra["quantize"] = quantize_line(m)
 
@@ -260,6 +262,56 @@ def main():
         log(f"cpu baseline {cb['value'] * 1e3:.2f} GFLOP/s on {cb['cores']} threads")
     print(json.dumps(result), flush=True)
     return 0
+
+
+def static_line(m, layers, x_all, steps, ub=1024):
+    """The long-prefill workload with static global scales: one dynamic
+    warm-up ubatch records every layer's input and GLU-output scales on the
+    device; the timed passes quantise the first layer's input with its given
+    scale, quantise each GLU output in the gate/up epilogue and let each down
+    projection but the last emit the next layer's NVFP4 input directly."""
+    t_all, k = x_all.shape
+    i = layers[0].w[0].rows
+    n_l = len(layers)
+    xq = [m.NVFP4.empty(ub, k) for _ in range(n_l)]
+    hq = [m.NVFP4.empty(ub, i) for _ in range(n_l)]
+    ws_q = torch.empty(m.ws_bytes_quantize(ub, k), dtype=torch.uint8, device="cuda")
+    ws_gu = torch.empty(max(m.mlp_gu_act_ws_bytes(ub, k, i), 256), dtype=torch.uint8, device="cuda")
+    ws_dn = torch.empty(max(m.mlp_down_ws_bytes(ub, i, k), 256), dtype=torch.uint8, device="cuda")
+    ybf = torch.empty((ub, k), dtype=torch.bfloat16, device="cuda")
+    out = torch.empty((t_all, k), dtype=torch.bfloat16, device="cuda")
+    # warm-up: the dynamic path on ubatch 0 writes each scale into the tensors kept for the static passes
+    cur = x_all[:ub]
+    for li, layer in enumerate(layers):
+        m.nvfp4_quantize_act(cur, xq[li], ws=ws_q)
+        m.nvfp4_mlp_gu_act(xq[li], layer.w[0], layer.w[1], hq[li], ws=ws_gu)
+        m.nvfp4_mlp_down(hq[li], layer.w[2], ybf, ws=ws_dn)
+        cur = ybf
+    torch.cuda.synchronize()
+
+    def step():
+        for u in range(t_all // ub):
+            m.nvfp4_quantize_act(x_all[u * ub:(u + 1) * ub], xq[0], gs_mode=m.GS_GIVEN, ws=ws_q)
+            for li, layer in enumerate(layers):
+                m.nvfp4_mlp_gu_act_static(xq[li], layer.w[0], layer.w[1], hq[li], ws=ws_gu)
+                if li + 1 < n_l:
+                    m.nvfp4_mlp_down_quant(hq[li], layer.w[2], xq[li + 1], ws=ws_dn)
+                else:
+                    m.nvfp4_mlp_down(hq[li], layer.w[2], out[u * ub:(u + 1) * ub], ws=ws_dn)
+
+    step()
+    torch.cuda.synchronize()
+    b0 = m.launch_count()
+    step()
+    launches = (m.launch_count() - b0) // (t_all // ub)
+    ms = sorted(time_events(step, steps, warm=1))
+    med = ms[len(ms) // 2]
+    flops = mlp_flops(t_all, k, i) * n_l
+    return {"workload": "mlp_long_prefill_16x1024_4layers, static global scales (warm-up on ubatch 0)",
+            "ms_per_step": med, "TFLOP/s": flops / (med * 1e-3) / 1e12, "tokens_per_s": t_all / (med * 1e-3),
+            "launches_per_ubatch": launches,
+            "path": "quantise(given gs) -> [gate/up with quantising epilogue -> down emitting the next "
+                    "layer's NVFP4 input] x 3 -> gate/up -> down (bf16)"}
 
 
 def extra_lines(m):
