@@ -8,11 +8,12 @@
 // combine weights are the softmax over those k logits; slots are the
 // (token, choice) pairs sorted by (expert, token).
 //
-// Three launches: route_topk_kernel (top-k, weights, each choice's rank among
-// its 64-token block's choices of the same expert, per-block expert counts),
-// route_scan_kernel (block counts -> slot offsets, one work-group) and
-// route_scatter_kernel (slot of every choice).  No atomics: the slot order is
-// the same on every run.
+// Three launches: route_topk_wave_kernel (route_topk_kernel for more than 128
+// experts) gives each token's top-k, its weights, each choice's rank among its
+// 64-token block's choices of the same expert and the per-block expert
+// counts; route_scan_kernel turns the counts into per-block and per-expert
+// offsets (one work-group); route_scatter_kernel places every choice in its
+// slot.  No atomics: the slot order is the same on every run.
 #include "device_common.h"
 #include "internal.h"
 
@@ -21,6 +22,7 @@ namespace nvfp4 {
 constexpr int kRouteWg = 256;      // threads per work-group; one token per thread
 constexpr int kRouteBlock = 64;    // tokens per routing block (one wave)
 constexpr int kScanThreads = 1024;
+constexpr int kTopkBatch = 16;     // logits loaded together per token
 
 __global__ void __launch_bounds__(kRouteWg) route_topk_kernel(const float* __restrict__ logits, int64_t T, int E,
                                                               int k, int64_t ld, int32_t* __restrict__ ids,
@@ -39,25 +41,33 @@ __global__ void __launch_bounds__(kRouteWg) route_topk_kernel(const float* __res
   }
   if (valid) {
     const float* row = logits + t * ld;
-    for (int e = 0; e < E; ++e) {
-      // insert into the list sorted by (logit desc, id asc): the new expert
-      // goes before the first entry with a strictly smaller logit (equal
-      // logits keep the lower, earlier id first); every entry below shifts
-      // down by one, the last one falls off
-      float cv = row[e];
-      int ci = e;
-      bool ins = false;
+    for (int e0 = 0; e0 < E; e0 += kTopkBatch) {
+      // the batch's logits are loaded together, then inserted in expert order
+      float lv[kTopkBatch];
 #pragma unroll
-      for (int j = 0; j < kMaxTopK; ++j) {
-        if (j < k) {
-          const bool take = ins || cv > val[j];
-          const float tv = val[j];
-          const int ti = id[j];
-          val[j] = take ? cv : tv;
-          id[j] = take ? ci : ti;
-          cv = take ? tv : cv;
-          ci = take ? ti : ci;
-          ins = take;
+      for (int i = 0; i < kTopkBatch; ++i) lv[i] = e0 + i < E ? row[e0 + i] : 0.f;
+#pragma unroll
+      for (int i = 0; i < kTopkBatch; ++i) {
+        if (e0 + i >= E) break;
+        // insert into the list sorted by (logit desc, id asc): the new expert
+        // goes before the first entry with a strictly smaller logit (equal
+        // logits keep the lower, earlier id first); every entry below shifts
+        // down by one, the last one falls off
+        float cv = lv[i];
+        int ci = e0 + i;
+        bool ins = false;
+#pragma unroll
+        for (int j = 0; j < kMaxTopK; ++j) {
+          if (j < k) {
+            const bool take = ins || cv > val[j];
+            const float tv = val[j];
+            const int ti = id[j];
+            val[j] = take ? cv : tv;
+            id[j] = take ? ci : ti;
+            cv = take ? tv : cv;
+            ci = take ? ti : ci;
+            ins = take;
+          }
         }
       }
     }
@@ -103,32 +113,152 @@ __global__ void __launch_bounds__(kRouteWg) route_topk_kernel(const float* __res
   }
 }
 
-// hist[b][e] (counts) -> hist[b][e] = first slot of block b's choices of
-// expert e; group_offsets[e] = first slot of expert e, group_offsets[E] = T*k.
+// The same results with more parallelism, for E <= kWaveTopkMaxE: one
+// work-group (8 waves) per 64-token routing block; each token gets 8 lanes
+// of a wave, each lane holding up to 16 of its logits (expert 8i + lane%8).
+// k rounds each pick the largest logit not yet chosen, ties to the lower
+// expert id (an arg-max within the 8 lanes), which is the order the insertion
+// above produces.  The block's choices go through LDS to the rank and count
+// pass, whose experts are shared out over the 8 waves.
+constexpr int kWaveTopkMaxE = 128;
+constexpr int kWaveTopkWaves = 8;
+constexpr int kTokLanes = 8;
+constexpr int kPerLane = kWaveTopkMaxE / kTokLanes;
+
+__device__ __forceinline__ void argmax_merge(float& v, int& i, float ov, int oi) {
+  // (v, i) = the better of two candidates: the larger logit, ties to the
+  // lower id.  "No candidate" is (-inf, INT_MAX), which every candidate
+  // (a -inf logit included) beats and which beats none.  Evaluated without
+  // short-circuit branches.
+  const bool take = (ov > v) | ((ov == v) & (oi < i));
+  v = take ? ov : v;
+  i = take ? oi : i;
+}
+
+__global__ void __launch_bounds__(kWaveTopkWaves * 64) route_topk_wave_kernel(
+    const float* __restrict__ logits, int64_t T, int E, int k, int64_t ld, int32_t* __restrict__ ids,
+    float* __restrict__ weights, int32_t* __restrict__ rank, int32_t* __restrict__ hist) {
+  static_assert(kWaveTopkWaves * (64 / kTokLanes) == kRouteBlock, "one token per 8 lanes of the block");
+  __shared__ int32_t sid[kRouteBlock * kMaxTopK];
+  const int lane = threadIdx.x & 63;
+  const int wv = threadIdx.x >> 6;
+  const int sub = lane & (kTokLanes - 1);
+  const int64_t blk = blockIdx.x;
+  const int64_t t0 = blk * kRouteBlock;
+  const int tb = wv * (64 / kTokLanes) + (lane >> 3);   // token within the block
+  const int64_t tt = t0 + tb;
+  const bool tvalid = tt < T;
+  float v[kPerLane];
+  bool free_[kPerLane];
+  const float* row = logits + (tvalid ? tt : 0) * ld;
+#pragma unroll
+  for (int i = 0; i < kPerLane; ++i) {
+    const int e = sub + kTokLanes * i;
+    free_[i] = tvalid && e < E;
+    v[i] = free_[i] ? row[e] : 0.f;
+  }
+  float val[kMaxTopK];
+  int id[kMaxTopK];
+#pragma unroll
+  for (int j = 0; j < kMaxTopK; ++j) {
+    val[j] = -__builtin_huge_valf();
+    id[j] = 0;
+    if (j < k) {                                    // wave-uniform
+      float bv = -__builtin_huge_valf();
+      int bi = INT_MAX;
+#pragma unroll
+      for (int i = 0; i < kPerLane; ++i)
+        argmax_merge(bv, bi, free_[i] ? v[i] : -__builtin_huge_valf(), free_[i] ? sub + kTokLanes * i : INT_MAX);
+#pragma unroll
+      for (int off = kTokLanes / 2; off >= 1; off >>= 1) {
+        const float ov = __shfl_xor(bv, off, kWave);
+        const int oi = __shfl_xor(bi, off, kWave);
+        argmax_merge(bv, bi, ov, oi);
+      }
+      val[j] = bv;
+      id[j] = bi;
+#pragma unroll
+      for (int i = 0; i < kPerLane; ++i) free_[i] = free_[i] & (sub + kTokLanes * i != bi);
+    }
+  }
+  if (tvalid && sub == 0) {
+    float z[kMaxTopK];
+    float sum = 0.f;
+#pragma unroll
+    for (int j = 0; j < kMaxTopK; ++j) {
+      z[j] = j < k ? expf(val[j] - val[0]) : 0.f;
+      sum += z[j];
+    }
+#pragma unroll
+    for (int j = 0; j < kMaxTopK; ++j)
+      if (j < k) {
+        ids[tt * k + j] = id[j];
+        weights[tt * k + j] = z[j] / sum;
+        sid[tb * kMaxTopK + j] = id[j];
+      }
+  }
+  __syncthreads();
+  // ranks and counts: lanes are the block's tokens, experts shared out by wave
+  const int64_t t = t0 + lane;
+  const bool valid = t < T;
+  const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+  int mine[kMaxTopK];
+#pragma unroll
+  for (int j = 0; j < kMaxTopK; ++j) mine[j] = (valid && j < k) ? sid[lane * kMaxTopK + j] : -1;
+  for (int e = wv; e < E; e += kWaveTopkWaves) {
+    bool chose = false;
+#pragma unroll
+    for (int j = 0; j < kMaxTopK; ++j) chose |= mine[j] == e;
+    const uint64_t m = __ballot(chose);
+    if (lane == 0) hist[blk * E + e] = __popcll(m);   // zero counts too
+    if (chose) {
+      const int r = __popcll(m & below);
+#pragma unroll
+      for (int j = 0; j < kMaxTopK; ++j)
+        if (mine[j] == e) rank[t * k + j] = r;
+    }
+  }
+}
+
+// hist[b][e] (counts) -> hist[b][e] = number of expert e's choices in the
+// blocks before b (exclusive scan over the blocks, in place);
+// group_offsets[e] = first slot of expert e, group_offsets[E] = T*k.  A slot
+// is group_offsets[e] + hist[b][e] + the choice's rank in its block.  One
+// thread per expert (kMaxExperts / kScanThreads experts each when E is
+// larger); the block counts are read kScanBatch at a time so that the loads of
+// one expert's column are in flight together.
+constexpr int kScanBatch = 16;
+
 __global__ void __launch_bounds__(kScanThreads) route_scan_kernel(int32_t* __restrict__ hist, int64_t nb, int E,
                                                                   int32_t* __restrict__ group_offsets) {
-  __shared__ int32_t part[kScanThreads];
   constexpr int kPer = kMaxExperts / kScanThreads;
-  int32_t tot[kPer];
-  // per expert: exclusive scan over the blocks (in place), total count
+  __shared__ int32_t totals[kMaxExperts];
+  __shared__ int32_t part[kScanThreads];
 #pragma unroll
   for (int q = 0; q < kPer; ++q) {
-    const int e = threadIdx.x * kPer + q;
+    const int e = q * kScanThreads + threadIdx.x;
     int32_t run = 0;
     if (e < E) {
-      for (int64_t b = 0; b < nb; ++b) {
-        const int32_t h = hist[b * E + e];
-        hist[b * E + e] = run;
-        run += h;
+      for (int64_t b0 = 0; b0 < nb; b0 += kScanBatch) {
+        int32_t h[kScanBatch];
+#pragma unroll
+        for (int i = 0; i < kScanBatch; ++i) h[i] = b0 + i < nb ? hist[(b0 + i) * E + e] : 0;
+#pragma unroll
+        for (int i = 0; i < kScanBatch; ++i)
+          if (b0 + i < nb) {
+            hist[(b0 + i) * E + e] = run;
+            run += h[i];
+          }
       }
     }
-    tot[q] = run;
+    totals[e] = run;
   }
-  // exclusive scan of the totals over experts (thread-major: thread i owns
-  // experts kPer*i .. kPer*i+kPer-1)
+  __syncthreads();
+  // exclusive scan of the totals in expert order: thread i owns experts
+  // kPer*i .. kPer*i+kPer-1
   int32_t mine = 0;
 #pragma unroll
-  for (int q = 0; q < kPer; ++q) mine += tot[q];
+  for (int q = 0; q < kPer; ++q) mine += totals[threadIdx.x * kPer + q];
   part[threadIdx.x] = mine;
   __syncthreads();
   for (int off = 1; off < kScanThreads; off <<= 1) {
@@ -137,27 +267,27 @@ __global__ void __launch_bounds__(kScanThreads) route_scan_kernel(int32_t* __res
     part[threadIdx.x] += v;
     __syncthreads();
   }
-  int32_t base = part[threadIdx.x] - mine;          // exclusive prefix of this thread's experts
+  int32_t base = part[threadIdx.x] - mine;
 #pragma unroll
   for (int q = 0; q < kPer; ++q) {
     const int e = threadIdx.x * kPer + q;
-    if (e < E) {
-      group_offsets[e] = base;
-      for (int64_t b = 0; b < nb; ++b) hist[b * E + e] += base;
-    }
-    base += tot[q];
+    if (e < E) group_offsets[e] = base;
+    base += totals[e];
   }
   if (threadIdx.x == kScanThreads - 1) group_offsets[E] = part[kScanThreads - 1];
 }
 
 __global__ void __launch_bounds__(256) route_scatter_kernel(const int32_t* __restrict__ ids,
                                                             const int32_t* __restrict__ rank,
-                                                            const int32_t* __restrict__ hist, int64_t T, int E, int k,
-                                                            int32_t* __restrict__ a_rows, int32_t* __restrict__ slot_of) {
+                                                            const int32_t* __restrict__ hist,
+                                                            const int32_t* __restrict__ group_offsets, int64_t T,
+                                                            int E, int k, int32_t* __restrict__ a_rows,
+                                                            int32_t* __restrict__ slot_of) {
   const int64_t n = T * k;
   for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256) {
     const int64_t t = i / k;
-    const int32_t s = hist[(t / kRouteBlock) * E + ids[i]] + rank[i];
+    const int32_t e = ids[i];
+    const int32_t s = group_offsets[e] + hist[(t / kRouteBlock) * E + e] + rank[i];
     if (s >= 0 && s < n) a_rows[s] = (int32_t)t;   // always true; keeps the write in bounds regardless
     slot_of[i] = s;
   }
@@ -221,10 +351,15 @@ int route_launch(const float* logits, int64_t T, int E, int k, int64_t ld, int32
   int32_t* ids = reinterpret_cast<int32_t*>(ws);
   int32_t* rank = reinterpret_cast<int32_t*>(reinterpret_cast<char*>(ws) + a256((size_t)T * k * 4));
   int32_t* hist = reinterpret_cast<int32_t*>(reinterpret_cast<char*>(ws) + 2 * a256((size_t)T * k * 4));
-  const uint32_t g1 = (uint32_t)((T + kRouteWg - 1) / kRouteWg);
   int slot = launch_begin(KC_ROUTE, st);
-  hipLaunchKernelGGL(route_topk_kernel, dim3(g1), dim3(kRouteWg), 0, st, logits, T, E, k, ld, ids, weights, rank,
-                     hist);
+  if (E <= kWaveTopkMaxE) {
+    hipLaunchKernelGGL(route_topk_wave_kernel, dim3((uint32_t)nb), dim3(kWaveTopkWaves * 64), 0, st, logits, T, E,
+                       k, ld, ids, weights, rank, hist);
+  } else {
+    const uint32_t g1 = (uint32_t)((T + kRouteWg - 1) / kRouteWg);
+    hipLaunchKernelGGL(route_topk_kernel, dim3(g1), dim3(kRouteWg), 0, st, logits, T, E, k, ld, ids, weights, rank,
+                       hist);
+  }
   launch_end(slot, st);
   slot = launch_begin(KC_ROUTE, st);
   hipLaunchKernelGGL(route_scan_kernel, dim3(1), dim3(kScanThreads), 0, st, hist, nb, E, group_offsets);
@@ -232,8 +367,8 @@ int route_launch(const float* logits, int64_t T, int E, int k, int64_t ld, int32
   int64_t g3 = (T * k + 255) / 256;
   if (g3 > 4096) g3 = 4096;
   slot = launch_begin(KC_ROUTE, st);
-  hipLaunchKernelGGL(route_scatter_kernel, dim3((uint32_t)g3), dim3(256), 0, st, ids, rank, hist, T, E, k, a_rows,
-                     slot_of);
+  hipLaunchKernelGGL(route_scatter_kernel, dim3((uint32_t)g3), dim3(256), 0, st, ids, rank, hist, group_offsets, T,
+                     E, k, a_rows, slot_of);
   launch_end(slot, st);
   return hipGetLastError() == hipSuccess ? 0 : 7;
 }

@@ -51,6 +51,7 @@ def check_route(logits, k, label):
 
 
 @pytest.mark.parametrize("t,e,k", [(1, 8, 2), (63, 8, 2), (64, 64, 8), (200, 64, 8), (333, 16, 16), (70, 300, 3),
+                                   (100, 256, 8), (64, 65, 4), (65, 255, 16), (90, 128, 16), (64, 129, 8),
                                    (5, 4, 4), (129, 5, 1)])
 def test_route_matches_oracle(t, e, k):
     check_route(router_logits(1000 + t + e + k, t, e), k, f"T={t} E={e} k={k}")
