@@ -351,9 +351,29 @@ def extra_lines(m):
         # from the 256 MB MALL and the L2s (a read leaves no dirty lines whose
         # write-back would compete with the timed call)
         cold = float(np.median(time_events(lambda: run(x, lay, y), 20, scrub=lambda: scrub_buf.sum())))
+        # static global scales (warm-up = this call's own scales): quantise with
+        # the given scale (1 launch), gate/up with the quantising epilogue (2),
+        # down (3)
+        xq_s, hq_s = m.NVFP4.empty(tt, K_HID), m.NVFP4.empty(tt, lay.w[0].rows)
+        xq_s.gscale.copy_(run.xq.gscale)
+        hq_s.gscale.copy_(run.hq.gscale)
+        ws_s = torch.empty(max(m.mlp_gu_act_static_ws_bytes(tt, K_HID, lay.w[0].rows), 256), dtype=torch.uint8,
+                           device="cuda")
+
+        def run_static():
+            m.nvfp4_quantize_act(x, xq_s, gs_mode=m.GS_GIVEN, ws=run.ws_q)
+            m.nvfp4_mlp_gu_act_static(xq_s, lay.w[0], lay.w[1], hq_s, ws=ws_s)
+            m.nvfp4_mlp_down(hq_s, lay.w[2], y, ws=run.ws_dn)
+        run_static()
+        b0 = m.launch_count()
+        run_static()
+        static_launches = m.launch_count() - b0
+        cold_s = float(np.median(time_events(run_static, 20, scrub=lambda: scrub_buf.sum())))
         dec[f"T{tt}"] = {"ms_hot": hot, "ms_cold": cold, "hbm_gbs_cold": wbytes / (cold * 1e-3) / 1e9,
                          "hbm_gbs_hot": wbytes / (hot * 1e-3) / 1e9,
-                         "frac_hbm_peak_cold": wbytes / (cold * 1e-3) / 1e9 / PEAK_HBM_GBS}
+                         "frac_hbm_peak_cold": wbytes / (cold * 1e-3) / 1e9 / PEAK_HBM_GBS,
+                         "static_gs_ms_cold": cold_s, "static_gs_hbm_gbs_cold": wbytes / (cold_s * 1e-3) / 1e9,
+                         "static_gs_launches": static_launches}
     dec["launches_per_call"] = launches
     dec["t5_over_t1_cold"] = dec["T5"]["ms_cold"] / dec["T1"]["ms_cold"]
     out["decode"] = dec
@@ -383,9 +403,10 @@ def extra_lines(m):
 
 
 def quantize_line(m):
-    """Activation quantisation (A1+A2, two launches) and the fused RMSNorm variant
-    (N2), bf16 input: GB/s of the algorithmic traffic, 2 B read + 0.5625 B
-    written per element, at the 1024-token shape and on a 65536 x 5120 probe."""
+    """Activation quantisation (A1+A2, two launches), the same with a given
+    (static) global scale (one launch) and the fused RMSNorm variant (N2), bf16
+    input: GB/s of the algorithmic traffic, 2 B read + 0.5625 B written per
+    element, at the 1024-token shape and on a 65536 x 5120 probe."""
     from synthetic import bf16_normal
     log("extra: quantisation kernels (plain and RMSNorm-fused)")
     out = {"unit_bytes_per_element": 2.5625}
@@ -397,9 +418,11 @@ def quantize_line(m):
                          dtype=torch.uint8, device="cuda")
         nbytes = rows * K_HID * 2.5625
         tq = float(np.median(time_events(lambda: m.nvfp4_quantize_act(x, q, ws=ws), 20)))
+        tg = float(np.median(time_events(lambda: m.nvfp4_quantize_act(x, q, gs_mode=m.GS_GIVEN, ws=ws), 20)))
         tn = float(np.median(time_events(lambda: m.nvfp4_rmsnorm_quantize_act(x, g, 1e-6, q, ws=ws), 20)))
         out[f"rows{rows}"] = {"quantize_ms": tq, "quantize_gbs": nbytes / (tq * 1e-3) / 1e9,
                               "quantize_frac_hbm": nbytes / (tq * 1e-3) / 1e9 / PEAK_HBM_GBS,
+                              "given_gs_quantize_ms": tg, "given_gs_quantize_gbs": nbytes / (tg * 1e-3) / 1e9,
                               "rmsnorm_quantize_ms": tn, "rmsnorm_quantize_gbs": nbytes / (tn * 1e-3) / 1e9}
         del x, q, ws
     return out
