@@ -463,20 +463,36 @@ __global__ void __launch_bounds__(WN * 64, MINWG) gemm_kernel(GemmArgs p) {
   int e = 0;
   if constexpr (GROUPED) {
     // (expert, tile within the expert) from the device-resident offsets;
-    // tiles past the last expert have no work.
+    // tiles past the last expert have no work.  The lanes of each wave take
+    // 64 experts at a time (one pair of loads each instead of a chain of
+    // dependent loads), add up the experts' tile counts with a wave prefix
+    // sum, and the first expert whose running count passes the tile wins.
+    const int lane = threadIdx.x & 63;
     uint32_t cum = 0;
     m0 = -1;
     m_end = 0;
-    for (int xe = 0; xe < p.E; ++xe) {
-      const int64_t s0 = p.off[xe], s1 = p.off[xe + 1];
+    for (int g0 = 0; g0 < p.E; g0 += 64) {
+      const int xe = g0 + lane;
+      const int32_t s0 = xe < p.E ? p.off[xe] : 0;
+      const int32_t s1 = xe < p.E ? p.off[xe + 1] : 0;
       const uint32_t nt = (uint32_t)((s1 - s0 + BM - 1) / BM);
-      if (mt < cum + nt) {
-        e = xe;
-        m0 = s0 + (int64_t)(mt - cum) * BM;
-        m_end = s1;
+      uint32_t incl = nt;
+#pragma unroll
+      for (int d = 1; d < 64; d <<= 1) {
+        const uint32_t v = __shfl_up(incl, d, 64);
+        if (lane >= d) incl += v;
+      }
+      const uint32_t group = (uint32_t)__builtin_amdgcn_readfirstlane(__shfl(incl, 63, 64));
+      if (mt < cum + group) {                      // wave-uniform
+        const uint64_t hit = __ballot(cum + incl > mt);
+        const int l = __builtin_amdgcn_readfirstlane(__ffsll((unsigned long long)hit) - 1);
+        e = g0 + l;
+        const uint32_t before = (uint32_t)__builtin_amdgcn_readfirstlane(__shfl(incl - nt, l, 64));
+        m0 = (int64_t)__builtin_amdgcn_readfirstlane(__shfl(s0, l, 64)) + (int64_t)(mt - cum - before) * BM;
+        m_end = (int64_t)__builtin_amdgcn_readfirstlane(__shfl(s1, l, 64));
         break;
       }
-      cum += nt;
+      cum += group;
     }
     if (m0 < 0) {
       if constexpr (EPI == EPI_GLU) {
