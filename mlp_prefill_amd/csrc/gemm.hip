@@ -440,6 +440,8 @@ __device__ __forceinline__ void xchunk(Ctx<WN, TM, TN, DUAL>& x, const Lds& lc, 
 #define NVFP4_STORE_MINWG NVFP4_MIN_WG_PER_CU
 #endif
 
+constexpr uint32_t kGroupGm = 8;   // m tiles per super-tile of the expert-grouped tile order
+
 template <int WN, int TM, int TN, bool DUAL, bool GROUPED, int EPI, int NS, int MINWG>
 __global__ void __launch_bounds__(WN * 64, MINWG) gemm_kernel(GemmArgs p) {
   using C = Cfg<WN, TM, TN, DUAL>;
@@ -454,11 +456,25 @@ __global__ void __launch_bounds__(WN * 64, MINWG) gemm_kernel(GemmArgs p) {
   const int r32 = lane & 31, hh = lane >> 5;
 
   // ---- tile: consecutive ids share (split, n_tile) and walk the m tiles ------
+  // (expert-grouped, unsplit: super-tiles of kGroupGm m tiles x all n tiles,
+  // m fastest inside, so that the work-groups on one XCD share both the
+  // activation rows and the weight columns -- the gathered activations of all
+  // experts do not fit the MALL)
   const uint32_t t = xcd_remap(blockIdx.x, gridDim.x);
-  const uint32_t mt = t % p.m_tiles;
-  const uint32_t rest = t / p.m_tiles;
-  const uint32_t split = rest % p.splits;
-  const uint32_t n_tile = rest / p.splits;
+  uint32_t mt, split, n_tile;
+  if (GROUPED && p.splits == 1) {
+    const uint32_t span = kGroupGm * p.n_tiles;
+    const uint32_t sup = t / span, r = t - sup * span;
+    const uint32_t gm = (sup + 1) * kGroupGm <= p.m_tiles ? kGroupGm : p.m_tiles - sup * kGroupGm;
+    mt = sup * kGroupGm + r % gm;
+    n_tile = r / gm;
+    split = 0;
+  } else {
+    mt = t % p.m_tiles;
+    const uint32_t rest = t / p.m_tiles;
+    split = rest % p.splits;
+    n_tile = rest / p.splits;
+  }
   int64_t m0, m_end;
   int e = 0;
   if constexpr (GROUPED) {
