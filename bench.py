@@ -516,7 +516,31 @@ def moe_line(m):
             layer()
         n, _, tot = m.nvfp4_timing_end()
         parts[f"{name}_ms"] = tot / 5
+    # static global scales (warm-up = the dynamic layer just run): quantise with
+    # the given scale, gate/up with the quantising epilogue (no float32 H, no
+    # requantisation)
+    xq_s, hq_s = m.NVFP4.empty(t, k), m.NVFP4.empty(slots, i)
+    xq_s.gscale.copy_(xq.gscale)
+    hq_s.gscale.copy_(hq.gscale)
+    ws_gs = torch.empty(max(m.grouped_ws_bytes(slots, i, k, e, m.EPI_SILU_MUL_QUANT_GIVEN), 256), dtype=torch.uint8,
+                        device="cuda")
+
+    def layer_static():
+        m.nvfp4_moe_route(logits, top, offs, rows, slot_of, cw, ws=ws_r)
+        m.nvfp4_quantize_act(x, xq_s, gs_mode=m.GS_GIVEN, ws=ws_q)
+        m.nvfp4_grouped_gemm(xq_s, rows, offs, wg, wu, out_q=hq_s, epilogue=m.EPI_SILU_MUL_QUANT_GIVEN, m=slots,
+                             ws=ws_gs)
+        m.nvfp4_grouped_gemm(hq_s, None, offs, wd, out=ys, epilogue=m.EPI_STORE, ws=ws_d)
+        m.nvfp4_moe_combine(ys, slot_of, cw, y)
+
+    before = m.launch_count()
+    layer_static()
+    launches_s = m.launch_count() - before
+    ms_s = float(np.median(time_events(layer_static, 10)))
+    parts["static_gs_ms"] = ms_s
+    parts["static_gs_launches_per_call"] = launches_s
     flops = mlp_flops(slots, k, i)
+    parts["static_gs_tflops"] = flops / (ms_s * 1e-3) / 1e12
     tf = flops / (ms * 1e-3) / 1e12
     comb_bytes = slots * k * 2 + t * k * 2 + t * top * 8
     return {"workload": "moe_4096_top8_of_64", "ms": ms, "tflops": tf, "frac_f16_peak": tf / PEAK_F16_TFLOPS,

@@ -98,7 +98,9 @@ enum nvfp4_gs_mode {
 
 enum nvfp4_epilogue {
   NVFP4_EPI_STORE = 0,             /* out = A~ . W~^T scaled, float32 or bf16         */
-  NVFP4_EPI_SILU_MUL_REQUANT = 1   /* out_q = NVFP4(SiLU(A~ . Wg~^T) * (A~ . Wu~^T))  */
+  NVFP4_EPI_SILU_MUL_REQUANT = 1,  /* out_q = NVFP4(SiLU(A~ . Wg~^T) * (A~ . Wu~^T))  */
+  NVFP4_EPI_SILU_MUL_QUANT_GIVEN = 2 /* the same with the static global scale already
+                                        stored at *out_q.gscale (read on the device) */
 };
 
 /*
@@ -242,8 +244,12 @@ int nvfp4_mlp_down_quant(nvfp4_tensor h, nvfp4_tensor w_down, int64_t T, int64_t
  *                   SiLU(gate) * up with one global scale over all M slots
  *                   (written to *out_q.gscale)
  *   K, N          : multiples of 128;  E >= 1
- *   ws            : GLU epilogue: its first M*N*4 bytes hold the float32 GLU
- *                   output [M][N] on return
+ *                   NVFP4_EPI_SILU_MUL_QUANT_GIVEN -> as the previous, with the
+ *                   global scale *out_q.gscale given ([dsv4] P0 fix 1, a warm-up
+ *                   scale) and the GLU output quantised in the contraction's
+ *                   epilogue: no float32 output, no requantisation launch
+ *   ws            : NVFP4_EPI_SILU_MUL_REQUANT: its first M*N*4 bytes hold the
+ *                   float32 GLU output [M][N] on return
  */
 int nvfp4_grouped_gemm(nvfp4_tensor a, const int32_t *a_rows, const int32_t *group_offsets,
                        int E, int64_t M, nvfp4_tensor w0, nvfp4_tensor w1, int64_t N, int64_t K,

@@ -33,7 +33,7 @@ class nvfp4_tensor(ctypes.Structure):
 OK, ERR_NULL, ERR_SHAPE, ERR_ALIGN, ERR_WORKSPACE, ERR_ARG, ERR_DEVICE, ERR_LAUNCH = range(8)
 F32, BF16 = 0, 1
 GS_COMPUTE, GS_GIVEN = 0, 1
-EPI_STORE, EPI_SILU_MUL_REQUANT = 0, 1
+EPI_STORE, EPI_SILU_MUL_REQUANT, EPI_SILU_MUL_QUANT_GIVEN = 0, 1, 2
 KC_QUANTIZE, KC_EXPAND, KC_GEMM_GLU, KC_GEMM_STORE, KC_REDUCE, KC_ROUTE, KC_COMBINE = range(7)
 
 _sig = {

@@ -634,11 +634,11 @@ __global__ void __launch_bounds__(WN * 64, MINWG) gemm_kernel(GemmArgs p) {
     // whole 16-column blocks of it with the given global scale.  Columns are
     // XOR-swizzled in units of four floats by the row, so the two row halves
     // of an MFMA fragment store to different banks.
-    static_assert(DUAL && !GROUPED, "quantising GLU epilogue: dense gate/up pair");
+    static_assert(DUAL, "quantising GLU epilogue: gate/up pair");
     static_assert(BM * C::BN * 4 <= (int)sizeof(lds_b), "GLU tile must fit the stage buffers");
     float* tile = reinterpret_cast<float*>(&lds_b[0][0]);
-    const float alpha = p.a_gs[0] * p.b_gs[0];
-    const float alpha_u = p.a_gs[0] * p.u_gs[0];
+    const float alpha = p.a_gs[0] * p.b_gs[GROUPED ? e : 0];
+    const float alpha_u = p.a_gs[0] * p.u_gs[GROUPED ? e : 0];
     __syncthreads();
 #pragma unroll
     for (int i = 0; i < TM; ++i)
@@ -1132,10 +1132,11 @@ int glu_launch(Operand a, const int32_t* a_rows, const int32_t* off, int E, int6
 
 size_t glu_static_ws_bytes(int64_t M, int64_t K) { return align256((size_t)M * K * 2); }
 
-int glu_static_launch(Operand a, int64_t M, Operand gt, Operand up, int64_t N, int64_t K, uint8_t* hq_codes,
-                      uint8_t* hq_scales, const float* hq_gs, void* ws, hipStream_t st) {
+int glu_static_launch(Operand a, const int32_t* a_rows, const int32_t* off, int E, int64_t M, Operand gt,
+                      Operand up, int64_t N, int64_t K, uint8_t* hq_codes, uint8_t* hq_scales, const float* hq_gs,
+                      void* ws, hipStream_t st) {
   _Float16* a16 = reinterpret_cast<_Float16*>(ws);
-  launch_expand(a.codes, a.scales, nullptr, M, K, a16, st);
+  launch_expand(a.codes, a.scales, a_rows, M, K, a16, st);
   GemmArgs g = base_args(a16, a.gscale, gt, M, N, K);
   g.u_codes = up.codes;
   g.u_scales = up.scales;
@@ -1144,7 +1145,13 @@ int glu_static_launch(Operand a, int64_t M, Operand gt, Operand up, int64_t N, i
   g.q_scales = hq_scales;
   g.q_gs = hq_gs;
   g.chunks_per_split = (uint32_t)(K / 128);
-  if (M <= 32) {
+  g.off = off;
+  g.E = E;
+  if (off) {
+    g.m_tiles = cdiv(M, 32 * NVFP4_GLU_TM) + (uint32_t)E;
+    g.n_tiles = cdiv(N, 32 * NVFP4_GLU_WN);
+    launch_cfg<NVFP4_GLU_WN, NVFP4_GLU_TM, 1, true, true, EPI_GLUQ>(g, st);
+  } else if (M <= 32) {
     g.m_tiles = 1;
     g.n_tiles = cdiv(N, 32);
     launch_skinny<true, EPI_GLUQ>(g, st);

@@ -66,12 +66,13 @@ int glu_launch(Operand a, const int32_t* a_rows, const int32_t* off, int E, int6
                int64_t N, int64_t K, uint8_t* hq_codes, uint8_t* hq_scales, float* hq_gs, void* ws,
                hipStream_t st);
 
-// The same GLU output quantised in the contraction's epilogue with the given
-// global scale *hq_gs (two launches: expansion, contraction).  Workspace: the
-// f16 copy of A.
+// The same GLU output (dense, or expert-grouped when `off` is given)
+// quantised in the contraction's epilogue with the given global scale *hq_gs
+// (two launches: expansion, contraction).  Workspace: the f16 copy of A.
 size_t glu_static_ws_bytes(int64_t M, int64_t K);
-int glu_static_launch(Operand a, int64_t M, Operand gt, Operand up, int64_t N, int64_t K, uint8_t* hq_codes,
-                      uint8_t* hq_scales, const float* hq_gs, void* ws, hipStream_t st);
+int glu_static_launch(Operand a, const int32_t* a_rows, const int32_t* off, int E, int64_t M, Operand gt,
+                      Operand up, int64_t N, int64_t K, uint8_t* hq_codes, uint8_t* hq_scales, const float* hq_gs,
+                      void* ws, hipStream_t st);
 
 // C = A . W^T * gs_a * gs_w quantised to NVFP4 with the given global scale
 // *yq_gs by the (always launched) fixed-order split reduction.  Workspace as

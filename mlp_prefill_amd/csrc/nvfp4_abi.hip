@@ -270,8 +270,8 @@ int nvfp4_mlp_gu_act_static(nvfp4_tensor x, nvfp4_tensor w_gate, nvfp4_tensor w_
       (rc = check_tensor(w_up)) != NVFP4_OK || (rc = check_tensor(h_out)) != NVFP4_OK)
     return rc;
   if ((rc = check_device()) != NVFP4_OK) return rc;
-  return nvfp4::glu_static_launch(op(x), T, op(w_gate), op(w_up), I, K, h_out.codes, h_out.scales, h_out.gscale, ws,
-                                  reinterpret_cast<hipStream_t>(stream));
+  return nvfp4::glu_static_launch(op(x), nullptr, nullptr, 1, T, op(w_gate), op(w_up), I, K, h_out.codes,
+                                  h_out.scales, h_out.gscale, ws, reinterpret_cast<hipStream_t>(stream));
 }
 
 int nvfp4_mlp_down_quant(nvfp4_tensor h, nvfp4_tensor w_down, int64_t T, int64_t I, int64_t K, nvfp4_tensor y_out,
@@ -328,7 +328,8 @@ int nvfp4_grouped_gemm(nvfp4_tensor a, const int32_t* a_rows, const int32_t* gro
                        nvfp4_tensor w0, nvfp4_tensor w1, int64_t N, int64_t K, int epilogue, void* out,
                        int out_dtype, int64_t ld_out, nvfp4_tensor out_q, void* ws, size_t* ws_bytes,
                        void* stream) {
-  const bool glu = (epilogue == NVFP4_EPI_SILU_MUL_REQUANT);
+  const bool gluq = (epilogue == NVFP4_EPI_SILU_MUL_QUANT_GIVEN);
+  const bool glu = (epilogue == NVFP4_EPI_SILU_MUL_REQUANT) || gluq;
   if (epilogue != NVFP4_EPI_STORE && !glu) return NVFP4_ERR_ARG;
   if (!glu && !dtype_ok(out_dtype)) return NVFP4_ERR_ARG;
   if (E < 1 || E > 4096) return NVFP4_ERR_ARG;
@@ -337,7 +338,10 @@ int nvfp4_grouped_gemm(nvfp4_tensor a, const int32_t* a_rows, const int32_t* gro
   if (M * (N / 16) >= ((int64_t)1 << 31)) return NVFP4_ERR_SHAPE;
   if (M * (K / 16) >= ((int64_t)1 << 31)) return NVFP4_ERR_SHAPE;
   bool query;
-  const size_t need = M == 0 ? 0 : (glu ? nvfp4::glu_ws_bytes(M, N, K, E, true) : nvfp4::store_ws_bytes(M, N, K, E, true));
+  const size_t need = M == 0 ? 0
+                              : gluq ? nvfp4::glu_static_ws_bytes(M, K)
+                              : glu  ? nvfp4::glu_ws_bytes(M, N, K, E, true)
+                                     : nvfp4::store_ws_bytes(M, N, K, E, true);
   int rc = workspace(ws, ws_bytes, need, &query);
   if (rc != NVFP4_OK || query) return rc;
   if (M == 0) return NVFP4_OK;
@@ -355,6 +359,9 @@ int nvfp4_grouped_gemm(nvfp4_tensor a, const int32_t* a_rows, const int32_t* gro
   if (!glu)
     return nvfp4::store_launch(op(a), a_rows, group_offsets, E, M, op(w0), N, K, out, out_dtype == NVFP4_BF16,
                                ld_out, ws, st);
+  if (gluq)
+    return nvfp4::glu_static_launch(op(a), a_rows, group_offsets, E, M, op(w0), op(w1), N, K, out_q.codes,
+                                    out_q.scales, out_q.gscale, ws, st);
   return nvfp4::glu_launch(op(a), a_rows, group_offsets, E, M, op(w0), op(w1), N, K, out_q.codes, out_q.scales,
                            out_q.gscale, ws, st);
 }

@@ -154,6 +154,7 @@ def test_grouped_validation():
                  a["out"], a["dt"], a["ld"], a["oq"], FAKE, ctypes.byref(sz), None)
     assert call(E=0) == m.ERR_ARG
     assert call(epi=5) == m.ERR_ARG
+    assert call(epi=m.EPI_SILU_MUL_QUANT_GIVEN, oq=nvfp4_tensor(FAKE, FAKE, 0)) == m.ERR_NULL   # scale is read
     assert call(N=100) == m.ERR_SHAPE
     assert call(off=None) == m.ERR_NULL
     assert call(out=None) == m.ERR_NULL
@@ -165,6 +166,10 @@ def test_grouped_validation():
     assert f(z, None, None, 64, 32768, z, z, 2048, 4096, m.EPI_SILU_MUL_REQUANT, None, m.F32, 2048, z, None,
              ctypes.byref(s), None) == m.OK
     assert s.value >= 32768 * 2048 * 4
+    s2 = _size()
+    assert f(z, None, None, 64, 32768, z, z, 2048, 4096, m.EPI_SILU_MUL_QUANT_GIVEN, None, m.F32, 2048, z, None,
+             ctypes.byref(s2), None) == m.OK
+    assert s2.value == 32768 * 4096 * 2                   # no float32 GLU output with a given scale
 
 
 @no_gpu

@@ -185,3 +185,46 @@ def test_two_layer_static_chain_through_down_quant():
     legit_requant_flips(h1.astype(np.float32), to_host(hq1), ref_hq1)
     corr = omlp.mlp_down(to_host(hq1), layers[1][1][2])
     assert max_norm_err(y.cpu().numpy(), corr) <= TOL
+
+
+def _grouped_static_check(t, e, k, i, top, seed, sample_rows=None):
+    """The expert-grouped gate/up with a given scale must give exactly the NVFP4
+    encoding of the float32 GLU output the dynamic grouped call computes."""
+    import mlp_prefill_amd as m
+    from oracle import moe as omoe
+    from synthetic import expert_seeds, router_logits
+    r = omoe.route(router_logits(seed, t, e), top)
+    slots = len(r.a_rows)
+    mats = [[], []]
+    for x in range(e):
+        for j, (s, shp) in enumerate(zip(expert_seeds(seed + 1, x)[:2], [(i, k), (i, k)])):
+            mats[j].append(dev_quantize(bf16_normal(s, shp, sigma=0.02)))
+    wg, wu = m.NVFP4.stack(mats[0]), m.NVFP4.stack(mats[1])
+    xq = dev_quantize(bf16_normal(seed + 2, (t, k)))
+    rows = torch.from_numpy(np.ascontiguousarray(r.a_rows, dtype=np.int32)).cuda()
+    offs = torch.from_numpy(np.ascontiguousarray(r.group_offsets, dtype=np.int32)).cuda()
+    hq_dyn = m.NVFP4.empty(slots, i)
+    ws = m.nvfp4_grouped_gemm(xq, rows, offs, wg, wu, out_q=hq_dyn, epilogue=m.EPI_SILU_MUL_REQUANT, m=slots)
+    torch.cuda.synchronize()
+    sel = np.arange(slots) if sample_rows is None else np.unique(np.linspace(0, slots - 1, sample_rows).astype(int))
+    h32 = ws[: slots * i * 4].view(torch.float32).view(slots, i)[torch.from_numpy(sel).cuda()].cpu().numpy()
+    gs_dyn = np.float32(hq_dyn.gscale.cpu().numpy()[0])
+    need = m.grouped_ws_bytes(slots, i, k, e, m.EPI_SILU_MUL_QUANT_GIVEN)
+    assert need == slots * k * 2 + (-(slots * k * 2)) % 256      # only the f16 copy of the gathered x~
+    for gs in (gs_dyn, np.float32(gs_dyn * 0.25)):
+        hq = _with_gs(slots, i, gs)
+        m.nvfp4_grouped_gemm(xq, rows, offs, wg, wu, out_q=hq, epilogue=m.EPI_SILU_MUL_QUANT_GIVEN, m=slots)
+        got = to_host(hq)
+        got_sel = quant.NVFP4(got.codes[sel], got.scales[sel], got.gs, len(sel), i)
+        assert_nvfp4_equal(got_sel, quant.quantize(h32, gs=gs), f"grouped static gs={gs!r}")
+
+
+def test_grouped_static_scale_small_routed():
+    announce("grouped gate/up static scale: 200 tokens, top-2 of 8 experts")
+    _grouped_static_check(200, 8, 256, 384, 2, 9101)
+
+
+def test_grouped_static_scale_moe_workload_sampled():
+    p = WORKLOADS["moe_4096_top8_of_64"].params
+    announce("grouped gate/up static scale: 4096 tokens, top-8 of 64 (sampled rows)")
+    _grouped_static_check(p["T"], p["E"], p["K"], p["I"], p["topk"], 9201, sample_rows=3000)
