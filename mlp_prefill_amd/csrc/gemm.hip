@@ -899,6 +899,269 @@ __global__ void __launch_bounds__(kSkWaves * 64) skinny_kernel(GemmArgs p) {
   }
 }
 
+// ---- weight stream for one or two tokens ---------------------------------------------
+// At T <= 2 the contraction is a matrix-vector product bound by reading the
+// weights once.  Reading them at full HBM speed needs long contiguous runs
+// per wave instruction: the MFMA fragment layout (32 weight rows x 32 bytes
+// per instruction) streams at about half the rate of a layout where a wave
+// reads one row at a time.  So here the lanes run along K: K is cut into
+// units of 1024 elements (64 blocks of 16), a split takes BPL consecutive
+// units, and lane l takes the BPL consecutive blocks l*BPL .. l*BPL+BPL-1 of
+// it (8*BPL code bytes, BPL scale bytes).  The activation (f16, expanded
+// once per call) follows the same layout and stays in registers for the
+// whole wave.
+//
+// Each block's 16 products code * x are summed by v_dot2_f32_f16 on the
+// plain code values (the converter's scale is 1, so they are exact in f16;
+// each product is exact in float32), then multiplied once by the block's
+// E4M3 scale.  The scale is decoded through f16: the bits (s << 7) are
+// dec(s) * 2^-8 for every E4M3 code, and the final * 256 restores it
+// exactly.  Lane partial sums are added across the wave in a fixed butterfly
+// order.
+//
+// A wave owns a few consecutive output columns (weight rows) of one split
+// and walks them in groups of RP columns (with the gate/up pair, RP gate rows
+// and the same RP up rows), the loads of the next DEPTH-1 groups in flight
+// while a group is computed.  The results per token stay in registers until
+// the epilogue: the GLU output and its max (one partial per wave), the GLU
+// output quantised in 16-column blocks with a given scale (the work-group's
+// four waves hold consecutive columns and gather them in LDS), or the
+// store / split-K partial store.
+#ifndef NVFP4_GV_DEPTH
+#define NVFP4_GV_DEPTH 2
+#endif
+#ifndef NVFP4_GV_MAXT
+#define NVFP4_GV_MAXT 2
+#endif
+// Output columns per wave (4, 8 or 16): fewer columns give more waves and
+// more weight bytes in flight per CU.
+#ifndef NVFP4_GV_COLS
+#define NVFP4_GV_COLS 4
+#endif
+constexpr int kGvCols = NVFP4_GV_COLS;
+static_assert(kGvCols == 4 || kGvCols == 8 || kGvCols == 16, "a work-group must cover whole 16-column blocks");
+
+__device__ __forceinline__ float e4m3_over_256(uint32_t s) {
+  return (float)bitcast<_Float16>((uint16_t)(s << 7));
+}
+
+// Sum over the 64 lanes of a wave in a fixed order with DPP row shifts and
+// row broadcasts (16-lane prefix sums, then rows 0+1 and 2+3, then all);
+// lane 63 ends with the total, which is returned to every lane.
+__device__ __forceinline__ float wave_sum_dpp(float v) {
+  v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x111, 0xF, 0xF, true));
+  v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x112, 0xF, 0xF, true));
+  v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x114, 0xF, 0xF, true));
+  v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x118, 0xF, 0xF, true));
+  v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x142, 0xA, 0xF, false));
+  v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x143, 0xC, 0xF, false));
+  return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 63));
+}
+
+template <int T, int BPL, bool DUAL, int EPI>
+__global__ void __launch_bounds__(256) gemv_kernel(GemmArgs p) {
+  constexpr int PER = BPL * (DUAL ? 2 : 1);
+  constexpr int RP0 = (8 / PER) > 0 ? (8 / PER) : 1;
+  constexpr int RP = RP0 < kGvCols ? RP0 : kGvCols;       // columns per group
+  constexpr int NR = DUAL ? 2 * RP : RP;                  // weight rows per group
+  constexpr int G = kGvCols / RP;                         // groups per wave
+  constexpr int D = NVFP4_GV_DEPTH < G ? NVFP4_GV_DEPTH : G;
+  static_assert(kGvCols % RP == 0, "groups must tile the wave's columns");
+  __shared__ float hq[EPI == EPI_GLUQ && kGvCols < 16 ? T * 4 * kGvCols : 1];
+  const int lane = threadIdx.x & 63;
+  const int wi = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int64_t wave = (int64_t)blockIdx.x * 4 + wi;
+  const int64_t N = p.N, K = p.K, M = p.M;
+  const int64_t wps = (N + kGvCols - 1) / kGvCols;       // waves per split
+  // Only the store epilogue can have waves past the end (the gate/up pair
+  // has N % 128 == 0 and one split, so its work-groups are full); the
+  // quantising epilogue's barrier below is never skipped by any wave.
+  if (wave >= wps * (int64_t)p.splits) return;
+  const int64_t split = wave / wps;
+  const int64_t n0 = (wave - split * wps) * kGvCols;
+  const int64_t e0 = split * BPL * 1024 + (int64_t)lane * BPL * 16;   // first K element of this lane
+  const int64_t kb = K >> 1, ks = K >> 4;
+
+  // activation blocks of this lane, f16 pairs; tokens past M read as zero
+  f16x8 xa[T][BPL][2];
+#pragma unroll
+  for (int t = 0; t < T; ++t)
+#pragma unroll
+    for (int b = 0; b < BPL; ++b)
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        if (t < M) {
+          xa[t][b][h] = *reinterpret_cast<const f16x8*>(p.a + t * K + e0 + 16 * b + 8 * h);
+        } else {
+#pragma unroll
+          for (int i = 0; i < 8; ++i) xa[t][b][h][i] = (_Float16)0.f;
+        }
+      }
+
+  struct Slot {
+    uint2 c[NR][BPL];
+    uint32_t s[NR][BPL];
+  };
+  // Weight loads are buffer-load intrinsics over one row (a wave-uniform
+  // resource): the compiler keeps them where they are written and does not
+  // merge the scale bytes into wider loads whose unpacking would wait for
+  // them at once, so the loads of later groups stay in flight.
+  const int32_t vo_c = (int32_t)(e0 / 2), vo_s = (int32_t)(e0 / 16);
+  auto load = [&](int g, Slot& sl) {
+#pragma unroll
+    for (int r = 0; r < NR; ++r) {
+      const int q = r % RP;
+      int64_t row = n0 + g * RP + q;
+      row = row < N ? row : N - 1;                          // columns past N: valid rows, never stored
+      const bool up = DUAL && r >= RP;
+      const __amdgpu_buffer_rsrc_t rc = make_rsrc((up ? p.u_codes : p.b_codes) + row * kb, kb);
+      const __amdgpu_buffer_rsrc_t rs = make_rsrc((up ? p.u_scales : p.b_scales) + row * ks, ks);
+#pragma unroll
+      for (int b = 0; b < BPL; ++b) {
+        sl.c[r][b] = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(rc, vo_c + 8 * b, 0, 0));
+        sl.s[r][b] = __builtin_amdgcn_raw_buffer_load_b8(rs, vo_s + b, 0, 0);
+      }
+    }
+  };
+
+  float res[T][kGvCols];
+  float resu[DUAL ? T : 1][DUAL ? kGvCols : 1];
+  Slot ring[D];
+#pragma unroll
+  for (int d = 0; d < D; ++d) {
+    load(d, ring[d]);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+#pragma unroll
+  for (int g = 0; g < G; ++g) {
+    Slot& sl = ring[g % D];
+    float acc[NR][T];
+#pragma unroll
+    for (int r = 0; r < NR; ++r) {
+#pragma unroll
+      for (int t = 0; t < T; ++t) acc[r][t] = 0.f;
+#pragma unroll
+      for (int b = 0; b < BPL; ++b) {
+        const uint32_t w0 = sl.c[r][b].x, w1 = sl.c[r][b].y;
+        const f16x2 cp[8] = {__builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w0, 1.0f, 0),
+                             __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w0, 1.0f, 1),
+                             __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w0, 1.0f, 2),
+                             __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w0, 1.0f, 3),
+                             __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w1, 1.0f, 0),
+                             __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w1, 1.0f, 1),
+                             __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w1, 1.0f, 2),
+                             __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w1, 1.0f, 3)};
+        const float sc = e4m3_over_256(sl.s[r][b]);
+#pragma unroll
+        for (int t = 0; t < T; ++t) {
+          float d = 0.f;
+#pragma unroll
+          for (int i = 0; i < 8; ++i) {
+            const f16x8& xv = xa[t][b][i >> 2];
+            const f16x2 xp = {xv[2 * (i & 3)], xv[2 * (i & 3) + 1]};
+            d = __builtin_amdgcn_fdot2(cp[i], xp, d, false);
+          }
+          acc[r][t] = fmaf(d, sc, acc[r][t]);
+        }
+      }
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    if (g + D < G) load(g + D, sl);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int q = 0; q < RP; ++q)
+#pragma unroll
+      for (int t = 0; t < T; ++t) {
+        res[t][g * RP + q] = wave_sum_dpp(acc[q][t]) * 256.f;
+        if constexpr (DUAL) resu[t][g * RP + q] = wave_sum_dpp(acc[RP + q][t]) * 256.f;
+      }
+  }
+
+  // ---- epilogue: lane t < M writes token t's 16 columns ----------------------------
+  float v[kGvCols], vu[DUAL ? kGvCols : 1];
+#pragma unroll
+  for (int c = 0; c < kGvCols; ++c) {
+    v[c] = res[0][c];
+    if constexpr (DUAL) vu[c] = resu[0][c];
+  }
+#pragma unroll
+  for (int t = 1; t < T; ++t)
+    if (lane == t) {
+#pragma unroll
+      for (int c = 0; c < kGvCols; ++c) {
+        v[c] = res[t][c];
+        if constexpr (DUAL) vu[c] = resu[t][c];
+      }
+    }
+  const bool active = lane < M && lane < T;
+  if constexpr (DUAL) {
+    const float alpha = p.a_gs[0] * p.b_gs[0], alpha_u = p.a_gs[0] * p.u_gs[0];
+    float hmax = 0.f;
+#pragma unroll
+    for (int c = 0; c < kGvCols; ++c) {
+      v[c] = silu_mul(v[c] * alpha, vu[c] * alpha_u);
+      hmax = fmaxf(hmax, active ? fabsf(v[c]) : 0.f);
+    }
+    if constexpr (EPI == EPI_GLU) {
+      if (active) {
+        float4* dst = reinterpret_cast<float4*>(p.h + lane * N + n0);   // N % 128 == 0: 16-B aligned
+#pragma unroll
+        for (int c = 0; c < kGvCols / 4; ++c) dst[c] = make_float4(v[4 * c], v[4 * c + 1], v[4 * c + 2], v[4 * c + 3]);
+      }
+      hmax = wave_max(hmax);
+      if (lane == 0) p.partials[wave] = hmax;
+    } else if constexpr (kGvCols == 16) {
+      if (active) {
+        uint32_t w0, w1;
+        const uint32_t sc = quantize_block16(v, p.q_gs[0], w0, w1);
+        *reinterpret_cast<uint2*>(p.q_codes + lane * (N / 2) + n0 / 2) = make_uint2(w0, w1);
+        p.q_scales[lane * (N / 16) + n0 / 16] = (uint8_t)sc;
+      }
+    } else {
+      // the work-group's 4 waves hold 4 * kGvCols consecutive columns: gather
+      // them per token, then one thread per (16-column block, token) quantises
+      constexpr int WC = 4 * kGvCols;
+      if (active) {
+#pragma unroll
+        for (int c = 0; c < kGvCols; ++c) hq[lane * WC + wi * kGvCols + c] = v[c];
+      }
+      __syncthreads();
+      const int tid = (int)threadIdx.x;
+      const int blk = tid % (WC / 16), t = tid / (WC / 16);
+      if (t < T && t < M) {
+        float b16[16];
+#pragma unroll
+        for (int c = 0; c < 16; ++c) b16[c] = hq[t * WC + blk * 16 + c];
+        const int64_t c0 = (int64_t)blockIdx.x * WC + blk * 16;
+        uint32_t w0, w1;
+        const uint32_t sc = quantize_block16(b16, p.q_gs[0], w0, w1);
+        *reinterpret_cast<uint2*>(p.q_codes + t * (N / 2) + c0 / 2) = make_uint2(w0, w1);
+        p.q_scales[t * (N / 16) + c0 / 16] = (uint8_t)sc;
+      }
+    }
+  } else {
+    if (active) {
+      if (p.splits > 1 || p.force_split) {
+        float* dst = p.split_out + (split * M + lane) * N + n0;
+#pragma unroll
+        for (int c = 0; c < kGvCols; ++c)
+          if (n0 + c < N) dst[c] = v[c];
+      } else {
+        const float alpha = p.a_gs[0] * p.b_gs[0];
+#pragma unroll
+        for (int c = 0; c < kGvCols; ++c) {
+          if (n0 + c >= N) continue;
+          const float o = v[c] * alpha;
+          if (p.c_bf16)
+            reinterpret_cast<uint16_t*>(p.c)[lane * p.ldc + n0 + c] = (uint16_t)f32_to_bf16_bits(o);
+          else
+            reinterpret_cast<float*>(p.c)[lane * p.ldc + n0 + c] = o;
+        }
+      }
+    }
+  }
+}
+
 // out[m][n] = (sum over splits, in split order) * gs_a * gs_b[expert of slot m].
 __global__ void __launch_bounds__(256) splitk_reduce_kernel(const float* __restrict__ part, uint32_t splits,
                                                             int64_t M, int64_t N, const float* a_gs,
@@ -908,8 +1171,17 @@ __global__ void __launch_bounds__(256) splitk_reduce_kernel(const float* __restr
   const float ga = a_gs[0];
   for (int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x; idx < total; idx += (int64_t)gridDim.x * 256) {
     const int64_t m = idx / N, n = idx - m * N;
+    // loads in batches of eight, added in split order
     float acc = 0.f;
-    for (uint32_t s = 0; s < splits; ++s) acc += part[(int64_t)s * total + idx];
+    uint32_t s = 0;
+    for (; s + 8u <= splits; s += 8u) {
+      float v[8];
+#pragma unroll
+      for (int k = 0; k < 8; ++k) v[k] = part[(int64_t)(s + k) * total + idx];
+#pragma unroll
+      for (int k = 0; k < 8; ++k) acc += v[k];
+    }
+    for (; s < splits; ++s) acc += part[(int64_t)s * total + idx];
     int e = 0;
     if (off) {
       while (e < E - 1 && off[e + 1] <= m) ++e;
@@ -940,7 +1212,26 @@ __global__ void __launch_bounds__(256) splitk_reduce_quant_kernel(const float* _
     float v[16];
 #pragma unroll
     for (int c = 0; c < 16; ++c) v[c] = 0.f;
-    for (uint32_t sp = 0; sp < splits; ++sp) {
+    // loads of two splits in flight at a time, added in split order
+    uint32_t sp = 0;
+    for (; sp + 2u <= splits; sp += 2u) {
+      float4 t4[2][4];
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+#pragma unroll
+        for (int g4 = 0; g4 < 4; ++g4)
+          t4[h][g4] = *reinterpret_cast<const float4*>(src + (int64_t)(sp + h) * plane + 4 * g4);
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+#pragma unroll
+        for (int g4 = 0; g4 < 4; ++g4) {
+          v[4 * g4] += t4[h][g4].x;
+          v[4 * g4 + 1] += t4[h][g4].y;
+          v[4 * g4 + 2] += t4[h][g4].z;
+          v[4 * g4 + 3] += t4[h][g4].w;
+        }
+    }
+    for (; sp < splits; ++sp) {
 #pragma unroll
       for (int g4 = 0; g4 < 4; ++g4) {
         const float4 t4 = *reinterpret_cast<const float4*>(src + (int64_t)sp * plane + 4 * g4);
@@ -966,13 +1257,51 @@ __global__ void __launch_bounds__(256) splitk_reduce_quant_kernel(const float* _
 // store epilogue, over work-groups too).
 struct Plan {
   bool small;
+  int gv_bpl;   // > 0: the one/two-token weight stream with BPL units of K per split
   uint32_t m_tiles, n_tiles, splits, chunks_per_split;
 };
 
 static uint32_t cdiv(int64_t a, int64_t b) { return (uint32_t)((a + b - 1) / b); }
 
+// The weight stream takes M <= NVFP4_GV_MAXT tokens and K a multiple of 1024;
+// a split covers BPL units (the largest divisor of K/1024 up to 5).  The
+// gate/up pair needs whole rows in one split (GLU epilogue), so there K <= 5120.
+struct GvPlan {
+  int bpl;          // 0: not applicable
+  uint32_t splits;
+};
+
+static GvPlan plan_gemv(int64_t M, int64_t K, bool dual) {
+  GvPlan pl{0, 0};
+  if (M < 1 || M > NVFP4_GV_MAXT || K % 1024 != 0) return pl;
+  const int64_t U = K / 1024;
+  int bpl = 1;
+  for (int b = 5; b >= 2; --b)
+    if (U % b == 0) {
+      bpl = b;
+      break;
+    }
+  const int64_t S = U / bpl;
+  if ((dual && S != 1) || S > 64) return pl;
+  pl.bpl = bpl;
+  pl.splits = (uint32_t)S;
+  return pl;
+}
+
 static Plan plan_store(int64_t M, int64_t N, int64_t K, int E, bool grouped) {
   Plan pl{};
+  if (!grouped) {
+    const GvPlan gv = plan_gemv(M, K, false);
+    if (gv.bpl > 0) {
+      pl.small = true;
+      pl.gv_bpl = gv.bpl;
+      pl.m_tiles = 1;
+      pl.n_tiles = cdiv(N, kGvCols);
+      pl.splits = gv.splits;
+      pl.chunks_per_split = 0;
+      return pl;
+    }
+  }
   pl.small = !grouped && M <= 32;
   const uint32_t chunks = (uint32_t)(K / 128);
   uint32_t s = 1;
@@ -999,6 +1328,28 @@ static void launch_skinny(const GemmArgs& g, hipStream_t st) {
   const uint32_t grid = g.n_tiles * g.splits;
   const int slot = launch_begin(EPI != EPI_STORE ? KC_GEMM_GLU : KC_GEMM_STORE, st);
   hipLaunchKernelGGL((skinny_kernel<DUAL, EPI>), dim3(grid), dim3(kSkWaves * 64), 0, st, g);
+  launch_end(slot, st);
+}
+
+template <int T, bool DUAL, int EPI>
+static void launch_gemv_t(const GemmArgs& g, int bpl, uint32_t grid, hipStream_t st) {
+  switch (bpl) {
+    case 1: hipLaunchKernelGGL((gemv_kernel<T, 1, DUAL, EPI>), dim3(grid), dim3(256), 0, st, g); break;
+    case 2: hipLaunchKernelGGL((gemv_kernel<T, 2, DUAL, EPI>), dim3(grid), dim3(256), 0, st, g); break;
+    case 3: hipLaunchKernelGGL((gemv_kernel<T, 3, DUAL, EPI>), dim3(grid), dim3(256), 0, st, g); break;
+    case 4: hipLaunchKernelGGL((gemv_kernel<T, 4, DUAL, EPI>), dim3(grid), dim3(256), 0, st, g); break;
+    default: hipLaunchKernelGGL((gemv_kernel<T, 5, DUAL, EPI>), dim3(grid), dim3(256), 0, st, g); break;
+  }
+}
+
+// g.splits holds the K splits; one wave per 16 output columns per split.
+template <bool DUAL, int EPI>
+static void launch_gemv(const GemmArgs& g, int bpl, hipStream_t st) {
+  const uint32_t waves = cdiv(g.N, kGvCols) * g.splits;
+  const uint32_t grid = cdiv(waves, 4);
+  const int slot = launch_begin(EPI != EPI_STORE ? KC_GEMM_GLU : KC_GEMM_STORE, st);
+  if (g.M <= 1) launch_gemv_t<1, DUAL, EPI>(g, bpl, grid, st);
+  else launch_gemv_t<NVFP4_GV_MAXT, DUAL, EPI>(g, bpl, grid, st);
   launch_end(slot, st);
 }
 
@@ -1077,6 +1428,7 @@ int store_launch(Operand a, const int32_t* rows, const int32_t* off, int E, int6
   g.m_tiles = pl.m_tiles;
   g.n_tiles = pl.n_tiles;
   if (grouped) launch_cfg<NVFP4_STORE_WN, NVFP4_STORE_TM, 1, false, true, EPI_STORE>(g, st);
+  else if (pl.gv_bpl > 0) launch_gemv<false, EPI_STORE>(g, pl.gv_bpl, st);
   else if (pl.small) launch_skinny<false, EPI_STORE>(g, st);
   else launch_cfg<NVFP4_STORE_WN, NVFP4_STORE_TM, 1, false, false, EPI_STORE>(g, st);
   // The reduction always runs (over zero rows when K was not split), so the
@@ -1086,14 +1438,15 @@ int store_launch(Operand a, const int32_t* rows, const int32_t* off, int E, int6
 }
 
 // GLU GEMM.  Workspace: [H float32 M x N][A f16 M x K][partials].
-static uint32_t glu_parts(int64_t M, int64_t N, int E, bool grouped) {
+static uint32_t glu_parts(int64_t M, int64_t N, int64_t K, int E, bool grouped) {
   if (grouped) return (cdiv(M, 32 * NVFP4_GLU_TM) + (uint32_t)E) * cdiv(N, 32 * NVFP4_GLU_WN);
+  if (plan_gemv(M, K, true).bpl > 0) return cdiv(N, kGvCols);   // one partial per wave
   if (M <= 32) return cdiv(N, 32);
   return cdiv(M, 32 * NVFP4_GLU_TM) * cdiv(N, 32 * NVFP4_GLU_WN);
 }
 
 size_t glu_ws_bytes(int64_t M, int64_t N, int64_t K, int E, bool grouped) {
-  return align256((size_t)M * N * 4) + align256((size_t)M * K * 2) + align256((size_t)glu_parts(M, N, E, grouped) * 4);
+  return align256((size_t)M * N * 4) + align256((size_t)M * K * 2) + align256((size_t)glu_parts(M, N, K, E, grouped) * 4);
 }
 
 int glu_launch(Operand a, const int32_t* a_rows, const int32_t* off, int E, int64_t M, Operand gt, Operand up,
@@ -1117,6 +1470,8 @@ int glu_launch(Operand a, const int32_t* a_rows, const int32_t* off, int E, int6
     g.m_tiles = cdiv(M, 32 * NVFP4_GLU_TM) + (uint32_t)E;
     g.n_tiles = cdiv(N, 32 * NVFP4_GLU_WN);
     launch_cfg<NVFP4_GLU_WN, NVFP4_GLU_TM, 1, true, true, EPI_GLU>(g, st);
+  } else if (const GvPlan gv = plan_gemv(M, K, true); gv.bpl > 0) {
+    launch_gemv<true, EPI_GLU>(g, gv.bpl, st);
   } else if (M <= 32) {
     g.m_tiles = 1;
     g.n_tiles = cdiv(N, 32);
@@ -1127,7 +1482,7 @@ int glu_launch(Operand a, const int32_t* a_rows, const int32_t* off, int E, int6
     launch_cfg<NVFP4_GLU_WN, NVFP4_GLU_TM, 1, true, false, EPI_GLU>(g, st);
   }
   if (hipGetLastError() != hipSuccess) return 7;
-  return requant_f32_launch(h, M, N, hq_codes, hq_scales, hq_gs, partials, glu_parts(M, N, E, grouped), st);
+  return requant_f32_launch(h, M, N, hq_codes, hq_scales, hq_gs, partials, glu_parts(M, N, K, E, grouped), st);
 }
 
 size_t glu_static_ws_bytes(int64_t M, int64_t K) { return align256((size_t)M * K * 2); }
@@ -1151,6 +1506,8 @@ int glu_static_launch(Operand a, const int32_t* a_rows, const int32_t* off, int 
     g.m_tiles = cdiv(M, 32 * NVFP4_GLU_TM) + (uint32_t)E;
     g.n_tiles = cdiv(N, 32 * NVFP4_GLU_WN);
     launch_cfg<NVFP4_GLU_WN, NVFP4_GLU_TM, 1, true, true, EPI_GLUQ>(g, st);
+  } else if (const GvPlan gv = plan_gemv(M, K, true); gv.bpl > 0) {
+    launch_gemv<true, EPI_GLUQ>(g, gv.bpl, st);
   } else if (M <= 32) {
     g.m_tiles = 1;
     g.n_tiles = cdiv(N, 32);
@@ -1176,7 +1533,8 @@ int store_quant_launch(Operand a, int64_t M, Operand w, int64_t N, int64_t K, ui
   g.force_split = 1;
   g.m_tiles = pl.m_tiles;
   g.n_tiles = pl.n_tiles;
-  if (pl.small) launch_skinny<false, EPI_STORE>(g, st);
+  if (pl.gv_bpl > 0) launch_gemv<false, EPI_STORE>(g, pl.gv_bpl, st);
+  else if (pl.small) launch_skinny<false, EPI_STORE>(g, st);
   else launch_cfg<NVFP4_STORE_WN, NVFP4_STORE_TM, 1, false, false, EPI_STORE>(g, st);
   int64_t blocks = (M * (N / 16) + 255) / 256;
   if (blocks > 8192) blocks = 8192;

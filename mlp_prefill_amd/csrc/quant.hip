@@ -81,8 +81,18 @@ __global__ void __launch_bounds__(256) quantize_kernel(const T* __restrict__ x, 
   __shared__ float red[4];
   float gs;
   if (mode == 0) {
+    // eight independent loads per step: the reduction is latency-bound when
+    // there are thousands of partials (max is exact in any order)
     float m = 0.f;
-    for (uint32_t i = threadIdx.x; i < npart; i += 256u) m = fmaxf(m, partials[i]);
+    uint32_t i = threadIdx.x;
+    for (; i + 7u * 256u < npart; i += 8u * 256u) {
+      float v[8];
+#pragma unroll
+      for (int k = 0; k < 8; ++k) v[k] = partials[i + k * 256u];
+#pragma unroll
+      for (int k = 0; k < 8; ++k) m = fmaxf(m, v[k]);
+    }
+    for (; i < npart; i += 256u) m = fmaxf(m, partials[i]);
     m = block_max(m, red);
     gs = global_scale_from_amax(m);
     if (blockIdx.x == 0 && threadIdx.x == 0) *gs_ptr = gs;

@@ -1,0 +1,116 @@
+"""The one/two-token weight stream (M <= 2, K a multiple of 1024) against the oracle.
+
+It covers every K split width (1 to 5 units of 1024), split-K with a partial
+reduction (K = 8192, 17408), ragged N (columns past N), fp32 and bf16 outputs,
+the gate/up GLU with its requantisation, the quantising GLU epilogue, and
+per-token independence (token 0 of a 2-token call is bit-identical to the
+1-token call: the accumulation order does not depend on the batch).
+"""
+import numpy as np
+import pytest
+import torch
+
+from oracle import gemm as ogemm
+from oracle import quant
+from synthetic import bf16_bits_to_f32, bf16_normal
+from tests.gpu_util import (announce, assert_bf16_rounding_close, assert_nvfp4_equal, bf16_tensor_to_f32,
+                            dev_quantize, max_norm_err, require_gpu, to_host)
+from tests.test_gpu_mlp import _weights, check_mlp
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(autouse=True, scope="module")
+def _gpu():
+    require_gpu()
+
+
+def _pair(m, n, k, xs, ws):
+    xb = bf16_normal(xs, (m, k))
+    wb = bf16_normal(ws, (n, k), sigma=0.02)
+    a, b = dev_quantize(xb), dev_quantize(wb)
+    ra, rb = quant.quantize(bf16_bits_to_f32(xb)), quant.quantize(bf16_bits_to_f32(wb))
+    assert_nvfp4_equal(to_host(a), ra, "A")
+    assert_nvfp4_equal(to_host(b), rb, "B")
+    return a, b, ra, rb
+
+
+def _gemm(a, b, m, n, dtype=torch.float32):
+    import mlp_prefill_amd as mm
+    c = torch.empty((m, n), dtype=dtype, device="cuda")
+    mm.nvfp4_gemm(a, b, c)
+    torch.cuda.synchronize()
+    return c.cpu().numpy() if dtype == torch.float32 else bf16_tensor_to_f32(c)
+
+
+# (M, N, K): K/1024 = 1, 2, 3, 4, 5 (one split), 8 (2 splits of 4), 7 (7 splits of 1),
+# 17 (17 splits of 1); N multiples of 16 and ragged
+STREAM_SHAPES = [(1, 64, 1024), (2, 48, 2048), (1, 200, 3072), (2, 128, 4096), (1, 96, 5120), (2, 100, 5120),
+                 (1, 36, 8192), (2, 160, 7168), (1, 5120, 17408), (2, 332, 17408)]
+
+
+@pytest.mark.parametrize("m,n,k", STREAM_SHAPES, ids=[f"{m}x{n}x{k}" for m, n, k in STREAM_SHAPES])
+def test_stream_gemm(m, n, k):
+    announce(f"stream gemm {m}x{n}x{k}")
+    a, b, ra, rb = _pair(m, n, k, 500 + m + k // 1024, 600 + n)
+    ref = ogemm.gemm(ra, rb)
+    y = _gemm(a, b, m, n)
+    err = max_norm_err(y, ref)
+    print(f"max-normalised error fp32 {err:.3e}")
+    assert err <= 1e-5
+    if n % 8 == 0:   # a bf16 row stride must be a multiple of 16 bytes
+        y16 = _gemm(a, b, m, n, torch.bfloat16)
+        print(f"max-normalised error bf16 {max_norm_err(y16, ref):.3e}")
+        assert_bf16_rounding_close(y16, ref)
+
+
+def test_stream_token_independence():
+    """Row 0 of a two-token product equals the one-token product bit for bit."""
+    announce("stream gemm token independence 2x512x17408 vs 1x512x17408")
+    xb = bf16_normal(801, (2, 17408))
+    wb = bf16_normal(802, (512, 17408), sigma=0.02)
+    a2, b = dev_quantize(xb), dev_quantize(wb)
+    # quantise the first row alone with the two-row tensor's global scale so x~ is identical
+    a1 = dev_quantize(xb[:1], gs_mode=1, gs=float(a2.gscale.cpu().numpy()[0]))
+    assert np.array_equal(a1.codes.cpu().numpy().reshape(-1), a2.codes.cpu().numpy().reshape(-1)[: a1.codes.numel()])
+    y2 = _gemm(a2, b, 2, 512)
+    y1 = _gemm(a1, b, 1, 512)
+    assert np.array_equal(y1[0].view(np.uint32), y2[0].view(np.uint32))
+
+
+GLU_SHAPES = [(1, 1024, 256), (2, 2048, 384), (1, 3072, 128), (2, 5120, 640), (1, 4096, 1024)]
+
+
+@pytest.mark.parametrize("t,k,i", GLU_SHAPES, ids=[f"T{t}_K{k}_I{i}" for t, k, i in GLU_SHAPES])
+def test_stream_mlp(t, k, i):
+    """Gate/up GLU + requantisation on the weight stream, then the down
+    projection (K = I is not a multiple of 1024 for most shapes: it takes the
+    MFMA weight-stream kernel), staged against the oracle."""
+    announce(f"stream mlp T={t} K={k} I={i}")
+    wdev, wref = _weights(k, i, (900 + t, 910 + t, 920 + t))
+    check_mlp(bf16_normal(930 + t, (t, k)), wdev, wref, f"stream T{t}")
+
+
+@pytest.mark.parametrize("t", [1, 2])
+def test_stream_glu_quant_epilogue(t):
+    """The quantising GLU epilogue (static scale) on the weight stream gives
+    exactly the NVFP4 encoding, under that scale, of the float32 H the
+    dynamic call writes."""
+    import mlp_prefill_amd as m
+    k, i = 5120, 1024
+    announce(f"stream gate/up quantising epilogue T={t} K={k} I={i}")
+    wdev, _ = _weights(k, i, (940, 941, 942))
+    xq = dev_quantize(bf16_normal(943 + t, (t, k)))
+    hq = m.NVFP4.empty(t, i)
+    ws = m.nvfp4_mlp_gu_act(xq, wdev[0], wdev[1], hq)
+    torch.cuda.synchronize()
+    h = ws[: t * i * 4].view(torch.float32).view(t, i).cpu().numpy().copy()
+    for gs in (float(hq.gscale.cpu().numpy()[0]), float(hq.gscale.cpu().numpy()[0]) * 0.37):
+        hs = m.NVFP4.empty(t, i)
+        hs.gscale.fill_(gs)
+        m.nvfp4_mlp_gu_act_static(xq, wdev[0], wdev[1], hs)
+        torch.cuda.synchronize()
+        ref = quant.quantize(h, gs=np.float32(gs))
+        got = to_host(hs)
+        assert np.array_equal(got.scales, ref.scales)
+        assert np.array_equal(got.codes, ref.codes)
