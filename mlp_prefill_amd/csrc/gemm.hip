@@ -1162,6 +1162,205 @@ __global__ void __launch_bounds__(256) gemv_kernel(GemmArgs p) {
   }
 }
 
+// ---- weight stream for 3 to 8 tokens on the 4x4x4 matrix core ----------------------------
+// With a few tokens the dot products of the one/two-token stream grow with T
+// on the vector ALU.  v_mfma_f32_4x4x4_16b_f16 runs 16 independent 4x4x4
+// products per wave: for block b = lane / 4, A row i and B row j are the four
+// f16 values of lanes 4b+i and 4b+j, and C[i][j] accumulates in lane 4b+j,
+// entry i.  Here B row j is weight row j of a quad of rows and A row i is
+// token i of a set of four, so one instruction adds 4 tokens x 4 rows of
+// products over four K positions of each of 16 segments; the token count
+// costs matrix-core time only.
+//
+// Lane l takes row j = l % 4 of the quad and segment s = l / 4 of a 1024-wide
+// unit of K: the four blocks 4s .. 4s+3 (32 code bytes and 4 scale bytes,
+// 16 lanes per row: 256 contiguous bytes of each of 4 rows per load).  The
+// weights are expanded to code * scale in f16 (exact) as in the large-batch
+// kernels.  A work-group of WK waves covers 16 output columns; wave w takes
+// unit split * WK + w and keeps that unit's activation in registers.  The
+// segment partial sums are added within each 16-lane row by DPP shifts, and
+// the rows and waves through LDS in a fixed order.
+constexpr int kQdCols = 16;   // output columns per work-group
+constexpr int kQdMaxWaves = 8;
+
+template <int NTS, bool DUAL, int EPI>
+__global__ void __launch_bounds__(kQdMaxWaves * 64) quad_kernel(GemmArgs p, int wk) {
+  typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
+  constexpr int NQ = DUAL ? kQdCols / 2 : kQdCols / 4;   // row quads per wave
+  constexpr int NV = NQ * NTS * 4;                       // accumulator values per lane
+  __shared__ float red[kQdMaxWaves * 4 * NV * 4];
+  __shared__ float hq[EPI == EPI_GLUQ ? 8 * kQdCols : 1];
+  __shared__ float redmax[kQdMaxWaves];
+  const int lane = threadIdx.x & 63;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int j = lane & 3, s = lane >> 2;
+  const int64_t N = p.N, K = p.K, M = p.M;
+  const int64_t ctiles = (N + kQdCols - 1) / kQdCols;
+  const int64_t split = blockIdx.x / ctiles;
+  const int64_t n0 = (blockIdx.x - split * ctiles) * kQdCols;
+  const int64_t u = split * wk + w;                       // this wave's unit of K
+  const int64_t kb = K >> 1, ks = K >> 4;
+
+  // activation: token 4*ts + j (the A row of this lane), elements 64 s .. 64 s + 63 of the unit
+  f16x8 xa[NTS][8];
+#pragma unroll
+  for (int ts = 0; ts < NTS; ++ts) {
+    const int64_t t = 4 * ts + j;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      if (t < M) {
+        xa[ts][e] = *reinterpret_cast<const f16x8*>(p.a + t * K + u * 1024 + s * 64 + 8 * e);
+      } else {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) xa[ts][e][i] = (_Float16)0.f;
+      }
+    }
+  }
+
+  // weight row of this lane in quad q
+  auto row_ptrs = [&](int q, const uint8_t*& cp, const uint8_t*& sp) {
+    int64_t row;
+    const uint8_t *cbase, *sbase;
+    if constexpr (DUAL) {
+      row = n0 + 2 * q + (j & 1);
+      cbase = j < 2 ? p.b_codes : p.u_codes;
+      sbase = j < 2 ? p.b_scales : p.u_scales;
+    } else {
+      row = n0 + 4 * q + j;
+      cbase = p.b_codes;
+      sbase = p.b_scales;
+    }
+    row = row < N ? row : N - 1;                            // columns past N: valid rows, never stored
+    cp = cbase + row * kb + u * 512 + s * 32;
+    sp = sbase + row * ks + u * 64 + s * 4;
+  };
+  struct Slot {
+    u32x4 c0, c1;
+    uint32_t sc;
+  };
+  auto load = [&](int q, Slot& sl) {
+    const uint8_t *cp, *sp;
+    row_ptrs(q, cp, sp);
+    sl.c0 = *reinterpret_cast<const u32x4*>(cp);
+    sl.c1 = *reinterpret_cast<const u32x4*>(cp + 16);
+    sl.sc = *reinterpret_cast<const uint32_t*>(sp);
+  };
+
+  f32x4 acc[NQ][NTS];
+#pragma unroll
+  for (int q = 0; q < NQ; ++q)
+#pragma unroll
+    for (int ts = 0; ts < NTS; ++ts) acc[q][ts] = (f32x4){0.f, 0.f, 0.f, 0.f};
+  Slot ring[2];
+  load(0, ring[0]);
+  __builtin_amdgcn_sched_barrier(0);
+  load(1, ring[1]);
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int q = 0; q < NQ; ++q) {
+    Slot& sl = ring[q & 1];
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {
+      const uint32_t w0 = b < 2 ? sl.c0[2 * b] : sl.c1[2 * b - 4];
+      const uint32_t w1 = b < 2 ? sl.c0[2 * b + 1] : sl.c1[2 * b - 3];
+      const uint32_t scb = (sl.sc >> (8 * b)) & 0xFFu;
+      const f16x8 lo = expand8(w0, scb), hi = expand8(w1, scb);
+      const f16x4 bk[4] = {{lo[0], lo[1], lo[2], lo[3]}, {lo[4], lo[5], lo[6], lo[7]},
+                           {hi[0], hi[1], hi[2], hi[3]}, {hi[4], hi[5], hi[6], hi[7]}};
+#pragma unroll
+      for (int ts = 0; ts < NTS; ++ts) {
+        const f16x8& x0 = xa[ts][2 * b];
+        const f16x8& x1 = xa[ts][2 * b + 1];
+        const f16x4 ak[4] = {{x0[0], x0[1], x0[2], x0[3]}, {x0[4], x0[5], x0[6], x0[7]},
+                             {x1[0], x1[1], x1[2], x1[3]}, {x1[4], x1[5], x1[6], x1[7]}};
+#pragma unroll
+        for (int k = 0; k < 4; ++k) acc[q][ts] = __builtin_amdgcn_mfma_f32_4x4x4f16(ak[k], bk[k], acc[q][ts], 0, 0, 0);
+      }
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    if (q + 2 < NQ) load(q + 2, sl);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+
+  // segments within each 16-lane row (lanes 16r + 4s' + j, s' = 0..3): two DPP
+  // shifts leave the row's sum in s' = 3; those 16 lanes write it to LDS
+  const bool writer = (lane & 12) == 12;
+  const int r = lane >> 4;
+#pragma unroll
+  for (int q = 0; q < NQ; ++q)
+#pragma unroll
+    for (int ts = 0; ts < NTS; ++ts)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        float v = acc[q][ts][i];
+        v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x114, 0xF, 0xF, true));
+        v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x118, 0xF, 0xF, true));
+        if (writer) red[((w * 4 + r) * NV + (q * NTS + ts) * 4 + i) * 4 + j] = v;
+      }
+  __syncthreads();
+
+  // sum over the 4 rows of each wave and over the waves, in order; one thread per output
+  const int nthreads = (int)blockDim.x;
+  auto total = [&](int vi, int jj) {
+    float t = 0.f;
+    for (int w2 = 0; w2 < wk; ++w2)
+#pragma unroll
+      for (int r2 = 0; r2 < 4; ++r2) t += red[((w2 * 4 + r2) * NV + vi) * 4 + jj];
+    return t;
+  };
+  if constexpr (DUAL) {
+    const float alpha = p.a_gs[0] * p.b_gs[0], alpha_u = p.a_gs[0] * p.u_gs[0];
+    float hmax = 0.f;
+    for (int o = (int)threadIdx.x; o < NV * 2; o += nthreads) {
+      const int vi = o >> 1, jj = o & 1;
+      const int q = vi / (NTS * 4), ts = (vi / 4) % NTS, i = vi & 3;
+      const int64_t t = 4 * ts + i, c = 2 * q + jj;
+      const float h = silu_mul(total(vi, jj) * alpha, total(vi, jj + 2) * alpha_u);
+      if (t < M) {
+        if constexpr (EPI == EPI_GLU) {
+          p.h[t * N + n0 + c] = h;
+          hmax = fmaxf(hmax, fabsf(h));
+        } else {
+          hq[t * kQdCols + c] = h;
+        }
+      }
+    }
+    if constexpr (EPI == EPI_GLU) {
+      hmax = block_max(hmax, redmax);
+      if (threadIdx.x == 0) p.partials[blockIdx.x] = hmax;
+    } else {
+      __syncthreads();
+      const int t = (int)threadIdx.x;
+      if (t < M) {
+        float b16[16];
+#pragma unroll
+        for (int c = 0; c < 16; ++c) b16[c] = hq[t * kQdCols + c];
+        uint32_t w0, w1;
+        const uint32_t sc = quantize_block16(b16, p.q_gs[0], w0, w1);
+        *reinterpret_cast<uint2*>(p.q_codes + t * (N / 2) + n0 / 2) = make_uint2(w0, w1);
+        p.q_scales[t * (N / 16) + n0 / 16] = (uint8_t)sc;
+      }
+    }
+  } else {
+    const bool part = p.splits > 1 || p.force_split;
+    const float alpha = p.a_gs[0] * p.b_gs[0];
+    for (int o = (int)threadIdx.x; o < NV * 4; o += nthreads) {
+      const int vi = o >> 2, jj = o & 3;
+      const int q = vi / (NTS * 4), ts = (vi / 4) % NTS, i = vi & 3;
+      const int64_t t = 4 * ts + i, c = n0 + 4 * q + jj;
+      if (t >= M || c >= N) continue;
+      const float v = total(vi, jj);
+      if (part) {
+        p.split_out[(split * M + t) * N + c] = v;
+      } else if (p.c_bf16) {
+        reinterpret_cast<uint16_t*>(p.c)[t * p.ldc + c] = (uint16_t)f32_to_bf16_bits(v * alpha);
+      } else {
+        reinterpret_cast<float*>(p.c)[t * p.ldc + c] = v * alpha;
+      }
+    }
+  }
+}
+
 // out[m][n] = (sum over splits, in split order) * gs_a * gs_b[expert of slot m].
 __global__ void __launch_bounds__(256) splitk_reduce_kernel(const float* __restrict__ part, uint32_t splits,
                                                             int64_t M, int64_t N, const float* a_gs,
@@ -1258,6 +1457,7 @@ __global__ void __launch_bounds__(256) splitk_reduce_quant_kernel(const float* _
 struct Plan {
   bool small;
   int gv_bpl;   // > 0: the one/two-token weight stream with BPL units of K per split
+  int qd_wk;    // > 0: the 3-8 token stream with WK waves (units of K) per split
   uint32_t m_tiles, n_tiles, splits, chunks_per_split;
 };
 
@@ -1288,6 +1488,31 @@ static GvPlan plan_gemv(int64_t M, int64_t K, bool dual) {
   return pl;
 }
 
+// The 3-8 token stream: K a multiple of 1024; a work-group of WK waves (the
+// largest divisor of K/1024 up to 8) takes WK units.  The gate/up pair needs
+// one split (K <= 8192).
+struct QdPlan {
+  int wk;           // 0: not applicable
+  uint32_t splits;
+};
+
+static QdPlan plan_quad(int64_t M, int64_t K, bool dual) {
+  QdPlan pl{0, 0};
+  if (M < 3 || M > 8 || K % 1024 != 0) return pl;
+  const int64_t U = K / 1024;
+  int wk = 1;
+  for (int w = kQdMaxWaves; w >= 2; --w)
+    if (U % w == 0) {
+      wk = w;
+      break;
+    }
+  const int64_t S = U / wk;
+  if ((dual && S != 1) || S > 64) return pl;
+  pl.wk = wk;
+  pl.splits = (uint32_t)S;
+  return pl;
+}
+
 static Plan plan_store(int64_t M, int64_t N, int64_t K, int E, bool grouped) {
   Plan pl{};
   if (!grouped) {
@@ -1298,6 +1523,16 @@ static Plan plan_store(int64_t M, int64_t N, int64_t K, int E, bool grouped) {
       pl.m_tiles = 1;
       pl.n_tiles = cdiv(N, kGvCols);
       pl.splits = gv.splits;
+      pl.chunks_per_split = 0;
+      return pl;
+    }
+    const QdPlan qd = plan_quad(M, K, false);
+    if (qd.wk > 0) {
+      pl.small = true;
+      pl.qd_wk = qd.wk;
+      pl.m_tiles = 1;
+      pl.n_tiles = cdiv(N, kQdCols);
+      pl.splits = qd.splits;
       pl.chunks_per_split = 0;
       return pl;
     }
@@ -1350,6 +1585,16 @@ static void launch_gemv(const GemmArgs& g, int bpl, hipStream_t st) {
   const int slot = launch_begin(EPI != EPI_STORE ? KC_GEMM_GLU : KC_GEMM_STORE, st);
   if (g.M <= 1) launch_gemv_t<1, DUAL, EPI>(g, bpl, grid, st);
   else launch_gemv_t<NVFP4_GV_MAXT, DUAL, EPI>(g, bpl, grid, st);
+  launch_end(slot, st);
+}
+
+// g.splits holds the K splits; one work-group of wk waves per 16 columns per split.
+template <bool DUAL, int EPI>
+static void launch_quad(const GemmArgs& g, int wk, hipStream_t st) {
+  const uint32_t grid = cdiv(g.N, kQdCols) * g.splits;
+  const int slot = launch_begin(EPI != EPI_STORE ? KC_GEMM_GLU : KC_GEMM_STORE, st);
+  if (g.M <= 4) hipLaunchKernelGGL((quad_kernel<1, DUAL, EPI>), dim3(grid), dim3(64 * wk), 0, st, g, wk);
+  else hipLaunchKernelGGL((quad_kernel<2, DUAL, EPI>), dim3(grid), dim3(64 * wk), 0, st, g, wk);
   launch_end(slot, st);
 }
 
@@ -1429,6 +1674,7 @@ int store_launch(Operand a, const int32_t* rows, const int32_t* off, int E, int6
   g.n_tiles = pl.n_tiles;
   if (grouped) launch_cfg<NVFP4_STORE_WN, NVFP4_STORE_TM, 1, false, true, EPI_STORE>(g, st);
   else if (pl.gv_bpl > 0) launch_gemv<false, EPI_STORE>(g, pl.gv_bpl, st);
+  else if (pl.qd_wk > 0) launch_quad<false, EPI_STORE>(g, pl.qd_wk, st);
   else if (pl.small) launch_skinny<false, EPI_STORE>(g, st);
   else launch_cfg<NVFP4_STORE_WN, NVFP4_STORE_TM, 1, false, false, EPI_STORE>(g, st);
   // The reduction always runs (over zero rows when K was not split), so the
@@ -1441,6 +1687,7 @@ int store_launch(Operand a, const int32_t* rows, const int32_t* off, int E, int6
 static uint32_t glu_parts(int64_t M, int64_t N, int64_t K, int E, bool grouped) {
   if (grouped) return (cdiv(M, 32 * NVFP4_GLU_TM) + (uint32_t)E) * cdiv(N, 32 * NVFP4_GLU_WN);
   if (plan_gemv(M, K, true).bpl > 0) return cdiv(N, kGvCols);   // one partial per wave
+  if (plan_quad(M, K, true).wk > 0) return cdiv(N, kQdCols);     // one partial per work-group
   if (M <= 32) return cdiv(N, 32);
   return cdiv(M, 32 * NVFP4_GLU_TM) * cdiv(N, 32 * NVFP4_GLU_WN);
 }
@@ -1472,6 +1719,8 @@ int glu_launch(Operand a, const int32_t* a_rows, const int32_t* off, int E, int6
     launch_cfg<NVFP4_GLU_WN, NVFP4_GLU_TM, 1, true, true, EPI_GLU>(g, st);
   } else if (const GvPlan gv = plan_gemv(M, K, true); gv.bpl > 0) {
     launch_gemv<true, EPI_GLU>(g, gv.bpl, st);
+  } else if (const QdPlan qd = plan_quad(M, K, true); qd.wk > 0) {
+    launch_quad<true, EPI_GLU>(g, qd.wk, st);
   } else if (M <= 32) {
     g.m_tiles = 1;
     g.n_tiles = cdiv(N, 32);
@@ -1508,6 +1757,8 @@ int glu_static_launch(Operand a, const int32_t* a_rows, const int32_t* off, int 
     launch_cfg<NVFP4_GLU_WN, NVFP4_GLU_TM, 1, true, true, EPI_GLUQ>(g, st);
   } else if (const GvPlan gv = plan_gemv(M, K, true); gv.bpl > 0) {
     launch_gemv<true, EPI_GLUQ>(g, gv.bpl, st);
+  } else if (const QdPlan qd = plan_quad(M, K, true); qd.wk > 0) {
+    launch_quad<true, EPI_GLUQ>(g, qd.wk, st);
   } else if (M <= 32) {
     g.m_tiles = 1;
     g.n_tiles = cdiv(N, 32);
@@ -1534,6 +1785,7 @@ int store_quant_launch(Operand a, int64_t M, Operand w, int64_t N, int64_t K, ui
   g.m_tiles = pl.m_tiles;
   g.n_tiles = pl.n_tiles;
   if (pl.gv_bpl > 0) launch_gemv<false, EPI_STORE>(g, pl.gv_bpl, st);
+  else if (pl.qd_wk > 0) launch_quad<false, EPI_STORE>(g, pl.qd_wk, st);
   else if (pl.small) launch_skinny<false, EPI_STORE>(g, st);
   else launch_cfg<NVFP4_STORE_WN, NVFP4_STORE_TM, 1, false, false, EPI_STORE>(g, st);
   int64_t blocks = (M * (N / 16) + 255) / 256;

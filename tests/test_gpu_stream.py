@@ -114,3 +114,45 @@ def test_stream_glu_quant_epilogue(t):
         got = to_host(hs)
         assert np.array_equal(got.scales, ref.scales)
         assert np.array_equal(got.codes, ref.codes)
+
+
+# ---- the 3-8 token stream (4x4x4 matrix core) --------------------------------------
+# (M, N, K): work-groups of 1 (K = 17408: 17 splits), 2, 3, 5, 6, 7 and 8 waves
+QUAD_SHAPES = [(3, 64, 1024), (4, 48, 2048), (5, 200, 3072), (8, 128, 4096), (5, 96, 5120), (6, 100, 5120),
+               (7, 36, 8192), (8, 160, 7168), (8, 20, 6144), (5, 5120, 17408), (3, 332, 17408)]
+
+
+@pytest.mark.parametrize("m,n,k", QUAD_SHAPES, ids=[f"{m}x{n}x{k}" for m, n, k in QUAD_SHAPES])
+def test_quad_stream_gemm(m, n, k):
+    test_stream_gemm(m, n, k)
+
+
+def test_quad_stream_token_independence():
+    """Rows 0-2 of a 5-token product (two token sets) equal the 3-token product
+    (one set) bit for bit, and row 0 of the 3-token product does not depend on
+    rows 1-2."""
+    announce("quad stream token independence 5/3 x 256 x 5120")
+    xb = bf16_normal(811, (5, 5120))
+    wb = bf16_normal(812, (256, 5120), sigma=0.02)
+    a5, b = dev_quantize(xb), dev_quantize(wb)
+    gs = float(a5.gscale.cpu().numpy()[0])
+    a3 = dev_quantize(xb[:3], gs_mode=1, gs=gs)
+    xb2 = xb[:3].copy()
+    xb2[1:] = bf16_normal(813, (2, 5120))
+    a3b = dev_quantize(xb2, gs_mode=1, gs=gs)
+    y5, y3, y3b = _gemm(a5, b, 5, 256), _gemm(a3, b, 3, 256), _gemm(a3b, b, 3, 256)
+    assert np.array_equal(y3.view(np.uint32), y5[:3].view(np.uint32))
+    assert np.array_equal(y3[0].view(np.uint32), y3b[0].view(np.uint32))
+
+
+QUAD_GLU = [(3, 1024, 256), (4, 3072, 128), (5, 5120, 640), (6, 7168, 384), (8, 4096, 1024)]
+
+
+@pytest.mark.parametrize("t,k,i", QUAD_GLU, ids=[f"T{t}_K{k}_I{i}" for t, k, i in QUAD_GLU])
+def test_quad_stream_mlp(t, k, i):
+    test_stream_mlp(t, k, i)
+
+
+@pytest.mark.parametrize("t", [3, 5, 8])
+def test_quad_stream_glu_quant_epilogue(t):
+    test_stream_glu_quant_epilogue(t)
