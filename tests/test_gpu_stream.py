@@ -1,10 +1,15 @@
-"""The one/two-token weight stream (M <= 2, K a multiple of 1024) against the oracle.
+"""The small-batch weight streams against the oracle.
 
-It covers every K split width (1 to 5 units of 1024), split-K with a partial
-reduction (K = 8192, 17408), ragged N (columns past N), fp32 and bf16 outputs,
-the gate/up GLU with its requantisation, the quantising GLU epilogue, and
-per-token independence (token 0 of a 2-token call is bit-identical to the
-1-token call: the accumulation order does not depend on the batch).
+One or two tokens (K a multiple of 1024): every split width (1 to 5 units of
+1024), split K with a partial reduction (K = 7168: 7 splits of 1 unit, 8192:
+2 of 4, 17408: 17 of 1), ragged N (columns past N), fp32 and bf16
+outputs, the gate/up GLU with its requantisation, the quantising GLU
+epilogue, and per-token independence (token 0 of a 2-token call is
+bit-identical to the 1-token call: the accumulation order does not depend on
+the batch).  Three to eight tokens (4x4x4 matrix core): work-groups of 1-8
+waves, split K, the same epilogues and token independence.  Shapes next to
+those limits (K not a multiple of 1024, 9-16 tokens) take the MFMA weight
+stream and are checked the same way.
 """
 import numpy as np
 import pytest
@@ -155,4 +160,28 @@ def test_quad_stream_mlp(t, k, i):
 
 @pytest.mark.parametrize("t", [3, 5, 8])
 def test_quad_stream_glu_quant_epilogue(t):
+    test_stream_glu_quant_epilogue(t)
+
+
+# ---- batches around the stream limits: K not a multiple of 1024 (3 tokens, MFMA weight
+# stream) and 9-16 tokens (MFMA weight stream) --------------------------------------------
+MFMA_SHAPES = [(3, 48, 768), (9, 64, 1280), (12, 200, 5120), (16, 96, 2048), (16, 100, 17408), (11, 5120, 17408),
+              (13, 36, 4352)]
+
+
+@pytest.mark.parametrize("m,n,k", MFMA_SHAPES, ids=[f"{m}x{n}x{k}" for m, n, k in MFMA_SHAPES])
+def test_mfma_stream_gemm(m, n, k):
+    test_stream_gemm(m, n, k)
+
+
+MFMA_GLU = [(9, 1280, 256), (12, 5120, 640), (16, 2304, 384)]
+
+
+@pytest.mark.parametrize("t,k,i", MFMA_GLU, ids=[f"T{t}_K{k}_I{i}" for t, k, i in MFMA_GLU])
+def test_mfma_stream_mlp(t, k, i):
+    test_stream_mlp(t, k, i)
+
+
+@pytest.mark.parametrize("t", [10, 16])
+def test_mfma_stream_glu_quant_epilogue(t):
     test_stream_glu_quant_epilogue(t)
