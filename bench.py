@@ -153,6 +153,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extra", action="store_true", help="skip the 1024-token, decode and expert-grouped lines")
     ap.add_argument("--cpu-ubatches", type=int, default=8, help="ubatches the CPU oracle runs (about 10-15 s)")
+    ap.add_argument("--decode-only", action="store_true",
+                    help="print only the decode-shaped MLP line (T = 1 and T = 5) and exit")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported (the path is built and measured "
@@ -162,6 +164,9 @@ def main():
     import mlp_prefill_amd as m
     from synthetic import WORKLOADS, bf16_normal, layer_seeds
     torch.cuda.set_device(0)
+    if args.decode_only:
+        print(json.dumps({"decode": decode_line(m)}), flush=True)
+        return 0
     p = WORKLOADS["mlp_long_prefill_16x1024_4layers"].params
     T, UB, L = p["T"], p["ubatch"], p["layers"]
 
@@ -314,24 +319,9 @@ def static_line(m, layers, x_all, steps, ub=1024):
                     "layer's NVFP4 input] x 3 -> gate/up -> down (bf16)"}
 
 
-def extra_lines(m):
-    """1024-token MLP and decode-shaped T=1/T=5 MLP (separate weights, as their workloads define)."""
-    from synthetic import WORKLOADS, bf16_normal, outlier_channels
-    out = {}
-    p3 = WORKLOADS["mlp_prefill_1024x5120x17408"].params
-    log("extra: 1024-token MLP")
-    lay = Layer(m, (p3["wg_seed"], p3["wu_seed"], p3["wd_seed"]))
-    x = m.bf16_from_bits(bf16_normal(p3["x_seed"], (p3["T"], K_HID),
-                                     outliers=outlier_channels(p3["outlier_seed"], K_HID)))
-    run = MlpRunner(m, p3["T"])
-    y = torch.empty((p3["T"], K_HID), dtype=torch.float32, device="cuda")
-    t = time_events(lambda: run(x, lay, y), 20)
-    ms = float(np.median(t))
-    out["prefill_1024"] = {"workload": "mlp_prefill_1024x5120x17408", "ms": ms,
-                           "tflops": mlp_flops(p3["T"]) / (ms * 1e-3) / 1e12,
-                           "tokens_per_s": p3["T"] / (ms * 1e-3),
-                           "frac_f16_peak": mlp_flops(p3["T"]) / (ms * 1e-3) / 1e12 / PEAK_F16_TFLOPS}
-    del lay, run, x, y
+def decode_line(m):
+    """Decode-shaped MLP (5120/17408) at T = 1 and T = 5: weight-streaming GB/s cold and hot."""
+    from synthetic import WORKLOADS, bf16_normal
     p2 = WORKLOADS["mlp_decode_5120x17408"].params
     log("extra: decode-shaped MLP T=1, T=5")
     lay = Layer(m, (p2["wg_seed"], p2["wu_seed"], p2["wd_seed"]))
@@ -376,11 +366,34 @@ def extra_lines(m):
                          "static_gs_launches": static_launches}
     dec["launches_per_call"] = launches
     dec["t5_over_t1_cold"] = dec["T5"]["ms_cold"] / dec["T1"]["ms_cold"]
-    out["decode"] = dec
-    del lay
+    del lay, scrub_buf
+    return dec
+
+
+def extra_lines(m):
+    """1024-token MLP and decode-shaped T=1/T=5 MLP (separate weights, as their workloads define)."""
+    from synthetic import WORKLOADS, bf16_normal, outlier_channels
+    out = {}
+    p3 = WORKLOADS["mlp_prefill_1024x5120x17408"].params
+    log("extra: 1024-token MLP")
+    lay = Layer(m, (p3["wg_seed"], p3["wu_seed"], p3["wd_seed"]))
+    x = m.bf16_from_bits(bf16_normal(p3["x_seed"], (p3["T"], K_HID),
+                                     outliers=outlier_channels(p3["outlier_seed"], K_HID)))
+    run = MlpRunner(m, p3["T"])
+    y = torch.empty((p3["T"], K_HID), dtype=torch.float32, device="cuda")
+    t = time_events(lambda: run(x, lay, y), 20)
+    ms = float(np.median(t))
+    out["prefill_1024"] = {"workload": "mlp_prefill_1024x5120x17408", "ms": ms,
+                           "tflops": mlp_flops(p3["T"]) / (ms * 1e-3) / 1e12,
+                           "tokens_per_s": p3["T"] / (ms * 1e-3),
+                           "frac_f16_peak": mlp_flops(p3["T"]) / (ms * 1e-3) / 1e12 / PEAK_F16_TFLOPS}
+    del lay, run, x, y
+    out["decode"] = decode_line(m)
     # the tensor-parallel (tp = 2) shard on one GPU: intermediate 8704
     log("extra: tp=2 shard MLP (5120 -> 2 x 8704 -> 5120), T = 1024 and T = 1")
+    scrub_buf = torch.ones(1 << 27, dtype=torch.int64, device="cuda")
     ih = I_INT // 2
+
     lay = Layer(m, (6001, 6002, 6003), i=ih)
     shard = {"workload": "mlp_prefill_1024x5120x17408 tp=2 shard (intermediate 8704)"}
     for tt in (1024, 1):
