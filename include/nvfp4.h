@@ -145,11 +145,13 @@ int nvfp4_rmsnorm_quantize_act(const void *x, int x_dtype, int64_t rows, int64_t
 /*
  * nvfp4_gemm -- C[M][N] = (A~ . B~^T) * gscale_a * gscale_b.
  * One NVFP4 x NVFP4 contraction, K-contiguous operands as a linear layer
- * stores them ([llama] "Verified", MUL_MAT).  Three launches per call
- * whatever M is ([vllm] Fix directions 1): expansion of a~ to f16 (exact),
- * the contraction, and a fixed-order split-K reduction (over zero rows when
- * K is not split).  Accumulation in float32 on the matrix cores, every
- * product exact.
+ * stores them ([llama] "Verified", MUL_MAT).  One launch set per
+ * call whatever M is ([vllm] Fix directions 1): expansion of a~ to f16
+ * (exact), the contraction, and a fixed-order split-K reduction (over zero
+ * rows when K is not split); with M <= 8 and K a multiple of 1024 the
+ * contraction is a weight stream that expands a~ itself, so two launches.
+ * Accumulation in float32 (matrix cores, or dot products of exact f16
+ * products on the one/two-token stream); every product is exact.
  *   a  : [M][K] NVFP4, b : [N][K] NVFP4 (one gscale each)
  *   K  : multiple of 128
  *   c  : float32 or bf16 (c_dtype), row stride ldc >= N elements
@@ -173,7 +175,9 @@ int nvfp4_gemm(nvfp4_tensor a, nvfp4_tensor b, int64_t M, int64_t N, int64_t K,
  *            row-major [T][I] (the value that was quantised); then the f16
  *            copy of x~ and the per-tile maxima of |H|
  * Three launches per call (expansion, contraction with the SiLU*up epilogue
- * and the |H| tile maxima, requantisation), independent of T.
+ * and the |H| tile maxima, requantisation); two when T <= 8 and K is a
+ * multiple of 1024 (the weight stream expands x~ itself).  One launch set per
+ * batch: the count never grows with T within either range.
  */
 int nvfp4_mlp_gu_act(nvfp4_tensor x, nvfp4_tensor w_gate, nvfp4_tensor w_up,
                      int64_t T, int64_t K, int64_t I, nvfp4_tensor h_out,
@@ -187,7 +191,8 @@ int nvfp4_mlp_gu_act(nvfp4_tensor x, nvfp4_tensor w_gate, nvfp4_tensor w_up,
  *   h  : [T][I] NVFP4;  w_down : [K][I] NVFP4;  I multiple of 128
  *   y  : row stride ldy >= K elements
  *   ws : required, as for nvfp4_gemm (f16 copy of h~, split-K partials)
- * Three launches per call, independent of T.
+ * Three launches per call (two when T <= 8 and I is a multiple of 1024, as
+ * for nvfp4_gemm).
  */
 int nvfp4_mlp_down(nvfp4_tensor h, nvfp4_tensor w_down, int64_t T, int64_t I, int64_t K,
                    void *y, int y_dtype, int64_t ldy, void *ws, size_t *ws_bytes, void *stream);
@@ -205,7 +210,8 @@ int nvfp4_mlp_down(nvfp4_tensor h, nvfp4_tensor w_down, int64_t T, int64_t I, in
  *   x, w_gate, w_up, K, I : as nvfp4_mlp_gu_act
  *   h_out : [T][I] NVFP4; codes and scales written, gscale read
  *   ws    : required (the f16 copy of x~)
- * Two launches per call (expansion, contraction), independent of T.
+ * Two launches per call (expansion, contraction); one when T <= 8 and K is a
+ * multiple of 1024.
  */
 int nvfp4_mlp_gu_act_static(nvfp4_tensor x, nvfp4_tensor w_gate, nvfp4_tensor w_up,
                             int64_t T, int64_t K, int64_t I, nvfp4_tensor h_out,
@@ -222,7 +228,7 @@ int nvfp4_mlp_gu_act_static(nvfp4_tensor x, nvfp4_tensor w_gate, nvfp4_tensor w_
  *   K multiple of 16;  y_out : [T][K] NVFP4 (codes, scales written)
  *   ws : required, as nvfp4_mlp_down
  * Three launches per call (expansion, contraction, quantising split
- * reduction), independent of T.
+ * reduction); two when T <= 8 and I is a multiple of 1024.
  */
 int nvfp4_mlp_down_quant(nvfp4_tensor h, nvfp4_tensor w_down, int64_t T, int64_t I, int64_t K,
                          nvfp4_tensor y_out, void *ws, size_t *ws_bytes, void *stream);

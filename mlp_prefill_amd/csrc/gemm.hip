@@ -52,6 +52,8 @@ typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
 
 struct GemmArgs {
   const _Float16* a;      // expanded activations, f16 [rows][K] (slot order when grouped)
+  const uint8_t* a_codes; // the activation itself, NVFP4 [M][K] (the weight streams expand it in registers)
+  const uint8_t* a_scales;
   const float* a_gs;
   const uint8_t* b_codes;
   const uint8_t* b_scales;
@@ -982,22 +984,6 @@ __global__ void __launch_bounds__(256) gemv_kernel(GemmArgs p) {
   const int64_t e0 = split * BPL * 1024 + (int64_t)lane * BPL * 16;   // first K element of this lane
   const int64_t kb = K >> 1, ks = K >> 4;
 
-  // activation blocks of this lane, f16 pairs; tokens past M read as zero
-  f16x8 xa[T][BPL][2];
-#pragma unroll
-  for (int t = 0; t < T; ++t)
-#pragma unroll
-    for (int b = 0; b < BPL; ++b)
-#pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        if (t < M) {
-          xa[t][b][h] = *reinterpret_cast<const f16x8*>(p.a + t * K + e0 + 16 * b + 8 * h);
-        } else {
-#pragma unroll
-          for (int i = 0; i < 8; ++i) xa[t][b][h][i] = (_Float16)0.f;
-        }
-      }
-
   struct Slot {
     uint2 c[NR][BPL];
     uint32_t s[NR][BPL];
@@ -1032,6 +1018,27 @@ __global__ void __launch_bounds__(256) gemv_kernel(GemmArgs p) {
     load(d, ring[d]);
     __builtin_amdgcn_sched_barrier(0);
   }
+  // the weight loads of the first groups are in flight before the activation is read
+  // activation blocks of this lane, expanded here from the NVFP4 activation
+  // (code * scale in f16, exact); tokens past M are zero
+  f16x8 xa[T][BPL][2];
+#pragma unroll
+  for (int t = 0; t < T; ++t)
+#pragma unroll
+    for (int b = 0; b < BPL; ++b) {
+      if (t < M) {
+        const uint2 cw = *reinterpret_cast<const uint2*>(p.a_codes + t * (K >> 1) + e0 / 2 + 8 * b);
+        const uint32_t sc = p.a_scales[t * (K >> 4) + e0 / 16 + b];
+        xa[t][b][0] = expand8(cw.x, sc);
+        xa[t][b][1] = expand8(cw.y, sc);
+      } else {
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+#pragma unroll
+          for (int i = 0; i < 8; ++i) xa[t][b][h][i] = (_Float16)0.f;
+      }
+    }
+
 #pragma unroll
   for (int g = 0; g < G; ++g) {
     Slot& sl = ring[g % D];
@@ -1201,22 +1208,6 @@ __global__ void __launch_bounds__(kQdMaxWaves * 64) quad_kernel(GemmArgs p, int 
   const int64_t u = split * wk + w;                       // this wave's unit of K
   const int64_t kb = K >> 1, ks = K >> 4;
 
-  // activation: token 4*ts + j (the A row of this lane), elements 64 s .. 64 s + 63 of the unit
-  f16x8 xa[NTS][8];
-#pragma unroll
-  for (int ts = 0; ts < NTS; ++ts) {
-    const int64_t t = 4 * ts + j;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      if (t < M) {
-        xa[ts][e] = *reinterpret_cast<const f16x8*>(p.a + t * K + u * 1024 + s * 64 + 8 * e);
-      } else {
-#pragma unroll
-        for (int i = 0; i < 8; ++i) xa[ts][e][i] = (_Float16)0.f;
-      }
-    }
-  }
-
   // weight row of this lane in quad q
   auto row_ptrs = [&](int q, const uint8_t*& cp, const uint8_t*& sp) {
     int64_t row;
@@ -1256,6 +1247,26 @@ __global__ void __launch_bounds__(kQdMaxWaves * 64) quad_kernel(GemmArgs p, int 
   __builtin_amdgcn_sched_barrier(0);
   load(1, ring[1]);
   __builtin_amdgcn_sched_barrier(0);
+  // activation: token 4*ts + j (the A row of this lane), elements 64 s .. 64 s + 63 of the unit
+  // (expanded here from the NVFP4 activation: 32 code bytes and 4 scale bytes)
+  f16x8 xa[NTS][8];
+#pragma unroll
+  for (int ts = 0; ts < NTS; ++ts) {
+    const int64_t t = 4 * ts + j;
+    if (t < M) {
+      const u32x4* cp = reinterpret_cast<const u32x4*>(p.a_codes + t * kb + u * 512 + s * 32);
+      const u32x4 c0 = cp[0], c1 = cp[1];
+      const uint32_t sc = *reinterpret_cast<const uint32_t*>(p.a_scales + t * ks + u * 64 + s * 4);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) xa[ts][e] = expand8(e < 4 ? c0[e] : c1[e - 4], (sc >> (8 * (e >> 1))) & 0xFFu);
+    } else {
+#pragma unroll
+      for (int e = 0; e < 8; ++e)
+#pragma unroll
+        for (int i = 0; i < 8; ++i) xa[ts][e][i] = (_Float16)0.f;
+    }
+  }
+
 #pragma unroll
   for (int q = 0; q < NQ; ++q) {
     Slot& sl = ring[q & 1];
@@ -1659,9 +1670,12 @@ int store_launch(Operand a, const int32_t* rows, const int32_t* off, int E, int6
   const bool grouped = off != nullptr;
   _Float16* a16 = reinterpret_cast<_Float16*>(ws);
   float* part = reinterpret_cast<float*>(reinterpret_cast<char*>(ws) + align256((size_t)M * K * 2));
-  launch_expand(a.codes, a.scales, rows, M, K, a16, st);
   const Plan pl = plan_store(M, N, K, E, grouped);
+  // the weight streams expand the activation themselves
+  if (grouped || (pl.gv_bpl == 0 && pl.qd_wk == 0)) launch_expand(a.codes, a.scales, rows, M, K, a16, st);
   GemmArgs g = base_args(a16, a.gscale, w, M, N, K);
+  g.a_codes = a.codes;
+  g.a_scales = a.scales;
   g.c = c;
   g.ldc = ldc;
   g.c_bf16 = c_bf16;
@@ -1703,8 +1717,11 @@ int glu_launch(Operand a, const int32_t* a_rows, const int32_t* off, int E, int6
   float* h = reinterpret_cast<float*>(ws);
   _Float16* a16 = reinterpret_cast<_Float16*>(reinterpret_cast<char*>(ws) + align256((size_t)M * N * 4));
   float* partials = reinterpret_cast<float*>(reinterpret_cast<char*>(a16) + align256((size_t)M * K * 2));
-  launch_expand(a.codes, a.scales, a_rows, M, K, a16, st);
+  const bool stream = !grouped && (plan_gemv(M, K, true).bpl > 0 || plan_quad(M, K, true).wk > 0);
+  if (!stream) launch_expand(a.codes, a.scales, a_rows, M, K, a16, st);   // the streams expand x~ themselves
   GemmArgs g = base_args(a16, a.gscale, gt, M, N, K);
+  g.a_codes = a.codes;
+  g.a_scales = a.scales;
   g.u_codes = up.codes;
   g.u_scales = up.scales;
   g.u_gs = up.gscale;
@@ -1740,8 +1757,11 @@ int glu_static_launch(Operand a, const int32_t* a_rows, const int32_t* off, int 
                       Operand up, int64_t N, int64_t K, uint8_t* hq_codes, uint8_t* hq_scales, const float* hq_gs,
                       void* ws, hipStream_t st) {
   _Float16* a16 = reinterpret_cast<_Float16*>(ws);
-  launch_expand(a.codes, a.scales, a_rows, M, K, a16, st);
+  const bool stream = !off && (plan_gemv(M, K, true).bpl > 0 || plan_quad(M, K, true).wk > 0);
+  if (!stream) launch_expand(a.codes, a.scales, a_rows, M, K, a16, st);   // the streams expand x~ themselves
   GemmArgs g = base_args(a16, a.gscale, gt, M, N, K);
+  g.a_codes = a.codes;
+  g.a_scales = a.scales;
   g.u_codes = up.codes;
   g.u_scales = up.scales;
   g.u_gs = up.gscale;
@@ -1775,9 +1795,11 @@ int store_quant_launch(Operand a, int64_t M, Operand w, int64_t N, int64_t K, ui
                        const float* yq_gs, void* ws, hipStream_t st) {
   _Float16* a16 = reinterpret_cast<_Float16*>(ws);
   float* part = reinterpret_cast<float*>(reinterpret_cast<char*>(ws) + align256((size_t)M * K * 2));
-  launch_expand(a.codes, a.scales, nullptr, M, K, a16, st);
   const Plan pl = plan_store(M, N, K, 1, false);
+  if (pl.gv_bpl == 0 && pl.qd_wk == 0) launch_expand(a.codes, a.scales, nullptr, M, K, a16, st);
   GemmArgs g = base_args(a16, a.gscale, w, M, N, K);
+  g.a_codes = a.codes;
+  g.a_scales = a.scales;
   g.splits = pl.splits;
   g.chunks_per_split = pl.chunks_per_split;
   g.split_out = part;

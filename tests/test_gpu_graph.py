@@ -78,5 +78,6 @@ def test_decode_stack_graph_replays_match_eager(t):
         assert torch.equal(stack.hq.codes, ref_hq), f"replay {rep}: H~ differs from the eager run"
         other(x * 0.5)                         # eager work between replays
         torch.cuda.synchronize()
-    # replays enqueue no new host-side launches; the eager calls between them do
-    assert m.launch_count() - launches_before == 3 * 2 * 8
+    # replays enqueue no new host-side launches; the eager calls between them
+    # do (6 per MLP call on the decode weight streams: quantise 2, gate/up 2, down 2)
+    assert m.launch_count() - launches_before == 3 * 2 * 6

@@ -185,3 +185,37 @@ def test_mfma_stream_mlp(t, k, i):
 @pytest.mark.parametrize("t", [10, 16])
 def test_mfma_stream_glu_quant_epilogue(t):
     test_stream_glu_quant_epilogue(t)
+
+
+def test_stream_launch_counts():
+    """One launch set per batch: the weight streams (1-8 tokens, K a multiple of
+    1024) expand the activation themselves, so a dynamic-scale MLP call is 6
+    launches at every such T (quantise 2, gate/up 2, down 2) and the
+    static-scale pair 1 + 2; larger batches add the expansion launch of each
+    projection (8; static 2 + 3)."""
+    import mlp_prefill_amd as m
+    from tests.test_gpu_mlp import run_device_mlp
+    k, i = 1024, 2048
+    wdev, _ = _weights(k, i, (960, 961, 962))
+    dyn, sta = {}, {}
+    for t in (1, 2, 3, 5, 8, 9, 64):
+        announce(f"stream launch counts T={t}")
+        xbits = bf16_normal(963, (t, k))
+        b0 = m.launch_count()
+        run_device_mlp(xbits, wdev)
+        dyn[t] = m.launch_count() - b0
+        xq = dev_quantize(xbits)
+        hq = m.NVFP4.empty(t, i)
+        hq.gscale.fill_(0.01)
+        yq = m.NVFP4.empty(t, k)
+        yq.gscale.fill_(0.01)
+        b0 = m.launch_count()
+        m.nvfp4_mlp_gu_act_static(xq, wdev[0], wdev[1], hq)
+        b1 = m.launch_count()
+        m.nvfp4_mlp_down_quant(hq, wdev[2], yq)
+        sta[t] = (b1 - b0, m.launch_count() - b1)
+    torch.cuda.synchronize()
+    assert all(dyn[t] == 6 for t in (1, 2, 3, 5, 8)), dyn
+    assert dyn[9] == dyn[64] == 8, dyn
+    assert all(sta[t] == (1, 2) for t in (1, 2, 3, 5, 8)), sta
+    assert sta[9] == sta[64] == (2, 3), sta
