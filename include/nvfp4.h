@@ -119,7 +119,10 @@ enum nvfp4_epilogue {
  *   cols    : multiple of 16
  *   ws      : NVFP4_GS_COMPUTE needs a small workspace (block partial
  *             maxima, at most 4 KiB); NVFP4_GS_GIVEN needs none
- * Two kernel launches (COMPUTE) or one (GIVEN), independent of rows.
+ * Two kernel launches (COMPUTE) or one (GIVEN); a COMPUTE call on at most
+ * 4096 blocks of 16 (rows * cols <= 65536, e.g. decode activations) takes
+ * the amax, the global scale and the codes in one launch.  One launch set
+ * per call, never one per row.
  */
 int nvfp4_quantize_act(const void *x, int x_dtype, int64_t rows, int64_t cols, int64_t ld_x,
                        nvfp4_tensor out, int gs_mode, void *ws, size_t *ws_bytes, void *stream);

@@ -6,7 +6,8 @@
 // on the device and never read back to the host.  Packing happens on the
 // device (vllm.cpp issue, "Fix directions" 3).
 //
-// Two kernels: amax_partials writes one partial maximum per work-group;
+// Two kernels (one for tensors of at most 4096 blocks, see
+// quantize_small_kernel): amax_partials writes one partial maximum per work-group;
 // quantize reduces those partials again in every work-group (a few KiB from
 // L2, no atomics, no zero-initialised state), forms the global scale, and
 // quantises 16-element blocks in a grid-stride loop (one block per thread per
@@ -154,6 +155,42 @@ __global__ void __launch_bounds__(256) rms_amax_kernel(const T* __restrict__ x, 
   if (threadIdx.x == 0) partials[blockIdx.x] = m;
 }
 
+// Small tensors (decode activations: at most kSmallBlocks blocks of 16): one
+// work-group of 1024 threads takes the amax, forms the global scale and
+// quantises, in one launch instead of two; a kernel boundary costs more than
+// this work.  The max is exact in any order and the per-block routine is the
+// same, so the result equals the two-kernel path bit for bit.
+constexpr uint32_t kSmallBlocks = 4096;
+
+template <typename T>
+__global__ void __launch_bounds__(1024) quantize_small_kernel(const T* __restrict__ x, uint32_t nbc,
+                                                              uint32_t nblocks, int64_t ld, float* gs_ptr,
+                                                              uint8_t* __restrict__ codes,
+                                                              uint8_t* __restrict__ scales) {
+  __shared__ float red[16];
+  float m = 0.f;
+  for (uint32_t b = threadIdx.x; b < nblocks; b += 1024u) {
+    const uint32_t row = b / nbc, cb = b - row * nbc;
+    float v[16];
+    Load16<T>::run(x + (int64_t)row * ld + (int64_t)cb * kBlock, v);
+#pragma unroll
+    for (int i = 0; i < 16; ++i) m = fmaxf(m, fabsf(v[i]));
+  }
+  m = block_max(m, red);
+  const float gs = global_scale_from_amax(m);
+  if (threadIdx.x == 0) *gs_ptr = gs;
+  for (uint32_t b = threadIdx.x; b < nblocks; b += 1024u) {
+    const uint32_t row = b / nbc, cb = b - row * nbc;
+    float v[16];
+    Load16<T>::run(x + (int64_t)row * ld + (int64_t)cb * kBlock, v);
+    uint32_t w0, w1;
+    const uint32_t sc = quantize_block16(v, gs, w0, w1);
+    const int64_t boff = (int64_t)row * nbc + cb;
+    *reinterpret_cast<uint2*>(codes + boff * 8) = make_uint2(w0, w1);
+    scales[boff] = (uint8_t)sc;
+  }
+}
+
 // Work-groups of the quantiser: enough to fill the chip, few enough that the
 // per-work-group re-reduction of the partial maxima stays cheap.
 constexpr uint32_t kQuantGrid = 2048;
@@ -180,7 +217,11 @@ static int quantize_launch_t(const T* x, int64_t rows, int64_t cols, int64_t ld,
   uint32_t qgrid = (nblocks + 255u) / 256u;
   if (qgrid > kQuantGrid) qgrid = kQuantGrid;
   if (qgrid < 1) qgrid = 1;
-  if (gs_mode == 0 && ext_partials == nullptr) {
+  if (gs_mode == 0 && ext_partials == nullptr && nblocks <= kSmallBlocks) {
+    const int s0 = launch_begin(KC_QUANTIZE, st);
+    hipLaunchKernelGGL(quantize_small_kernel<T>, dim3(1), dim3(1024), 0, st, x, nbc, nblocks, ld, gs, codes, scales);
+    launch_end(s0, st);
+  } else if (gs_mode == 0 && ext_partials == nullptr) {
     const uint32_t g = amax_grid(nblocks);
     const int s0 = launch_begin(KC_QUANTIZE, st);
     hipLaunchKernelGGL(amax_partials_kernel<T>, dim3(g), dim3(256), 0, st, x, nbc, nblocks, ld, partials);
