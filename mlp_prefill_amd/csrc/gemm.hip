@@ -1004,8 +1004,10 @@ __global__ void __launch_bounds__(256) gemv_kernel(GemmArgs p) {
       const __amdgpu_buffer_rsrc_t rs = make_rsrc((up ? p.u_scales : p.b_scales) + row * ks, ks);
 #pragma unroll
       for (int b = 0; b < BPL; ++b) {
-        sl.c[r][b] = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(rc, vo_c + 8 * b, 0, 0));
-        sl.s[r][b] = __builtin_amdgcn_raw_buffer_load_b8(rs, vo_s + b, 0, 0);
+        // a block past K reads past the row's resource: zero, and no memory traffic
+        const bool in = e0 + 16 * b < K;
+        sl.c[r][b] = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(rc, in ? vo_c + 8 * b : 0x7FFFFFF0, 0, 0));
+        sl.s[r][b] = __builtin_amdgcn_raw_buffer_load_b8(rs, in ? vo_s + b : 0x7FFFFFF0, 0, 0);
       }
     }
   };
@@ -1026,7 +1028,7 @@ __global__ void __launch_bounds__(256) gemv_kernel(GemmArgs p) {
   for (int t = 0; t < T; ++t)
 #pragma unroll
     for (int b = 0; b < BPL; ++b) {
-      if (t < M) {
+      if (t < M && e0 + 16 * b < K) {                    // blocks past K (last unit partial): zero
         const uint2 cw = *reinterpret_cast<const uint2*>(p.a_codes + t * (K >> 1) + e0 / 2 + 8 * b);
         const uint32_t sc = p.a_scales[t * (K >> 4) + e0 / 16 + b];
         xa[t][b][0] = expand8(cw.x, sc);
@@ -1474,9 +1476,10 @@ struct Plan {
 
 static uint32_t cdiv(int64_t a, int64_t b) { return (uint32_t)((a + b - 1) / b); }
 
-// The weight stream takes M <= NVFP4_GV_MAXT tokens and K a multiple of 1024;
-// a split covers BPL units (the largest divisor of K/1024 up to 5).  The
-// gate/up pair needs whole rows in one split (GLU epilogue), so there K <= 5120.
+// The weight stream takes M <= NVFP4_GV_MAXT tokens and K >= 1024 (a multiple
+// of 16; the last 1024-wide unit may be partial); a split covers BPL units (the
+// largest divisor of the unit count up to 5).  The gate/up pair needs whole
+// rows in one split (GLU epilogue), so there K <= 5120.
 struct GvPlan {
   int bpl;          // 0: not applicable
   uint32_t splits;
@@ -1484,8 +1487,8 @@ struct GvPlan {
 
 static GvPlan plan_gemv(int64_t M, int64_t K, bool dual) {
   GvPlan pl{0, 0};
-  if (M < 1 || M > NVFP4_GV_MAXT || K % 1024 != 0) return pl;
-  const int64_t U = K / 1024;
+  if (M < 1 || M > NVFP4_GV_MAXT || K % 16 != 0 || K < 1024) return pl;
+  const int64_t U = (K + 1023) / 1024;            // the last unit may be partial
   int bpl = 1;
   for (int b = 5; b >= 2; --b)
     if (U % b == 0) {
