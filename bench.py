@@ -460,6 +460,9 @@ def decode_stack_line(m, layers):
                 run(cur, lay, ys[li % 2])
                 cur = ys[li % 2]
         eager = float(np.median(time_events(stack, 20)))
+        b0 = m.launch_count()
+        stack()
+        launches = m.launch_count() - b0
         s = torch.cuda.Stream()
         s.wait_stream(torch.cuda.current_stream())
         g = torch.cuda.CUDAGraph()
@@ -472,7 +475,7 @@ def decode_stack_line(m, layers):
         out[f"T{t}"] = {"ms_eager": eager, "ms_graph": graph, "ms_per_layer_graph": graph / len(layers),
                         "hbm_gbs_graph": wbytes / (graph * 1e-3) / 1e9,
                         "frac_hbm_peak_graph": wbytes / (graph * 1e-3) / 1e9 / PEAK_HBM_GBS,
-                        "launches_per_pass": 8 * len(layers)}
+                        "launches_per_pass": launches}
         del g
     return out
 
