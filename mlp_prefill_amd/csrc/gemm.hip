@@ -1406,6 +1406,54 @@ __global__ void __launch_bounds__(256) splitk_reduce_kernel(const float* __restr
   }
 }
 
+// The same reduction with four consecutive outputs of one row per thread
+// (N % 4 == 0): 16-byte loads of each split's partials, added in split order,
+// so the sums are those of splitk_reduce_kernel bit for bit.
+__global__ void __launch_bounds__(256) splitk_reduce4_kernel(const float* __restrict__ part, uint32_t splits,
+                                                             int64_t M, int64_t N, const float* a_gs,
+                                                             const float* b_gs, const int32_t* off, int E,
+                                                             void* out, int out_bf16, int64_t ldo) {
+  const int64_t total = M * N, total4 = total / 4;
+  const float ga = a_gs[0];
+  for (int64_t i4 = (int64_t)blockIdx.x * 256 + threadIdx.x; i4 < total4; i4 += (int64_t)gridDim.x * 256) {
+    const int64_t idx = 4 * i4, m = idx / N, n = idx - m * N;
+    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+    uint32_t s = 0;
+    for (; s + 4u <= splits; s += 4u) {
+      float4 v[4];
+#pragma unroll
+      for (int k = 0; k < 4; ++k) v[k] = *reinterpret_cast<const float4*>(part + (int64_t)(s + k) * total + idx);
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        acc.x += v[k].x;
+        acc.y += v[k].y;
+        acc.z += v[k].z;
+        acc.w += v[k].w;
+      }
+    }
+    for (; s < splits; ++s) {
+      const float4 v = *reinterpret_cast<const float4*>(part + (int64_t)s * total + idx);
+      acc.x += v.x;
+      acc.y += v.y;
+      acc.z += v.z;
+      acc.w += v.w;
+    }
+    int e = 0;
+    if (off) {
+      while (e < E - 1 && off[e + 1] <= m) ++e;
+    }
+    const float sc = ga * b_gs[e];
+    const float4 o = make_float4(acc.x * sc, acc.y * sc, acc.z * sc, acc.w * sc);
+    if (out_bf16) {
+      const uint32_t lo = f32_to_bf16_bits(o.x) | (f32_to_bf16_bits(o.y) << 16);
+      const uint32_t hi = f32_to_bf16_bits(o.z) | (f32_to_bf16_bits(o.w) << 16);
+      *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(out) + m * ldo + n) = make_uint2(lo, hi);
+    } else {
+      *reinterpret_cast<float4*>(reinterpret_cast<float*>(out) + m * ldo + n) = o;
+    }
+  }
+}
+
 // The same reduction, quantised: each thread takes whole 16-column blocks,
 // adds the splits in split order, scales by gs_a * gs_b (the float32 values
 // splitk_reduce_kernel would store) and quantises them with the given global
@@ -1637,12 +1685,17 @@ static void launch_expand(const uint8_t* codes, const uint8_t* scales, const int
 static void launch_reduce(const float* part, uint32_t splits, int64_t M, int64_t N, const float* a_gs,
                           const float* b_gs, const int32_t* off, int E, void* out, int bf16, int64_t ldo,
                           hipStream_t st) {
-  int64_t blocks = (M * N + 255) / 256;
+  const bool vec = N % 4 == 0;   // four outputs per thread (partials, rows and output rows 16-B aligned)
+  int64_t blocks = (M * N / (vec ? 4 : 1) + 255) / 256;
   if (blocks > 8192) blocks = 8192;
   if (blocks < 1) blocks = 1;
   const int slot = launch_begin(KC_REDUCE, st);
-  hipLaunchKernelGGL(splitk_reduce_kernel, dim3((uint32_t)blocks), dim3(256), 0, st, part, splits, M, N, a_gs,
-                     b_gs, off, E, out, bf16, ldo);
+  if (vec)
+    hipLaunchKernelGGL(splitk_reduce4_kernel, dim3((uint32_t)blocks), dim3(256), 0, st, part, splits, M, N, a_gs,
+                       b_gs, off, E, out, bf16, ldo);
+  else
+    hipLaunchKernelGGL(splitk_reduce_kernel, dim3((uint32_t)blocks), dim3(256), 0, st, part, splits, M, N, a_gs,
+                       b_gs, off, E, out, bf16, ldo);
   launch_end(slot, st);
 }
 
