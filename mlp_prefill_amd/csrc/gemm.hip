@@ -1004,10 +1004,10 @@ __global__ void __launch_bounds__(256) gemv_kernel(GemmArgs p) {
       const __amdgpu_buffer_rsrc_t rs = make_rsrc((up ? p.u_scales : p.b_scales) + row * ks, ks);
 #pragma unroll
       for (int b = 0; b < BPL; ++b) {
-        // a block past K reads past the row's resource: zero, and no memory traffic
-        const bool in = e0 + 16 * b < K;
-        sl.c[r][b] = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(rc, in ? vo_c + 8 * b : 0x7FFFFFF0, 0, 0));
-        sl.s[r][b] = __builtin_amdgcn_raw_buffer_load_b8(rs, in ? vo_s + b : 0x7FFFFFF0, 0, 0);
+        // the resources span one row: a block past K (last unit partial) reads
+        // past them and gets zero, with no memory traffic
+        sl.c[r][b] = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(rc, vo_c + 8 * b, 0, 0));
+        sl.s[r][b] = __builtin_amdgcn_raw_buffer_load_b8(rs, vo_s + b, 0, 0);
       }
     }
   };
@@ -1022,22 +1022,29 @@ __global__ void __launch_bounds__(256) gemv_kernel(GemmArgs p) {
   }
   // the weight loads of the first groups are in flight before the activation is read
   // activation blocks of this lane, expanded here from the NVFP4 activation
-  // (code * scale in f16, exact); tokens past M are zero
-  f16x8 xa[T][BPL][2];
+  // into the f16 pairs the dot products take (code * scale, exact; the
+  // converter is given 2^8 and the pair of E4M3 scale bits (s << 7), which is
+  // dec(s) * 2^-8, so the product is code * dec(s)); tokens past M are zero
+  f16x2 xp[T][BPL][8];
 #pragma unroll
   for (int t = 0; t < T; ++t)
 #pragma unroll
     for (int b = 0; b < BPL; ++b) {
       if (t < M && e0 + 16 * b < K) {                    // blocks past K (last unit partial): zero
         const uint2 cw = *reinterpret_cast<const uint2*>(p.a_codes + t * (K >> 1) + e0 / 2 + 8 * b);
-        const uint32_t sc = p.a_scales[t * (K >> 4) + e0 / 16 + b];
-        xa[t][b][0] = expand8(cw.x, sc);
-        xa[t][b][1] = expand8(cw.y, sc);
+        const uint32_t sh = (uint32_t)p.a_scales[t * (K >> 4) + e0 / 16 + b] << 7;
+        const f16x2 sc = bitcast<f16x2>(sh | (sh << 16));
+        xp[t][b][0] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(cw.x, 256.0f, 0) * sc;
+        xp[t][b][1] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(cw.x, 256.0f, 1) * sc;
+        xp[t][b][2] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(cw.x, 256.0f, 2) * sc;
+        xp[t][b][3] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(cw.x, 256.0f, 3) * sc;
+        xp[t][b][4] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(cw.y, 256.0f, 0) * sc;
+        xp[t][b][5] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(cw.y, 256.0f, 1) * sc;
+        xp[t][b][6] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(cw.y, 256.0f, 2) * sc;
+        xp[t][b][7] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(cw.y, 256.0f, 3) * sc;
       } else {
 #pragma unroll
-        for (int h = 0; h < 2; ++h)
-#pragma unroll
-          for (int i = 0; i < 8; ++i) xa[t][b][h][i] = (_Float16)0.f;
+        for (int i = 0; i < 8; ++i) xp[t][b][i] = (f16x2){(_Float16)0.f, (_Float16)0.f};
       }
     }
 
@@ -1065,11 +1072,7 @@ __global__ void __launch_bounds__(256) gemv_kernel(GemmArgs p) {
         for (int t = 0; t < T; ++t) {
           float d = 0.f;
 #pragma unroll
-          for (int i = 0; i < 8; ++i) {
-            const f16x8& xv = xa[t][b][i >> 2];
-            const f16x2 xp = {xv[2 * (i & 3)], xv[2 * (i & 3) + 1]};
-            d = __builtin_amdgcn_fdot2(cp[i], xp, d, false);
-          }
+          for (int i = 0; i < 8; ++i) d = __builtin_amdgcn_fdot2(cp[i], xp[t][b][i], d, false);
           acc[r][t] = fmaf(d, sc, acc[r][t]);
         }
       }
