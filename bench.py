@@ -155,6 +155,8 @@ def main():
     ap.add_argument("--cpu-ubatches", type=int, default=8, help="ubatches the CPU oracle runs (about 10-15 s)")
     ap.add_argument("--decode-only", action="store_true",
                     help="print only the decode-shaped MLP line (T = 1 and T = 5) and exit")
+    ap.add_argument("--moe-only", action="store_true",
+                    help="print only the expert-grouped MLP line (4096 tokens, top-8 of 64 experts) and exit")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported (the path is built and measured "
@@ -166,6 +168,9 @@ def main():
     torch.cuda.set_device(0)
     if args.decode_only:
         print(json.dumps({"decode": decode_line(m)}), flush=True)
+        return 0
+    if args.moe_only:
+        print(json.dumps({"moe": moe_line(m)}), flush=True)
         return 0
     p = WORKLOADS["mlp_long_prefill_16x1024_4layers"].params
     T, UB, L = p["T"], p["ubatch"], p["layers"]
