@@ -175,8 +175,9 @@ int nvfp4_gemm(nvfp4_tensor a, nvfp4_tensor b, int64_t M, int64_t N, int64_t K,
  *   h_out  : [T][I] NVFP4 (codes, scales, gscale written)
  *   K, I   : multiples of 128
  *   ws     : required; on return its first T*I*4 bytes hold H in float32,
- *            row-major [T][I] (the value that was quantised); then the f16
- *            copy of x~ and the per-tile maxima of |H|
+ *            row-major [T][I] (the value that was quantised); then room for
+ *            the f16 copy of x~ (written on the matrix-core paths, unused by
+ *            the weight streams) and the partial maxima of |H|
  * Three launches per call (expansion, contraction with the SiLU*up epilogue
  * and the |H| tile maxima, requantisation); two when T <= 8 and K is a
  * multiple of 1024 (the weight stream expands x~ itself).  One launch set per
