@@ -428,6 +428,14 @@ __device__ __forceinline__ void xchunk(Ctx<WN, TM, TN, DUAL>& x, const Lds& lc, 
 #ifndef NVFP4_STORE_WN
 #define NVFP4_STORE_WN 4
 #endif
+// 32-column sub-tiles per wave of the store-epilogue kernels: two give every
+// activation fragment read from LDS two MFMAs, as the gate/up pair does.
+#ifndef NVFP4_STORE_TN
+#define NVFP4_STORE_TN 2
+#endif
+#ifndef NVFP4_GROUPED_STORE_TN
+#define NVFP4_GROUPED_STORE_TN 1
+#endif
 // LDS buffers of the chunk ring (2 to 4).
 #ifndef NVFP4_GLU_STAGES
 #define NVFP4_GLU_STAGES 2
@@ -1613,7 +1621,7 @@ static Plan plan_store(int64_t M, int64_t N, int64_t K, int E, bool grouped) {
     while (s < 16 && pl.n_tiles * s < 512 && chunks / (s + 1) >= 4u * kSkWaves) ++s;
   } else {
     pl.m_tiles = grouped ? cdiv(M, 32 * NVFP4_STORE_TM) + (uint32_t)E : cdiv(M, 32 * NVFP4_STORE_TM);
-    pl.n_tiles = cdiv(N, 32 * NVFP4_STORE_WN);
+    pl.n_tiles = cdiv(N, 32 * NVFP4_STORE_WN * (grouped ? NVFP4_GROUPED_STORE_TN : NVFP4_STORE_TN));
     // Split K until there are enough work-groups, keeping >= 8 chunks per split.
     const uint32_t tiles = pl.m_tiles * pl.n_tiles;
     while (s < 8 && tiles * s < NVFP4_SPLIT_TARGET && chunks / (s + 1) >= 8) ++s;
@@ -1745,11 +1753,11 @@ int store_launch(Operand a, const int32_t* rows, const int32_t* off, int E, int6
   g.E = E;
   g.m_tiles = pl.m_tiles;
   g.n_tiles = pl.n_tiles;
-  if (grouped) launch_cfg<NVFP4_STORE_WN, NVFP4_STORE_TM, 1, false, true, EPI_STORE>(g, st);
+  if (grouped) launch_cfg<NVFP4_STORE_WN, NVFP4_STORE_TM, NVFP4_GROUPED_STORE_TN, false, true, EPI_STORE>(g, st);
   else if (pl.gv_bpl > 0) launch_gemv<false, EPI_STORE>(g, pl.gv_bpl, st);
   else if (pl.qd_wk > 0) launch_quad<false, EPI_STORE>(g, pl.qd_wk, st);
   else if (pl.small) launch_skinny<false, EPI_STORE>(g, st);
-  else launch_cfg<NVFP4_STORE_WN, NVFP4_STORE_TM, 1, false, false, EPI_STORE>(g, st);
+  else launch_cfg<NVFP4_STORE_WN, NVFP4_STORE_TM, NVFP4_STORE_TN, false, false, EPI_STORE>(g, st);
   // The reduction always runs (over zero rows when K was not split), so the
   // number of launches never depends on the shape.
   launch_reduce(part, pl.splits, pl.splits > 1 ? M : 0, N, a.gscale, w.gscale, off, E, c, c_bf16, ldc, st);
@@ -1868,7 +1876,7 @@ int store_quant_launch(Operand a, int64_t M, Operand w, int64_t N, int64_t K, ui
   if (pl.gv_bpl > 0) launch_gemv<false, EPI_STORE>(g, pl.gv_bpl, st);
   else if (pl.qd_wk > 0) launch_quad<false, EPI_STORE>(g, pl.qd_wk, st);
   else if (pl.small) launch_skinny<false, EPI_STORE>(g, st);
-  else launch_cfg<NVFP4_STORE_WN, NVFP4_STORE_TM, 1, false, false, EPI_STORE>(g, st);
+  else launch_cfg<NVFP4_STORE_WN, NVFP4_STORE_TM, NVFP4_STORE_TN, false, false, EPI_STORE>(g, st);
   int64_t blocks = (M * (N / 16) + 255) / 256;
   if (blocks > 8192) blocks = 8192;
   if (blocks < 1) blocks = 1;
