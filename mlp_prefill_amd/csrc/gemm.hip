@@ -611,11 +611,15 @@ __global__ void __launch_bounds__(WN * 64, MINWG) gemm_kernel(GemmArgs p) {
     read_a<0, 0>(x, l0);
     read_a<1, 1>(x, l0);
     expand_b<TN, DUAL, 0>(f0, e0);
-    for (int64_t c = 0; c < nch; c += 2) {
+    // Chunk pairs in one loop body (no exit between them, so the
+    // accumulators keep their registers across the back edge), then the odd
+    // last chunk.
+    int64_t c = 0;
+    for (; c + 1 < nch; c += 2) {
       xchunk(x, l0, l1, f0, f1, e0, e1, c + 2 < nch, c + 2, la(0), lb(0), ls(0));
-      if (c + 1 >= nch) break;
       xchunk(x, l1, l0, f1, f0, e0, e1, c + 3 < nch, c + 3, la(1), lb(1), ls(1));
     }
+    if (c < nch) xchunk(x, l0, l1, f0, f1, e0, e1, false, c + 2, la(0), lb(0), ls(0));
   } else {
     // NS-buffer ring: the copies of chunks c+1 .. c+NS-2 stay in flight while
     // chunk c is consumed; the buffer of chunk c-1 is refilled with chunk
