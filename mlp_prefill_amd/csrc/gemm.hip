@@ -1527,7 +1527,8 @@ __global__ void __launch_bounds__(256) splitk_reduce_quant_kernel(const float* _
 
 // ---- launch configurations ----------------------------------------------------------
 // Large batches: four waves side by side in N, each 32 * TM rows x 32 columns
-// (x2 with the gate/up pair).  Small batches (M <= 32): the weight-stream
+// of both the gate and the up matrix, or (store epilogue) 32 * TM rows x
+// 32 * NVFP4_STORE_TN columns of one matrix.  Small batches (M <= 32): the weight-stream
 // kernel, 32 weight rows per work-group, K split over its waves (and, for the
 // store epilogue, over work-groups too).
 struct Plan {
