@@ -96,7 +96,12 @@ def test_gemm_and_down_validation():
     s = _size()
     assert g(nvfp4_tensor(0, 0, 0), nvfp4_tensor(0, 0, 0), 1024, 5120, 17408, None, m.F32, 5120, None,
              ctypes.byref(s), None) == m.OK
-    assert s.value >= 1024 * 17408 * 2                                        # f16 activation copy
+    # f16 activation copy + float32 partials of the 3 K splits: 1024 tokens in
+    # 64 x 256 tiles make 16 x 20 = 320 work-groups, split 3 ways to 960
+    assert s.value == 1024 * 17408 * 2 + 3 * 1024 * 5120 * 4
+    assert g(nvfp4_tensor(0, 0, 0), nvfp4_tensor(0, 0, 0), 4096, 4096, 4096, None, m.F32, 4096, None,
+             ctypes.byref(s), None) == m.OK
+    assert s.value == 4096 * 4096 * 2 + 4096 * 4096 * 4   # 64 x 16 = 1024 tiles: one split
     d = m.lib.nvfp4_mlp_down
     assert d(_t(), _t(), 4, 100, 64, FAKE, m.F32, 64, *ws) == m.ERR_SHAPE      # I % 128
     assert d(_t(), _t(), 4, 128, 64, FAKE, m.BF16, 60, *ws) == m.ERR_SHAPE     # ldy < K
