@@ -451,6 +451,13 @@ __device__ __forceinline__ void xchunk(Ctx<WN, TM, TN, DUAL>& x, const Lds& lc, 
 #endif
 
 constexpr uint32_t kGroupGm = 8;   // m tiles per super-tile of the expert-grouped tile order
+// m tiles per super-tile of the dense, unsplit tile order (0: all m tiles of
+// one n tile, then the next n tile).  With 4, the 64 work-groups resident on
+// one XCD cover 4 m tiles x 16 n tiles instead of 16 x 4, which reads fewer
+// activation tiles past its L2.
+#ifndef NVFP4_DENSE_GROUP_M
+#define NVFP4_DENSE_GROUP_M 4
+#endif
 
 template <int WN, int TM, int TN, bool DUAL, bool GROUPED, int EPI, int NS, int MINWG>
 __global__ void __launch_bounds__(WN * 64, MINWG) gemm_kernel(GemmArgs p) {
@@ -466,17 +473,18 @@ __global__ void __launch_bounds__(WN * 64, MINWG) gemm_kernel(GemmArgs p) {
   const int r32 = lane & 31, hh = lane >> 5;
 
   // ---- tile: consecutive ids share (split, n_tile) and walk the m tiles ------
-  // (expert-grouped, unsplit: super-tiles of kGroupGm m tiles x all n tiles,
-  // m fastest inside, so that the work-groups on one XCD share both the
-  // activation rows and the weight columns -- the gathered activations of all
+  // (unsplit: super-tiles of kGm m tiles x all n tiles, m fastest inside, so
+  // that the work-groups on one XCD share both the activation rows and the
+  // weight columns -- for expert groups the gathered activations of all
   // experts do not fit the MALL)
   const uint32_t t = xcd_remap(blockIdx.x, gridDim.x);
   uint32_t mt, split, n_tile;
-  if (GROUPED && p.splits == 1) {
-    const uint32_t span = kGroupGm * p.n_tiles;
+  constexpr uint32_t kGm = GROUPED ? kGroupGm : (uint32_t)NVFP4_DENSE_GROUP_M;
+  if (kGm > 0 && p.splits == 1) {
+    const uint32_t span = kGm * p.n_tiles;
     const uint32_t sup = t / span, r = t - sup * span;
-    const uint32_t gm = (sup + 1) * kGroupGm <= p.m_tiles ? kGroupGm : p.m_tiles - sup * kGroupGm;
-    mt = sup * kGroupGm + r % gm;
+    const uint32_t gm = (sup + 1) * kGm <= p.m_tiles ? kGm : p.m_tiles - sup * kGm;
+    mt = sup * kGm + r % gm;
     n_tile = r / gm;
     split = 0;
   } else {
