@@ -472,26 +472,26 @@ __global__ void __launch_bounds__(WN * 64, MINWG) gemm_kernel(GemmArgs p) {
   const int wn = threadIdx.x >> 6;
   const int r32 = lane & 31, hh = lane >> 5;
 
-  // ---- tile: consecutive ids share (split, n_tile) and walk the m tiles ------
-  // (unsplit: super-tiles of kGm m tiles x all n tiles, m fastest inside, so
-  // that the work-groups on one XCD share both the activation rows and the
-  // weight columns -- for expert groups the gathered activations of all
-  // experts do not fit the MALL)
+  // ---- tile: K splits slowest, then super-tiles of kGm m tiles x all n tiles
+  // (m fastest inside), so that the work-groups resident on one XCD work on
+  // one K range and share both activation rows and weight columns in its L2
+  // (for expert groups the gathered activations of all experts do not fit
+  // the MALL); kGm = 0: m fastest, then n
   const uint32_t t = xcd_remap(blockIdx.x, gridDim.x);
   uint32_t mt, split, n_tile;
   constexpr uint32_t kGm = GROUPED ? kGroupGm : (uint32_t)NVFP4_DENSE_GROUP_M;
-  if (kGm > 0 && p.splits == 1) {
+  const uint32_t per_split = p.m_tiles * p.n_tiles;
+  split = t / per_split;
+  const uint32_t u = t - split * per_split;
+  if (kGm > 0) {
     const uint32_t span = kGm * p.n_tiles;
-    const uint32_t sup = t / span, r = t - sup * span;
+    const uint32_t sup = u / span, r = u - sup * span;
     const uint32_t gm = (sup + 1) * kGm <= p.m_tiles ? kGm : p.m_tiles - sup * kGm;
     mt = sup * kGm + r % gm;
     n_tile = r / gm;
-    split = 0;
   } else {
-    mt = t % p.m_tiles;
-    const uint32_t rest = t / p.m_tiles;
-    split = rest % p.splits;
-    n_tile = rest / p.splits;
+    mt = u % p.m_tiles;
+    n_tile = u / p.m_tiles;
   }
   int64_t m0, m_end;
   int e = 0;
