@@ -12,9 +12,10 @@ Steps, in the order the pages give them:
    batch of T tokens at once (vllm.cpp issue, "Fix directions" 1).
 3. H = SiLU(G) * U with SiLU(g) = g / (1 + e^-g), in float64.  Which projection
    is the gate is not stated on the pages; the gate is the operand under SiLU.
-4. H is quantised straight into the down projection's NVFP4 input format
-   ("GLU output quantized directly into the MMQ activation format"), with a
-   per-call global scale over the whole [T, I] tensor.  The float64 H is first
+4. H is quantised straight into the down projection's NVFP4 input format,
+   with no wider intermediate tensor in between (the llama.cpp discussion's
+   patch fuses the GLU with the quantisation of the next matrix product's
+   activation), with a per-call global scale over the whole [T, I] tensor.  The float64 H is first
    rounded to float32 (RN32), the precision a device epilogue holds it in; it
    is not rounded to bf16.
 5. Y = H~ . Wd~^T (exact), reported in float64; a device emits it as float32
