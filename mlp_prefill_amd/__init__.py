@@ -153,13 +153,38 @@ def _dtype_code(t):
     raise TypeError(f"unsupported dtype {t.dtype}")
 
 
-def _workspace(query, ws, device):
-    """Query the required size, allocate (or check) a byte workspace."""
+def _foreign_stream(stream):
+    """torch's handle of `stream` when it is not torch's current stream, else None."""
+    if stream is None:
+        return None
+    ptr = stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+    if ptr == torch.cuda.current_stream().cuda_stream:
+        return None
+    if isinstance(stream, torch.cuda.Stream):
+        return stream
+    return torch.cuda.ExternalStream(ptr)
+
+
+def _scratch(need, ws, device, stream):
+    """The workspace of one call: the caller's `ws`, or a new one.  A new one is
+    allocated on torch's current stream and dropped when the call returns; when
+    the call runs on another stream, that stream is recorded on it, so the
+    caching allocator does not hand the memory to a later allocation before the
+    call's kernels on that stream are done with it."""
+    if ws is not None:
+        return ws
+    ws = torch.empty(max(need, 256), dtype=torch.uint8, device=device)
+    other = _foreign_stream(stream)
+    if other is not None:
+        ws.record_stream(other)
+    return ws
+
+
+def _workspace(query, ws, device, stream=None):
+    """Query the required size, allocate (or take) a byte workspace."""
     size = ctypes.c_size_t(0)
     _check(query(_vp(0), ctypes.byref(size)), "workspace query")
-    need = size.value
-    if ws is None:
-        ws = torch.empty(max(need, 256), dtype=torch.uint8, device=device)
+    ws = _scratch(size.value, ws, device, stream)
     return ws, ctypes.c_size_t(ws.numel())
 
 
@@ -174,7 +199,7 @@ def nvfp4_quantize_act(x, out, gs_mode=GS_COMPUTE, ws=None, stream=None):
 
     def q(wsp, szp):
         return _lib.nvfp4_quantize_act(_vp(0), dt, rows, cols, ld, _null_tensor(), gs_mode, wsp, szp, _vp(0))
-    ws, sz = _workspace(q, ws, x.device)
+    ws, sz = _workspace(q, ws, x.device, stream)
     _check(_lib.nvfp4_quantize_act(_ptr(x), dt, rows, cols, ld, out.c(), gs_mode, _ptr(ws), ctypes.byref(sz),
                                    _stream(stream)), "nvfp4_quantize_act")
     return out
@@ -192,8 +217,7 @@ def nvfp4_gemm(a, b, c, ws=None, stream=None):
     """c [M, N] (float32 or bf16) = A~ . B~^T * gs_a * gs_b."""
     m, n = c.shape
     need = gemm_ws_bytes(m, n, a.cols)
-    if ws is None:
-        ws = torch.empty(max(need, 256), dtype=torch.uint8, device=c.device)
+    ws = _scratch(need, ws, c.device, stream)
     sz = ctypes.c_size_t(ws.numel())
     _check(_lib.nvfp4_gemm(a.c(), b.c(), m, n, a.cols, _ptr(c), _dtype_code(c), c.stride(0), _ptr(ws),
                            ctypes.byref(sz), _stream(stream)), "nvfp4_gemm")
@@ -219,8 +243,7 @@ def nvfp4_mlp_gu_act(x, w_gate, w_up, h_out, ws=None, stream=None):
     """h_out (NVFP4 [T, I]) = requant(SiLU(x~ . Wg~^T) * (x~ . Wu~^T)); ws keeps float32 H."""
     t, k, i = x.rows, x.cols, w_gate.rows
     need = mlp_gu_act_ws_bytes(t, k, i)
-    if ws is None:
-        ws = torch.empty(max(need, 256), dtype=torch.uint8, device=x.codes.device)
+    ws = _scratch(need, ws, x.codes.device, stream)
     sz = ctypes.c_size_t(ws.numel())
     _check(_lib.nvfp4_mlp_gu_act(x.c(), w_gate.c(), w_up.c(), t, k, i, h_out.c(), _ptr(ws), ctypes.byref(sz),
                                  _stream(stream)), "nvfp4_mlp_gu_act")
@@ -240,8 +263,7 @@ def nvfp4_mlp_gu_act_static(x, w_gate, w_up, h_out, ws=None, stream=None):
     scale already stored in h_out.gscale (read on the device)."""
     t, k, i = x.rows, x.cols, w_gate.rows
     need = mlp_gu_act_static_ws_bytes(t, k, i)
-    if ws is None:
-        ws = torch.empty(max(need, 256), dtype=torch.uint8, device=x.codes.device)
+    ws = _scratch(need, ws, x.codes.device, stream)
     sz = ctypes.c_size_t(ws.numel())
     _check(_lib.nvfp4_mlp_gu_act_static(x.c(), w_gate.c(), w_up.c(), t, k, i, h_out.c(), _ptr(ws),
                                         ctypes.byref(sz), _stream(stream)), "nvfp4_mlp_gu_act_static")
@@ -261,8 +283,7 @@ def nvfp4_mlp_down_quant(h, w_down, y_out, ws=None, stream=None):
     already stored in y_out.gscale (read on the device)."""
     t, i, kk = h.rows, h.cols, w_down.rows
     need = mlp_down_quant_ws_bytes(t, i, kk)
-    if ws is None:
-        ws = torch.empty(max(need, 256), dtype=torch.uint8, device=h.codes.device)
+    ws = _scratch(need, ws, h.codes.device, stream)
     sz = ctypes.c_size_t(ws.numel())
     _check(_lib.nvfp4_mlp_down_quant(h.c(), w_down.c(), t, i, kk, y_out.c(), _ptr(ws), ctypes.byref(sz),
                                      _stream(stream)), "nvfp4_mlp_down_quant")
@@ -281,8 +302,7 @@ def nvfp4_mlp_down(h, w_down, y, ws=None, stream=None):
     """y [T, K] (float32 or bf16) = H~ . Wd~^T * gs_h * gs_wd."""
     t, kk = y.shape
     need = mlp_down_ws_bytes(t, h.cols, kk)
-    if ws is None:
-        ws = torch.empty(max(need, 256), dtype=torch.uint8, device=y.device)
+    ws = _scratch(need, ws, y.device, stream)
     sz = ctypes.c_size_t(ws.numel())
     _check(_lib.nvfp4_mlp_down(h.c(), w_down.c(), t, h.cols, kk, _ptr(y), _dtype_code(y), y.stride(0), _ptr(ws),
                                ctypes.byref(sz), _stream(stream)), "nvfp4_mlp_down")
@@ -305,8 +325,8 @@ def nvfp4_grouped_gemm(a, a_rows, group_offsets, w0, w1=None, out=None, out_q=No
     if m is None:
         m = out.shape[0] if out is not None else out_q.rows
     need = grouped_ws_bytes(m, n, k, e, epilogue)
-    if need and ws is None:
-        ws = torch.empty(need, dtype=torch.uint8, device=w0.codes.device)
+    if need:
+        ws = _scratch(need, ws, w0.codes.device, stream)
     sz = ctypes.c_size_t(ws.numel() if ws is not None else 0)
     out_dt = _dtype_code(out) if out is not None else F32
     ld = out.stride(0) if out is not None else n
@@ -329,8 +349,7 @@ def nvfp4_rmsnorm_quantize_act(x, gamma, eps, out, ws=None, stream=None):
     Returns the workspace (its first rows floats hold 1/rms)."""
     rows, cols = x.shape
     need = rmsnorm_quantize_ws_bytes(rows, cols)
-    if ws is None:
-        ws = torch.empty(max(need, 256), dtype=torch.uint8, device=x.device)
+    ws = _scratch(need, ws, x.device, stream)
     sz = ctypes.c_size_t(ws.numel())
     _check(_lib.nvfp4_rmsnorm_quantize_act(_ptr(x), _dtype_code(x), rows, cols, x.stride(0), _ptr(gamma), float(eps),
                                            out.c(), _ptr(ws), ctypes.byref(sz), _stream(stream)),
@@ -349,8 +368,7 @@ def nvfp4_moe_route(logits, k, group_offsets, a_rows, slot_of, weights, ws=None,
     """Top-k routing on the device; see include/nvfp4.h.  logits: float32 [T][E] device tensor."""
     t, e = logits.shape
     need = moe_route_ws_bytes(t, e, k)
-    if ws is None:
-        ws = torch.empty(max(need, 256), dtype=torch.uint8, device=logits.device)
+    ws = _scratch(need, ws, logits.device, stream)
     sz = ctypes.c_size_t(ws.numel())
     _check(_lib.nvfp4_moe_route(_ptr(logits), t, e, k, logits.stride(0), _ptr(group_offsets), _ptr(a_rows),
                                 _ptr(slot_of), _ptr(weights), _ptr(ws), ctypes.byref(sz), _stream(stream)),
