@@ -1,4 +1,6 @@
 """Helpers for the GPU parity tests: device setup, host<->device NVFP4, metrics."""
+import json
+import os
 import sys
 
 import numpy as np
@@ -15,6 +17,18 @@ def require_gpu():
     if not torch.cuda.is_available():
         pytest.fail("GPU test on a host without a GPU")
     import mlp_prefill_amd  # noqa: F401  (fails loudly when the library is missing)
+
+
+def record(case, **stats):
+    """Append one JSON line of parity statistics to the file named by the
+    environment variable NVFP4_PARITY_LOG (nothing when it is unset)."""
+    path = os.environ.get("NVFP4_PARITY_LOG")
+    if not path:
+        return
+    os.makedirs(os.path.dirname(os.path.abspath(path)), exist_ok=True)
+    with open(path, "a") as f:
+        f.write(json.dumps({"case": case, **{k: (float(v) if isinstance(v, (np.floating, float)) else v)
+                                               for k, v in stats.items()}}) + "\n")
 
 
 def announce(msg):

@@ -2,14 +2,21 @@
 
 Stages compared (all against the oracle's own end-to-end run):
   S1  x~ bit-exact;
-  S2  the float32 GLU output H the device quantised vs the oracle's H;
-  S3  H~: every code or scale that differs from the oracle's must be a
+  S2  the float32 GLU output H the device quantised vs the oracle's H
+      (max-normalised error gated), and the device's requantisation of its own
+      H bit-exact: gs_h equals the oracle's global scale of the device's H,
+      and the oracle's quantisation of the device's H with that scale equals
+      the device's H~ code for code; gs_h within 2^-20 (relative) of the
+      oracle's own gs_h;
+  S3  H~ against the oracle's H~: every code or scale that differs must be a
       rounding decision the oracle takes within 2^-14 (relative) of a
-      boundary -- the device's float32 accumulation moves H by ~1e-6, so
+      boundary -- the device's float32 accumulation moves H by ~1e-7, so
       such decisions can legitimately go either way;
   S4  Y vs the oracle's Y after accounting for those boundary flips
       (the oracle's down projection of the difference of the two H~), gate
-      2e-3 max-normalised; the raw end-to-end error is reported.
+      2e-3 max-normalised.  The raw end-to-end error is recorded (it can
+      exceed 2e-3 when a block scale of H~ flips: one flipped E4M3 scale moves
+      16 H~ values by 1/8 of their scale).
 """
 import numpy as np
 import pytest
@@ -20,7 +27,9 @@ from oracle import mlp as omlp
 from oracle import quant
 from synthetic import WORKLOADS, bf16_bits_to_f32, bf16_normal, outlier_channels
 from tests.gpu_util import (TOL, announce, assert_nvfp4_equal, dev_bf16, dev_quantize, legit_requant_flips,
-                            max_norm_err, require_gpu, to_host)
+                            max_norm_err, record, require_gpu, to_host)
+
+H_TOL = 1e-6          # float32 accumulation of exact products, SiLU in float32 (measured <= 1.8e-7)
 
 pytestmark = pytest.mark.gpu
 
@@ -64,16 +73,22 @@ def check_mlp(xbits, wdev, wref, label):
     assert_nvfp4_equal(to_host(xq), ref["xq"], f"{label} x~")                       # S1
     eh = max_norm_err(h, ref["h"])                                                  # S2
     hq_dev = to_host(hq)
+    # the device requantised its own float32 H exactly: same global scale, same codes
+    assert hq_dev.gs.view(np.uint32) == quant.global_scale(h).view(np.uint32), (hq_dev.gs, quant.global_scale(h))
+    assert_nvfp4_equal(hq_dev, quant.quantize(h, gs=hq_dev.gs), f"{label} H~ of the device's own H")
+    gs_rel = abs(float(hq_dev.gs) / float(ref["hq"].gs) - 1.0)
     nflip, nsflip = legit_requant_flips(ref["h"].astype(np.float32), hq_dev, ref["hq"])  # S3
     y = y.cpu().numpy()
     e2e = max_norm_err(y, ref["y"])
     corr = ref["y"] + ogemm.gemm(hq_dev, wref[2]) - ogemm.gemm(ref["hq"], wref[2])
     ecorr = max_norm_err(y, corr)                                                   # S4
-    print(f"{label}: H err {eh:.2e}  requant flips {nflip} codes / {nsflip} scales  "
-          f"Y err e2e {e2e:.2e}  flip-corrected {ecorr:.2e}  gs_h dev {hq_dev.gs!r} ref {ref['hq'].gs!r}")
-    assert eh <= 1e-4
-    # gs_h = amax(H)/2688 moves with the device's H (float32 accumulation)
-    assert abs(float(hq_dev.gs) / float(ref["hq"].gs) - 1.0) <= 2.0 ** -16
+    print(f"{label}: H err {eh:.2e}  gs_h rel {gs_rel:.2e}  requant flips {nflip} codes / {nsflip} scales  "
+          f"Y err e2e {e2e:.2e}  flip-corrected {ecorr:.2e}")
+    record(label, h_err=eh, gs_h_rel=gs_rel, code_flips=nflip, scale_flips=nsflip, y_err_e2e=e2e,
+           y_err_flip_corrected=ecorr, tokens=int(t), hidden=int(k), intermediate=int(h.shape[1]))
+    assert eh <= H_TOL
+    # gs_h = RN32(amax(H)/2688) moves with the device's H by at most its error
+    assert gs_rel <= 2.0 ** -20
     assert ecorr <= TOL
     return e2e
 

@@ -17,7 +17,7 @@ from oracle import mlp as omlp
 from oracle import quant
 from synthetic import WORKLOADS, bf16_bits_to_f32, bf16_normal, layer_seeds
 from tests.gpu_util import (announce, assert_bf16_rounding_close, bf16_tensor_to_f32, dev_bf16, dev_quantize,
-                            legit_requant_flips, max_norm_err, require_gpu, to_host)
+                            legit_requant_flips, max_norm_err, record, require_gpu, to_host)
 
 pytestmark = pytest.mark.gpu
 
@@ -70,10 +70,14 @@ def test_stacked_layers_device_resident_bf16_chain():
             y = bf16_tensor_to_f32(outs[u][li])
             print(f"ubatch {u} layer {li}: input rms {np.sqrt(np.mean(layer_in.astype(np.float64) ** 2)):.3g}  "
                   f"flips {nflip}/{nsflip}  Y err (bf16 out) {max_norm_err(y, corr):.2e}")
+            record(f"stacked ubatch {u} layer {li}", code_flips=nflip, scale_flips=nsflip,
+                   y_err_flip_corrected_bf16=max_norm_err(y, corr), y_err_e2e_bf16=max_norm_err(y, ref["y"]))
             assert_bf16_rounding_close(y, corr)
             layer_in = y                         # the device's bf16 activation is the next layer's input
 
     # drift of the whole chain against the pure oracle chain (reported)
     y_last, _ = omlp.stacked_mlp(x0, wref, ubatch=ub)
     got = np.concatenate([bf16_tensor_to_f32(outs[u][nl - 1]) for u in range(nub)])
-    print(f"4-layer chain vs pure oracle chain: max-normalised error {max_norm_err(got, y_last):.2e}")
+    drift = max_norm_err(got, y_last)
+    print(f"4-layer chain vs pure oracle chain: max-normalised error {drift:.2e}")
+    record("stacked 4-layer chain vs pure oracle chain", y_err_e2e_bf16=drift, tokens=ub * nub)
