@@ -118,7 +118,7 @@ enum nvfp4_epilogue {
  *             ld_x elements (ld_x >= cols)
  *   cols    : multiple of 16
  *   ws      : NVFP4_GS_COMPUTE needs a small workspace (block partial
- *             maxima, at most 4 KiB); NVFP4_GS_GIVEN needs none
+ *             maxima, 16 KiB); NVFP4_GS_GIVEN needs none
  * Two kernel launches (COMPUTE) or one (GIVEN); a COMPUTE call on at most
  * 4096 blocks of 16 (rows * cols <= 65536, e.g. decode activations) takes
  * the amax, the global scale and the codes in one launch.  One launch set
@@ -126,6 +126,25 @@ enum nvfp4_epilogue {
  */
 int nvfp4_quantize_act(const void *x, int x_dtype, int64_t rows, int64_t cols, int64_t ld_x,
                        nvfp4_tensor out, int gs_mode, void *ws, size_t *ws_bytes, void *stream);
+
+/*
+ * nvfp4_quantize_act_noalloc -- nvfp4_quantize_act without a workspace, for
+ * callers that cannot allocate device memory (code under HIP graph capture,
+ * tight serving loops, harnesses that forbid hipMalloc).  Same arguments,
+ * results, launches and errors as nvfp4_quantize_act, minus ws / ws_bytes: the
+ * partial maxima of the amax pass go to a scratch array of 16 KiB (4096
+ * float32) that the library holds in device memory, one copy per GPU, for the
+ * life of the process.  The call allocates nothing.  Every call on a GPU
+ * shares that GPU's array: calls that overlap on one GPU (on different
+ * streams, or from different threads without ordering) race on it and give
+ * unspecified results; calls ordered on one stream are safe.  The array needs
+ * no initialisation (the amax pass writes every entry the quantise pass
+ * reads).  Tensors of every size nvfp4_quantize_act accepts fit the array;
+ * NVFP4_ERR_WORKSPACE would report one that did not.  NVFP4_ERR_DEVICE also
+ * reports a failed lookup of the array's device address.
+ */
+int nvfp4_quantize_act_noalloc(const void *x, int x_dtype, int64_t rows, int64_t cols, int64_t ld_x,
+                               nvfp4_tensor out, int gs_mode, void *stream);
 
 /*
  * nvfp4_rmsnorm_quantize_act -- NVFP4 quantisation of RMSNorm(x), fused:

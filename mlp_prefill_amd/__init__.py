@@ -39,6 +39,7 @@ KC_QUANTIZE, KC_EXPAND, KC_GEMM_GLU, KC_GEMM_STORE, KC_REDUCE, KC_ROUTE, KC_COMB
 _sig = {
     "nvfp4_quantize_act": [_vp, ctypes.c_int, _i64, _i64, _i64, nvfp4_tensor, ctypes.c_int, _vp,
                            ctypes.POINTER(ctypes.c_size_t), _vp],
+    "nvfp4_quantize_act_noalloc": [_vp, ctypes.c_int, _i64, _i64, _i64, nvfp4_tensor, ctypes.c_int, _vp],
     "nvfp4_gemm": [nvfp4_tensor, nvfp4_tensor, _i64, _i64, _i64, _vp, ctypes.c_int, _i64, _vp,
                    ctypes.POINTER(ctypes.c_size_t), _vp],
     "nvfp4_mlp_gu_act": [nvfp4_tensor, nvfp4_tensor, nvfp4_tensor, _i64, _i64, _i64, nvfp4_tensor, _vp,
@@ -202,6 +203,16 @@ def nvfp4_quantize_act(x, out, gs_mode=GS_COMPUTE, ws=None, stream=None):
     ws, sz = _workspace(q, ws, x.device, stream)
     _check(_lib.nvfp4_quantize_act(_ptr(x), dt, rows, cols, ld, out.c(), gs_mode, _ptr(ws), ctypes.byref(sz),
                                    _stream(stream)), "nvfp4_quantize_act")
+    return out
+
+
+def nvfp4_quantize_act_noalloc(x, out, gs_mode=GS_COMPUTE, stream=None):
+    """nvfp4_quantize_act with the library's per-GPU scratch array instead of a workspace."""
+    rows, cols = x.shape
+    if x.stride(1) != 1:
+        raise ValueError("x must be row-major")
+    _check(_lib.nvfp4_quantize_act_noalloc(_ptr(x), _dtype_code(x), rows, cols, x.stride(0), out.c(), gs_mode,
+                                           _stream(stream)), "nvfp4_quantize_act_noalloc")
     return out
 
 

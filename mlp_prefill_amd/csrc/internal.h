@@ -32,6 +32,10 @@ void launch_end(int slot, hipStream_t st);
 size_t quantize_ws_bytes(int64_t rows, int64_t cols, int gs_mode);
 int quantize_launch(const void* x, int x_dtype, int64_t rows, int64_t cols, int64_t ld, uint8_t* codes,
                     uint8_t* scales, float* gs, int gs_mode, void* ws, hipStream_t st);
+// Allocation-free quantiser: bytes of the per-device scratch array, and its
+// device address on the current device (0, or 6 when it cannot be looked up).
+size_t quantize_scratch_bytes();
+int quantize_scratch(void** out);
 // Requantise a float32 [rows][cols] matrix whose amax is the max of
 // `partials` (written by an earlier kernel on the same stream).
 int requant_f32_launch(const float* h, int64_t rows, int64_t cols, uint8_t* codes, uint8_t* scales,

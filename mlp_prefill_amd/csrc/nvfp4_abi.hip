@@ -189,6 +189,25 @@ int nvfp4_quantize_act(const void* x, int x_dtype, int64_t rows, int64_t cols, i
                                 reinterpret_cast<hipStream_t>(stream));
 }
 
+int nvfp4_quantize_act_noalloc(const void* x, int x_dtype, int64_t rows, int64_t cols, int64_t ld_x,
+                               nvfp4_tensor out, int gs_mode, void* stream) {
+  if (!dtype_ok(x_dtype) || (gs_mode != NVFP4_GS_COMPUTE && gs_mode != NVFP4_GS_GIVEN)) return NVFP4_ERR_ARG;
+  if (rows < 0 || cols < 0 || cols % 16 != 0 || ld_x < cols) return NVFP4_ERR_SHAPE;
+  if (rows * (cols / 16) >= ((int64_t)1 << 31)) return NVFP4_ERR_SHAPE;
+  // the scratch array replaces the workspace: it must hold what a workspace would
+  if (nvfp4::quantize_ws_bytes(rows, cols, gs_mode) > nvfp4::quantize_scratch_bytes()) return NVFP4_ERR_WORKSPACE;
+  if (rows == 0 || cols == 0) return NVFP4_OK;
+  if (!x) return NVFP4_ERR_NULL;
+  int rc;
+  if ((rc = check_tensor(out)) != NVFP4_OK) return rc;
+  if (!aligned(x, 16) || (ld_x * elem_size(x_dtype)) % 16 != 0) return NVFP4_ERR_ALIGN;
+  if ((rc = check_device()) != NVFP4_OK) return rc;
+  void* ws = nullptr;
+  if (nvfp4::quantize_scratch(&ws) != 0) return NVFP4_ERR_DEVICE;
+  return nvfp4::quantize_launch(x, x_dtype, rows, cols, ld_x, out.codes, out.scales, out.gscale, gs_mode, ws,
+                                reinterpret_cast<hipStream_t>(stream));
+}
+
 int nvfp4_rmsnorm_quantize_act(const void* x, int x_dtype, int64_t rows, int64_t cols, int64_t ld_x,
                                const float* gamma, float eps, nvfp4_tensor out, void* ws, size_t* ws_bytes,
                                void* stream) {

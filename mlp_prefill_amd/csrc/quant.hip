@@ -14,6 +14,8 @@
 // iteration, at most 2048 work-groups).  Both are HBM-bound: the
 // quantiser reads 2 (bf16) or 4 (float32) bytes per element and writes
 // 0.5 + 1/16 bytes.
+#include <mutex>
+
 #include "device_common.h"
 #include "internal.h"
 
@@ -251,6 +253,43 @@ int quantize_launch(const void* x, int x_dtype, int64_t rows, int64_t cols, int6
                              gs_mode, partials, nullptr, 0, st);
   return quantize_launch_t(reinterpret_cast<const float*>(x), rows, cols, ld, codes, scales, gs, gs_mode,
                            partials, nullptr, 0, st);
+}
+
+// ---- allocation-free variant ---------------------------------------------------
+// The partial maxima of the amax pass (the whole workspace a COMPUTE call
+// needs, at most kMaxPartials floats = 16 KiB whatever the tensor size) live in
+// this array instead of a caller's workspace.  Each GPU holds its own copy
+// until the process ends; every call on that GPU shares it.
+static __device__ __align__(256) float scratch[kMaxPartials];
+
+namespace {
+constexpr int kScratchDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kScratchDevices];
+}  // namespace
+
+size_t quantize_scratch_bytes() { return sizeof(scratch); }
+
+// Device address of `scratch` on the current device: looked up once per device
+// (hipGetSymbolAddress with that device current), then reused.  In host code
+// the name `scratch` is only a handle for the lookup, never an address.
+int quantize_scratch(void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kScratchDevices) {
+    (void)hipGetLastError();
+    return 6;
+  }
+  std::lock_guard<std::mutex> lk(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || p == nullptr) {
+      (void)hipGetLastError();
+      return 6;
+    }
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return 0;
 }
 
 size_t rmsnorm_quantize_ws_bytes(int64_t rows) {

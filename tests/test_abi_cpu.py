@@ -71,6 +71,25 @@ def test_quantize_validation():
     assert q(None, m.BF16, 0, 32, 32, nvfp4_tensor(0, 0, 0), 0, FAKE, ctypes.byref(sz), None) == m.OK
 
 
+def test_quantize_noalloc_validation():
+    q = m.lib.nvfp4_quantize_act_noalloc
+    assert q(FAKE, 7, 4, 32, 32, _t(), 0, None) == m.ERR_ARG                  # dtype
+    assert q(FAKE, m.BF16, 4, 32, 32, _t(), 9, None) == m.ERR_ARG             # gs mode
+    assert q(FAKE, m.BF16, 4, 24, 24, _t(), 0, None) == m.ERR_SHAPE           # cols % 16
+    assert q(FAKE, m.BF16, 4, 32, 16, _t(), 0, None) == m.ERR_SHAPE           # ld < cols
+    assert q(FAKE, m.BF16, 1 << 28, 256, 256, _t(), 0, None) == m.ERR_SHAPE   # 2^32 blocks
+    assert q(None, m.BF16, 4, 32, 32, _t(), 0, None) == m.ERR_NULL
+    assert q(FAKE, m.BF16, 4, 32, 32, _t(s=0), 0, None) == m.ERR_NULL
+    assert q(FAKE + 2, m.BF16, 4, 32, 32, _t(), 0, None) == m.ERR_ALIGN
+    assert q(FAKE, m.BF16, 4, 32, 36, _t(), 0, None) == m.ERR_ALIGN           # row stride
+    assert q(None, m.BF16, 0, 32, 32, nvfp4_tensor(0, 0, 0), 0, None) == m.OK  # empty: no-op
+
+
+@no_gpu
+def test_quantize_noalloc_without_device():
+    assert m.lib.nvfp4_quantize_act_noalloc(FAKE, m.BF16, 4, 32, 32, _t(), 0, None) == m.ERR_DEVICE
+
+
 def test_quantize_workspace_query():
     q = m.lib.nvfp4_quantize_act
     s = _size()
