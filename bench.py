@@ -84,7 +84,12 @@ class Layer:
 
 
 class MlpRunner:
-    """Preallocated buffers for one MLP call shape (T tokens)."""
+    """Preallocated buffers for one MLP call shape (T tokens).
+
+    chained=True: the down projection also writes max|y| (its output-amax
+    epilogue), and a call marked `from_amax` quantises its input with the
+    global scale formed from the amax the previous call wrote (one launch
+    instead of the amax pass + quantise)."""
 
     def __init__(self, m, t, k=K_HID, i=I_INT):
         self.m, self.t, self.k, self.i = m, t, k, i
@@ -93,12 +98,16 @@ class MlpRunner:
         self.ws_q = torch.empty(m.ws_bytes_quantize(t, k), dtype=torch.uint8, device="cuda")
         self.ws_gu = torch.empty(max(m.mlp_gu_act_ws_bytes(t, k, i), 256), dtype=torch.uint8, device="cuda")
         self.ws_dn = torch.empty(max(m.mlp_down_ws_bytes(t, i, k), 256), dtype=torch.uint8, device="cuda")
+        self.amax = m.amax_buffer()
 
-    def __call__(self, x, layer, y):
+    def __call__(self, x, layer, y, chained=False, from_amax=False):
         m = self.m
-        m.nvfp4_quantize_act(x, self.xq, ws=self.ws_q)
+        if from_amax:
+            m.nvfp4_quantize_act(x, self.xq, gs_mode=m.GS_FROM_AMAX, ws=self.amax)
+        else:
+            m.nvfp4_quantize_act(x, self.xq, ws=self.ws_q)
         m.nvfp4_mlp_gu_act(self.xq, layer.w[0], layer.w[1], self.hq, ws=self.ws_gu)
-        m.nvfp4_mlp_down(self.hq, layer.w[2], y, ws=self.ws_dn)
+        m.nvfp4_mlp_down(self.hq, layer.w[2], y, ws=self.ws_dn, amax=self.amax if chained else None)
 
 
 def time_events(fn, reps, warm=2, scrub=None):
@@ -116,6 +125,17 @@ def time_events(fn, reps, warm=2, scrub=None):
         e.synchronize()
         out.append(s.elapsed_time(e))
     return out
+
+
+def cpu_model():
+    """The host CPU's model name (from /proc/cpuinfo), or None."""
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
 
 
 def cpu_baseline(n_ubatch):
@@ -139,6 +159,7 @@ def cpu_baseline(n_ubatch):
     t_sample = n_ubatch * ub
     threads = max([d.get("num_threads", 1) for d in threadpool_info()] or [1])
     return {"value": mlp_flops(t_sample) / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
+            "cpu_model": cpu_model(), "host_cores_available": len(os.sched_getaffinity(0)),
             "sample": f"the first {n_ubatch} ubatches ({t_sample} tokens) of the long-prefill input through "
                       f"layer 0 (quantise x, gate/up, SiLU*up, requantise, down; float64 numpy); {dt:.2f} s, "
                       f"{t_sample / dt:.1f} tokens/s; weight quantisation excluded",
@@ -184,11 +205,12 @@ def main():
     torch.cuda.synchronize()
 
     def step():
+        # each layer's down projection hands max|y| to the next layer's quantiser
         for u in range(T // UB):
             cur = x_all[u * UB:(u + 1) * UB]
             for li, layer in enumerate(layers):
                 dst = out[u * UB:(u + 1) * UB] if li == L - 1 else y_buf[li % 2]
-                run(cur, layer, dst)
+                run(cur, layer, dst, chained=li < L - 1, from_amax=li > 0)
                 cur = dst
 
     log(f"warmup {args.warmup} steps")
@@ -375,10 +397,38 @@ def decode_line(m):
     return dec
 
 
+def gemm_small_line(m):
+    """The single 16 x 256 x 512 NVFP4 GEMM workload: activation quantisation on
+    the device plus the contraction (float32 out), launch-latency bound."""
+    from synthetic import WORKLOADS, bf16_normal
+    p = WORKLOADS["gemm_16x256x512"].params
+    log("extra: single GEMM 16x256x512")
+    x = m.bf16_from_bits(bf16_normal(p["x_seed"], (p["T"], p["K"])))
+    w = m.NVFP4.empty(p["N"], p["K"])
+    m.nvfp4_quantize_act(m.bf16_from_bits(bf16_normal(p["w_seed"], (p["N"], p["K"]), sigma=0.02)), w)
+    xq = m.NVFP4.empty(p["T"], p["K"])
+    c = torch.empty((p["T"], p["N"]), dtype=torch.float32, device="cuda")
+    ws_q = torch.empty(m.ws_bytes_quantize(p["T"], p["K"]), dtype=torch.uint8, device="cuda")
+    ws_g = torch.empty(max(m.gemm_ws_bytes(p["T"], p["N"], p["K"]), 256), dtype=torch.uint8, device="cuda")
+
+    def call():
+        m.nvfp4_quantize_act(x, xq, ws=ws_q)
+        m.nvfp4_gemm(xq, w, c, ws=ws_g)
+    b0 = m.launch_count()
+    call()
+    launches = m.launch_count() - b0
+    ts = sorted(time_events(call, 50, warm=5))
+    med = ts[len(ts) // 2]
+    flops = 2.0 * p["T"] * p["K"] * p["N"]
+    return {"workload": "gemm_16x256x512", "ms": med, "ms_min": ts[0], "ms_p90": ts[int(0.9 * (len(ts) - 1))],
+            "gflops": flops / (med * 1e-3) / 1e9, "launches_per_call": launches,
+            "note": "quantise x (device global scale) + contraction; a few microseconds of launch latency dominate"}
+
+
 def extra_lines(m):
     """1024-token MLP and decode-shaped T=1/T=5 MLP (separate weights, as their workloads define)."""
     from synthetic import WORKLOADS, bf16_normal, outlier_channels
-    out = {}
+    out = {"gemm_16x256x512": gemm_small_line(m)}
     p3 = WORKLOADS["mlp_prefill_1024x5120x17408"].params
     log("extra: 1024-token MLP")
     lay = Layer(m, (p3["wg_seed"], p3["wu_seed"], p3["wd_seed"]))

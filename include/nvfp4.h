@@ -92,9 +92,14 @@ enum nvfp4_status {
 enum nvfp4_dtype { NVFP4_F32 = 0, NVFP4_BF16 = 1 };
 
 enum nvfp4_gs_mode {
-  NVFP4_GS_COMPUTE = 0,  /* amax over the whole input on the device; writes *gscale */
-  NVFP4_GS_GIVEN = 1     /* use the float32 already stored at *gscale            */
+  NVFP4_GS_COMPUTE = 0,   /* amax over the whole input on the device; writes *gscale        */
+  NVFP4_GS_GIVEN = 1,     /* use the float32 already stored at *gscale                     */
+  NVFP4_GS_FROM_AMAX = 2  /* the amax is given on the device (ws); writes *gscale from it   */
 };
+
+/* Output-amax epilogues write this many float32 partial maxima (4 KiB); the
+ * largest of them is max |output|. */
+#define NVFP4_AMAX_SLOTS 1024
 
 enum nvfp4_epilogue {
   NVFP4_EPI_STORE = 0,             /* out = A~ . W~^T scaled, float32 or bf16         */
@@ -118,11 +123,17 @@ enum nvfp4_epilogue {
  *             ld_x elements (ld_x >= cols)
  *   cols    : multiple of 16
  *   ws      : NVFP4_GS_COMPUTE needs a small workspace (block partial
- *             maxima, 16 KiB); NVFP4_GS_GIVEN needs none
- * Two kernel launches (COMPUTE) or one (GIVEN); a COMPUTE call on at most
- * 4096 blocks of 16 (rows * cols <= 65536, e.g. decode activations) takes
- * the amax, the global scale and the codes in one launch.  One launch set
- * per call, never one per row.
+ *             maxima, 16 KiB); NVFP4_GS_GIVEN needs none;
+ *             NVFP4_GS_FROM_AMAX: ws points to NVFP4_AMAX_SLOTS float32
+ *             whose largest is max|x| over the whole tensor (written on the
+ *             device by an earlier call on the stream: the y_amax output of
+ *             the nvfp4_mlp_down whose output is x), *ws_bytes >= 4096,
+ *             16-byte aligned; gscale is formed from it exactly as COMPUTE
+ *             would (the max is exact)
+ * Two kernel launches (COMPUTE) or one (GIVEN, FROM_AMAX); a COMPUTE call on
+ * at most 4096 blocks of 16 (rows * cols <= 65536, e.g. decode activations)
+ * takes the amax, the global scale and the codes in one launch.  One launch
+ * set per call, never one per row.
  */
 int nvfp4_quantize_act(const void *x, int x_dtype, int64_t rows, int64_t cols, int64_t ld_x,
                        nvfp4_tensor out, int gs_mode, void *ws, size_t *ws_bytes, void *stream);
@@ -131,7 +142,9 @@ int nvfp4_quantize_act(const void *x, int x_dtype, int64_t rows, int64_t cols, i
  * nvfp4_quantize_act_noalloc -- nvfp4_quantize_act without a workspace, for
  * callers that cannot allocate device memory (code under HIP graph capture,
  * tight serving loops, harnesses that forbid hipMalloc).  Same arguments,
- * results, launches and errors as nvfp4_quantize_act, minus ws / ws_bytes: the
+ * results, launches and errors as nvfp4_quantize_act, minus ws / ws_bytes
+ * (so gs_mode is NVFP4_GS_COMPUTE or NVFP4_GS_GIVEN; NVFP4_GS_FROM_AMAX,
+ * whose amax travels in ws, is NVFP4_ERR_ARG here): the
  * partial maxima of the amax pass go to a scratch array of 16 KiB (4096
  * float32) that the library holds in device memory, one copy per GPU, for the
  * life of the process.  The call allocates nothing.  Every call on a GPU
@@ -177,11 +190,21 @@ int nvfp4_rmsnorm_quantize_act(const void *x, int x_dtype, int64_t rows, int64_t
  *   a  : [M][K] NVFP4, b : [N][K] NVFP4 (one gscale each)
  *   K  : multiple of 128
  *   c  : float32 or bf16 (c_dtype), row stride ldc >= N elements
- *   ws : required: the f16 copy of a~ (M*K*2 bytes) and, when K is split,
- *        the float32 partial sums; contents unspecified on return
+ *   c_amax : NULL, or NVFP4_AMAX_SLOTS device float32 (16-byte aligned)
+ *        that receive partial maxima of |c| as stored (after the bf16
+ *        rounding for bf16 outputs): the largest of them is max |c|, the
+ *        amax the next NVFP4 linear's activation global scale needs ([dsv4]
+ *        P0), produced in the output epilogue so that no pass re-reads c for
+ *        it; pass the array to nvfp4_quantize_act as ws with
+ *        NVFP4_GS_FROM_AMAX.  Every slot is written (no initialisation, no
+ *        atomics).  With c_amax the reduction launch stores every output
+ *        (the contraction writes partial sums even when K is not split); the
+ *        launch count is unchanged.
+ *   ws : required: the f16 copy of a~ (M*K*2 bytes) and the float32
+ *        partial sums; contents unspecified on return
  */
 int nvfp4_gemm(nvfp4_tensor a, nvfp4_tensor b, int64_t M, int64_t N, int64_t K,
-               void *c, int c_dtype, int64_t ldc, void *ws, size_t *ws_bytes, void *stream);
+               void *c, int c_dtype, int64_t ldc, float *c_amax, void *ws, size_t *ws_bytes, void *stream);
 
 /*
  * nvfp4_mlp_gu_act -- gate/up projections, SiLU(gate) * up, requantisation.
@@ -213,12 +236,16 @@ int nvfp4_mlp_gu_act(nvfp4_tensor x, nvfp4_tensor w_gate, nvfp4_tensor w_up,
  * kept on the device: [vllm] Fix directions 2).
  *   h  : [T][I] NVFP4;  w_down : [K][I] NVFP4;  I multiple of 128
  *   y  : row stride ldy >= K elements
+ *   y_amax : NULL, or NVFP4_AMAX_SLOTS device float32 receiving partial
+ *        maxima of |y| as stored, as c_amax of nvfp4_gemm: a chained layer's
+ *        input amax, so the next nvfp4_quantize_act (NVFP4_GS_FROM_AMAX) is
+ *        one launch
  *   ws : required, as for nvfp4_gemm (f16 copy of h~, split-K partials)
  * Three launches per call (two when T <= 8 and I is a multiple of 1024, as
  * for nvfp4_gemm).
  */
 int nvfp4_mlp_down(nvfp4_tensor h, nvfp4_tensor w_down, int64_t T, int64_t I, int64_t K,
-                   void *y, int y_dtype, int64_t ldy, void *ws, size_t *ws_bytes, void *stream);
+                   void *y, int y_dtype, int64_t ldy, float *y_amax, void *ws, size_t *ws_bytes, void *stream);
 
 /*
  * nvfp4_mlp_gu_act_static -- nvfp4_mlp_gu_act with a static global scale

@@ -32,7 +32,8 @@ class nvfp4_tensor(ctypes.Structure):
 
 OK, ERR_NULL, ERR_SHAPE, ERR_ALIGN, ERR_WORKSPACE, ERR_ARG, ERR_DEVICE, ERR_LAUNCH = range(8)
 F32, BF16 = 0, 1
-GS_COMPUTE, GS_GIVEN = 0, 1
+GS_COMPUTE, GS_GIVEN, GS_FROM_AMAX = 0, 1, 2
+AMAX_SLOTS = 1024     # partial maxima written by an output-amax epilogue
 EPI_STORE, EPI_SILU_MUL_REQUANT, EPI_SILU_MUL_QUANT_GIVEN = 0, 1, 2
 KC_QUANTIZE, KC_EXPAND, KC_GEMM_GLU, KC_GEMM_STORE, KC_REDUCE, KC_ROUTE, KC_COMBINE = range(7)
 
@@ -40,11 +41,11 @@ _sig = {
     "nvfp4_quantize_act": [_vp, ctypes.c_int, _i64, _i64, _i64, nvfp4_tensor, ctypes.c_int, _vp,
                            ctypes.POINTER(ctypes.c_size_t), _vp],
     "nvfp4_quantize_act_noalloc": [_vp, ctypes.c_int, _i64, _i64, _i64, nvfp4_tensor, ctypes.c_int, _vp],
-    "nvfp4_gemm": [nvfp4_tensor, nvfp4_tensor, _i64, _i64, _i64, _vp, ctypes.c_int, _i64, _vp,
+    "nvfp4_gemm": [nvfp4_tensor, nvfp4_tensor, _i64, _i64, _i64, _vp, ctypes.c_int, _i64, _vp, _vp,
                    ctypes.POINTER(ctypes.c_size_t), _vp],
     "nvfp4_mlp_gu_act": [nvfp4_tensor, nvfp4_tensor, nvfp4_tensor, _i64, _i64, _i64, nvfp4_tensor, _vp,
                          ctypes.POINTER(ctypes.c_size_t), _vp],
-    "nvfp4_mlp_down": [nvfp4_tensor, nvfp4_tensor, _i64, _i64, _i64, _vp, ctypes.c_int, _i64, _vp,
+    "nvfp4_mlp_down": [nvfp4_tensor, nvfp4_tensor, _i64, _i64, _i64, _vp, ctypes.c_int, _i64, _vp, _vp,
                        ctypes.POINTER(ctypes.c_size_t), _vp],
     "nvfp4_mlp_gu_act_static": [nvfp4_tensor, nvfp4_tensor, nvfp4_tensor, _i64, _i64, _i64, nvfp4_tensor, _vp,
                                 ctypes.POINTER(ctypes.c_size_t), _vp],
@@ -190,13 +191,27 @@ def _workspace(query, ws, device, stream=None):
 
 
 # ---- entry points ----------------------------------------------------------------
+def amax_buffer(device="cuda"):
+    """Device float32 [AMAX_SLOTS]: the output-amax argument of nvfp4_gemm / nvfp4_mlp_down."""
+    return torch.empty(AMAX_SLOTS, dtype=torch.float32, device=device)
+
+
 def nvfp4_quantize_act(x, out, gs_mode=GS_COMPUTE, ws=None, stream=None):
-    """Quantise x [rows, cols] (bf16 or float32, device) into `out` (NVFP4)."""
+    """Quantise x [rows, cols] (bf16 or float32, device) into `out` (NVFP4).
+    With gs_mode=GS_FROM_AMAX, `ws` is the amax buffer an earlier
+    nvfp4_mlp_down(..., amax=) or nvfp4_gemm(..., amax=) filled for x."""
     rows, cols = x.shape
     ld = x.stride(0)
     if x.stride(1) != 1:
         raise ValueError("x must be row-major")
     dt = _dtype_code(x)
+    if gs_mode == GS_FROM_AMAX:
+        if ws is None or ws.dtype != torch.float32 or ws.numel() < AMAX_SLOTS:
+            raise ValueError("GS_FROM_AMAX takes the partial maxima as ws (float32 device tensor of AMAX_SLOTS)")
+        sz = ctypes.c_size_t(ws.numel() * 4)
+        _check(_lib.nvfp4_quantize_act(_ptr(x), dt, rows, cols, ld, out.c(), gs_mode, _ptr(ws), ctypes.byref(sz),
+                                       _stream(stream)), "nvfp4_quantize_act")
+        return out
 
     def q(wsp, szp):
         return _lib.nvfp4_quantize_act(_vp(0), dt, rows, cols, ld, _null_tensor(), gs_mode, wsp, szp, _vp(0))
@@ -219,18 +234,19 @@ def nvfp4_quantize_act_noalloc(x, out, gs_mode=GS_COMPUTE, stream=None):
 def gemm_ws_bytes(m, n, k):
     """Workspace bytes nvfp4_gemm needs for C [m, n] with K = k."""
     size = ctypes.c_size_t(0)
-    _check(_lib.nvfp4_gemm(_null_tensor(), _null_tensor(), m, n, k, _vp(0), F32, max(n, 1), _vp(0),
+    _check(_lib.nvfp4_gemm(_null_tensor(), _null_tensor(), m, n, k, _vp(0), F32, max(n, 1), _vp(0), _vp(0),
                            ctypes.byref(size), _vp(0)), "workspace query")
     return size.value
 
 
-def nvfp4_gemm(a, b, c, ws=None, stream=None):
-    """c [M, N] (float32 or bf16) = A~ . B~^T * gs_a * gs_b."""
+def nvfp4_gemm(a, b, c, ws=None, stream=None, amax=None):
+    """c [M, N] (float32 or bf16) = A~ . B~^T * gs_a * gs_b; amax (optional, see
+    amax_buffer) receives partial maxima of |c| as stored."""
     m, n = c.shape
     need = gemm_ws_bytes(m, n, a.cols)
     ws = _scratch(need, ws, c.device, stream)
     sz = ctypes.c_size_t(ws.numel())
-    _check(_lib.nvfp4_gemm(a.c(), b.c(), m, n, a.cols, _ptr(c), _dtype_code(c), c.stride(0), _ptr(ws),
+    _check(_lib.nvfp4_gemm(a.c(), b.c(), m, n, a.cols, _ptr(c), _dtype_code(c), c.stride(0), _ptr(amax), _ptr(ws),
                            ctypes.byref(sz), _stream(stream)), "nvfp4_gemm")
     return c
 
@@ -304,19 +320,20 @@ def nvfp4_mlp_down_quant(h, w_down, y_out, ws=None, stream=None):
 def mlp_down_ws_bytes(t, i, k):
     """Workspace bytes nvfp4_mlp_down needs for T tokens, intermediate i, hidden k."""
     size = ctypes.c_size_t(0)
-    _check(_lib.nvfp4_mlp_down(_null_tensor(), _null_tensor(), t, i, k, _vp(0), F32, k, _vp(0),
+    _check(_lib.nvfp4_mlp_down(_null_tensor(), _null_tensor(), t, i, k, _vp(0), F32, k, _vp(0), _vp(0),
                                ctypes.byref(size), _vp(0)), "workspace query")
     return size.value
 
 
-def nvfp4_mlp_down(h, w_down, y, ws=None, stream=None):
-    """y [T, K] (float32 or bf16) = H~ . Wd~^T * gs_h * gs_wd."""
+def nvfp4_mlp_down(h, w_down, y, ws=None, stream=None, amax=None):
+    """y [T, K] (float32 or bf16) = H~ . Wd~^T * gs_h * gs_wd; amax (optional, see
+    amax_buffer) receives partial maxima of |y| as stored -- the next layer's input amax."""
     t, kk = y.shape
     need = mlp_down_ws_bytes(t, h.cols, kk)
     ws = _scratch(need, ws, y.device, stream)
     sz = ctypes.c_size_t(ws.numel())
-    _check(_lib.nvfp4_mlp_down(h.c(), w_down.c(), t, h.cols, kk, _ptr(y), _dtype_code(y), y.stride(0), _ptr(ws),
-                               ctypes.byref(sz), _stream(stream)), "nvfp4_mlp_down")
+    _check(_lib.nvfp4_mlp_down(h.c(), w_down.c(), t, h.cols, kk, _ptr(y), _dtype_code(y), y.stride(0), _ptr(amax),
+                               _ptr(ws), ctypes.byref(sz), _stream(stream)), "nvfp4_mlp_down")
     return y
 
 

@@ -1397,13 +1397,30 @@ __global__ void __launch_bounds__(kQdMaxWaves * 64) quad_kernel(GemmArgs p, int 
   }
 }
 
+// Output amax: each work-group writes the largest |stored value| it produced
+// (after the bf16 rounding for bf16 outputs: rounding is monotone, so the max
+// of the rounded values is the rounded max) to its own slot; with an amax
+// output the reduction runs exactly kAmaxSlots work-groups, so the max over
+// the slots is max |C|.  No atomics (thousands of work-groups taking turns on
+// one word cost tens of microseconds) and nothing to clear.
+__device__ __forceinline__ void fold_amax(float m, float* amax) {
+  __shared__ float red[4];
+  m = block_max(m, red);
+  if (threadIdx.x == 0) amax[blockIdx.x] = m;
+}
+
+__device__ __forceinline__ float stored_abs(float v, int bf16) {
+  return bf16 ? __uint_as_float(f32_to_bf16_bits(fabsf(v)) << 16) : fabsf(v);
+}
+
 // out[m][n] = (sum over splits, in split order) * gs_a * gs_b[expert of slot m].
 __global__ void __launch_bounds__(256) splitk_reduce_kernel(const float* __restrict__ part, uint32_t splits,
                                                             int64_t M, int64_t N, const float* a_gs,
                                                             const float* b_gs, const int32_t* off, int E,
-                                                            void* out, int out_bf16, int64_t ldo) {
+                                                            void* out, int out_bf16, int64_t ldo, float* amax) {
   const int64_t total = M * N;
   const float ga = a_gs[0];
+  float vmax = 0.f;
   for (int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x; idx < total; idx += (int64_t)gridDim.x * 256) {
     const int64_t m = idx / N, n = idx - m * N;
     // loads in batches of eight, added in split order
@@ -1426,7 +1443,9 @@ __global__ void __launch_bounds__(256) splitk_reduce_kernel(const float* __restr
       reinterpret_cast<uint16_t*>(out)[m * ldo + n] = (uint16_t)f32_to_bf16_bits(v);
     else
       reinterpret_cast<float*>(out)[m * ldo + n] = v;
+    vmax = fmaxf(vmax, stored_abs(v, out_bf16));
   }
+  if (amax) fold_amax(vmax, amax);
 }
 
 // The same reduction with four consecutive outputs of one row per thread
@@ -1435,9 +1454,10 @@ __global__ void __launch_bounds__(256) splitk_reduce_kernel(const float* __restr
 __global__ void __launch_bounds__(256) splitk_reduce4_kernel(const float* __restrict__ part, uint32_t splits,
                                                              int64_t M, int64_t N, const float* a_gs,
                                                              const float* b_gs, const int32_t* off, int E,
-                                                             void* out, int out_bf16, int64_t ldo) {
+                                                             void* out, int out_bf16, int64_t ldo, float* amax) {
   const int64_t total = M * N, total4 = total / 4;
   const float ga = a_gs[0];
+  float vmax = 0.f;
   for (int64_t i4 = (int64_t)blockIdx.x * 256 + threadIdx.x; i4 < total4; i4 += (int64_t)gridDim.x * 256) {
     const int64_t idx = 4 * i4, m = idx / N, n = idx - m * N;
     float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
@@ -1474,7 +1494,10 @@ __global__ void __launch_bounds__(256) splitk_reduce4_kernel(const float* __rest
     } else {
       *reinterpret_cast<float4*>(reinterpret_cast<float*>(out) + m * ldo + n) = o;
     }
+    vmax = fmaxf(fmaxf(vmax, stored_abs(o.x, out_bf16)), stored_abs(o.y, out_bf16));
+    vmax = fmaxf(fmaxf(vmax, stored_abs(o.z, out_bf16)), stored_abs(o.w, out_bf16));
   }
+  if (amax) fold_amax(vmax, amax);
 }
 
 // The same reduction, quantised: each thread takes whole 16-column blocks,
@@ -1708,18 +1731,19 @@ static void launch_expand(const uint8_t* codes, const uint8_t* scales, const int
 
 static void launch_reduce(const float* part, uint32_t splits, int64_t M, int64_t N, const float* a_gs,
                           const float* b_gs, const int32_t* off, int E, void* out, int bf16, int64_t ldo,
-                          hipStream_t st) {
+                          float* amax, hipStream_t st) {
   const bool vec = N % 4 == 0;   // four outputs per thread (partials, rows and output rows 16-B aligned)
   int64_t blocks = (M * N / (vec ? 4 : 1) + 255) / 256;
   if (blocks > 8192) blocks = 8192;
   if (blocks < 1) blocks = 1;
+  if (amax) blocks = kAmaxSlots;  // one partial maximum per slot (grid-stride over the outputs)
   const int slot = launch_begin(KC_REDUCE, st);
   if (vec)
     hipLaunchKernelGGL(splitk_reduce4_kernel, dim3((uint32_t)blocks), dim3(256), 0, st, part, splits, M, N, a_gs,
-                       b_gs, off, E, out, bf16, ldo);
+                       b_gs, off, E, out, bf16, ldo, amax);
   else
     hipLaunchKernelGGL(splitk_reduce_kernel, dim3((uint32_t)blocks), dim3(256), 0, st, part, splits, M, N, a_gs,
-                       b_gs, off, E, out, bf16, ldo);
+                       b_gs, off, E, out, bf16, ldo, amax);
   launch_end(slot, st);
 }
 
@@ -1746,7 +1770,7 @@ size_t store_ws_bytes(int64_t M, int64_t N, int64_t K, int E, bool grouped) {
 }
 
 int store_launch(Operand a, const int32_t* rows, const int32_t* off, int E, int64_t M, Operand w, int64_t N,
-                 int64_t K, void* c, int c_bf16, int64_t ldc, void* ws, hipStream_t st) {
+                 int64_t K, void* c, int c_bf16, int64_t ldc, float* c_amax, void* ws, hipStream_t st) {
   const bool grouped = off != nullptr;
   _Float16* a16 = reinterpret_cast<_Float16*>(ws);
   float* part = reinterpret_cast<float*>(reinterpret_cast<char*>(ws) + align256((size_t)M * K * 2));
@@ -1766,6 +1790,10 @@ int store_launch(Operand a, const int32_t* rows, const int32_t* off, int E, int6
   g.E = E;
   g.m_tiles = pl.m_tiles;
   g.n_tiles = pl.n_tiles;
+  // With an output amax every output goes through the reduction (the
+  // contraction writes partial sums even when K is not split), which takes the
+  // amax of what it stores.
+  g.force_split = c_amax != nullptr;
   if (grouped) launch_cfg<NVFP4_STORE_WN, NVFP4_STORE_TM, NVFP4_GROUPED_STORE_TN, false, true, EPI_STORE>(g, st);
   else if (pl.gv_bpl > 0) launch_gemv<false, EPI_STORE>(g, pl.gv_bpl, st);
   else if (pl.qd_wk > 0) launch_quad<false, EPI_STORE>(g, pl.qd_wk, st);
@@ -1773,7 +1801,8 @@ int store_launch(Operand a, const int32_t* rows, const int32_t* off, int E, int6
   else launch_cfg<NVFP4_STORE_WN, NVFP4_STORE_TM, NVFP4_STORE_TN, false, false, EPI_STORE>(g, st);
   // The reduction always runs (over zero rows when K was not split), so the
   // number of launches never depends on the shape.
-  launch_reduce(part, pl.splits, pl.splits > 1 ? M : 0, N, a.gscale, w.gscale, off, E, c, c_bf16, ldc, st);
+  launch_reduce(part, pl.splits, (pl.splits > 1 || c_amax) ? M : 0, N, a.gscale, w.gscale, off, E, c, c_bf16, ldc,
+                c_amax, st);
   return hipGetLastError() == hipSuccess ? 0 : 7;
 }
 

@@ -11,6 +11,8 @@ namespace nvfp4 {
 
 // Largest number of partial maxima any amax reduction produces.
 constexpr uint32_t kMaxPartials = 4096;
+// Partial maxima of an output-amax epilogue (NVFP4_AMAX_SLOTS in the header).
+constexpr uint32_t kAmaxSlots = 1024;
 
 // Kernel classes of the timing window (same values as the public enum).
 enum KernelClass {
@@ -57,10 +59,11 @@ struct Operand {
 // Store-epilogue contraction C[M][N] = A . W^T * gs_a * gs_w (float32 or bf16),
 // dense (off == nullptr) or expert-grouped (slot s reads activation row
 // rows[s] or s; slots [off[e], off[e+1]) use expert e's weights, stride N*K).
+// c_amax (nullable): kAmaxSlots float32 partial maxima of |C| as stored.
 // Workspace: f16-expanded activations, then split-K partial sums.
 size_t store_ws_bytes(int64_t M, int64_t N, int64_t K, int E, bool grouped);
 int store_launch(Operand a, const int32_t* rows, const int32_t* off, int E, int64_t M, Operand w, int64_t N,
-                 int64_t K, void* c, int c_bf16, int64_t ldc, void* ws, hipStream_t st);
+                 int64_t K, void* c, int c_bf16, int64_t ldc, float* c_amax, void* ws, hipStream_t st);
 
 // H = SiLU(A . G^T * gs_a*gs_g) * (A . U^T * gs_a*gs_u) (float32, row-major
 // [M][N], at the start of the workspace), then its NVFP4 requantisation with a

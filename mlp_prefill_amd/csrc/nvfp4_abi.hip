@@ -174,12 +174,26 @@ int nvfp4_timing_end(int64_t* launches, int64_t* dropped, double* total_ms) {
 
 int nvfp4_quantize_act(const void* x, int x_dtype, int64_t rows, int64_t cols, int64_t ld_x, nvfp4_tensor out,
                        int gs_mode, void* ws, size_t* ws_bytes, void* stream) {
-  if (!dtype_ok(x_dtype) || (gs_mode != NVFP4_GS_COMPUTE && gs_mode != NVFP4_GS_GIVEN)) return NVFP4_ERR_ARG;
+  if (!dtype_ok(x_dtype) || (gs_mode != NVFP4_GS_COMPUTE && gs_mode != NVFP4_GS_GIVEN && gs_mode != NVFP4_GS_FROM_AMAX))
+    return NVFP4_ERR_ARG;
   if (rows < 0 || cols < 0 || cols % 16 != 0 || ld_x < cols) return NVFP4_ERR_SHAPE;
   if (rows * (cols / 16) >= ((int64_t)1 << 31)) return NVFP4_ERR_SHAPE;
   bool query;
-  int rc = workspace(ws, ws_bytes, nvfp4::quantize_ws_bytes(rows, cols, gs_mode), &query);
-  if (rc != NVFP4_OK || query) return rc;
+  int rc;
+  if (gs_mode == NVFP4_GS_FROM_AMAX) {
+    // ws holds the given partial maxima: NVFP4_AMAX_SLOTS float32, 16-byte aligned
+    static_assert(NVFP4_AMAX_SLOTS == nvfp4::kAmaxSlots, "slot count");
+    query = false;
+    if (ws == nullptr && ws_bytes != nullptr) {
+      *ws_bytes = NVFP4_AMAX_SLOTS * sizeof(float);
+      return NVFP4_OK;
+    }
+    if (ws == nullptr || ws_bytes == nullptr || *ws_bytes < NVFP4_AMAX_SLOTS * sizeof(float)) return NVFP4_ERR_WORKSPACE;
+    if (!aligned(ws, 16)) return NVFP4_ERR_ALIGN;
+  } else {
+    rc = workspace(ws, ws_bytes, nvfp4::quantize_ws_bytes(rows, cols, gs_mode), &query);
+    if (rc != NVFP4_OK || query) return rc;
+  }
   if (rows == 0 || cols == 0) return NVFP4_OK;
   if (!x) return NVFP4_ERR_NULL;
   if ((rc = check_tensor(out)) != NVFP4_OK) return rc;
@@ -228,7 +242,7 @@ int nvfp4_rmsnorm_quantize_act(const void* x, int x_dtype, int64_t rows, int64_t
 }
 
 int nvfp4_gemm(nvfp4_tensor a, nvfp4_tensor b, int64_t M, int64_t N, int64_t K, void* c, int c_dtype,
-               int64_t ldc, void* ws, size_t* ws_bytes, void* stream) {
+               int64_t ldc, float* c_amax, void* ws, size_t* ws_bytes, void* stream) {
   if (!dtype_ok(c_dtype)) return NVFP4_ERR_ARG;
   if (M < 0 || N < 0 || K <= 0 || K % 128 != 0 || ldc < N) return NVFP4_ERR_SHAPE;
   if (M * (K / 16) >= ((int64_t)1 << 31)) return NVFP4_ERR_SHAPE;
@@ -238,9 +252,9 @@ int nvfp4_gemm(nvfp4_tensor a, nvfp4_tensor b, int64_t M, int64_t N, int64_t K, 
   if (M == 0 || N == 0) return NVFP4_OK;
   if ((rc = check_tensor(a)) != NVFP4_OK || (rc = check_tensor(b)) != NVFP4_OK) return rc;
   if (!c) return NVFP4_ERR_NULL;
-  if (!aligned(c, 16) || (ldc * elem_size(c_dtype)) % 16 != 0) return NVFP4_ERR_ALIGN;
+  if (!aligned(c, 16) || (ldc * elem_size(c_dtype)) % 16 != 0 || !aligned(c_amax, 16)) return NVFP4_ERR_ALIGN;
   if ((rc = check_device()) != NVFP4_OK) return rc;
-  return nvfp4::store_launch(op(a), nullptr, nullptr, 1, M, op(b), N, K, c, c_dtype == NVFP4_BF16, ldc, ws,
+  return nvfp4::store_launch(op(a), nullptr, nullptr, 1, M, op(b), N, K, c, c_dtype == NVFP4_BF16, ldc, c_amax, ws,
                              reinterpret_cast<hipStream_t>(stream));
 }
 
@@ -261,7 +275,7 @@ int nvfp4_mlp_gu_act(nvfp4_tensor x, nvfp4_tensor w_gate, nvfp4_tensor w_up, int
 }
 
 int nvfp4_mlp_down(nvfp4_tensor h, nvfp4_tensor w_down, int64_t T, int64_t I, int64_t K, void* y, int y_dtype,
-                   int64_t ldy, void* ws, size_t* ws_bytes, void* stream) {
+                   int64_t ldy, float* y_amax, void* ws, size_t* ws_bytes, void* stream) {
   if (!dtype_ok(y_dtype)) return NVFP4_ERR_ARG;
   if (T < 0 || I <= 0 || K <= 0 || I % 128 != 0 || ldy < K) return NVFP4_ERR_SHAPE;
   if (T * (I / 16) >= ((int64_t)1 << 31)) return NVFP4_ERR_SHAPE;
@@ -271,10 +285,10 @@ int nvfp4_mlp_down(nvfp4_tensor h, nvfp4_tensor w_down, int64_t T, int64_t I, in
   if (T == 0) return NVFP4_OK;
   if ((rc = check_tensor(h)) != NVFP4_OK || (rc = check_tensor(w_down)) != NVFP4_OK) return rc;
   if (!y) return NVFP4_ERR_NULL;
-  if (!aligned(y, 16) || (ldy * elem_size(y_dtype)) % 16 != 0) return NVFP4_ERR_ALIGN;
+  if (!aligned(y, 16) || (ldy * elem_size(y_dtype)) % 16 != 0 || !aligned(y_amax, 16)) return NVFP4_ERR_ALIGN;
   if ((rc = check_device()) != NVFP4_OK) return rc;
-  return nvfp4::store_launch(op(h), nullptr, nullptr, 1, T, op(w_down), K, I, y, y_dtype == NVFP4_BF16, ldy, ws,
-                             reinterpret_cast<hipStream_t>(stream));
+  return nvfp4::store_launch(op(h), nullptr, nullptr, 1, T, op(w_down), K, I, y, y_dtype == NVFP4_BF16, ldy, y_amax,
+                             ws, reinterpret_cast<hipStream_t>(stream));
 }
 
 int nvfp4_mlp_gu_act_static(nvfp4_tensor x, nvfp4_tensor w_gate, nvfp4_tensor w_up, int64_t T, int64_t K, int64_t I,
@@ -377,7 +391,7 @@ int nvfp4_grouped_gemm(nvfp4_tensor a, const int32_t* a_rows, const int32_t* gro
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
   if (!glu)
     return nvfp4::store_launch(op(a), a_rows, group_offsets, E, M, op(w0), N, K, out, out_dtype == NVFP4_BF16,
-                               ld_out, ws, st);
+                               ld_out, nullptr, ws, st);
   if (gluq)
     return nvfp4::glu_static_launch(op(a), a_rows, group_offsets, E, M, op(w0), op(w1), N, K, out_q.codes,
                                     out_q.scales, out_q.gscale, ws, st);

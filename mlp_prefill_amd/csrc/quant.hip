@@ -205,6 +205,7 @@ static uint32_t amax_grid(uint32_t nblocks) {
 }
 
 size_t quantize_ws_bytes(int64_t rows, int64_t cols, int gs_mode) {
+  if (gs_mode == 2) return kAmaxSlots * sizeof(float);   // the given partial maxima
   if (gs_mode != 0) return 0;
   (void)rows; (void)cols;
   return kMaxPartials * sizeof(float);
@@ -248,6 +249,16 @@ static int quantize_launch_t(const T* x, int64_t rows, int64_t cols, int64_t ld,
 int quantize_launch(const void* x, int x_dtype, int64_t rows, int64_t cols, int64_t ld, uint8_t* codes,
                     uint8_t* scales, float* gs, int gs_mode, void* ws, hipStream_t st) {
   float* partials = reinterpret_cast<float*>(ws);
+  if (gs_mode == 2) {
+    // the workspace holds kAmaxSlots partial maxima of |x| (written on the
+    // device by an earlier call's output-amax epilogue): the quantise kernel
+    // reduces them, forms the global scale and quantises, in one launch
+    if (x_dtype == 1)
+      return quantize_launch_t(reinterpret_cast<const uint16_t*>(x), rows, cols, ld, codes, scales, gs, 0, nullptr,
+                               partials, kAmaxSlots, st);
+    return quantize_launch_t(reinterpret_cast<const float*>(x), rows, cols, ld, codes, scales, gs, 0, nullptr,
+                             partials, kAmaxSlots, st);
+  }
   if (x_dtype == 1)
     return quantize_launch_t(reinterpret_cast<const uint16_t*>(x), rows, cols, ld, codes, scales, gs,
                              gs_mode, partials, nullptr, 0, st);

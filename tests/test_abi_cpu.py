@@ -69,6 +69,16 @@ def test_quantize_validation():
     assert q(FAKE, m.BF16, 4, 32, 32, _t(), 0, FAKE, None, None) == m.ERR_WORKSPACE
     # zero rows: a successful no-op even with NULL data pointers
     assert q(None, m.BF16, 0, 32, 32, nvfp4_tensor(0, 0, 0), 0, FAKE, ctypes.byref(sz), None) == m.OK
+    # NVFP4_GS_FROM_AMAX: ws holds the AMAX_SLOTS partial maxima (float32, 16-byte aligned)
+    slots = ctypes.c_size_t(4 * m.AMAX_SLOTS)
+    assert q(FAKE, m.BF16, 4, 32, 32, _t(), m.GS_FROM_AMAX, None, None, None) == m.ERR_WORKSPACE
+    assert q(FAKE, m.BF16, 4, 32, 32, _t(), m.GS_FROM_AMAX, FAKE, ctypes.byref(ctypes.c_size_t(4)), None) \
+        == m.ERR_WORKSPACE
+    assert q(FAKE, m.BF16, 4, 32, 32, _t(), m.GS_FROM_AMAX, FAKE + 4, ctypes.byref(slots), None) == m.ERR_ALIGN
+    s = _size()
+    assert q(None, m.BF16, 4, 32, 32, nvfp4_tensor(0, 0, 0), m.GS_FROM_AMAX, None, ctypes.byref(s), None) == m.OK
+    assert s.value == 4 * m.AMAX_SLOTS
+    assert m.lib.nvfp4_quantize_act_noalloc(FAKE, m.BF16, 4, 32, 32, _t(), m.GS_FROM_AMAX, None) == m.ERR_ARG
 
 
 def test_quantize_noalloc_validation():
@@ -104,27 +114,29 @@ def test_gemm_and_down_validation():
     g = m.lib.nvfp4_gemm
     big = ctypes.c_size_t(1 << 30)
     ws = (FAKE, ctypes.byref(big), None)
-    assert g(_t(), _t(), 4, 8, 100, FAKE, m.F32, 8, *ws) == m.ERR_SHAPE        # K % 128
-    assert g(_t(), _t(), 4, 8, 128, FAKE, 5, 8, *ws) == m.ERR_ARG
-    assert g(_t(), _t(), 4, 8, 128, FAKE, m.F32, 4, *ws) == m.ERR_SHAPE        # ldc < N
-    assert g(_t(), _t(), 4, 8, 128, None, m.F32, 8, *ws) == m.ERR_NULL
-    assert g(_t(), _t(), 4, 6, 128, FAKE, m.F32, 6, *ws) == m.ERR_ALIGN        # row stride 24 B
-    assert g(_t(), _t(s=FAKE + 4), 4, 8, 128, FAKE, m.F32, 8, *ws) == m.ERR_ALIGN
-    assert g(_t(), _t(), 4, 8, 128, FAKE, m.F32, 8, None, None, None) == m.ERR_WORKSPACE
-    assert g(_t(), _t(), 0, 8, 128, None, m.F32, 8, None, None, None) == m.OK   # empty
+    assert g(_t(), _t(), 4, 8, 100, FAKE, m.F32, 8, None, *ws) == m.ERR_SHAPE        # K % 128
+    assert g(_t(), _t(), 4, 8, 128, FAKE, 5, 8, None, *ws) == m.ERR_ARG
+    assert g(_t(), _t(), 4, 8, 128, FAKE, m.F32, 4, None, *ws) == m.ERR_SHAPE        # ldc < N
+    assert g(_t(), _t(), 4, 8, 128, None, m.F32, 8, None, *ws) == m.ERR_NULL
+    assert g(_t(), _t(), 4, 6, 128, FAKE, m.F32, 6, None, *ws) == m.ERR_ALIGN        # row stride 24 B
+    assert g(_t(), _t(s=FAKE + 4), 4, 8, 128, FAKE, m.F32, 8, None, *ws) == m.ERR_ALIGN
+    assert g(_t(), _t(), 4, 8, 128, FAKE, m.F32, 8, None, None, None, None) == m.ERR_WORKSPACE
+    assert g(_t(), _t(), 0, 8, 128, None, m.F32, 8, None, None, None, None) == m.OK   # empty
     s = _size()
-    assert g(nvfp4_tensor(0, 0, 0), nvfp4_tensor(0, 0, 0), 1024, 5120, 17408, None, m.F32, 5120, None,
+    assert g(nvfp4_tensor(0, 0, 0), nvfp4_tensor(0, 0, 0), 1024, 5120, 17408, None, m.F32, 5120, None, None,
              ctypes.byref(s), None) == m.OK
     # f16 activation copy + float32 partials of the 3 K splits: 1024 tokens in
     # 64 x 256 tiles make 16 x 20 = 320 work-groups, split 3 ways to 960
     assert s.value == 1024 * 17408 * 2 + 3 * 1024 * 5120 * 4
-    assert g(nvfp4_tensor(0, 0, 0), nvfp4_tensor(0, 0, 0), 4096, 4096, 4096, None, m.F32, 4096, None,
+    assert g(nvfp4_tensor(0, 0, 0), nvfp4_tensor(0, 0, 0), 4096, 4096, 4096, None, m.F32, 4096, None, None,
              ctypes.byref(s), None) == m.OK
     assert s.value == 4096 * 4096 * 2 + 4096 * 4096 * 4   # 64 x 16 = 1024 tiles: one split
+    assert g(_t(), _t(), 4, 8, 128, FAKE, m.F32, 8, FAKE + 4, *ws) == m.ERR_ALIGN  # c_amax
     d = m.lib.nvfp4_mlp_down
-    assert d(_t(), _t(), 4, 100, 64, FAKE, m.F32, 64, *ws) == m.ERR_SHAPE      # I % 128
-    assert d(_t(), _t(), 4, 128, 64, FAKE, m.BF16, 60, *ws) == m.ERR_SHAPE     # ldy < K
-    assert d(_t(), _t(), 4, 128, 64, None, m.F32, 64, *ws) == m.ERR_NULL
+    assert d(_t(), _t(), 4, 128, 64, FAKE, m.F32, 64, FAKE + 8, *ws) == m.ERR_ALIGN  # y_amax
+    assert d(_t(), _t(), 4, 100, 64, FAKE, m.F32, 64, None, *ws) == m.ERR_SHAPE      # I % 128
+    assert d(_t(), _t(), 4, 128, 64, FAKE, m.BF16, 60, None, *ws) == m.ERR_SHAPE     # ldy < K
+    assert d(_t(), _t(), 4, 128, 64, None, m.F32, 64, None, *ws) == m.ERR_NULL
 
 
 def test_gu_act_validation_and_workspace():
@@ -158,7 +170,7 @@ def test_static_scale_entry_points_validation_and_workspace():
     d = m.lib.nvfp4_mlp_down_quant
     assert d(z, z, 1024, 17408, 5120, z, None, ctypes.byref(s), None) == m.OK
     s2 = _size()
-    assert m.lib.nvfp4_mlp_down(z, z, 1024, 17408, 5120, None, m.F32, 5120, None, ctypes.byref(s2), None) == m.OK
+    assert m.lib.nvfp4_mlp_down(z, z, 1024, 17408, 5120, None, m.F32, 5120, None, None, ctypes.byref(s2), None) == m.OK
     assert s.value == s2.value                            # same split plan as the float32 down projection
     assert d(_t(), _t(), 4, 100, 64, _t(), FAKE, ctypes.byref(big), None) == m.ERR_SHAPE      # I % 128
     assert d(_t(), _t(), 4, 128, 40, _t(), FAKE, ctypes.byref(big), None) == m.ERR_SHAPE      # K % 16
@@ -202,9 +214,9 @@ def test_valid_calls_report_missing_device_and_launch_nothing():
     sz = ctypes.c_size_t(1 << 20)
     assert m.lib.nvfp4_quantize_act(FAKE, m.BF16, 4, 32, 32, _t(), 0, FAKE, ctypes.byref(sz), None) == m.ERR_DEVICE
     big = ctypes.c_size_t(1 << 24)
-    assert m.lib.nvfp4_gemm(_t(), _t(), 4, 8, 128, FAKE, m.F32, 8, FAKE, ctypes.byref(big), None) == m.ERR_DEVICE
+    assert m.lib.nvfp4_gemm(_t(), _t(), 4, 8, 128, FAKE, m.F32, 8, None, FAKE, ctypes.byref(big), None) == m.ERR_DEVICE
     assert m.lib.nvfp4_mlp_gu_act(_t(), _t(), _t(), 4, 128, 128, _t(), FAKE, ctypes.byref(big), None) == m.ERR_DEVICE
-    assert m.lib.nvfp4_mlp_down(_t(), _t(), 4, 128, 64, FAKE, m.F32, 64, FAKE, ctypes.byref(big), None) == m.ERR_DEVICE
+    assert m.lib.nvfp4_mlp_down(_t(), _t(), 4, 128, 64, FAKE, m.F32, 64, None, FAKE, ctypes.byref(big), None) == m.ERR_DEVICE
     assert m.lib.nvfp4_mlp_gu_act_static(_t(), _t(), _t(), 4, 128, 128, _t(), FAKE, ctypes.byref(big),
                                          None) == m.ERR_DEVICE
     assert m.lib.nvfp4_mlp_down_quant(_t(), _t(), 4, 128, 64, _t(), FAKE, ctypes.byref(big), None) == m.ERR_DEVICE

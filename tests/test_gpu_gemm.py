@@ -77,3 +77,35 @@ def test_gemm_is_deterministic():
     y1 = _run(a, b, 200, 384, torch.float32)
     y2 = _run(a, b, 200, 384, torch.float32)
     assert np.array_equal(y1, y2)
+
+
+AMAX_SHAPES = [(1, 512, 1024), (2, 640, 3072), (5, 512, 2048), (20, 384, 256), (300, 640, 512), (1024, 5120, 17408)]
+
+
+@pytest.mark.parametrize("m,n,k", AMAX_SHAPES, ids=[f"{m}x{n}x{k}" for m, n, k in AMAX_SHAPES])
+def test_output_amax_epilogue(m, n, k):
+    """The largest of the c_amax slots is max|c| as stored, bit-exact (float32
+    and bf16 outputs); every slot is written (the buffer is pre-filled with a
+    larger value); the output itself is unchanged by asking for it; the next
+    quantisation formed from the slots (NVFP4_GS_FROM_AMAX, one launch) equals
+    the computed-scale quantisation."""
+    import mlp_prefill_amd as mm
+    announce(f"output amax {m}x{n}x{k}")
+    a, b, ra, rb = _pair(m, n, k, 900 + m, 950 + n)
+    for dt in (torch.float32, torch.bfloat16):
+        c0 = torch.empty((m, n), dtype=dt, device="cuda")
+        mm.nvfp4_gemm(a, b, c0)
+        c = torch.empty((m, n), dtype=dt, device="cuda")
+        amax = mm.amax_buffer().fill_(3.0e38)
+        mm.nvfp4_gemm(a, b, c, amax=amax)
+        torch.cuda.synchronize()
+        assert torch.equal(c, c0), f"{dt}: output changed by the amax epilogue"
+        want = c.float().abs().max()
+        assert amax.max().item() == want.item(), (dt, amax.max().item(), want.item())
+        if n % 16 == 0:
+            q1, q2 = mm.NVFP4.empty(m, n), mm.NVFP4.empty(m, n)
+            mm.nvfp4_quantize_act(c, q1)
+            before = mm.launch_count()
+            mm.nvfp4_quantize_act(c, q2, gs_mode=mm.GS_FROM_AMAX, ws=amax)
+            assert mm.launch_count() - before == 1
+            assert_nvfp4_equal(to_host(q2), to_host(q1), f"{dt} quantise from the output amax")

@@ -2,11 +2,14 @@
 
 The long-prefill workload (hidden 5120, intermediate 17408, 4 layers,
 1024-token ubatches) on a reduced number of tokens: two 128-token ubatches
-through all four full-size layers.  Layer 1 is compared with the oracle end
-to end; every later layer is compared with the oracle applied to the layer's
-actual (device) bf16 input, so that legitimate requantisation flips in one
-layer are not charged to the next.  The drift of the whole 4-layer chain
-against the pure oracle chain is reported.
+through all four full-size layers, chained as the benchmark chains them: each
+layer's down projection also writes max|y|, and the next layer quantises its
+input with the global scale formed from that amax (one launch).  Layer 1 is
+compared with the oracle end to end; every later layer is compared with the
+oracle applied to the layer's actual (device) bf16 input, so that legitimate
+requantisation flips in one layer are not charged to the next; every layer's
+x~ must equal the oracle's quantisation of that input bit for bit.  The drift
+of the whole 4-layer chain against the pure oracle chain is reported.
 """
 import numpy as np
 import pytest
@@ -16,7 +19,8 @@ from oracle import gemm as ogemm
 from oracle import mlp as omlp
 from oracle import quant
 from synthetic import WORKLOADS, bf16_bits_to_f32, bf16_normal, layer_seeds
-from tests.gpu_util import (announce, assert_bf16_rounding_close, bf16_tensor_to_f32, dev_bf16, dev_quantize,
+from tests.gpu_util import (announce, assert_bf16_rounding_close, assert_nvfp4_equal, bf16_tensor_to_f32, dev_bf16,
+                            dev_quantize,
                             legit_requant_flips, max_norm_err, record, require_gpu, to_host)
 
 pytestmark = pytest.mark.gpu
@@ -47,13 +51,19 @@ def test_stacked_layers_device_resident_bf16_chain():
     ws_gu = torch.empty(m.mlp_gu_act_ws_bytes(ub, k, i), dtype=torch.uint8, device="cuda")
     outs = [[None] * nl for _ in range(nub)]
     hqs = [[None] * nl for _ in range(nub)]
+    xqs = [[None] * nl for _ in range(nub)]
+    amax = m.amax_buffer()
     for u in range(nub):
         cur = x_all[u * ub:(u + 1) * ub]
         for li in range(nl):
-            m.nvfp4_quantize_act(cur, xq)
+            if li == 0:
+                m.nvfp4_quantize_act(cur, xq)
+            else:                                # the previous down projection's max|y|
+                m.nvfp4_quantize_act(cur, xq, gs_mode=m.GS_FROM_AMAX, ws=amax)
             m.nvfp4_mlp_gu_act(xq, wdev[li][0], wdev[li][1], hq, ws=ws_gu)
             y = torch.empty((ub, k), dtype=torch.bfloat16, device="cuda")
-            m.nvfp4_mlp_down(hq, wdev[li][2], y)
+            m.nvfp4_mlp_down(hq, wdev[li][2], y, amax=amax)
+            xqs[u][li] = to_host(xq)
             hqs[u][li] = to_host(hq)
             outs[u][li] = y
             cur = y                              # stays on the device
@@ -64,6 +74,7 @@ def test_stacked_layers_device_resident_bf16_chain():
         layer_in = x0[u * ub:(u + 1) * ub]
         for li in range(nl):
             ref = omlp.mlp(layer_in, *wref[li])
+            assert_nvfp4_equal(xqs[u][li], ref["xq"], f"ubatch {u} layer {li} x~")
             got_hq = hqs[u][li]
             nflip, nsflip = legit_requant_flips(ref["h"].astype(np.float32), got_hq, ref["hq"])
             corr = ref["y"] + ogemm.gemm(got_hq, wref[li][2]) - ogemm.gemm(ref["hq"], wref[li][2])
