@@ -386,13 +386,29 @@ def decode_line(m):
         run_static()
         static_launches = m.launch_count() - b0
         cold_s = float(np.median(time_events(run_static, 20, scrub=lambda: scrub_buf.sum())))
+        # the whole-MLP call (one entry point, the decode path's four launches)
+        ws_f = torch.empty(m.mlp_ws_bytes(tt, K_HID, lay.w[0].rows), dtype=torch.uint8, device="cuda")
+
+        def run_fused():
+            m.nvfp4_mlp(x, lay.w[0], lay.w[1], lay.w[2], run.xq, run.hq, y, ws=ws_f)
+        run_fused()
+        b0 = m.launch_count()
+        run_fused()
+        fused_launches = m.launch_count() - b0
+        cold_f = float(np.median(time_events(run_fused, 20, scrub=lambda: scrub_buf.sum())))
+        hot_f = float(np.median(time_events(run_fused, 50)))
         dec[f"T{tt}"] = {"ms_hot": hot, "ms_cold": cold, "hbm_gbs_cold": wbytes / (cold * 1e-3) / 1e9,
                          "hbm_gbs_hot": wbytes / (hot * 1e-3) / 1e9,
                          "frac_hbm_peak_cold": wbytes / (cold * 1e-3) / 1e9 / PEAK_HBM_GBS,
+                         "whole_mlp_ms_cold": cold_f, "whole_mlp_ms_hot": hot_f,
+                         "whole_mlp_hbm_gbs_cold": wbytes / (cold_f * 1e-3) / 1e9,
+                         "whole_mlp_frac_hbm_peak_cold": wbytes / (cold_f * 1e-3) / 1e9 / PEAK_HBM_GBS,
+                         "whole_mlp_launches": fused_launches,
                          "static_gs_ms_cold": cold_s, "static_gs_hbm_gbs_cold": wbytes / (cold_s * 1e-3) / 1e9,
                          "static_gs_launches": static_launches}
     dec["launches_per_call"] = launches
     dec["t5_over_t1_cold"] = dec["T5"]["ms_cold"] / dec["T1"]["ms_cold"]
+    dec["whole_mlp_t5_over_t1_cold"] = dec["T5"]["whole_mlp_ms_cold"] / dec["T1"]["whole_mlp_ms_cold"]
     del lay, scrub_buf
     return dec
 

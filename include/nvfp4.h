@@ -248,6 +248,40 @@ int nvfp4_mlp_down(nvfp4_tensor h, nvfp4_tensor w_down, int64_t T, int64_t I, in
                    void *y, int y_dtype, int64_t ldy, float *y_amax, void *ws, size_t *ws_bytes, void *stream);
 
 /*
+ * nvfp4_mlp -- one whole MLP call: y = down(requant(SiLU(x~ . Wg~^T) *
+ * (x~ . Wu~^T))) with x~ = NVFP4(x), i.e. nvfp4_quantize_act (computed
+ * global scale) + nvfp4_mlp_gu_act + nvfp4_mlp_down in one call, the MLP
+ * shard run over T tokens of [vllm] "Problem" done as one launch set per
+ * batch ([vllm] Fix directions 1).  x~ and H~ (codes, scales, global scales)
+ * are written to x_q and h_q as the separate calls write them, and y is
+ * bit-identical to theirs.
+ *   x      : float32 or bf16 (x_dtype) [T][K], row stride ld_x >= K
+ *   x_amax : NULL (gs_x from max|x| on the device), or the NVFP4_AMAX_SLOTS
+ *            partial maxima of |x| an earlier call wrote (the previous
+ *            layer's y_amax): gs_x is formed from them, no amax pass
+ *   w_gate, w_up : [I][K] NVFP4;  w_down : [K][I] NVFP4;  K, I multiples of 128
+ *   x_q    : [T][K] NVFP4 out;  h_q : [T][I] NVFP4 out
+ *   y      : float32 or bf16 (y_dtype) [T][K], row stride ldy >= K
+ *   y_amax : NULL, or NVFP4_AMAX_SLOTS float32 receiving partial maxima of
+ *            |y| as stored (every slot written), for the next layer's x_amax
+ *   ws     : required (size query as usual); contents unspecified on return
+ * Decode batches -- T <= 8 with both projections on the weight streams (T <=
+ * 2 with K >= 1024, or 3 <= T <= 8 with K a multiple of 1024; I >= 1024, or a
+ * multiple of 1024 for 3 <= T <= 8; T * K <= 65536) -- take four launches:
+ * (1) quantise x in one work-group, which also clears the per-column-group
+ * tickets and the y_amax slots; (2) the gate/up weight stream with the
+ * SiLU*up epilogue, float32 H and its partial maxima; (3) requantisation of H;
+ * (4) the down weight stream, whose K splits are added, in split order, by
+ * the last-arriving wave (or work-group) of each column group after an
+ * agent-scope fence and a ticket increment -- nothing waits for anything, and
+ * no reduction launch follows.  Other shapes take the separate calls' launch
+ * sequence (seven or eight launches; one fewer with x_amax).
+ */
+int nvfp4_mlp(const void *x, int x_dtype, int64_t ld_x, const float *x_amax, int64_t T, int64_t K, int64_t I,
+              nvfp4_tensor w_gate, nvfp4_tensor w_up, nvfp4_tensor w_down, nvfp4_tensor x_q, nvfp4_tensor h_q,
+              void *y, int y_dtype, int64_t ldy, float *y_amax, void *ws, size_t *ws_bytes, void *stream);
+
+/*
  * nvfp4_mlp_gu_act_static -- nvfp4_mlp_gu_act with a static global scale
  * for H~.  [dsv4] P0, fix 1: the activation global scales are measured once
  * by a warm-up pass (for instance the scale nvfp4_mlp_gu_act wrote to its

@@ -47,6 +47,8 @@ _sig = {
                          ctypes.POINTER(ctypes.c_size_t), _vp],
     "nvfp4_mlp_down": [nvfp4_tensor, nvfp4_tensor, _i64, _i64, _i64, _vp, ctypes.c_int, _i64, _vp, _vp,
                        ctypes.POINTER(ctypes.c_size_t), _vp],
+    "nvfp4_mlp": [_vp, ctypes.c_int, _i64, _vp, _i64, _i64, _i64, nvfp4_tensor, nvfp4_tensor, nvfp4_tensor,
+                  nvfp4_tensor, nvfp4_tensor, _vp, ctypes.c_int, _i64, _vp, _vp, ctypes.POINTER(ctypes.c_size_t), _vp],
     "nvfp4_mlp_gu_act_static": [nvfp4_tensor, nvfp4_tensor, nvfp4_tensor, _i64, _i64, _i64, nvfp4_tensor, _vp,
                                 ctypes.POINTER(ctypes.c_size_t), _vp],
     "nvfp4_mlp_down_quant": [nvfp4_tensor, nvfp4_tensor, _i64, _i64, _i64, nvfp4_tensor, _vp,
@@ -275,6 +277,31 @@ def nvfp4_mlp_gu_act(x, w_gate, w_up, h_out, ws=None, stream=None):
     _check(_lib.nvfp4_mlp_gu_act(x.c(), w_gate.c(), w_up.c(), t, k, i, h_out.c(), _ptr(ws), ctypes.byref(sz),
                                  _stream(stream)), "nvfp4_mlp_gu_act")
     return ws
+
+
+def mlp_ws_bytes(t, k, i):
+    """Workspace bytes nvfp4_mlp needs for T tokens, hidden k, intermediate i."""
+    size = ctypes.c_size_t(0)
+    z = _null_tensor()
+    _check(_lib.nvfp4_mlp(_vp(0), BF16, k, _vp(0), t, k, i, z, z, z, z, z, _vp(0), F32, k, _vp(0), _vp(0),
+                          ctypes.byref(size), _vp(0)), "workspace query")
+    return size.value
+
+
+def nvfp4_mlp(x, w_gate, w_up, w_down, x_q, h_q, y, x_amax=None, y_amax=None, ws=None, stream=None):
+    """One whole MLP call (see include/nvfp4.h): x [T, K] (bf16 or float32) -> y [T, K]
+    (float32 or bf16); x_q and h_q receive x~ and H~; x_amax / y_amax are amax buffers."""
+    t, k = x.shape
+    i = w_gate.rows
+    if x.stride(1) != 1 or y.stride(1) != 1:
+        raise ValueError("x and y must be row-major")
+    need = mlp_ws_bytes(t, k, i)
+    ws = _scratch(need, ws, x.device, stream)
+    sz = ctypes.c_size_t(ws.numel())
+    _check(_lib.nvfp4_mlp(_ptr(x), _dtype_code(x), x.stride(0), _ptr(x_amax), t, k, i, w_gate.c(), w_up.c(),
+                          w_down.c(), x_q.c(), h_q.c(), _ptr(y), _dtype_code(y), y.stride(0), _ptr(y_amax), _ptr(ws),
+                          ctypes.byref(sz), _stream(stream)), "nvfp4_mlp")
+    return y
 
 
 def mlp_gu_act_static_ws_bytes(t, k, i):

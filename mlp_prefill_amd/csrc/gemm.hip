@@ -78,7 +78,63 @@ struct GemmArgs {
   uint8_t* q_codes;       // EPI_GLUQ output [M][N] NVFP4 and its given global scale
   uint8_t* q_scales;
   const float* q_gs;
+  // Split-K finished inside the weight streams (store epilogue, split_out
+  // written): one ticket per column group, cleared by an earlier launch; the
+  // wave (or work-group) of a group that arrives last adds the group's partial
+  // sums in split order and stores the outputs.  amax_slots (nullable, cleared
+  // too): max |stored output| of each group folded into slot group % kAmaxSlots.
+  uint32_t* tickets;
+  float* amax_slots;
 };
+
+// Partial sums shared between the work-groups of one launch go through the
+// device-coherent level (agent-scope accesses: the stores write through the
+// XCD's L2, the loads miss in it), so no L2 write-back or invalidation is
+// needed between them -- agent-scope fences per wave cost about 25 ns each,
+// serialised, which is most of a decode call at thousands of waves.  The
+// ordering that a fence would give comes from the hardware: a writer waits
+// until its stores are acknowledged (vmcnt) before it takes its ticket, and
+// the last arriver issues its loads only after its ticket returned.
+__device__ __forceinline__ void store_coherent(float* p, float v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float load_coherent(const float* p) {
+  return __hip_atomic_load(const_cast<float*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+// every store of this wave acknowledged (and no memory access moved across)
+__device__ __forceinline__ void stores_done() { asm volatile("s_waitcnt vmcnt(0)" : : : "memory"); }
+
+// Output (t, c) of a split-K store: the partial sums in split order (the
+// order and arithmetic of the reduction kernels), scaled by gs_a * gs_b and
+// stored; returns |stored value|.  Loads go eight splits at a time.
+__device__ __forceinline__ float finish_output(const GemmArgs& p, int64_t t, int64_t c) {
+  const int64_t plane = p.M * p.N, idx = t * p.N + c;
+  float acc = 0.f;
+  uint32_t s = 0;
+  for (; s + 8u <= p.splits; s += 8u) {
+    float v[8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) v[k] = load_coherent(p.split_out + (int64_t)(s + k) * plane + idx);
+#pragma unroll
+    for (int k = 0; k < 8; ++k) acc += v[k];
+  }
+  for (; s < p.splits; ++s) acc += load_coherent(p.split_out + (int64_t)s * plane + idx);
+  const float v = acc * (p.a_gs[0] * p.b_gs[0]);
+  if (p.c_bf16) {
+    const uint32_t b = f32_to_bf16_bits(v);
+    reinterpret_cast<uint16_t*>(p.c)[t * p.ldc + c] = (uint16_t)b;
+    return fabsf(__uint_as_float(b << 16));
+  }
+  reinterpret_cast<float*>(p.c)[t * p.ldc + c] = v;
+  return fabsf(v);
+}
+
+// Ticket of a column group after this caller's partial sums are stored and
+// acknowledged (one lane per wave, or one thread per work-group); true for the
+// arrival that completes the group.  No waiting: the others just leave.
+__device__ __forceinline__ bool last_arrival(uint32_t* ticket, uint32_t count) {
+  return __hip_atomic_fetch_add(ticket, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == count - 1u;
+}
 
 // ---- expansion of the activation operand ------------------------------------------
 // out[r][k] = code * scale (f16, exact) of row src(r) = rows ? rows[r] : r.
@@ -1172,12 +1228,16 @@ __global__ void __launch_bounds__(256) gemv_kernel(GemmArgs p) {
       }
     }
   } else {
+    const bool part = p.splits > 1 || p.force_split;
     if (active) {
-      if (p.splits > 1 || p.force_split) {
+      if (part) {
         float* dst = p.split_out + (split * M + lane) * N + n0;
 #pragma unroll
-        for (int c = 0; c < kGvCols; ++c)
-          if (n0 + c < N) dst[c] = v[c];
+        for (int c = 0; c < kGvCols; ++c) {
+          if (n0 + c >= N) continue;
+          if (p.tickets != nullptr) store_coherent(dst + c, v[c]);
+          else dst[c] = v[c];
+        }
       } else {
         const float alpha = p.a_gs[0] * p.b_gs[0];
 #pragma unroll
@@ -1188,6 +1248,25 @@ __global__ void __launch_bounds__(256) gemv_kernel(GemmArgs p) {
             reinterpret_cast<uint16_t*>(p.c)[lane * p.ldc + n0 + c] = (uint16_t)f32_to_bf16_bits(o);
           else
             reinterpret_cast<float*>(p.c)[lane * p.ldc + n0 + c] = o;
+        }
+      }
+    }
+    if (part && p.tickets != nullptr) {
+      // split-K finish: the wave of this column group that arrives last adds
+      // every split's partial sums (lane = token * kGvCols + column)
+      stores_done();
+      const int64_t grp = n0 / kGvCols;
+      uint32_t last = 0;
+      if (lane == 0) last = last_arrival(p.tickets + grp, p.splits) ? 1u : 0u;
+      last = (uint32_t)__builtin_amdgcn_readfirstlane((int)last);
+      if (last) {
+        const int64_t t = lane / kGvCols, c = n0 + lane % kGvCols;
+        float am = 0.f;
+        if (t < M && t < T && c < N) am = finish_output(p, t, c);
+        if (p.amax_slots != nullptr) {
+          am = wave_max(am);
+          if (lane == 0)
+            atomicMax(reinterpret_cast<unsigned int*>(p.amax_slots + grp % kAmaxSlots), __float_as_uint(am));
         }
       }
     }
@@ -1223,6 +1302,7 @@ __global__ void __launch_bounds__(kQdMaxWaves * 64) quad_kernel(GemmArgs p, int 
   __shared__ float red[kQdMaxWaves * 4 * NV * 4];
   __shared__ float hq[EPI == EPI_GLUQ ? 8 * kQdCols : 1];
   __shared__ float redmax[kQdMaxWaves];
+  __shared__ uint32_t last_wg;
   const int lane = threadIdx.x & 63;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int j = lane & 3, s = lane >> 2;
@@ -1387,11 +1467,33 @@ __global__ void __launch_bounds__(kQdMaxWaves * 64) quad_kernel(GemmArgs p, int 
       if (t >= M || c >= N) continue;
       const float v = total(vi, jj);
       if (part) {
-        p.split_out[(split * M + t) * N + c] = v;
+        if (p.tickets != nullptr) store_coherent(p.split_out + (split * M + t) * N + c, v);
+        else p.split_out[(split * M + t) * N + c] = v;
       } else if (p.c_bf16) {
         reinterpret_cast<uint16_t*>(p.c)[t * p.ldc + c] = (uint16_t)f32_to_bf16_bits(v * alpha);
       } else {
         reinterpret_cast<float*>(p.c)[t * p.ldc + c] = v * alpha;
+      }
+    }
+    if (part && p.tickets != nullptr) {
+      // split-K finish: the work-group of this column tile that arrives last
+      // adds every split's partial sums (one thread per output)
+      const int64_t ct = blockIdx.x - split * ctiles;
+      stores_done();
+      __syncthreads();
+      if (threadIdx.x == 0) last_wg = last_arrival(p.tickets + ct, p.splits) ? 1u : 0u;
+      __syncthreads();
+      if (last_wg) {
+        float am = 0.f;
+        for (int o = (int)threadIdx.x; o < (int)M * kQdCols; o += nthreads) {
+          const int64_t t = o / kQdCols, c = n0 + o % kQdCols;
+          if (c < N) am = fmaxf(am, finish_output(p, t, c));
+        }
+        if (p.amax_slots != nullptr) {
+          am = block_max(am, redmax);
+          if (threadIdx.x == 0)
+            atomicMax(reinterpret_cast<unsigned int*>(p.amax_slots + ct % kAmaxSlots), __float_as_uint(am));
+        }
       }
     }
   }
@@ -1926,6 +2028,105 @@ int store_quant_launch(Operand a, int64_t M, Operand w, int64_t N, int64_t K, ui
   hipLaunchKernelGGL(splitk_reduce_quant_kernel, dim3((uint32_t)blocks), dim3(256), 0, st, part, pl.splits, M, N,
                      a.gscale, w.gscale, yq_gs, yq_codes, yq_scales);
   launch_end(slot, st);
+  return hipGetLastError() == hipSuccess ? 0 : 7;
+}
+
+// ---- whole MLP ---------------------------------------------------------------------
+// Decode path: both projections on the weight streams and x small enough for
+// the one-work-group quantiser.
+struct MlpDecodePlan {
+  bool ok;
+  GvPlan gu_gv;
+  QdPlan gu_qd;
+  Plan dn;
+  uint32_t groups;      // column groups of the down projection (tickets)
+};
+
+static MlpDecodePlan plan_mlp_decode(int64_t T, int64_t K, int64_t I) {
+  MlpDecodePlan d{};
+  if (T < 1 || T > 8 || T * (K / 16) > (int64_t)kSmallQuantBlocks) return d;
+  d.gu_gv = plan_gemv(T, K, true);
+  d.gu_qd = plan_quad(T, K, true);
+  if (d.gu_gv.bpl == 0 && d.gu_qd.wk == 0) return d;
+  d.dn = plan_store(T, K, I, 1, false);
+  if (d.dn.gv_bpl == 0 && d.dn.qd_wk == 0) return d;
+  d.groups = d.dn.gv_bpl > 0 ? cdiv(K, kGvCols) : cdiv(K, kQdCols);
+  d.ok = true;
+  return d;
+}
+
+size_t mlp_ws_bytes(int64_t T, int64_t K, int64_t I) {
+  const MlpDecodePlan d = plan_mlp_decode(T, K, I);
+  if (d.ok)   // [H float32][|H| partials][down partial sums][tickets]
+    return align256((size_t)T * I * 4) + align256((size_t)glu_parts(T, I, K, 1, false) * 4) +
+           align256((size_t)d.dn.splits * T * K * 4) + align256((size_t)d.groups * 4);
+  // [quantiser partial maxima][gate/up workspace][down workspace]
+  return align256(quantize_ws_bytes(T, K, 0)) + align256(glu_ws_bytes(T, I, K, 1, false)) +
+         align256(store_ws_bytes(T, K, I, 1, false));
+}
+
+int mlp_launch(const void* x, int x_dtype, int64_t ld_x, int64_t T, int64_t K, int64_t I, Operand wg, Operand wu,
+               Operand wd, uint8_t* xq_codes, uint8_t* xq_scales, float* xq_gs, uint8_t* hq_codes, uint8_t* hq_scales,
+               float* hq_gs, void* y, int y_bf16, int64_t ldy, const float* x_amax, float* y_amax, void* ws,
+               hipStream_t st) {
+  char* w = reinterpret_cast<char*>(ws);
+  const MlpDecodePlan d = plan_mlp_decode(T, K, I);
+  if (!d.ok) {
+    const size_t q_bytes = align256(quantize_ws_bytes(T, K, 0));
+    const size_t g_bytes = align256(glu_ws_bytes(T, I, K, 1, false));
+    int rc = x_amax ? quantize_launch(x, x_dtype, T, K, ld_x, xq_codes, xq_scales, xq_gs, 2, const_cast<float*>(x_amax), st)
+                    : quantize_launch(x, x_dtype, T, K, ld_x, xq_codes, xq_scales, xq_gs, 0, w, st);
+    if (rc) return rc;
+    const Operand xq{xq_codes, xq_scales, xq_gs};
+    if ((rc = glu_launch(xq, nullptr, nullptr, 1, T, wg, wu, I, K, hq_codes, hq_scales, hq_gs, w + q_bytes, st)))
+      return rc;
+    const Operand hq{hq_codes, hq_scales, hq_gs};
+    return store_launch(hq, nullptr, nullptr, 1, T, wd, K, I, y, y_bf16, ldy, y_amax, w + q_bytes + g_bytes, st);
+  }
+  float* h = reinterpret_cast<float*>(w);
+  w += align256((size_t)T * I * 4);
+  float* partials = reinterpret_cast<float*>(w);
+  const uint32_t npart = glu_parts(T, I, K, 1, false);
+  w += align256((size_t)npart * 4);
+  float* part = reinterpret_cast<float*>(w);
+  w += align256((size_t)d.dn.splits * T * K * 4);
+  uint32_t* tickets = reinterpret_cast<uint32_t*>(w);
+
+  // 1: quantise x; clear the tickets and the output-amax slots
+  int rc = mlp_prologue_launch(x, x_dtype, T, K, ld_x, xq_codes, xq_scales, xq_gs, x_amax, tickets, d.groups,
+                               reinterpret_cast<uint32_t*>(y_amax), y_amax ? kAmaxSlots : 0u, st);
+  if (rc) return rc;
+  // 2: gate/up weight stream, SiLU*up epilogue, float32 H and its partial maxima
+  GemmArgs g = base_args(nullptr, xq_gs, wg, T, I, K);
+  g.a_codes = xq_codes;
+  g.a_scales = xq_scales;
+  g.u_codes = wu.codes;
+  g.u_scales = wu.scales;
+  g.u_gs = wu.gscale;
+  g.h = h;
+  g.partials = partials;
+  if (d.gu_gv.bpl > 0) launch_gemv<true, EPI_GLU>(g, d.gu_gv.bpl, st);
+  else launch_quad<true, EPI_GLU>(g, d.gu_qd.wk, st);
+  if (hipGetLastError() != hipSuccess) return 7;
+  // 3: requantise H with its global scale
+  if ((rc = requant_f32_launch(h, T, I, hq_codes, hq_scales, hq_gs, partials, npart, st))) return rc;
+  // 4: down weight stream; the last-arriving wave (work-group) of each column
+  // group adds the K splits and stores y (and its amax)
+  GemmArgs dn = base_args(nullptr, hq_gs, wd, T, K, I);
+  dn.a_codes = hq_codes;
+  dn.a_scales = hq_scales;
+  dn.c = y;
+  dn.ldc = ldy;
+  dn.c_bf16 = y_bf16;
+  dn.splits = d.dn.splits;
+  dn.split_out = part;
+  dn.force_split = 1;
+  dn.tickets = tickets;
+  dn.amax_slots = y_amax;
+  dn.m_tiles = d.dn.m_tiles;
+  dn.n_tiles = d.dn.n_tiles;
+  if (d.dn.gv_bpl > 0) launch_gemv<false, EPI_STORE>(dn, d.dn.gv_bpl, st);
+  else launch_quad<false, EPI_STORE>(dn, d.dn.qd_wk, st);
   return hipGetLastError() == hipSuccess ? 0 : 7;
 }
 

@@ -43,6 +43,15 @@ int quantize_scratch(void** out);
 int requant_f32_launch(const float* h, int64_t rows, int64_t cols, uint8_t* codes, uint8_t* scales,
                        float* gs, const float* partials, uint32_t npart, hipStream_t st);
 
+// First launch of the whole-MLP decode path: quantise x (at most 4096 blocks
+// of 16) in one work-group, with the amax reduced from x or taken from the
+// kAmaxSlots partial maxima `x_amax` (nullable), and clear the words
+// [zero, zero + nzero) and [zero2, zero2 + nzero2) for the launches that follow.
+constexpr uint32_t kSmallQuantBlocks = 4096;
+int mlp_prologue_launch(const void* x, int x_dtype, int64_t rows, int64_t cols, int64_t ld, uint8_t* codes,
+                        uint8_t* scales, float* gs, const float* x_amax, uint32_t* zero, uint32_t nzero,
+                        uint32_t* zero2, uint32_t nzero2, hipStream_t st);
+
 // RMSNorm fused into the quantiser: workspace = inverse rms per row, then the
 // partial maxima.
 size_t rmsnorm_quantize_ws_bytes(int64_t rows);
@@ -86,6 +95,19 @@ int glu_static_launch(Operand a, const int32_t* a_rows, const int32_t* off, int 
 // store_ws_bytes.
 int store_quant_launch(Operand a, int64_t M, Operand w, int64_t N, int64_t K, uint8_t* yq_codes, uint8_t* yq_scales,
                        const float* yq_gs, void* ws, hipStream_t st);
+
+// Whole MLP: quantise x, gate/up + SiLU*up + requantisation, down projection.
+// For decode batches (T <= 8 with both projections on the weight streams) four
+// launches: quantise x (also clearing the split-K tickets), gate/up, requantise
+// H, and the down projection whose last-arriving wave per column group adds the
+// K-split partial sums (no reduction launch); otherwise the launch sequence of
+// the separate calls.  x_amax (nullable): kAmaxSlots partial maxima of |x|
+// (the previous layer's y_amax); y_amax (nullable): the same for y.
+size_t mlp_ws_bytes(int64_t T, int64_t K, int64_t I);
+int mlp_launch(const void* x, int x_dtype, int64_t ld_x, int64_t T, int64_t K, int64_t I, Operand wg, Operand wu,
+               Operand wd, uint8_t* xq_codes, uint8_t* xq_scales, float* xq_gs, uint8_t* hq_codes, uint8_t* hq_scales,
+               float* hq_gs, void* y, int y_bf16, int64_t ldy, const float* x_amax, float* y_amax, void* ws,
+               hipStream_t st);
 
 // ---- expert routing and combine ----------------------------------------------
 size_t route_ws_bytes(int64_t T, int E, int k);

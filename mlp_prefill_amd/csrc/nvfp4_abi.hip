@@ -323,6 +323,30 @@ int nvfp4_mlp_down_quant(nvfp4_tensor h, nvfp4_tensor w_down, int64_t T, int64_t
                                    reinterpret_cast<hipStream_t>(stream));
 }
 
+int nvfp4_mlp(const void* x, int x_dtype, int64_t ld_x, const float* x_amax, int64_t T, int64_t K, int64_t I,
+              nvfp4_tensor w_gate, nvfp4_tensor w_up, nvfp4_tensor w_down, nvfp4_tensor x_q, nvfp4_tensor h_q,
+              void* y, int y_dtype, int64_t ldy, float* y_amax, void* ws, size_t* ws_bytes, void* stream) {
+  if (!dtype_ok(x_dtype) || !dtype_ok(y_dtype)) return NVFP4_ERR_ARG;
+  if (T < 0 || K <= 0 || I <= 0 || K % 128 != 0 || I % 128 != 0 || ld_x < K || ldy < K) return NVFP4_ERR_SHAPE;
+  if (T * (I / 16) >= ((int64_t)1 << 31) || T * (K / 16) >= ((int64_t)1 << 31)) return NVFP4_ERR_SHAPE;
+  bool query;
+  int rc = workspace(ws, ws_bytes, T > 0 ? nvfp4::mlp_ws_bytes(T, K, I) : 0, &query);
+  if (rc != NVFP4_OK || query) return rc;
+  if (T == 0) return NVFP4_OK;
+  if (!x || !y) return NVFP4_ERR_NULL;
+  if ((rc = check_tensor(w_gate)) != NVFP4_OK || (rc = check_tensor(w_up)) != NVFP4_OK ||
+      (rc = check_tensor(w_down)) != NVFP4_OK || (rc = check_tensor(x_q)) != NVFP4_OK ||
+      (rc = check_tensor(h_q)) != NVFP4_OK)
+    return rc;
+  if (!aligned(x, 16) || (ld_x * elem_size(x_dtype)) % 16 != 0 || !aligned(y, 16) ||
+      (ldy * elem_size(y_dtype)) % 16 != 0 || !aligned(x_amax, 16) || !aligned(y_amax, 16))
+    return NVFP4_ERR_ALIGN;
+  if ((rc = check_device()) != NVFP4_OK) return rc;
+  return nvfp4::mlp_launch(x, x_dtype, ld_x, T, K, I, op(w_gate), op(w_up), op(w_down), x_q.codes, x_q.scales,
+                           x_q.gscale, h_q.codes, h_q.scales, h_q.gscale, y, y_dtype == NVFP4_BF16, ldy, x_amax, y_amax,
+                           ws, reinterpret_cast<hipStream_t>(stream));
+}
+
 int nvfp4_moe_route(const float* logits, int64_t T, int E, int k, int64_t ld, int32_t* group_offsets,
                     int32_t* a_rows, int32_t* slot_of, float* weights, void* ws, size_t* ws_bytes, void* stream) {
   if (E < 1 || E > nvfp4::kMaxExperts || k < 1 || k > nvfp4::kMaxTopK || k > E) return NVFP4_ERR_ARG;

@@ -162,21 +162,38 @@ __global__ void __launch_bounds__(256) rms_amax_kernel(const T* __restrict__ x, 
 // quantises, in one launch instead of two; a kernel boundary costs more than
 // this work.  The max is exact in any order and the per-block routine is the
 // same, so the result equals the two-kernel path bit for bit.
-constexpr uint32_t kSmallBlocks = 4096;
+constexpr uint32_t kSmallBlocks = kSmallQuantBlocks;
 
+//
+// As the first launch of a whole-MLP call it also clears `nzero` words
+// (the split-K tickets and output-amax slots the later launches of the call
+// use), and it can take the amax from `given` (npart partial maxima written by
+// an earlier call's output-amax epilogue) instead of reducing x.
 template <typename T>
 __global__ void __launch_bounds__(1024) quantize_small_kernel(const T* __restrict__ x, uint32_t nbc,
                                                               uint32_t nblocks, int64_t ld, float* gs_ptr,
                                                               uint8_t* __restrict__ codes,
-                                                              uint8_t* __restrict__ scales) {
+                                                              uint8_t* __restrict__ scales,
+                                                              uint32_t* __restrict__ zero = nullptr,
+                                                              uint32_t nzero = 0,
+                                                              const float* __restrict__ given = nullptr,
+                                                              uint32_t npart = 0,
+                                                              uint32_t* __restrict__ zero2 = nullptr,
+                                                              uint32_t nzero2 = 0) {
   __shared__ float red[16];
+  for (uint32_t i = threadIdx.x; i < nzero; i += 1024u) zero[i] = 0u;
+  for (uint32_t i = threadIdx.x; i < nzero2; i += 1024u) zero2[i] = 0u;
   float m = 0.f;
-  for (uint32_t b = threadIdx.x; b < nblocks; b += 1024u) {
-    const uint32_t row = b / nbc, cb = b - row * nbc;
-    float v[16];
-    Load16<T>::run(x + (int64_t)row * ld + (int64_t)cb * kBlock, v);
+  if (given != nullptr) {
+    for (uint32_t i = threadIdx.x; i < npart; i += 1024u) m = fmaxf(m, given[i]);
+  } else {
+    for (uint32_t b = threadIdx.x; b < nblocks; b += 1024u) {
+      const uint32_t row = b / nbc, cb = b - row * nbc;
+      float v[16];
+      Load16<T>::run(x + (int64_t)row * ld + (int64_t)cb * kBlock, v);
 #pragma unroll
-    for (int i = 0; i < 16; ++i) m = fmaxf(m, fabsf(v[i]));
+      for (int i = 0; i < 16; ++i) m = fmaxf(m, fabsf(v[i]));
+    }
   }
   m = block_max(m, red);
   const float gs = global_scale_from_amax(m);
@@ -337,6 +354,24 @@ int rmsnorm_quantize_launch(const void* x, int x_dtype, int64_t rows, int64_t co
                               ws, st);
   return rmsnorm_quantize_t(reinterpret_cast<const float*>(x), rows, cols, ld, gamma, eps, codes, scales, gs, ws,
                             st);
+}
+
+int mlp_prologue_launch(const void* x, int x_dtype, int64_t rows, int64_t cols, int64_t ld, uint8_t* codes,
+                        uint8_t* scales, float* gs, const float* x_amax, uint32_t* zero, uint32_t nzero,
+                        uint32_t* zero2, uint32_t nzero2, hipStream_t st) {
+  const uint32_t nbc = (uint32_t)(cols / kBlock);
+  const uint32_t nblocks = (uint32_t)rows * nbc;
+  const uint32_t npart = x_amax ? kAmaxSlots : 0u;
+  const int s0 = launch_begin(KC_QUANTIZE, st);
+  if (x_dtype == 1)
+    hipLaunchKernelGGL(quantize_small_kernel<uint16_t>, dim3(1), dim3(1024), 0, st,
+                       reinterpret_cast<const uint16_t*>(x), nbc, nblocks, ld, gs, codes, scales, zero, nzero, x_amax,
+                       npart, zero2, nzero2);
+  else
+    hipLaunchKernelGGL(quantize_small_kernel<float>, dim3(1), dim3(1024), 0, st, reinterpret_cast<const float*>(x),
+                       nbc, nblocks, ld, gs, codes, scales, zero, nzero, x_amax, npart, zero2, nzero2);
+  launch_end(s0, st);
+  return hipGetLastError() == hipSuccess ? 0 : 7;
 }
 
 int requant_f32_launch(const float* h, int64_t rows, int64_t cols, uint8_t* codes, uint8_t* scales,

@@ -100,6 +100,50 @@ def test_quantize_noalloc_without_device():
     assert m.lib.nvfp4_quantize_act_noalloc(FAKE, m.BF16, 4, 32, 32, _t(), 0, None) == m.ERR_DEVICE
 
 
+def test_whole_mlp_validation_and_workspace():
+    f = m.lib.nvfp4_mlp
+    z = nvfp4_tensor(0, 0, 0)
+    big = ctypes.c_size_t(1 << 30)
+    t = _t()
+
+    def call(x=FAKE, xdt=m.BF16, ldx=5120, xa=None, T=4, K=5120, I=17408, wg=t, y=FAKE, ydt=m.F32, ldy=5120,
+             ya=None, ws=FAKE, sz=None):
+        return f(x, xdt, ldx, xa, T, K, I, wg, t, t, t, t, y, ydt, ldy, ya, ws,
+                 ctypes.byref(big if sz is None else sz), None)
+    assert call(xdt=5) == m.ERR_ARG
+    assert call(ydt=7) == m.ERR_ARG
+    assert call(K=5000, ldx=5000, ldy=5000) == m.ERR_SHAPE          # K % 128
+    assert call(I=17400) == m.ERR_SHAPE                              # I % 128
+    assert call(ldx=5000) == m.ERR_SHAPE                             # ld_x < K
+    assert call(ldy=4096) == m.ERR_SHAPE                             # ldy < K
+    assert call(T=-1) == m.ERR_SHAPE
+    assert call(x=None) == m.ERR_NULL
+    assert call(y=None) == m.ERR_NULL
+    assert call(wg=_t(g=0)) == m.ERR_NULL
+    assert call(x=FAKE + 8) == m.ERR_ALIGN
+    assert call(xa=FAKE + 4) == m.ERR_ALIGN                          # x_amax
+    assert call(ya=FAKE + 4) == m.ERR_ALIGN                          # y_amax
+    assert call(sz=ctypes.c_size_t(64)) == m.ERR_WORKSPACE
+    assert f(None, m.BF16, 5120, None, 0, 5120, 17408, z, z, z, z, z, None, m.F32, 5120, None, None, None,
+             None) == m.OK                                           # T = 0: no-op
+    # workspace: decode path [H][partials][down partial sums][tickets]; large batches: the separate calls' sum
+    s = _size()
+    assert f(None, m.BF16, 5120, None, 1, 5120, 17408, z, z, z, z, z, None, m.F32, 5120, None, None,
+             ctypes.byref(s), None) == m.OK
+    assert s.value == 17408 * 4 + 17408 // 4 * 4 + 17 * 5120 * 4 + 5120 // 4 * 4
+    assert f(None, m.BF16, 5120, None, 1024, 5120, 17408, z, z, z, z, z, None, m.F32, 5120, None, None,
+             ctypes.byref(s), None) == m.OK
+    assert s.value >= m.mlp_gu_act_ws_bytes(1024, 5120, 17408) + m.mlp_down_ws_bytes(1024, 17408, 5120)
+
+
+@no_gpu
+def test_whole_mlp_without_device():
+    t = _t()
+    big = ctypes.c_size_t(1 << 30)
+    assert m.lib.nvfp4_mlp(FAKE, m.BF16, 5120, None, 1, 5120, 17408, t, t, t, t, t, FAKE, m.F32, 5120, None, FAKE,
+                           ctypes.byref(big), None) == m.ERR_DEVICE
+
+
 def test_quantize_workspace_query():
     q = m.lib.nvfp4_quantize_act
     s = _size()
