@@ -37,6 +37,10 @@ def decode_weights():
     return _weights(p["K"], p["I"], (p["wg_seed"], p["wu_seed"], p["wd_seed"]))
 
 
+def decode_launches(t):
+    return 4
+
+
 def run_fused(xbits, wdev, y_dtype=torch.float32, x_amax=None, y_amax=None, ws=None, x=None):
     import mlp_prefill_amd as m
     t, k = xbits.shape if x is None else x.shape
@@ -67,7 +71,7 @@ def test_decode_equals_separate_calls(decode_weights, t):
     p = WORKLOADS["mlp_decode_5120x17408"].params
     announce(f"whole MLP decode T={t} vs separate calls")
     launches = assert_same_as_separate(bf16_normal(p["x_seed"] + t, (t, p["K"])), decode_weights[0], f"T{t}")
-    assert launches == 4, launches
+    assert launches == decode_launches(t), launches
 
 
 SHAPES = [(2, 1152, 3072), (1, 1024, 1024), (5, 2048, 3072), (7, 1024, 2048), (16, 512, 1024), (300, 512, 1024)]
@@ -83,7 +87,27 @@ def test_shapes_equal_separate_calls(t, k, i):
     before = m.launch_count()
     run_device_mlp(xbits, wdev)
     separate = m.launch_count() - before
-    assert launches == (4 if t <= 8 else separate), (launches, separate)
+    assert launches == (decode_launches(t) if t <= 8 else separate), (launches, separate)
+
+
+@pytest.mark.parametrize("t", [1, 2])
+def test_float32_input_equals_separate_calls(decode_weights, t):
+    """float32 x through the whole-MLP call equals the separate calls."""
+    import mlp_prefill_amd as m
+    p = WORKLOADS["mlp_decode_5120x17408"].params
+    announce(f"whole MLP float32 x T={t}")
+    x = torch.from_numpy(np.random.default_rng(31 + t).standard_normal((t, p["K"])).astype(np.float32)).cuda()
+    wdev = decode_weights[0]
+    xq0, hq0 = m.NVFP4.empty(t, p["K"]), m.NVFP4.empty(t, p["I"])
+    y0 = torch.empty((t, p["K"]), dtype=torch.float32, device="cuda")
+    m.nvfp4_quantize_act(x, xq0)
+    m.nvfp4_mlp_gu_act(xq0, wdev[0], wdev[1], hq0)
+    m.nvfp4_mlp_down(hq0, wdev[2], y0)
+    xq, hq, y, launches = run_fused(None, wdev, x=x)
+    assert launches == decode_launches(t)
+    assert_nvfp4_equal(to_host(xq), to_host(xq0), "x~")
+    assert_nvfp4_equal(to_host(hq), to_host(hq0), "H~")
+    assert torch.equal(y, y0)
 
 
 @pytest.mark.parametrize("t", [1, 5])
@@ -123,7 +147,7 @@ def test_output_amax_and_chained_layer(t):
     assert_nvfp4_equal(to_host(xq_a), to_host(xq_b), "x~ from the amax slots")
     assert_nvfp4_equal(to_host(hq_a), to_host(hq_b), "H~")
     assert torch.equal(y_a, y_b)
-    assert la == (4 if t <= 8 else lb - 1), (la, lb)
+    assert la == (decode_launches(t) if t <= 8 else lb - 1), (la, lb)
 
 
 def test_repeated_calls_any_workspace(decode_weights):
