@@ -543,11 +543,37 @@ def decode_stack_line(m, layers):
         torch.cuda.current_stream().wait_stream(s)
         torch.cuda.synchronize()
         graph = float(np.median(time_events(g.replay, 20)))
+        del g
+        # the same stack through the whole-MLP call (4 launches per layer)
+        ws_f = torch.empty(m.mlp_ws_bytes(t, K_HID, layers[0].w[0].rows), dtype=torch.uint8, device="cuda")
+
+        def stack_whole():
+            cur = x
+            for li, lay in enumerate(layers):
+                m.nvfp4_mlp(cur, lay.w[0], lay.w[1], lay.w[2], run.xq, run.hq, ys[li % 2], ws=ws_f)
+                cur = ys[li % 2]
+        eager_w = float(np.median(time_events(stack_whole, 20)))
+        b0 = m.launch_count()
+        stack_whole()
+        launches_w = m.launch_count() - b0
+        s = torch.cuda.Stream()
+        s.wait_stream(torch.cuda.current_stream())
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.stream(s):
+            with torch.cuda.graph(g, stream=s):
+                stack_whole()
+        torch.cuda.current_stream().wait_stream(s)
+        torch.cuda.synchronize()
+        graph_w = float(np.median(time_events(g.replay, 20)))
+        del g
         out[f"T{t}"] = {"ms_eager": eager, "ms_graph": graph, "ms_per_layer_graph": graph / len(layers),
                         "hbm_gbs_graph": wbytes / (graph * 1e-3) / 1e9,
                         "frac_hbm_peak_graph": wbytes / (graph * 1e-3) / 1e9 / PEAK_HBM_GBS,
-                        "launches_per_pass": launches}
-        del g
+                        "launches_per_pass": launches,
+                        "whole_mlp_ms_eager": eager_w, "whole_mlp_ms_graph": graph_w,
+                        "whole_mlp_hbm_gbs_graph": wbytes / (graph_w * 1e-3) / 1e9,
+                        "whole_mlp_frac_hbm_peak_graph": wbytes / (graph_w * 1e-3) / 1e9 / PEAK_HBM_GBS,
+                        "whole_mlp_launches_per_pass": launches_w}
     return out
 
 

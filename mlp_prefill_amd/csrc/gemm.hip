@@ -490,7 +490,7 @@ __device__ __forceinline__ void xchunk(Ctx<WN, TM, TN, DUAL>& x, const Lds& lc, 
 #define NVFP4_STORE_TN 2
 #endif
 #ifndef NVFP4_GROUPED_STORE_TN
-#define NVFP4_GROUPED_STORE_TN 1
+#define NVFP4_GROUPED_STORE_TN 2
 #endif
 // LDS buffers of the chunk ring (2 to 4).
 #ifndef NVFP4_GLU_STAGES
@@ -1515,6 +1515,18 @@ __device__ __forceinline__ float stored_abs(float v, int bf16) {
   return bf16 ? __uint_as_float(f32_to_bf16_bits(fabsf(v)) << 16) : fabsf(v);
 }
 
+// Expert of slot m: the last e with off[e] <= m (binary search over the
+// non-decreasing offsets; empty experts share their offset with the next one).
+__device__ __forceinline__ int expert_of(const int32_t* off, int E, int64_t m) {
+  int lo = 0, hi = E - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (off[mid] <= m) lo = mid;
+    else hi = mid - 1;
+  }
+  return lo;
+}
+
 // out[m][n] = (sum over splits, in split order) * gs_a * gs_b[expert of slot m].
 __global__ void __launch_bounds__(256) splitk_reduce_kernel(const float* __restrict__ part, uint32_t splits,
                                                             int64_t M, int64_t N, const float* a_gs,
@@ -1536,10 +1548,7 @@ __global__ void __launch_bounds__(256) splitk_reduce_kernel(const float* __restr
       for (int k = 0; k < 8; ++k) acc += v[k];
     }
     for (; s < splits; ++s) acc += part[(int64_t)s * total + idx];
-    int e = 0;
-    if (off) {
-      while (e < E - 1 && off[e + 1] <= m) ++e;
-    }
+    const int e = off ? expert_of(off, E, m) : 0;
     const float v = acc * (ga * b_gs[e]);
     if (out_bf16)
       reinterpret_cast<uint16_t*>(out)[m * ldo + n] = (uint16_t)f32_to_bf16_bits(v);
@@ -1583,10 +1592,7 @@ __global__ void __launch_bounds__(256) splitk_reduce4_kernel(const float* __rest
       acc.z += v.z;
       acc.w += v.w;
     }
-    int e = 0;
-    if (off) {
-      while (e < E - 1 && off[e + 1] <= m) ++e;
-    }
+    const int e = off ? expert_of(off, E, m) : 0;
     const float sc = ga * b_gs[e];
     const float4 o = make_float4(acc.x * sc, acc.y * sc, acc.z * sc, acc.w * sc);
     if (out_bf16) {

@@ -118,3 +118,58 @@ def test_decode_stack_graph_replays_match_eager(t):
     assert m.launch_count() - launches_before == 3 * 2 * 5
     # the buffers now hold the last replay (the eager calls between replays used `other`)
     stage_against_oracle(stack, xbits, wref, f"graph replay T={t}")
+
+
+class WholeStack(Stack):
+    """The same stack through the whole-MLP call (nvfp4_mlp, 4 launches per layer on decode batches)."""
+
+    def __init__(self, m, layers, t, k, i):
+        super().__init__(m, layers, t, k, i)
+        self.ws = torch.empty(m.mlp_ws_bytes(t, k, i), dtype=torch.uint8, device="cuda")
+
+    def __call__(self, x):
+        cur = x
+        for li, w in enumerate(self.layers):
+            self.m.nvfp4_mlp(cur, w[0], w[1], w[2], self.xq[li], self.hq[li], self.ys[li], ws=self.ws)
+            cur = self.ys[li]
+
+
+@pytest.mark.parametrize("t", [1, 5])
+def test_whole_mlp_stack_graph_replays_match_eager_and_oracle(t):
+    """Graph capture of the whole-MLP decode path: its first launch clears the
+    down stream's tickets with a kernel (no memset node), so every replay
+    starts from cleared tickets; replays equal the eager run bit for bit and
+    are staged against the oracle layer by layer."""
+    import mlp_prefill_amd as m
+    p = WORKLOADS["mlp_long_prefill_16x1024_4layers"].params
+    k, i = p["K"], p["I"]
+    announce(f"graph: 2-layer whole-MLP decode stack T={t}")
+    bits = [[bf16_normal(s, shp, sigma=p["w_sigma"])
+             for s, shp in zip(layer_seeds(p["layer_seed0"], li), [(i, k), (i, k), (k, i)])] for li in range(2)]
+    layers = [[dev_quantize(b) for b in lb] for lb in bits]
+    wref = [[quant.quantize(bf16_bits_to_f32(b)) for b in lb] for lb in bits]
+    xbits = bf16_normal(177 + t, (t, k))
+    x = dev_bf16(xbits)
+    stack = WholeStack(m, layers, t, k, i)
+    other = WholeStack(m, layers, t, k, i)
+    stack(x)
+    torch.cuda.synchronize()
+    ref = stack.out.clone()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(s):
+        with torch.cuda.graph(g, stream=s):
+            stack(x)
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    for rep in range(3):
+        for buf in stack.ys:
+            buf.zero_()
+        stack.ws.fill_(0xFF)                   # tickets and partial sums left dirty on purpose
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(stack.out, ref), f"replay {rep}: output differs from the eager run"
+        other(x * 0.5)
+        torch.cuda.synchronize()
+    stage_against_oracle(stack, xbits, wref, f"whole-MLP graph replay T={t}")

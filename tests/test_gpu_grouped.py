@@ -8,8 +8,8 @@ from oracle import mlp as omlp
 from oracle import moe as omoe
 from oracle import quant
 from synthetic import WORKLOADS, bf16_bits_to_f32, bf16_normal, expert_seeds, router_logits
-from tests.gpu_util import (TOL, announce, assert_nvfp4_equal, dev_quantize, legit_requant_flips, max_norm_err,
-                            require_gpu, to_host)
+from tests.gpu_util import (TOL, announce, assert_bf16_rounding_close, assert_nvfp4_equal, bf16_tensor_to_f32,
+                            dev_quantize, legit_requant_flips, max_norm_err, require_gpu, to_host)
 
 pytestmark = pytest.mark.gpu
 
@@ -98,6 +98,31 @@ def test_grouped_store_gemm_matches_per_expert_gemm():
     err = max_norm_err(out.cpu().numpy(), omlp.grouped_gemm(xq_ref, a_rows, offsets, wref))
     print(f"grouped store gemm error {err:.2e}")
     assert err <= 1e-5
+
+
+@pytest.mark.parametrize("offsets", [[0, 20, 20, 43], [0, 0, 43, 43], [0, 13, 30, 43]],
+                         ids=["empty_middle", "one_nonempty", "three"])
+def test_grouped_store_gemm_split_k(offsets):
+    """Few tiles and a long K: the store contraction splits K and the fixed-order
+    reduction scales each slot by its expert's weight scale (the expert found from
+    the offsets, with empty experts sharing an offset); bf16 output."""
+    import mlp_prefill_amd as m
+    announce(f"grouped store gemm, split K, offsets {offsets}")
+    t, k, n, e = 40, 4096, 256, 3
+    assert m.grouped_ws_bytes(43, n, k, e, m.EPI_STORE) > 43 * k * 2 + 43 * n * 4   # more than one split
+    xb = bf16_normal(31, (t, k))
+    xq = dev_quantize(xb)
+    xq_ref = quant.quantize(bf16_bits_to_f32(xb))
+    # weight scales differ by expert (sigma 0.02, 0.05, 0.1), so a wrong expert shows
+    wbits = [bf16_normal(40 + x, (n, k), sigma=(0.02, 0.05, 0.1)[x]) for x in range(e)]
+    wdev = m.NVFP4.stack([dev_quantize(b) for b in wbits])
+    wref = [quant.quantize(bf16_bits_to_f32(b)) for b in wbits]
+    a_rows = np.array([(7 * s) % t for s in range(43)], dtype=np.int32)
+    offs = np.array(offsets, dtype=np.int32)
+    out = torch.empty((43, n), dtype=torch.bfloat16, device="cuda")
+    m.nvfp4_grouped_gemm(xq, torch.from_numpy(a_rows).cuda(), torch.from_numpy(offs).cuda(), wdev, out=out)
+    ref = omlp.grouped_gemm(xq_ref, a_rows, offs, wref)
+    assert_bf16_rounding_close(bf16_tensor_to_f32(out), ref)
 
 
 def test_grouped_mlp_moe_workload_full_size_sampled():
