@@ -263,7 +263,9 @@ int nvfp4_mlp_down(nvfp4_tensor h, nvfp4_tensor w_down, int64_t T, int64_t I, in
  *   x_q    : [T][K] NVFP4 out;  h_q : [T][I] NVFP4 out
  *   y      : float32 or bf16 (y_dtype) [T][K], row stride ldy >= K
  *   y_amax : NULL, or NVFP4_AMAX_SLOTS float32 receiving partial maxima of
- *            |y| as stored (every slot written), for the next layer's x_amax
+ *            |y| as stored (every slot written), for the next layer's x_amax;
+ *            not the same buffer as x_amax (NVFP4_ERR_ARG): chained layers
+ *            alternate two buffers
  *   ws     : required (size query as usual); contents unspecified on return
  * Decode batches -- T <= 8 with both projections on the weight streams (T <=
  * 2 with K >= 1024, or 3 <= T <= 8 with K a multiple of 1024; I >= 1024, or a
@@ -274,8 +276,11 @@ int nvfp4_mlp_down(nvfp4_tensor h, nvfp4_tensor w_down, int64_t T, int64_t I, in
  * (4) the down weight stream, whose K splits are added, in split order, by
  * the last-arriving wave (or work-group) of each column group after an
  * agent-scope fence and a ticket increment -- nothing waits for anything, and
- * no reduction launch follows.  Other shapes take the separate calls' launch
- * sequence (seven or eight launches; one fewer with x_amax).
+ * no reduction launch follows.  Other shapes run the separate calls' kernels
+ * minus their two expansion launches -- the quantisers of x and H also write
+ * the f16 operand copies the matrix-core contractions read -- so six launches
+ * (quantise 2, gate/up contraction, requantisation, down contraction, split-K
+ * reduction), five with x_amax or an x of at most 4096 blocks of 16.
  */
 int nvfp4_mlp(const void *x, int x_dtype, int64_t ld_x, const float *x_amax, int64_t T, int64_t K, int64_t I,
               nvfp4_tensor w_gate, nvfp4_tensor w_up, nvfp4_tensor w_down, nvfp4_tensor x_q, nvfp4_tensor h_q,

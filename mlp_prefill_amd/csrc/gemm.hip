@@ -1878,13 +1878,15 @@ size_t store_ws_bytes(int64_t M, int64_t N, int64_t K, int E, bool grouped) {
 }
 
 int store_launch(Operand a, const int32_t* rows, const int32_t* off, int E, int64_t M, Operand w, int64_t N,
-                 int64_t K, void* c, int c_bf16, int64_t ldc, float* c_amax, void* ws, hipStream_t st) {
+                 int64_t K, void* c, int c_bf16, int64_t ldc, float* c_amax, void* ws, hipStream_t st,
+                 const _Float16* a16_given) {
   const bool grouped = off != nullptr;
   _Float16* a16 = reinterpret_cast<_Float16*>(ws);
   float* part = reinterpret_cast<float*>(reinterpret_cast<char*>(ws) + align256((size_t)M * K * 2));
   const Plan pl = plan_store(M, N, K, E, grouped);
-  // the weight streams expand the activation themselves
-  if (grouped || (pl.gv_bpl == 0 && pl.qd_wk == 0)) launch_expand(a.codes, a.scales, rows, M, K, a16, st);
+  // the weight streams expand the activation themselves; a given copy needs no expansion
+  if (a16_given != nullptr && !grouped) a16 = const_cast<_Float16*>(a16_given);
+  else if (grouped || (pl.gv_bpl == 0 && pl.qd_wk == 0)) launch_expand(a.codes, a.scales, rows, M, K, a16, st);
   GemmArgs g = base_args(a16, a.gscale, w, M, N, K);
   g.a_codes = a.codes;
   g.a_scales = a.scales;
@@ -1929,13 +1931,14 @@ size_t glu_ws_bytes(int64_t M, int64_t N, int64_t K, int E, bool grouped) {
 
 int glu_launch(Operand a, const int32_t* a_rows, const int32_t* off, int E, int64_t M, Operand gt, Operand up,
                int64_t N, int64_t K, uint8_t* hq_codes, uint8_t* hq_scales, float* hq_gs, void* ws,
-               hipStream_t st) {
+               hipStream_t st, const _Float16* a16_given, _Float16* hq16) {
   const bool grouped = off != nullptr;
   float* h = reinterpret_cast<float*>(ws);
   _Float16* a16 = reinterpret_cast<_Float16*>(reinterpret_cast<char*>(ws) + align256((size_t)M * N * 4));
   float* partials = reinterpret_cast<float*>(reinterpret_cast<char*>(a16) + align256((size_t)M * K * 2));
   const bool stream = !grouped && (plan_gemv(M, K, true).bpl > 0 || plan_quad(M, K, true).wk > 0);
-  if (!stream) launch_expand(a.codes, a.scales, a_rows, M, K, a16, st);   // the streams expand x~ themselves
+  if (a16_given != nullptr && !grouped) a16 = const_cast<_Float16*>(a16_given);
+  else if (!stream) launch_expand(a.codes, a.scales, a_rows, M, K, a16, st);   // the streams expand x~ themselves
   GemmArgs g = base_args(a16, a.gscale, gt, M, N, K);
   g.a_codes = a.codes;
   g.a_scales = a.scales;
@@ -1965,7 +1968,7 @@ int glu_launch(Operand a, const int32_t* a_rows, const int32_t* off, int E, int6
     launch_cfg<NVFP4_GLU_WN, NVFP4_GLU_TM, 1, true, false, EPI_GLU>(g, st);
   }
   if (hipGetLastError() != hipSuccess) return 7;
-  return requant_f32_launch(h, M, N, hq_codes, hq_scales, hq_gs, partials, glu_parts(M, N, K, E, grouped), st);
+  return requant_f32_launch(h, M, N, hq_codes, hq_scales, hq_gs, partials, glu_parts(M, N, K, E, grouped), st, hq16);
 }
 
 size_t glu_static_ws_bytes(int64_t M, int64_t K) { return align256((size_t)M * K * 2); }
@@ -2078,16 +2081,24 @@ int mlp_launch(const void* x, int x_dtype, int64_t ld_x, int64_t T, int64_t K, i
   char* w = reinterpret_cast<char*>(ws);
   const MlpDecodePlan d = plan_mlp_decode(T, K, I);
   if (!d.ok) {
+    // The separate calls' kernels, but each quantiser also writes the f16
+    // operand copy the next contraction reads (into that contraction's
+    // workspace), so neither contraction needs an expansion launch.
     const size_t q_bytes = align256(quantize_ws_bytes(T, K, 0));
     const size_t g_bytes = align256(glu_ws_bytes(T, I, K, 1, false));
-    int rc = x_amax ? quantize_launch(x, x_dtype, T, K, ld_x, xq_codes, xq_scales, xq_gs, 2, const_cast<float*>(x_amax), st)
-                    : quantize_launch(x, x_dtype, T, K, ld_x, xq_codes, xq_scales, xq_gs, 0, w, st);
+    char* wg_ws = w + q_bytes;
+    char* wd_ws = w + q_bytes + g_bytes;
+    _Float16* x16 = reinterpret_cast<_Float16*>(wg_ws + align256((size_t)T * I * 4));   // the gate/up's a16 slot
+    _Float16* h16 = reinterpret_cast<_Float16*>(wd_ws);                                // the down's a16 slot
+    int rc = x_amax ? quantize_launch(x, x_dtype, T, K, ld_x, xq_codes, xq_scales, xq_gs, 2, const_cast<float*>(x_amax),
+                                      st, x16)
+                    : quantize_launch(x, x_dtype, T, K, ld_x, xq_codes, xq_scales, xq_gs, 0, w, st, x16);
     if (rc) return rc;
     const Operand xq{xq_codes, xq_scales, xq_gs};
-    if ((rc = glu_launch(xq, nullptr, nullptr, 1, T, wg, wu, I, K, hq_codes, hq_scales, hq_gs, w + q_bytes, st)))
+    if ((rc = glu_launch(xq, nullptr, nullptr, 1, T, wg, wu, I, K, hq_codes, hq_scales, hq_gs, wg_ws, st, x16, h16)))
       return rc;
     const Operand hq{hq_codes, hq_scales, hq_gs};
-    return store_launch(hq, nullptr, nullptr, 1, T, wd, K, I, y, y_bf16, ldy, y_amax, w + q_bytes + g_bytes, st);
+    return store_launch(hq, nullptr, nullptr, 1, T, wd, K, I, y, y_bf16, ldy, y_amax, wd_ws, st, h16);
   }
   float* h = reinterpret_cast<float*>(w);
   w += align256((size_t)T * I * 4);

@@ -32,8 +32,10 @@ void launch_end(int slot, hipStream_t st);
 
 // ---- quantisation -----------------------------------------------------------
 size_t quantize_ws_bytes(int64_t rows, int64_t cols, int gs_mode);
+// x16 (nullable): also write the dequantised values code * scale as f16
+// [rows][cols] (the operand copy a matrix-core contraction reads).
 int quantize_launch(const void* x, int x_dtype, int64_t rows, int64_t cols, int64_t ld, uint8_t* codes,
-                    uint8_t* scales, float* gs, int gs_mode, void* ws, hipStream_t st);
+                    uint8_t* scales, float* gs, int gs_mode, void* ws, hipStream_t st, _Float16* x16 = nullptr);
 // Allocation-free quantiser: bytes of the per-device scratch array, and its
 // device address on the current device (0, or 6 when it cannot be looked up).
 size_t quantize_scratch_bytes();
@@ -41,7 +43,7 @@ int quantize_scratch(void** out);
 // Requantise a float32 [rows][cols] matrix whose amax is the max of
 // `partials` (written by an earlier kernel on the same stream).
 int requant_f32_launch(const float* h, int64_t rows, int64_t cols, uint8_t* codes, uint8_t* scales,
-                       float* gs, const float* partials, uint32_t npart, hipStream_t st);
+                       float* gs, const float* partials, uint32_t npart, hipStream_t st, _Float16* h16 = nullptr);
 
 // First launch of the whole-MLP decode path: quantise x (at most 4096 blocks
 // of 16) in one work-group, with the amax reduced from x or taken from the
@@ -71,16 +73,21 @@ struct Operand {
 // c_amax (nullable): kAmaxSlots float32 partial maxima of |C| as stored.
 // Workspace: f16-expanded activations, then split-K partial sums.
 size_t store_ws_bytes(int64_t M, int64_t N, int64_t K, int E, bool grouped);
+// a16 (nullable): the f16 copy of the (dense) activation, already written by
+// the quantiser -- no expansion launch.
 int store_launch(Operand a, const int32_t* rows, const int32_t* off, int E, int64_t M, Operand w, int64_t N,
-                 int64_t K, void* c, int c_bf16, int64_t ldc, float* c_amax, void* ws, hipStream_t st);
+                 int64_t K, void* c, int c_bf16, int64_t ldc, float* c_amax, void* ws, hipStream_t st,
+                 const _Float16* a16 = nullptr);
 
 // H = SiLU(A . G^T * gs_a*gs_g) * (A . U^T * gs_a*gs_u) (float32, row-major
 // [M][N], at the start of the workspace), then its NVFP4 requantisation with a
 // global scale over all M rows.  Dense or grouped as above.
 size_t glu_ws_bytes(int64_t M, int64_t N, int64_t K, int E, bool grouped);
+// a16 (nullable): as for store_launch; hq16 (nullable): the requantisation
+// also writes the f16 copy of H~ there (for the down projection).
 int glu_launch(Operand a, const int32_t* a_rows, const int32_t* off, int E, int64_t M, Operand gt, Operand up,
                int64_t N, int64_t K, uint8_t* hq_codes, uint8_t* hq_scales, float* hq_gs, void* ws,
-               hipStream_t st);
+               hipStream_t st, const _Float16* a16 = nullptr, _Float16* hq16 = nullptr);
 
 // The same GLU output (dense, or expert-grouped when `off` is given)
 // quantised in the contraction's epilogue with the given global scale *hq_gs

@@ -327,6 +327,7 @@ int nvfp4_mlp(const void* x, int x_dtype, int64_t ld_x, const float* x_amax, int
               nvfp4_tensor w_gate, nvfp4_tensor w_up, nvfp4_tensor w_down, nvfp4_tensor x_q, nvfp4_tensor h_q,
               void* y, int y_dtype, int64_t ldy, float* y_amax, void* ws, size_t* ws_bytes, void* stream) {
   if (!dtype_ok(x_dtype) || !dtype_ok(y_dtype)) return NVFP4_ERR_ARG;
+  if (x_amax != nullptr && x_amax == y_amax) return NVFP4_ERR_ARG;   // read and cleared by the same launch
   if (T < 0 || K <= 0 || I <= 0 || K % 128 != 0 || I % 128 != 0 || ld_x < K || ldy < K) return NVFP4_ERR_SHAPE;
   if (T * (I / 16) >= ((int64_t)1 << 31) || T * (K / 16) >= ((int64_t)1 << 31)) return NVFP4_ERR_SHAPE;
   bool query;

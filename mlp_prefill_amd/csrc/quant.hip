@@ -68,6 +68,16 @@ __global__ void __launch_bounds__(256) amax_partials_kernel(const T* __restrict_
   if (threadIdx.x == 0) partials[blockIdx.x] = m;
 }
 
+// When x16 is given, the block's dequantised values code * scale (exact in
+// f16) also go to x16 [rows][cols]: the operand copy the matrix-core
+// contraction reads, written here instead of by a separate expansion pass.
+__device__ __forceinline__ void store_expanded(_Float16* x16, int64_t boff, uint32_t w0, uint32_t w1, uint32_t s) {
+  if (x16 == nullptr) return;
+  f16x8* o = reinterpret_cast<f16x8*>(x16 + boff * 16);
+  o[0] = expand8(w0, s);
+  o[1] = expand8(w1, s);
+}
+
 // mode 0: gs from the partial maxima (written to gs_ptr by work-group 0);
 // mode 1: gs read from gs_ptr.
 // NORM: quantise y = (x * rinv[row]) * gamma[col] (float32, the RMSNorm
@@ -80,7 +90,8 @@ __global__ void __launch_bounds__(256) quantize_kernel(const T* __restrict__ x, 
                                                        uint8_t* __restrict__ codes,
                                                        uint8_t* __restrict__ scales,
                                                        const float* __restrict__ rinv = nullptr,
-                                                       const float* __restrict__ gamma = nullptr) {
+                                                       const float* __restrict__ gamma = nullptr,
+                                                       _Float16* __restrict__ x16 = nullptr) {
   __shared__ float red[4];
   float gs;
   if (mode == 0) {
@@ -118,6 +129,7 @@ __global__ void __launch_bounds__(256) quantize_kernel(const T* __restrict__ x, 
     const int64_t boff = (int64_t)row * nbc + cb;
     *reinterpret_cast<uint2*>(codes + boff * 8) = make_uint2(w0, w1);
     scales[boff] = (uint8_t)s;
+    store_expanded(x16, boff, w0, w1, s);
   }
 }
 
@@ -179,7 +191,8 @@ __global__ void __launch_bounds__(1024) quantize_small_kernel(const T* __restric
                                                               const float* __restrict__ given = nullptr,
                                                               uint32_t npart = 0,
                                                               uint32_t* __restrict__ zero2 = nullptr,
-                                                              uint32_t nzero2 = 0) {
+                                                              uint32_t nzero2 = 0,
+                                                              _Float16* __restrict__ x16 = nullptr) {
   __shared__ float red[16];
   for (uint32_t i = threadIdx.x; i < nzero; i += 1024u) zero[i] = 0u;
   for (uint32_t i = threadIdx.x; i < nzero2; i += 1024u) zero2[i] = 0u;
@@ -207,6 +220,7 @@ __global__ void __launch_bounds__(1024) quantize_small_kernel(const T* __restric
     const int64_t boff = (int64_t)row * nbc + cb;
     *reinterpret_cast<uint2*>(codes + boff * 8) = make_uint2(w0, w1);
     scales[boff] = (uint8_t)sc;
+    store_expanded(x16, boff, w0, w1, sc);
   }
 }
 
@@ -231,7 +245,8 @@ size_t quantize_ws_bytes(int64_t rows, int64_t cols, int gs_mode) {
 template <typename T>
 static int quantize_launch_t(const T* x, int64_t rows, int64_t cols, int64_t ld, uint8_t* codes,
                              uint8_t* scales, float* gs, int gs_mode, float* partials,
-                             const float* ext_partials, uint32_t ext_npart, hipStream_t st) {
+                             const float* ext_partials, uint32_t ext_npart, hipStream_t st,
+                             _Float16* x16 = nullptr) {
   const uint32_t nbc = (uint32_t)(cols / kBlock);
   const uint32_t nblocks = (uint32_t)rows * nbc;
   uint32_t qgrid = (nblocks + 255u) / 256u;
@@ -239,7 +254,8 @@ static int quantize_launch_t(const T* x, int64_t rows, int64_t cols, int64_t ld,
   if (qgrid < 1) qgrid = 1;
   if (gs_mode == 0 && ext_partials == nullptr && nblocks <= kSmallBlocks) {
     const int s0 = launch_begin(KC_QUANTIZE, st);
-    hipLaunchKernelGGL(quantize_small_kernel<T>, dim3(1), dim3(1024), 0, st, x, nbc, nblocks, ld, gs, codes, scales);
+    hipLaunchKernelGGL(quantize_small_kernel<T>, dim3(1), dim3(1024), 0, st, x, nbc, nblocks, ld, gs, codes, scales,
+                       (uint32_t*)nullptr, 0u, (const float*)nullptr, 0u, (uint32_t*)nullptr, 0u, x16);
     launch_end(s0, st);
   } else if (gs_mode == 0 && ext_partials == nullptr) {
     const uint32_t g = amax_grid(nblocks);
@@ -248,23 +264,26 @@ static int quantize_launch_t(const T* x, int64_t rows, int64_t cols, int64_t ld,
     launch_end(s0, st);
     const int s1 = launch_begin(KC_QUANTIZE, st);
     hipLaunchKernelGGL(quantize_kernel<T>, dim3(qgrid), dim3(256), 0, st, x, nbc, nblocks, ld,
-                       (const float*)partials, g, gs, 0, codes, scales);
+                       (const float*)partials, g, gs, 0, codes, scales, (const float*)nullptr, (const float*)nullptr,
+                       x16);
     launch_end(s1, st);
   } else {
     const int s1 = launch_begin(KC_QUANTIZE, st);
     if (gs_mode == 0)
       hipLaunchKernelGGL(quantize_kernel<T>, dim3(qgrid), dim3(256), 0, st, x, nbc, nblocks, ld,
-                         ext_partials, ext_npart, gs, 0, codes, scales);
+                         ext_partials, ext_npart, gs, 0, codes, scales, (const float*)nullptr, (const float*)nullptr,
+                         x16);
     else
       hipLaunchKernelGGL(quantize_kernel<T>, dim3(qgrid), dim3(256), 0, st, x, nbc, nblocks, ld,
-                         (const float*)nullptr, 0u, gs, 1, codes, scales);
+                         (const float*)nullptr, 0u, gs, 1, codes, scales, (const float*)nullptr,
+                         (const float*)nullptr, x16);
     launch_end(s1, st);
   }
   return hipGetLastError() == hipSuccess ? 0 : 7;
 }
 
 int quantize_launch(const void* x, int x_dtype, int64_t rows, int64_t cols, int64_t ld, uint8_t* codes,
-                    uint8_t* scales, float* gs, int gs_mode, void* ws, hipStream_t st) {
+                    uint8_t* scales, float* gs, int gs_mode, void* ws, hipStream_t st, _Float16* x16) {
   float* partials = reinterpret_cast<float*>(ws);
   if (gs_mode == 2) {
     // the workspace holds kAmaxSlots partial maxima of |x| (written on the
@@ -272,15 +291,15 @@ int quantize_launch(const void* x, int x_dtype, int64_t rows, int64_t cols, int6
     // reduces them, forms the global scale and quantises, in one launch
     if (x_dtype == 1)
       return quantize_launch_t(reinterpret_cast<const uint16_t*>(x), rows, cols, ld, codes, scales, gs, 0, nullptr,
-                               partials, kAmaxSlots, st);
+                               partials, kAmaxSlots, st, x16);
     return quantize_launch_t(reinterpret_cast<const float*>(x), rows, cols, ld, codes, scales, gs, 0, nullptr,
-                             partials, kAmaxSlots, st);
+                             partials, kAmaxSlots, st, x16);
   }
   if (x_dtype == 1)
     return quantize_launch_t(reinterpret_cast<const uint16_t*>(x), rows, cols, ld, codes, scales, gs,
-                             gs_mode, partials, nullptr, 0, st);
+                             gs_mode, partials, nullptr, 0, st, x16);
   return quantize_launch_t(reinterpret_cast<const float*>(x), rows, cols, ld, codes, scales, gs, gs_mode,
-                           partials, nullptr, 0, st);
+                           partials, nullptr, 0, st, x16);
 }
 
 // ---- allocation-free variant ---------------------------------------------------
@@ -375,8 +394,8 @@ int mlp_prologue_launch(const void* x, int x_dtype, int64_t rows, int64_t cols, 
 }
 
 int requant_f32_launch(const float* h, int64_t rows, int64_t cols, uint8_t* codes, uint8_t* scales,
-                       float* gs, const float* partials, uint32_t npart, hipStream_t st) {
-  return quantize_launch_t(h, rows, cols, cols, codes, scales, gs, 0, nullptr, partials, npart, st);
+                       float* gs, const float* partials, uint32_t npart, hipStream_t st, _Float16* h16) {
+  return quantize_launch_t(h, rows, cols, cols, codes, scales, gs, 0, nullptr, partials, npart, st, h16);
 }
 
 }  // namespace nvfp4

@@ -124,6 +124,7 @@ def test_whole_mlp_validation_and_workspace():
     assert call(xa=FAKE + 4) == m.ERR_ALIGN                          # x_amax
     assert call(ya=FAKE + 4) == m.ERR_ALIGN                          # y_amax
     assert call(sz=ctypes.c_size_t(64)) == m.ERR_WORKSPACE
+    assert call(xa=FAKE, ya=FAKE) == m.ERR_ARG                       # x_amax and y_amax alias
     assert f(None, m.BF16, 5120, None, 0, 5120, 17408, z, z, z, z, z, None, m.F32, 5120, None, None, None,
              None) == m.OK                                           # T = 0: no-op
     # workspace: decode path [H][partials][down partial sums][tickets]; large batches: the separate calls' sum

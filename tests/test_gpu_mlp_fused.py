@@ -5,7 +5,8 @@
   the decode path runs the same kernels, and its in-kernel split-K finish adds
   the same partial sums in the same order as the reduction launch it replaces.
 - Launches: 4 for every decode batch (1 to 8 tokens at the full 5120 / 17408
-  shape), the separate calls' count otherwise.
+  shape); otherwise the separate calls' count minus their two expansion
+  launches (the quantisers write the f16 operand copies).
 - Staged against the oracle at T = 1 and 5 (full size) like every MLP test.
 - The output amax slots and a chained second layer that takes them as x_amax.
 - Two calls in a row give identical results (the tickets are cleared by each
@@ -87,7 +88,7 @@ def test_shapes_equal_separate_calls(t, k, i):
     before = m.launch_count()
     run_device_mlp(xbits, wdev)
     separate = m.launch_count() - before
-    assert launches == (decode_launches(t) if t <= 8 else separate), (launches, separate)
+    assert launches == (decode_launches(t) if t <= 8 else separate - 2), (launches, separate)
 
 
 @pytest.mark.parametrize("t", [1, 2])
@@ -148,6 +149,20 @@ def test_output_amax_and_chained_layer(t):
     assert_nvfp4_equal(to_host(hq_a), to_host(hq_b), "H~")
     assert torch.equal(y_a, y_b)
     assert la == (decode_launches(t) if t <= 8 else lb - 1), (la, lb)
+
+
+@pytest.mark.parametrize("t", [64, 1024])
+def test_large_batch_full_size_equals_separate_calls(t):
+    """Large batches at the full 5120 / 17408 shape (the long-prefill ubatch):
+    the quantisers' f16 operand copies replace the expansion launches, and x~,
+    H~ and y stay bit-identical to the separate calls; 6 launches (5 when the
+    input amax comes from the previous layer's slots)."""
+    import mlp_prefill_amd as m
+    p = WORKLOADS["mlp_prefill_1024x5120x17408"].params
+    announce(f"whole MLP large batch T={t} full size vs separate calls")
+    wdev, _ = _weights(p["K"], p["I"], (p["wg_seed"], p["wu_seed"], p["wd_seed"]))
+    launches = assert_same_as_separate(bf16_normal(p["x_seed"] + t, (t, p["K"])), wdev, f"T{t}")
+    assert launches == 6, launches
 
 
 def test_repeated_calls_any_workspace(decode_weights):
