@@ -104,6 +104,18 @@ __device__ __forceinline__ float load_coherent(const float* p) {
 // every store of this wave acknowledged (and no memory access moved across)
 __device__ __forceinline__ void stores_done() { asm volatile("s_waitcnt vmcnt(0)" : : : "memory"); }
 
+// Output (t, c) = sum * gs_a * gs_b stored (float32 or bf16); returns |stored value|.
+__device__ __forceinline__ float store_output(const GemmArgs& p, int64_t t, int64_t c, float sum) {
+  const float v = sum * (p.a_gs[0] * p.b_gs[0]);
+  if (p.c_bf16) {
+    const uint32_t b = f32_to_bf16_bits(v);
+    reinterpret_cast<uint16_t*>(p.c)[t * p.ldc + c] = (uint16_t)b;
+    return fabsf(__uint_as_float(b << 16));
+  }
+  reinterpret_cast<float*>(p.c)[t * p.ldc + c] = v;
+  return fabsf(v);
+}
+
 // Output (t, c) of a split-K store: the partial sums in split order (the
 // order and arithmetic of the reduction kernels), scaled by gs_a * gs_b and
 // stored; returns |stored value|.  Loads go eight splits at a time.
@@ -119,14 +131,7 @@ __device__ __forceinline__ float finish_output(const GemmArgs& p, int64_t t, int
     for (int k = 0; k < 8; ++k) acc += v[k];
   }
   for (; s < p.splits; ++s) acc += load_coherent(p.split_out + (int64_t)s * plane + idx);
-  const float v = acc * (p.a_gs[0] * p.b_gs[0]);
-  if (p.c_bf16) {
-    const uint32_t b = f32_to_bf16_bits(v);
-    reinterpret_cast<uint16_t*>(p.c)[t * p.ldc + c] = (uint16_t)b;
-    return fabsf(__uint_as_float(b << 16));
-  }
-  reinterpret_cast<float*>(p.c)[t * p.ldc + c] = v;
-  return fabsf(v);
+  return store_output(p, t, c, acc);
 }
 
 // Ticket of a column group after this caller's partial sums are stored and
@@ -1273,230 +1278,350 @@ __global__ void __launch_bounds__(256) gemv_kernel(GemmArgs p) {
   }
 }
 
-// ---- weight stream for 3 to 8 tokens on the 4x4x4 matrix core ----------------------------
-// With a few tokens the dot products of the one/two-token stream grow with T
-// on the vector ALU.  v_mfma_f32_4x4x4_16b_f16 runs 16 independent 4x4x4
-// products per wave: for block b = lane / 4, A row i and B row j are the four
-// f16 values of lanes 4b+i and 4b+j, and C[i][j] accumulates in lane 4b+j,
-// entry i.  Here B row j is weight row j of a quad of rows and A row i is
-// token i of a set of four, so one instruction adds 4 tokens x 4 rows of
-// products over four K positions of each of 16 segments; the token count
-// costs matrix-core time only.
+// ---- weight stream for 3 to 8 tokens on the 16x16x32 matrix core ------------------------
+// v_mfma_f32_16x16x32_f16 takes, in lane l, row l % 16 of the 16-row operand
+// A and K positions 8 * (l / 16) .. +7; the same lanes hold column l % 16 of
+// B at those K positions; lane l receives D[4 * (l / 16) + r][l % 16] in entry
+// r.  Here A holds the tokens (rows past M repeat the last token: computed,
+// never stored) and B sixteen weight rows, so one instruction takes 16 rows x
+// 32 K positions of the weights for every token at once, at the full
+// matrix-core rate (the 4x4x4 instruction runs at a fraction of it).
 //
-// Lane l takes row j = l % 4 of the quad and segment s = l / 4 of a 1024-wide
-// unit of K: the four blocks 4s .. 4s+3 (32 code bytes and 4 scale bytes,
-// 16 lanes per row: 256 contiguous bytes of each of 4 rows per load).  The
-// weights are expanded to code * scale in f16 (exact) as in the large-batch
-// kernels.  A work-group of WK waves covers 16 output columns; wave w takes
-// unit split * WK + w and keeps that unit's activation in registers.  The
-// segment partial sums are added within each 16-lane row by DPP shifts, and
-// the rows and waves through LDS in a fixed order.
-constexpr int kQdCols = 16;   // output columns per work-group
-constexpr int kQdMaxWaves = 8;
+// A wave is one work item: a column tile (16 output columns of the gate/up
+// pair, i.e. 16 gate rows and the same 16 up rows; or 32 output columns of
+// one weight) and one split of K.  Its K range is cut into stages of 256
+// elements; each stage of the tile's 32 weight rows (128 code bytes and 16
+// scale bytes per row) and of the tokens is copied from global memory straight
+// into the wave's own LDS ring by the LDS DMA path, kTlDepth stages ahead.
+// Every copy instruction moves whole 128-byte lines of a few rows (the
+// row-contiguous pattern a weight stream needs to run near the HBM rate), and
+// copies in flight hold no registers, so a CU keeps ~100 KiB of weights in
+// flight.  The wave reads a landed stage back in fragment layout and expands
+// it in registers (code * scale, exact in f16, as in the large-batch kernels).
+//
+// Within a stage, lane quarter g = l / 16 takes K elements 64g .. 64g+63 of
+// each row and step s (0..7) feeds elements 64g + 8s .. +7 of them to the
+// matrix core: one permutation of K applied to both operands leaves every
+// dot product as it is.  An LDS row is eight 16-byte units, unit u of row r
+// stored at position u ^ (r & 7), so the 8 lanes that read the same unit of 8
+// consecutive rows hit 8 different bank groups.
+//
+// The splits of a column tile store their partial sums (device-coherent
+// stores, as in the other weight streams); the wave that arrives last on the
+// tile's ticket (cleared by an earlier launch) adds them in split order and
+// runs the epilogue.  An unsplit tile runs it directly.  Without tickets (the
+// store epilogue of a separate call) the partial sums go to the reduction
+// launch.
+// Ring depth, waves per work-group and the target number of stages per split
+// of K: measured at 3-8 tokens on the 5120 / 17408 MLP, a shallow ring with
+// one-wave work-groups (about 13 waves per CU, bounded by LDS) beats deeper
+// rings with fewer waves, and 8-stage splits beat shorter ones.
+#ifndef NVFP4_TL_DEPTH
+#define NVFP4_TL_DEPTH 2
+#endif
+#ifndef NVFP4_TL_WAVES
+#define NVFP4_TL_WAVES 1
+#endif
+#ifndef NVFP4_TL_SPS
+#define NVFP4_TL_SPS 8
+#endif
+constexpr int kTlDepth = NVFP4_TL_DEPTH;
+constexpr int kTlWaves = NVFP4_TL_WAVES;
+constexpr int kTlMaxT = 8;
+constexpr int kTlStageK = 256;
+// Bytes of one stage in LDS: weight codes (32 rows x 8 units), weight scales
+// (32 rows x 16), token codes (8 rows x 8 units), token scales (16 slots x 16).
+constexpr int kTlBc = 0, kTlBs = 4096, kTlAc = 4608, kTlAs = 5632, kTlStage = 5888;
+constexpr int kTlDmaPerStage = 8;   // 4 + 2 weight copies, 2 token copies
 
-template <int NTS, bool DUAL, int EPI>
-__global__ void __launch_bounds__(kQdMaxWaves * 64) quad_kernel(GemmArgs p, int wk) {
-  typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
-  constexpr int NQ = DUAL ? kQdCols / 2 : kQdCols / 4;   // row quads per wave
-  constexpr int NV = NQ * NTS * 4;                       // accumulator values per lane
-  __shared__ float red[kQdMaxWaves * 4 * NV * 4];
-  __shared__ float hq[EPI == EPI_GLUQ ? 8 * kQdCols : 1];
-  __shared__ float redmax[kQdMaxWaves];
-  __shared__ uint32_t last_wg;
+// Wait until at most `ahead` stages' copies of this wave are in flight.
+__device__ __forceinline__ void tl_wait(int64_t ahead) {
+  static_assert(kTlDmaPerStage * (kTlDepth - 1) <= 63, "vmcnt range");
+  switch (ahead) {
+    case 0: asm volatile("s_waitcnt vmcnt(0)" : : : "memory"); break;
+    case 1: asm volatile("s_waitcnt vmcnt(%0)" : : "n"(kTlDmaPerStage) : "memory"); break;
+    case 2: asm volatile("s_waitcnt vmcnt(%0)" : : "n"(2 * kTlDmaPerStage) : "memory"); break;
+    case 3: asm volatile("s_waitcnt vmcnt(%0)" : : "n"(3 * kTlDmaPerStage) : "memory"); break;
+    case 4: asm volatile("s_waitcnt vmcnt(%0)" : : "n"(4 * kTlDmaPerStage) : "memory"); break;
+    case 5: asm volatile("s_waitcnt vmcnt(%0)" : : "n"(5 * kTlDmaPerStage) : "memory"); break;
+    case 6: asm volatile("s_waitcnt vmcnt(%0)" : : "n"(6 * kTlDmaPerStage) : "memory"); break;
+    default: asm volatile("s_waitcnt vmcnt(%0)" : : "n"(7 * kTlDmaPerStage) : "memory"); break;
+  }
+  __builtin_amdgcn_sched_barrier(0);
+}
+
+template <bool DUAL, int EPI>
+__global__ void __launch_bounds__(kTlWaves * 64) tile_kernel(GemmArgs p) {
+  static_assert(kTlDepth >= 1 && kTlDepth <= 8, "ring depth");
+  __shared__ __align__(16) uint8_t lds[kTlWaves * kTlDepth * kTlStage];
+  constexpr int CW = DUAL ? 16 : 32;                      // output columns per tile
   const int lane = threadIdx.x & 63;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int j = lane & 3, s = lane >> 2;
   const int64_t N = p.N, K = p.K, M = p.M;
-  const int64_t ctiles = (N + kQdCols - 1) / kQdCols;
-  const int64_t split = blockIdx.x / ctiles;
-  const int64_t n0 = (blockIdx.x - split * ctiles) * kQdCols;
-  const int64_t u = split * wk + w;                       // this wave's unit of K
+  const int64_t ntile = (N + CW - 1) / CW;
+  const int64_t item = (int64_t)blockIdx.x * kTlWaves + w;
+  if (item >= ntile * (int64_t)p.splits) return;         // no barrier below: a wave may leave
+  const int64_t split = item / ntile, ct = item - split * ntile;
+  const int64_t n0 = ct * CW;
+  const int64_t st0 = split * (int64_t)p.chunks_per_split;   // first stage of this split
+  const int64_t nst_all = K / kTlStageK;
+  const int64_t nst = (nst_all - st0) < (int64_t)p.chunks_per_split ? (nst_all - st0) : (int64_t)p.chunks_per_split;
   const int64_t kb = K >> 1, ks = K >> 4;
 
-  // weight row of this lane in quad q
-  auto row_ptrs = [&](int q, const uint8_t*& cp, const uint8_t*& sp) {
-    int64_t row;
-    const uint8_t *cbase, *sbase;
-    if constexpr (DUAL) {
-      row = n0 + 2 * q + (j & 1);
-      cbase = j < 2 ? p.b_codes : p.u_codes;
-      sbase = j < 2 ? p.b_scales : p.u_scales;
-    } else {
-      row = n0 + 4 * q + j;
-      cbase = p.b_codes;
-      sbase = p.b_scales;
-    }
-    row = row < N ? row : N - 1;                            // columns past N: valid rows, never stored
-    cp = cbase + row * kb + u * 512 + s * 32;
-    sp = sbase + row * ks + u * 64 + s * 4;
-  };
-  struct Slot {
-    u32x4 c0, c1;
-    uint32_t sc;
-  };
-  auto load = [&](int q, Slot& sl) {
-    const uint8_t *cp, *sp;
-    row_ptrs(q, cp, sp);
-    sl.c0 = *reinterpret_cast<const u32x4*>(cp);
-    sl.c1 = *reinterpret_cast<const u32x4*>(cp + 16);
-    sl.sc = *reinterpret_cast<const uint32_t*>(sp);
-  };
-
-  f32x4 acc[NQ][NTS];
-#pragma unroll
-  for (int q = 0; q < NQ; ++q)
-#pragma unroll
-    for (int ts = 0; ts < NTS; ++ts) acc[q][ts] = (f32x4){0.f, 0.f, 0.f, 0.f};
-  Slot ring[2];
-  load(0, ring[0]);
-  __builtin_amdgcn_sched_barrier(0);
-  load(1, ring[1]);
-  __builtin_amdgcn_sched_barrier(0);
-  // activation: token 4*ts + j (the A row of this lane), elements 64 s .. 64 s + 63 of the unit
-  // (expanded here from the NVFP4 activation: 32 code bytes and 4 scale bytes)
-  f16x8 xa[NTS][8];
-#pragma unroll
-  for (int ts = 0; ts < NTS; ++ts) {
-    const int64_t t = 4 * ts + j;
-    if (t < M) {
-      const u32x4* cp = reinterpret_cast<const u32x4*>(p.a_codes + t * kb + u * 512 + s * 32);
-      const u32x4 c0 = cp[0], c1 = cp[1];
-      const uint32_t sc = *reinterpret_cast<const uint32_t*>(p.a_scales + t * ks + u * 64 + s * 4);
-#pragma unroll
-      for (int e = 0; e < 8; ++e) xa[ts][e] = expand8(e < 4 ? c0[e] : c1[e - 4], (sc >> (8 * (e >> 1))) & 0xFFu);
-    } else {
-#pragma unroll
-      for (int e = 0; e < 8; ++e)
-#pragma unroll
-        for (int i = 0; i < 8; ++i) xa[ts][e][i] = (_Float16)0.f;
-    }
-  }
-
-#pragma unroll
-  for (int q = 0; q < NQ; ++q) {
-    Slot& sl = ring[q & 1];
-#pragma unroll
-    for (int b = 0; b < 4; ++b) {
-      const uint32_t w0 = b < 2 ? sl.c0[2 * b] : sl.c1[2 * b - 4];
-      const uint32_t w1 = b < 2 ? sl.c0[2 * b + 1] : sl.c1[2 * b - 3];
-      const uint32_t scb = (sl.sc >> (8 * b)) & 0xFFu;
-      const f16x8 lo = expand8(w0, scb), hi = expand8(w1, scb);
-      const f16x4 bk[4] = {{lo[0], lo[1], lo[2], lo[3]}, {lo[4], lo[5], lo[6], lo[7]},
-                           {hi[0], hi[1], hi[2], hi[3]}, {hi[4], hi[5], hi[6], hi[7]}};
-#pragma unroll
-      for (int ts = 0; ts < NTS; ++ts) {
-        const f16x8& x0 = xa[ts][2 * b];
-        const f16x8& x1 = xa[ts][2 * b + 1];
-        const f16x4 ak[4] = {{x0[0], x0[1], x0[2], x0[3]}, {x0[4], x0[5], x0[6], x0[7]},
-                             {x1[0], x1[1], x1[2], x1[3]}, {x1[4], x1[5], x1[6], x1[7]}};
-#pragma unroll
-        for (int k = 0; k < 4; ++k) acc[q][ts] = __builtin_amdgcn_mfma_f32_4x4x4f16(ak[k], bk[k], acc[q][ts], 0, 0, 0);
-      }
-    }
-    __builtin_amdgcn_sched_barrier(0);
-    if (q + 2 < NQ) load(q + 2, sl);
-    __builtin_amdgcn_sched_barrier(0);
-  }
-
-  // segments within each 16-lane row (lanes 16r + 4s' + j, s' = 0..3): two DPP
-  // shifts leave the row's sum in s' = 3; those 16 lanes write it to LDS
-  const bool writer = (lane & 12) == 12;
-  const int r = lane >> 4;
-#pragma unroll
-  for (int q = 0; q < NQ; ++q)
-#pragma unroll
-    for (int ts = 0; ts < NTS; ++ts)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        float v = acc[q][ts][i];
-        v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x114, 0xF, 0xF, true));
-        v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x118, 0xF, 0xF, true));
-        if (writer) red[((w * 4 + r) * NV + (q * NTS + ts) * 4 + i) * 4 + j] = v;
-      }
-  __syncthreads();
-
-  // sum over the 4 rows of each wave and over the waves, in order; one thread per output
-  const int nthreads = (int)blockDim.x;
-  auto total = [&](int vi, int jj) {
-    float t = 0.f;
-    for (int w2 = 0; w2 < wk; ++w2)
-#pragma unroll
-      for (int r2 = 0; r2 < 4; ++r2) t += red[((w2 * 4 + r2) * NV + vi) * 4 + jj];
-    return t;
-  };
+  // Buffer resources based at the tile's first weight row (rows past N read
+  // row N-1: valid memory, never stored) and at the first token.
+  const int64_t nrow = (N - n0) < (DUAL ? 16 : 32) ? (N - n0) : (DUAL ? 16 : 32);
+  const i32x4 rb = buf_desc(p.b_codes + n0 * kb, nrow * kb);
+  const i32x4 rbs = buf_desc(p.b_scales + n0 * ks, nrow * ks);
+  i32x4 ru = rb, rus = rbs;
   if constexpr (DUAL) {
-    const float alpha = p.a_gs[0] * p.b_gs[0], alpha_u = p.a_gs[0] * p.u_gs[0];
-    float hmax = 0.f;
-    for (int o = (int)threadIdx.x; o < NV * 2; o += nthreads) {
-      const int vi = o >> 1, jj = o & 1;
-      const int q = vi / (NTS * 4), ts = (vi / 4) % NTS, i = vi & 3;
-      const int64_t t = 4 * ts + i, c = 2 * q + jj;
-      const float h = silu_mul(total(vi, jj) * alpha, total(vi, jj + 2) * alpha_u);
-      if (t < M) {
-        if constexpr (EPI == EPI_GLU) {
-          p.h[t * N + n0 + c] = h;
-          hmax = fmaxf(hmax, fabsf(h));
-        } else {
-          hq[t * kQdCols + c] = h;
+    ru = buf_desc(p.u_codes + n0 * kb, nrow * kb);
+    rus = buf_desc(p.u_scales + n0 * ks, nrow * ks);
+  }
+  const i32x4 ra = buf_desc(p.a_codes, M * kb);
+  const i32x4 ras = buf_desc(p.a_scales, M * ks);
+
+  // Lane offsets of the copies (fixed for the whole loop; the stage goes in the
+  // scalar offset).  Code copy d writes LDS units 64d + l: row 8d + l/8 of the
+  // tile (with the gate/up pair, copies 2 and 3 hold the up rows), swizzled
+  // unit l % 8, i.e. source unit (l % 8) ^ (l / 8).  Scale copy e writes row
+  // 16e + l/4 (the up rows for e = 1 with the pair), 4-byte piece l % 4.
+  const uint32_t su = (uint32_t)((lane & 7) ^ (lane >> 3));
+  uint32_t vb[4], vs[2];
+#pragma unroll
+  for (int d = 0; d < 4; ++d) {
+    int64_t r = DUAL ? 8 * (d & 1) + (lane >> 3) : 8 * d + (lane >> 3);
+    r = r < nrow ? r : nrow - 1;
+    vb[d] = (uint32_t)(r * kb) + su * 16u;
+  }
+#pragma unroll
+  for (int e = 0; e < 2; ++e) {
+    int64_t r = DUAL ? (lane >> 2) : 16 * e + (lane >> 2);
+    r = r < nrow ? r : nrow - 1;
+    vs[e] = (uint32_t)(r * ks) + (uint32_t)(lane & 3) * 4u;
+  }
+  const int64_t tc = (lane >> 3) < M ? (lane >> 3) : M - 1;
+  const int64_t tsc = (lane >> 2) < M ? (lane >> 2) : M - 1;
+  const uint32_t va = (uint32_t)(tc * kb) + su * 16u;
+  const uint32_t vas = (uint32_t)(tsc * ks) + (uint32_t)(lane & 3) * 4u;
+
+  const uint32_t ring = (uint32_t)w * (kTlDepth * kTlStage);   // this wave's ring (byte offset in lds)
+  const uint32_t ring_addr = lds_addr(lds) + ring;
+  auto issue = [&](int64_t stg, uint32_t buf) {
+    const uint32_t sc = (uint32_t)stg * 128u, ss = (uint32_t)stg * 16u;
+    const uint32_t b = ring_addr + buf * kTlStage;
+#pragma unroll
+    for (int d = 0; d < 4; ++d) dma_b128((DUAL && d >= 2) ? ru : rb, vb[d], sc, b + kTlBc + d * 1024);
+#pragma unroll
+    for (int e = 0; e < 2; ++e) dma_b32((DUAL && e >= 1) ? rus : rbs, vs[e], ss, b + kTlBs + e * 256);
+    dma_b128(ra, va, sc, b + kTlAc);
+    dma_b32(ras, vas, ss, b + kTlAs);
+  };
+
+  // Fragment offsets of this lane within a stage: row t of each 16-row tile
+  // (t = l % 16), quarter g = l / 16 (units 2g and 2g+1, scale piece g).
+  const int t = lane & 15, g = lane >> 4;
+  uint32_t ob[2][2], obs[2], oa[2];
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+#pragma unroll
+    for (int h = 0; h < 2; ++h) ob[j][h] = kTlBc + (uint32_t)((16 * j + t) * 8 + ((2 * g + h) ^ (t & 7))) * 16u;
+    obs[j] = kTlBs + (uint32_t)(16 * j + t) * 16u + 4u * g;
+  }
+#pragma unroll
+  for (int h = 0; h < 2; ++h) oa[h] = kTlAc + (uint32_t)((t & 7) * 8 + ((2 * g + h) ^ (t & 7))) * 16u;
+  const uint32_t oas = kTlAs + (uint32_t)t * 16u + 4u * g;
+
+#pragma unroll
+  for (int d = 0; d < kTlDepth; ++d)
+    if (d < nst) issue(st0 + d, (uint32_t)d);
+
+  f32x4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
+  for (int64_t i = 0; i < nst; ++i) {
+    const int64_t left = nst - 1 - i;
+    tl_wait(left < kTlDepth - 1 ? left : kTlDepth - 1);
+    const uint32_t buf = (uint32_t)(i % kTlDepth);
+    const uint8_t* sb = lds + ring + buf * kTlStage;
+    u32x4 bc[2][2], ac[2];
+    uint32_t bs[2], as;
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+#pragma unroll
+      for (int h = 0; h < 2; ++h) bc[j][h] = *reinterpret_cast<const u32x4*>(sb + ob[j][h]);
+      bs[j] = *reinterpret_cast<const uint32_t*>(sb + obs[j]);
+    }
+#pragma unroll
+    for (int h = 0; h < 2; ++h) ac[h] = *reinterpret_cast<const u32x4*>(sb + oa[h]);
+    as = *reinterpret_cast<const uint32_t*>(sb + oas);
+    // the reads above have returned before the buffer is refilled
+    asm volatile("s_waitcnt lgkmcnt(0)" : : : "memory");
+    __builtin_amdgcn_sched_barrier(0);
+    if (i + kTlDepth < nst) issue(st0 + i + kTlDepth, buf);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int s = 0; s < 8; ++s) {
+      const int h = s >> 2, wd = s & 3, sh = 8 * (s >> 1);
+      const f16x8 a = expand8(ac[h][wd], (as >> sh) & 0xFFu);
+      const f16x8 b0 = expand8(bc[0][h][wd], (bs[0] >> sh) & 0xFFu);
+      const f16x8 b1 = expand8(bc[1][h][wd], (bs[1] >> sh) & 0xFFu);
+      acc0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b0, acc0, 0, 0, 0);
+      acc1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b1, acc1, 0, 0, 0);
+    }
+  }
+
+  // ---- epilogue: lane (t, g) holds tokens 4g + r (r = 0..3) of tile column t ----------
+  if constexpr (DUAL) {
+    const int64_t c = n0 + t;                    // N % 16 == 0: every column exists
+    float gv[4], uv[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      gv[r] = acc0[r];
+      uv[r] = acc1[r];
+    }
+    if (p.splits > 1) {
+      // partial sums [splits][M][2N]: gate at column c, up at N + c
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int64_t tok = 4 * g + r;
+        if (tok < M) {
+          float* dst = p.split_out + (split * M + tok) * 2 * N + c;
+          store_coherent(dst, gv[r]);
+          store_coherent(dst + N, uv[r]);
         }
       }
+      stores_done();
+      uint32_t last = 0;
+      if (lane == 0) last = last_arrival(p.tickets + ct, p.splits) ? 1u : 0u;
+      if (!__builtin_amdgcn_readfirstlane((int)last)) return;
+      // eight splits' loads in flight at a time, added in split order
+      const int64_t plane = M * 2 * N;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) gv[r] = uv[r] = 0.f;
+      for (uint32_t s0 = 0; s0 < p.splits; s0 += 8u) {
+        float lg[4][8], lu[4][8];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int64_t tok = (4 * g + r) < M ? 4 * g + r : M - 1;
+#pragma unroll
+          for (int k = 0; k < 8; ++k) {
+            const uint32_t s2 = s0 + k < p.splits ? s0 + k : p.splits - 1;
+            const float* src = p.split_out + (int64_t)s2 * plane + tok * 2 * N + c;
+            lg[r][k] = load_coherent(src);
+            lu[r][k] = load_coherent(src + N);
+          }
+        }
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+#pragma unroll
+          for (int k = 0; k < 8; ++k)
+            if (s0 + k < p.splits) {
+              gv[r] += lg[r][k];
+              uv[r] += lu[r][k];
+            }
+      }
     }
+    const float alpha = p.a_gs[0] * p.b_gs[0], alpha_u = p.a_gs[0] * p.u_gs[0];
     if constexpr (EPI == EPI_GLU) {
-      hmax = block_max(hmax, redmax);
-      if (threadIdx.x == 0) p.partials[blockIdx.x] = hmax;
+      float hmax = 0.f;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int64_t tok = 4 * g + r;
+        if (tok < M) {
+          const float hv = silu_mul(gv[r] * alpha, uv[r] * alpha_u);
+          p.h[tok * N + c] = hv;
+          hmax = fmaxf(hmax, fabsf(hv));
+        }
+      }
+      hmax = wave_max(hmax);
+      if (lane == 0) p.partials[ct] = hmax;
     } else {
-      __syncthreads();
-      const int t = (int)threadIdx.x;
-      if (t < M) {
+      // the tile's 16 columns are one block per token: gather each token's
+      // row in the wave's (drained) ring, then lane tok < M quantises it
+      float* hq = reinterpret_cast<float*>(lds + ring);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) hq[(4 * g + r) * 16 + t] = silu_mul(gv[r] * alpha, uv[r] * alpha_u);
+      __builtin_amdgcn_wave_barrier();
+      if (lane < M) {
         float b16[16];
 #pragma unroll
-        for (int c = 0; c < 16; ++c) b16[c] = hq[t * kQdCols + c];
+        for (int k = 0; k < 16; ++k) b16[k] = hq[lane * 16 + k];
         uint32_t w0, w1;
         const uint32_t sc = quantize_block16(b16, p.q_gs[0], w0, w1);
-        *reinterpret_cast<uint2*>(p.q_codes + t * (N / 2) + n0 / 2) = make_uint2(w0, w1);
-        p.q_scales[t * (N / 16) + n0 / 16] = (uint8_t)sc;
+        *reinterpret_cast<uint2*>(p.q_codes + lane * (N / 2) + n0 / 2) = make_uint2(w0, w1);
+        p.q_scales[lane * (N / 16) + n0 / 16] = (uint8_t)sc;
       }
     }
   } else {
     const bool part = p.splits > 1 || p.force_split;
     const float alpha = p.a_gs[0] * p.b_gs[0];
-    for (int o = (int)threadIdx.x; o < NV * 4; o += nthreads) {
-      const int vi = o >> 2, jj = o & 3;
-      const int q = vi / (NTS * 4), ts = (vi / 4) % NTS, i = vi & 3;
-      const int64_t t = 4 * ts + i, c = n0 + 4 * q + jj;
-      if (t >= M || c >= N) continue;
-      const float v = total(vi, jj);
-      if (part) {
-        if (p.tickets != nullptr) store_coherent(p.split_out + (split * M + t) * N + c, v);
-        else p.split_out[(split * M + t) * N + c] = v;
-      } else if (p.c_bf16) {
-        reinterpret_cast<uint16_t*>(p.c)[t * p.ldc + c] = (uint16_t)f32_to_bf16_bits(v * alpha);
-      } else {
-        reinterpret_cast<float*>(p.c)[t * p.ldc + c] = v * alpha;
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int64_t tok = 4 * g + r, c = n0 + 16 * j + t;
+        if (tok >= M || c >= N) continue;
+        const float v = j ? acc1[r] : acc0[r];
+        if (part) {
+          float* dst = p.split_out + (split * M + tok) * N + c;
+          if (p.tickets != nullptr) store_coherent(dst, v);
+          else *dst = v;
+        } else if (p.c_bf16) {
+          reinterpret_cast<uint16_t*>(p.c)[tok * p.ldc + c] = (uint16_t)f32_to_bf16_bits(v * alpha);
+        } else {
+          reinterpret_cast<float*>(p.c)[tok * p.ldc + c] = v * alpha;
+        }
       }
-    }
     if (part && p.tickets != nullptr) {
-      // split-K finish: the work-group of this column tile that arrives last
-      // adds every split's partial sums (one thread per output)
-      const int64_t ct = blockIdx.x - split * ctiles;
       stores_done();
-      __syncthreads();
-      if (threadIdx.x == 0) last_wg = last_arrival(p.tickets + ct, p.splits) ? 1u : 0u;
-      __syncthreads();
-      if (last_wg) {
-        float am = 0.f;
-        for (int o = (int)threadIdx.x; o < (int)M * kQdCols; o += nthreads) {
-          const int64_t t = o / kQdCols, c = n0 + o % kQdCols;
-          if (c < N) am = fmaxf(am, finish_output(p, t, c));
-        }
-        if (p.amax_slots != nullptr) {
-          am = block_max(am, redmax);
-          if (threadIdx.x == 0)
-            atomicMax(reinterpret_cast<unsigned int*>(p.amax_slots + ct % kAmaxSlots), __float_as_uint(am));
-        }
+      uint32_t last = 0;
+      if (lane == 0) last = last_arrival(p.tickets + ct, p.splits) ? 1u : 0u;
+      if (!__builtin_amdgcn_readfirstlane((int)last)) return;
+      // the tile's M x 32 outputs (M <= 8: at most four per lane), their
+      // partial sums added in split order as finish_output does, with sixteen
+      // splits' loads of all four in flight at a time
+      static_assert(kTlMaxT * CW <= 4 * 64, "four outputs per lane");
+      const int64_t plane = M * N;
+      float sum[4] = {0.f, 0.f, 0.f, 0.f};
+      int64_t idx[4];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int o = lane + 64 * q;
+        const int64_t tok = o / CW < M ? o / CW : M - 1, c = n0 + o % CW < N ? n0 + o % CW : N - 1;
+        idx[q] = tok * N + c;
+      }
+      for (uint32_t s0 = 0; s0 < p.splits; s0 += 16u) {
+        float l[4][16];
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+#pragma unroll
+          for (int k = 0; k < 16; ++k) {
+            const uint32_t s2 = s0 + k < p.splits ? s0 + k : p.splits - 1;
+            l[q][k] = load_coherent(p.split_out + (int64_t)s2 * plane + idx[q]);
+          }
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+#pragma unroll
+          for (int k = 0; k < 16; ++k)
+            if (s0 + k < p.splits) sum[q] += l[q][k];
+      }
+      float am = 0.f;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int o = lane + 64 * q;
+        const int64_t tok = o / CW, c = n0 + o % CW;
+        if (tok < M && c < N) am = fmaxf(am, store_output(p, tok, c, sum[q]));
+      }
+      if (p.amax_slots != nullptr) {
+        am = wave_max(am);
+        if (lane == 0) atomicMax(reinterpret_cast<unsigned int*>(p.amax_slots + ct % kAmaxSlots), __float_as_uint(am));
       }
     }
   }
+}
+
+// Words cleared before a launch whose work items take tickets.
+__global__ void __launch_bounds__(256) clear_words_kernel(uint32_t* __restrict__ p, uint32_t n) {
+  for (uint32_t i = blockIdx.x * 256u + threadIdx.x; i < n; i += gridDim.x * 256u) p[i] = 0u;
 }
 
 // Output amax: each work-group writes the largest |stored value| it produced
@@ -1673,7 +1798,7 @@ __global__ void __launch_bounds__(256) splitk_reduce_quant_kernel(const float* _
 struct Plan {
   bool small;
   int gv_bpl;   // > 0: the one/two-token weight stream with BPL units of K per split
-  int qd_wk;    // > 0: the 3-8 token stream with WK waves (units of K) per split
+  bool tl;      // the 3-8 token stream (chunks_per_split: stages of 256 per split)
   uint32_t m_tiles, n_tiles, splits, chunks_per_split;
 };
 
@@ -1705,28 +1830,22 @@ static GvPlan plan_gemv(int64_t M, int64_t K, bool dual) {
   return pl;
 }
 
-// The 3-8 token stream: K a multiple of 1024; a work-group of WK waves (the
-// largest divisor of K/1024 up to 8) takes WK units.  The gate/up pair needs
-// one split (K <= 8192).
-struct QdPlan {
-  int wk;           // 0: not applicable
-  uint32_t splits;
+// The 3-8 token stream: K a multiple of 256 (one stage); K is cut into
+// splits of about NVFP4_TL_SPS stages, so that thousands of waves share the
+// weights; with the gate/up pair N is a multiple of 16 (whole column tiles).
+struct TlPlan {
+  bool ok;
+  uint32_t splits, sps;   // K splits, stages per split
 };
 
-static QdPlan plan_quad(int64_t M, int64_t K, bool dual) {
-  QdPlan pl{0, 0};
-  if (M < 3 || M > 8 || K % 1024 != 0) return pl;
-  const int64_t U = K / 1024;
-  int wk = 1;
-  for (int w = kQdMaxWaves; w >= 2; --w)
-    if (U % w == 0) {
-      wk = w;
-      break;
-    }
-  const int64_t S = U / wk;
-  if ((dual && S != 1) || S > 64) return pl;
-  pl.wk = wk;
-  pl.splits = (uint32_t)S;
+static TlPlan plan_tile(int64_t M, int64_t N, int64_t K, bool dual) {
+  TlPlan pl{false, 0, 0};
+  if (M < 3 || M > kTlMaxT || K < kTlStageK || K % kTlStageK != 0 || (dual && N % 16 != 0)) return pl;
+  const int64_t U = K / kTlStageK;
+  const int64_t S0 = (U + NVFP4_TL_SPS - 1) / NVFP4_TL_SPS;
+  pl.sps = cdiv(U, S0);
+  pl.splits = cdiv(U, pl.sps);
+  pl.ok = true;
   return pl;
 }
 
@@ -1743,14 +1862,14 @@ static Plan plan_store(int64_t M, int64_t N, int64_t K, int E, bool grouped) {
       pl.chunks_per_split = 0;
       return pl;
     }
-    const QdPlan qd = plan_quad(M, K, false);
-    if (qd.wk > 0) {
+    const TlPlan tl = plan_tile(M, N, K, false);
+    if (tl.ok) {
       pl.small = true;
-      pl.qd_wk = qd.wk;
+      pl.tl = true;
       pl.m_tiles = 1;
-      pl.n_tiles = cdiv(N, kQdCols);
-      pl.splits = qd.splits;
-      pl.chunks_per_split = 0;
+      pl.n_tiles = cdiv(N, 32);
+      pl.splits = tl.splits;
+      pl.chunks_per_split = tl.sps;
       return pl;
     }
   }
@@ -1805,13 +1924,22 @@ static void launch_gemv(const GemmArgs& g, int bpl, hipStream_t st) {
   launch_end(slot, st);
 }
 
-// g.splits holds the K splits; one work-group of wk waves per 16 columns per split.
+// g.splits holds the K splits and g.chunks_per_split the stages per split;
+// one wave per column tile per split.
 template <bool DUAL, int EPI>
-static void launch_quad(const GemmArgs& g, int wk, hipStream_t st) {
-  const uint32_t grid = cdiv(g.N, kQdCols) * g.splits;
+static void launch_tile(const GemmArgs& g, hipStream_t st) {
+  const uint32_t items = cdiv(g.N, DUAL ? 16 : 32) * g.splits;
   const int slot = launch_begin(EPI != EPI_STORE ? KC_GEMM_GLU : KC_GEMM_STORE, st);
-  if (g.M <= 4) hipLaunchKernelGGL((quad_kernel<1, DUAL, EPI>), dim3(grid), dim3(64 * wk), 0, st, g, wk);
-  else hipLaunchKernelGGL((quad_kernel<2, DUAL, EPI>), dim3(grid), dim3(64 * wk), 0, st, g, wk);
+  hipLaunchKernelGGL((tile_kernel<DUAL, EPI>), dim3(cdiv(items, kTlWaves)), dim3(kTlWaves * 64), 0, st, g);
+  launch_end(slot, st);
+}
+
+static void launch_clear(uint32_t* p, uint32_t n, int kc, hipStream_t st) {
+  uint32_t grid = cdiv(n, 256);
+  if (grid > 64u) grid = 64u;
+  if (grid < 1u) grid = 1u;
+  const int slot = launch_begin(kc, st);
+  hipLaunchKernelGGL(clear_words_kernel, dim3(grid), dim3(256), 0, st, p, n);
   launch_end(slot, st);
 }
 
@@ -1886,7 +2014,7 @@ int store_launch(Operand a, const int32_t* rows, const int32_t* off, int E, int6
   const Plan pl = plan_store(M, N, K, E, grouped);
   // the weight streams expand the activation themselves; a given copy needs no expansion
   if (a16_given != nullptr && !grouped) a16 = const_cast<_Float16*>(a16_given);
-  else if (grouped || (pl.gv_bpl == 0 && pl.qd_wk == 0)) launch_expand(a.codes, a.scales, rows, M, K, a16, st);
+  else if (grouped || (pl.gv_bpl == 0 && !pl.tl)) launch_expand(a.codes, a.scales, rows, M, K, a16, st);
   GemmArgs g = base_args(a16, a.gscale, w, M, N, K);
   g.a_codes = a.codes;
   g.a_scales = a.scales;
@@ -1906,7 +2034,7 @@ int store_launch(Operand a, const int32_t* rows, const int32_t* off, int E, int6
   g.force_split = c_amax != nullptr;
   if (grouped) launch_cfg<NVFP4_STORE_WN, NVFP4_STORE_TM, NVFP4_GROUPED_STORE_TN, false, true, EPI_STORE>(g, st);
   else if (pl.gv_bpl > 0) launch_gemv<false, EPI_STORE>(g, pl.gv_bpl, st);
-  else if (pl.qd_wk > 0) launch_quad<false, EPI_STORE>(g, pl.qd_wk, st);
+  else if (pl.tl) launch_tile<false, EPI_STORE>(g, st);
   else if (pl.small) launch_skinny<false, EPI_STORE>(g, st);
   else launch_cfg<NVFP4_STORE_WN, NVFP4_STORE_TM, NVFP4_STORE_TN, false, false, EPI_STORE>(g, st);
   // The reduction always runs (over zero rows when K was not split), so the
@@ -1920,13 +2048,33 @@ int store_launch(Operand a, const int32_t* rows, const int32_t* off, int E, int6
 static uint32_t glu_parts(int64_t M, int64_t N, int64_t K, int E, bool grouped) {
   if (grouped) return (cdiv(M, 32 * NVFP4_GLU_TM) + (uint32_t)E) * cdiv(N, 32 * NVFP4_GLU_WN);
   if (plan_gemv(M, K, true).bpl > 0) return cdiv(N, kGvCols);   // one partial per wave
-  if (plan_quad(M, K, true).wk > 0) return cdiv(N, kQdCols);     // one partial per work-group
+  if (plan_tile(M, N, K, true).ok) return cdiv(N, 16);          // one partial per column tile
   if (M <= 32) return cdiv(N, 32);
   return cdiv(M, 32 * NVFP4_GLU_TM) * cdiv(N, 32 * NVFP4_GLU_WN);
 }
 
+// The gate/up pair on the 3-8 token stream with K split: partial sums
+// [splits][M][2N] (gate, then up, per token) and one ticket per column tile.
+static size_t tile_dual_bytes(int64_t M, int64_t N, int64_t K) {
+  const TlPlan tl = plan_tile(M, N, K, true);
+  if (!tl.ok || tl.splits < 2) return 0;
+  return align256((size_t)tl.splits * M * 2 * N * 4) + align256((size_t)cdiv(N, 16) * 4);
+}
+
+// Points g at the split partial sums and tickets in `w` (tile_dual_bytes of
+// space) and clears the tickets; no-op when K is not split.
+static void tile_dual_setup(GemmArgs& g, const TlPlan& tl, char* w, hipStream_t st) {
+  g.splits = tl.splits;
+  g.chunks_per_split = tl.sps;
+  if (tl.splits < 2) return;
+  g.split_out = reinterpret_cast<float*>(w);
+  g.tickets = reinterpret_cast<uint32_t*>(w + align256((size_t)tl.splits * g.M * 2 * g.N * 4));
+  launch_clear(g.tickets, cdiv(g.N, 16), KC_GEMM_GLU, st);
+}
+
 size_t glu_ws_bytes(int64_t M, int64_t N, int64_t K, int E, bool grouped) {
-  return align256((size_t)M * N * 4) + align256((size_t)M * K * 2) + align256((size_t)glu_parts(M, N, K, E, grouped) * 4);
+  return align256((size_t)M * N * 4) + align256((size_t)M * K * 2) + align256((size_t)glu_parts(M, N, K, E, grouped) * 4) +
+         (grouped ? 0 : tile_dual_bytes(M, N, K));
 }
 
 int glu_launch(Operand a, const int32_t* a_rows, const int32_t* off, int E, int64_t M, Operand gt, Operand up,
@@ -1936,7 +2084,7 @@ int glu_launch(Operand a, const int32_t* a_rows, const int32_t* off, int E, int6
   float* h = reinterpret_cast<float*>(ws);
   _Float16* a16 = reinterpret_cast<_Float16*>(reinterpret_cast<char*>(ws) + align256((size_t)M * N * 4));
   float* partials = reinterpret_cast<float*>(reinterpret_cast<char*>(a16) + align256((size_t)M * K * 2));
-  const bool stream = !grouped && (plan_gemv(M, K, true).bpl > 0 || plan_quad(M, K, true).wk > 0);
+  const bool stream = !grouped && (plan_gemv(M, K, true).bpl > 0 || plan_tile(M, N, K, true).ok);
   if (a16_given != nullptr && !grouped) a16 = const_cast<_Float16*>(a16_given);
   else if (!stream) launch_expand(a.codes, a.scales, a_rows, M, K, a16, st);   // the streams expand x~ themselves
   GemmArgs g = base_args(a16, a.gscale, gt, M, N, K);
@@ -1956,8 +2104,9 @@ int glu_launch(Operand a, const int32_t* a_rows, const int32_t* off, int E, int6
     launch_cfg<NVFP4_GLU_WN, NVFP4_GLU_TM, 1, true, true, EPI_GLU>(g, st);
   } else if (const GvPlan gv = plan_gemv(M, K, true); gv.bpl > 0) {
     launch_gemv<true, EPI_GLU>(g, gv.bpl, st);
-  } else if (const QdPlan qd = plan_quad(M, K, true); qd.wk > 0) {
-    launch_quad<true, EPI_GLU>(g, qd.wk, st);
+  } else if (const TlPlan tl = plan_tile(M, N, K, true); tl.ok) {
+    tile_dual_setup(g, tl, reinterpret_cast<char*>(partials) + align256((size_t)glu_parts(M, N, K, E, grouped) * 4), st);
+    launch_tile<true, EPI_GLU>(g, st);
   } else if (M <= 32) {
     g.m_tiles = 1;
     g.n_tiles = cdiv(N, 32);
@@ -1971,13 +2120,15 @@ int glu_launch(Operand a, const int32_t* a_rows, const int32_t* off, int E, int6
   return requant_f32_launch(h, M, N, hq_codes, hq_scales, hq_gs, partials, glu_parts(M, N, K, E, grouped), st, hq16);
 }
 
-size_t glu_static_ws_bytes(int64_t M, int64_t K) { return align256((size_t)M * K * 2); }
+size_t glu_static_ws_bytes(int64_t M, int64_t N, int64_t K, bool grouped) {
+  return align256((size_t)M * K * 2) + (grouped ? 0 : tile_dual_bytes(M, N, K));
+}
 
 int glu_static_launch(Operand a, const int32_t* a_rows, const int32_t* off, int E, int64_t M, Operand gt,
                       Operand up, int64_t N, int64_t K, uint8_t* hq_codes, uint8_t* hq_scales, const float* hq_gs,
                       void* ws, hipStream_t st) {
   _Float16* a16 = reinterpret_cast<_Float16*>(ws);
-  const bool stream = !off && (plan_gemv(M, K, true).bpl > 0 || plan_quad(M, K, true).wk > 0);
+  const bool stream = !off && (plan_gemv(M, K, true).bpl > 0 || plan_tile(M, N, K, true).ok);
   if (!stream) launch_expand(a.codes, a.scales, a_rows, M, K, a16, st);   // the streams expand x~ themselves
   GemmArgs g = base_args(a16, a.gscale, gt, M, N, K);
   g.a_codes = a.codes;
@@ -1997,8 +2148,9 @@ int glu_static_launch(Operand a, const int32_t* a_rows, const int32_t* off, int 
     launch_cfg<NVFP4_GLU_WN, NVFP4_GLU_TM, 1, true, true, EPI_GLUQ>(g, st);
   } else if (const GvPlan gv = plan_gemv(M, K, true); gv.bpl > 0) {
     launch_gemv<true, EPI_GLUQ>(g, gv.bpl, st);
-  } else if (const QdPlan qd = plan_quad(M, K, true); qd.wk > 0) {
-    launch_quad<true, EPI_GLUQ>(g, qd.wk, st);
+  } else if (const TlPlan tl = plan_tile(M, N, K, true); tl.ok) {
+    tile_dual_setup(g, tl, reinterpret_cast<char*>(ws) + align256((size_t)M * K * 2), st);
+    launch_tile<true, EPI_GLUQ>(g, st);
   } else if (M <= 32) {
     g.m_tiles = 1;
     g.n_tiles = cdiv(N, 32);
@@ -2016,7 +2168,7 @@ int store_quant_launch(Operand a, int64_t M, Operand w, int64_t N, int64_t K, ui
   _Float16* a16 = reinterpret_cast<_Float16*>(ws);
   float* part = reinterpret_cast<float*>(reinterpret_cast<char*>(ws) + align256((size_t)M * K * 2));
   const Plan pl = plan_store(M, N, K, 1, false);
-  if (pl.gv_bpl == 0 && pl.qd_wk == 0) launch_expand(a.codes, a.scales, nullptr, M, K, a16, st);
+  if (pl.gv_bpl == 0 && !pl.tl) launch_expand(a.codes, a.scales, nullptr, M, K, a16, st);
   GemmArgs g = base_args(a16, a.gscale, w, M, N, K);
   g.a_codes = a.codes;
   g.a_scales = a.scales;
@@ -2027,7 +2179,7 @@ int store_quant_launch(Operand a, int64_t M, Operand w, int64_t N, int64_t K, ui
   g.m_tiles = pl.m_tiles;
   g.n_tiles = pl.n_tiles;
   if (pl.gv_bpl > 0) launch_gemv<false, EPI_STORE>(g, pl.gv_bpl, st);
-  else if (pl.qd_wk > 0) launch_quad<false, EPI_STORE>(g, pl.qd_wk, st);
+  else if (pl.tl) launch_tile<false, EPI_STORE>(g, st);
   else if (pl.small) launch_skinny<false, EPI_STORE>(g, st);
   else launch_cfg<NVFP4_STORE_WN, NVFP4_STORE_TM, NVFP4_STORE_TN, false, false, EPI_STORE>(g, st);
   int64_t blocks = (M * (N / 16) + 255) / 256;
@@ -2046,29 +2198,32 @@ int store_quant_launch(Operand a, int64_t M, Operand w, int64_t N, int64_t K, ui
 struct MlpDecodePlan {
   bool ok;
   GvPlan gu_gv;
-  QdPlan gu_qd;
+  TlPlan gu_tl;
   Plan dn;
   uint32_t groups;      // column groups of the down projection (tickets)
+  uint32_t gu_groups;   // column tiles of the gate/up pair when its K is split (tickets)
 };
 
 static MlpDecodePlan plan_mlp_decode(int64_t T, int64_t K, int64_t I) {
   MlpDecodePlan d{};
   if (T < 1 || T > 8 || T * (K / 16) > (int64_t)kSmallQuantBlocks) return d;
   d.gu_gv = plan_gemv(T, K, true);
-  d.gu_qd = plan_quad(T, K, true);
-  if (d.gu_gv.bpl == 0 && d.gu_qd.wk == 0) return d;
+  d.gu_tl = plan_tile(T, I, K, true);
+  if (d.gu_gv.bpl == 0 && !d.gu_tl.ok) return d;
   d.dn = plan_store(T, K, I, 1, false);
-  if (d.dn.gv_bpl == 0 && d.dn.qd_wk == 0) return d;
-  d.groups = d.dn.gv_bpl > 0 ? cdiv(K, kGvCols) : cdiv(K, kQdCols);
+  if (d.dn.gv_bpl == 0 && !d.dn.tl) return d;
+  d.groups = d.dn.gv_bpl > 0 ? cdiv(K, kGvCols) : cdiv(K, 32);
+  d.gu_groups = d.gu_tl.ok && d.gu_tl.splits > 1 ? cdiv(I, 16) : 0;
   d.ok = true;
   return d;
 }
 
 size_t mlp_ws_bytes(int64_t T, int64_t K, int64_t I) {
   const MlpDecodePlan d = plan_mlp_decode(T, K, I);
-  if (d.ok)   // [H float32][|H| partials][down partial sums][tickets]
+  if (d.ok)   // [H float32][|H| partials][down partial sums][tickets: down, gate/up][gate/up partial sums]
     return align256((size_t)T * I * 4) + align256((size_t)glu_parts(T, I, K, 1, false) * 4) +
-           align256((size_t)d.dn.splits * T * K * 4) + align256((size_t)d.groups * 4);
+           align256((size_t)d.dn.splits * T * K * 4) + align256((size_t)(d.groups + d.gu_groups) * 4) +
+           (d.gu_groups ? align256((size_t)d.gu_tl.splits * T * 2 * I * 4) : 0);
   // [quantiser partial maxima][gate/up workspace][down workspace]
   return align256(quantize_ws_bytes(T, K, 0)) + align256(glu_ws_bytes(T, I, K, 1, false)) +
          align256(store_ws_bytes(T, K, I, 1, false));
@@ -2108,10 +2263,13 @@ int mlp_launch(const void* x, int x_dtype, int64_t ld_x, int64_t T, int64_t K, i
   float* part = reinterpret_cast<float*>(w);
   w += align256((size_t)d.dn.splits * T * K * 4);
   uint32_t* tickets = reinterpret_cast<uint32_t*>(w);
+  w += align256((size_t)(d.groups + d.gu_groups) * 4);
+  float* gu_part = reinterpret_cast<float*>(w);
 
   // 1: quantise x; clear the tickets and the output-amax slots
-  int rc = mlp_prologue_launch(x, x_dtype, T, K, ld_x, xq_codes, xq_scales, xq_gs, x_amax, tickets, d.groups,
-                               reinterpret_cast<uint32_t*>(y_amax), y_amax ? kAmaxSlots : 0u, st);
+  int rc = mlp_prologue_launch(x, x_dtype, T, K, ld_x, xq_codes, xq_scales, xq_gs, x_amax, tickets,
+                               d.groups + d.gu_groups, reinterpret_cast<uint32_t*>(y_amax), y_amax ? kAmaxSlots : 0u,
+                               st);
   if (rc) return rc;
   // 2: gate/up weight stream, SiLU*up epilogue, float32 H and its partial maxima
   GemmArgs g = base_args(nullptr, xq_gs, wg, T, I, K);
@@ -2122,8 +2280,17 @@ int mlp_launch(const void* x, int x_dtype, int64_t ld_x, int64_t T, int64_t K, i
   g.u_gs = wu.gscale;
   g.h = h;
   g.partials = partials;
-  if (d.gu_gv.bpl > 0) launch_gemv<true, EPI_GLU>(g, d.gu_gv.bpl, st);
-  else launch_quad<true, EPI_GLU>(g, d.gu_qd.wk, st);
+  if (d.gu_gv.bpl > 0) {
+    launch_gemv<true, EPI_GLU>(g, d.gu_gv.bpl, st);
+  } else {
+    g.splits = d.gu_tl.splits;
+    g.chunks_per_split = d.gu_tl.sps;
+    if (d.gu_groups) {
+      g.split_out = gu_part;
+      g.tickets = tickets + d.groups;
+    }
+    launch_tile<true, EPI_GLU>(g, st);
+  }
   if (hipGetLastError() != hipSuccess) return 7;
   // 3: requantise H with its global scale
   if ((rc = requant_f32_launch(h, T, I, hq_codes, hq_scales, hq_gs, partials, npart, st))) return rc;
@@ -2142,8 +2309,9 @@ int mlp_launch(const void* x, int x_dtype, int64_t ld_x, int64_t T, int64_t K, i
   dn.amax_slots = y_amax;
   dn.m_tiles = d.dn.m_tiles;
   dn.n_tiles = d.dn.n_tiles;
+  dn.chunks_per_split = d.dn.chunks_per_split;
   if (d.dn.gv_bpl > 0) launch_gemv<false, EPI_STORE>(dn, d.dn.gv_bpl, st);
-  else launch_quad<false, EPI_STORE>(dn, d.dn.qd_wk, st);
+  else launch_tile<false, EPI_STORE>(dn, st);
   return hipGetLastError() == hipSuccess ? 0 : 7;
 }
 

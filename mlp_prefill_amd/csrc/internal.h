@@ -81,7 +81,10 @@ int store_launch(Operand a, const int32_t* rows, const int32_t* off, int E, int6
 
 // H = SiLU(A . G^T * gs_a*gs_g) * (A . U^T * gs_a*gs_u) (float32, row-major
 // [M][N], at the start of the workspace), then its NVFP4 requantisation with a
-// global scale over all M rows.  Dense or grouped as above.
+// global scale over all M rows.  Dense or grouped as above.  On the 3-8 token
+// stream with K split, the workspace also holds the split partial sums and the
+// column tiles' tickets, cleared by a launch of their own before the
+// contraction.
 size_t glu_ws_bytes(int64_t M, int64_t N, int64_t K, int E, bool grouped);
 // a16 (nullable): as for store_launch; hq16 (nullable): the requantisation
 // also writes the f16 copy of H~ there (for the down projection).
@@ -91,8 +94,9 @@ int glu_launch(Operand a, const int32_t* a_rows, const int32_t* off, int E, int6
 
 // The same GLU output (dense, or expert-grouped when `off` is given)
 // quantised in the contraction's epilogue with the given global scale *hq_gs
-// (two launches: expansion, contraction).  Workspace: the f16 copy of A.
-size_t glu_static_ws_bytes(int64_t M, int64_t K);
+// (two launches: expansion or ticket clearing, contraction).  Workspace: the
+// f16 copy of A, then (3-8 token stream, K split) partial sums and tickets.
+size_t glu_static_ws_bytes(int64_t M, int64_t N, int64_t K, bool grouped);
 int glu_static_launch(Operand a, const int32_t* a_rows, const int32_t* off, int E, int64_t M, Operand gt,
                       Operand up, int64_t N, int64_t K, uint8_t* hq_codes, uint8_t* hq_scales, const float* hq_gs,
                       void* ws, hipStream_t st);
@@ -106,8 +110,9 @@ int store_quant_launch(Operand a, int64_t M, Operand w, int64_t N, int64_t K, ui
 // Whole MLP: quantise x, gate/up + SiLU*up + requantisation, down projection.
 // For decode batches (T <= 8 with both projections on the weight streams) four
 // launches: quantise x (also clearing the split-K tickets), gate/up, requantise
-// H, and the down projection whose last-arriving wave per column group adds the
-// K-split partial sums (no reduction launch); otherwise the launch sequence of
+// H, and the down projection; in each contraction whose K is split the wave
+// that arrives last on a column group adds the partial sums (no reduction
+// launch); otherwise the launch sequence of
 // the separate calls.  x_amax (nullable): kAmaxSlots partial maxima of |x|
 // (the previous layer's y_amax); y_amax (nullable): the same for y.
 size_t mlp_ws_bytes(int64_t T, int64_t K, int64_t I);

@@ -296,7 +296,7 @@ int nvfp4_mlp_gu_act_static(nvfp4_tensor x, nvfp4_tensor w_gate, nvfp4_tensor w_
   if (T < 0 || K <= 0 || I <= 0 || K % 128 != 0 || I % 128 != 0) return NVFP4_ERR_SHAPE;
   if (T * (I / 16) >= ((int64_t)1 << 31) || T * (K / 16) >= ((int64_t)1 << 31)) return NVFP4_ERR_SHAPE;
   bool query;
-  int rc = workspace(ws, ws_bytes, T > 0 ? nvfp4::glu_static_ws_bytes(T, K) : 0, &query);
+  int rc = workspace(ws, ws_bytes, T > 0 ? nvfp4::glu_static_ws_bytes(T, I, K, false) : 0, &query);
   if (rc != NVFP4_OK || query) return rc;
   if (T == 0) return NVFP4_OK;
   if ((rc = check_tensor(x)) != NVFP4_OK || (rc = check_tensor(w_gate)) != NVFP4_OK ||
@@ -397,7 +397,7 @@ int nvfp4_grouped_gemm(nvfp4_tensor a, const int32_t* a_rows, const int32_t* gro
   if (M * (K / 16) >= ((int64_t)1 << 31)) return NVFP4_ERR_SHAPE;
   bool query;
   const size_t need = M == 0 ? 0
-                              : gluq ? nvfp4::glu_static_ws_bytes(M, K)
+                              : gluq ? nvfp4::glu_static_ws_bytes(M, N, K, true)
                               : glu  ? nvfp4::glu_ws_bytes(M, N, K, E, true)
                                      : nvfp4::store_ws_bytes(M, N, K, E, true);
   int rc = workspace(ws, ws_bytes, need, &query);

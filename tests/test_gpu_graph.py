@@ -114,8 +114,9 @@ def test_decode_stack_graph_replays_match_eager(t):
         other(x * 0.5)                         # eager work between replays
         torch.cuda.synchronize()
     # replays enqueue no new host-side launches; the eager calls between them
-    # do (5 per MLP call on the decode weight streams: quantise 1, gate/up 2, down 2)
-    assert m.launch_count() - launches_before == 3 * 2 * 5
+    # do (per MLP call on the decode weight streams: quantise 1, gate/up 2, down 2,
+    # and at 3-8 tokens one more that clears the split gate/up's tickets)
+    assert m.launch_count() - launches_before == 3 * 2 * (5 if t <= 2 else 6)
     # the buffers now hold the last replay (the eager calls between replays used `other`)
     stage_against_oracle(stack, xbits, wref, f"graph replay T={t}")
 

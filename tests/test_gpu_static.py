@@ -91,14 +91,17 @@ def test_down_quant_is_the_exact_quantisation_of_the_device_Y(t, i, k):
 
 
 def test_static_launch_counts_independent_of_T():
+    """Expansion + contraction, and expansion + contraction + quantising
+    reduction, at every T (K = I = 384: too short for the one/two-token stream
+    and not a multiple of 256, so no weight stream is involved)."""
     import mlp_prefill_amd as m
-    wdev, _ = _weights(256, 384, (8201, 8202, 8203))
+    wdev, _ = _weights(384, 384, (8201, 8202, 8203))
     counts = []
     for t in (1, 5, 64, 1024):
         announce(f"static launch count T={t}")
-        xq = dev_quantize(bf16_normal(8204, (t, 256)))
+        xq = dev_quantize(bf16_normal(8204, (t, 384)))
         hq = _with_gs(t, 384, 0.01)
-        yq = _with_gs(t, 256, 0.01)
+        yq = _with_gs(t, 384, 0.01)
         b0 = m.launch_count()
         m.nvfp4_mlp_gu_act_static(xq, wdev[0], wdev[1], hq)
         b1 = m.launch_count()

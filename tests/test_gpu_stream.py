@@ -7,10 +7,12 @@ ragged N (columns past N), fp32 and bf16
 outputs, the gate/up GLU with its requantisation, the quantising GLU
 epilogue, and per-token independence (token 0 of a 2-token call is
 bit-identical to the 1-token call: the accumulation order does not depend on
-the batch).  Three to eight tokens (4x4x4 matrix core): work-groups of 1-8
-waves, split K, the same epilogues and token independence.  Shapes next to
-those limits (K not a multiple of 1024, 9-16 tokens) take the MFMA weight
-stream and are checked the same way.
+the batch).  Three to eight tokens (16x16x32 matrix core, K a multiple of
+256): one to seventeen K splits, even and uneven, with the split partial sums
+added by the last-arriving wave of the gate/up pair's column tiles (and by the
+reduction launch for a separate store), ragged N, the same epilogues and
+token independence.  Shapes next to those limits (K not a multiple of 256,
+9-16 tokens) take the MFMA weight stream and are checked the same way.
 """
 import numpy as np
 import pytest
@@ -125,22 +127,26 @@ def test_stream_glu_quant_epilogue(t):
         assert np.array_equal(got.codes, ref.codes)
 
 
-# ---- the 3-8 token stream (4x4x4 matrix core) --------------------------------------
-# (M, N, K): work-groups of 1 (K = 17408: 17 splits), 2, 3, 5, 6, 7 and 8 waves
-QUAD_SHAPES = [(3, 64, 1024), (4, 48, 2048), (5, 200, 3072), (8, 128, 4096), (5, 96, 5120), (6, 100, 5120),
-               (7, 36, 8192), (8, 160, 7168), (8, 20, 6144), (5, 5120, 17408), (3, 332, 17408)]
+# ---- the 3-8 token stream (16x16x32 matrix core) ------------------------------------
+# (M, N, K): K / 256 stages cut into splits of about 8 stages -- one split (768,
+# 1024, 1280, 2048), even splits (3072, 4096, 6144, 7168, 8192) and uneven ones
+# (2304: 5 + 4, 4352: 6 + 6 + 5, 5120: 7 + 7 + 6, 17408: 8 x 8 + 4); N multiples
+# of 32 and ragged
+TILE_SHAPES = [(3, 64, 1024), (4, 48, 2048), (5, 200, 3072), (8, 128, 4096), (5, 96, 5120), (6, 100, 5120),
+               (7, 36, 8192), (8, 160, 7168), (8, 20, 6144), (5, 5120, 17408), (3, 332, 17408),
+               (3, 48, 768), (7, 40, 1280), (8, 100, 2304), (4, 36, 4352)]
 
 
-@pytest.mark.parametrize("m,n,k", QUAD_SHAPES, ids=[f"{m}x{n}x{k}" for m, n, k in QUAD_SHAPES])
-def test_quad_stream_gemm(m, n, k):
+@pytest.mark.parametrize("m,n,k", TILE_SHAPES, ids=[f"{m}x{n}x{k}" for m, n, k in TILE_SHAPES])
+def test_tile_stream_gemm(m, n, k):
     test_stream_gemm(m, n, k)
 
 
-def test_quad_stream_token_independence():
-    """Rows 0-2 of a 5-token product (two token sets) equal the 3-token product
-    (one set) bit for bit, and row 0 of the 3-token product does not depend on
-    rows 1-2."""
-    announce("quad stream token independence 5/3 x 256 x 5120")
+def test_tile_stream_token_independence():
+    """Rows 0-2 of a 5-token product equal the 3-token product bit for bit, and
+    row 0 of the 3-token product does not depend on rows 1-2 (each token is a
+    row of the matrix-core tile; rows past the batch repeat the last token)."""
+    announce("tile stream token independence 5/3 x 256 x 5120")
     xb = bf16_normal(811, (5, 5120))
     wb = bf16_normal(812, (256, 5120), sigma=0.02)
     a5, b = dev_quantize(xb), dev_quantize(wb)
@@ -154,22 +160,23 @@ def test_quad_stream_token_independence():
     assert np.array_equal(y3[0].view(np.uint32), y3b[0].view(np.uint32))
 
 
-QUAD_GLU = [(3, 1024, 256), (4, 3072, 128), (5, 5120, 640), (6, 7168, 384), (8, 4096, 1024)]
+# gate/up K in 1 split (1024, 1280), 2 (3072, 4096), 3 uneven (5120), 4 (7168)
+TILE_GLU = [(3, 1024, 256), (4, 3072, 128), (5, 5120, 640), (6, 7168, 384), (8, 4096, 1024), (7, 1280, 512)]
 
 
-@pytest.mark.parametrize("t,k,i", QUAD_GLU, ids=[f"T{t}_K{k}_I{i}" for t, k, i in QUAD_GLU])
-def test_quad_stream_mlp(t, k, i):
+@pytest.mark.parametrize("t,k,i", TILE_GLU, ids=[f"T{t}_K{k}_I{i}" for t, k, i in TILE_GLU])
+def test_tile_stream_mlp(t, k, i):
     test_stream_mlp(t, k, i)
 
 
 @pytest.mark.parametrize("t", [3, 5, 8])
-def test_quad_stream_glu_quant_epilogue(t):
+def test_tile_stream_glu_quant_epilogue(t):
     test_stream_glu_quant_epilogue(t)
 
 
-# ---- batches around the stream limits: K not a multiple of 1024 (3 tokens, MFMA weight
+# ---- batches around the stream limits: K not a multiple of 256 (3 tokens, MFMA weight
 # stream) and 9-16 tokens (MFMA weight stream) --------------------------------------------
-MFMA_SHAPES = [(3, 48, 768), (9, 64, 1280), (12, 200, 5120), (16, 96, 2048), (16, 100, 17408), (11, 5120, 17408),
+MFMA_SHAPES = [(3, 48, 640), (9, 64, 1280), (12, 200, 5120), (16, 96, 2048), (16, 100, 17408), (11, 5120, 17408),
               (13, 36, 4352)]
 
 
@@ -192,12 +199,13 @@ def test_mfma_stream_glu_quant_epilogue(t):
 
 
 def test_stream_launch_counts():
-    """One launch set per batch: the weight streams (1-8 tokens, K a multiple of
-    1024) expand the activation themselves, and an activation of at most 4096
-    blocks is quantised in one launch, so a dynamic-scale MLP call is 5
-    launches at every such T (quantise 1, gate/up 2, down 2) and the
-    static-scale pair 1 + 2; larger batches add the expansion launch of each
-    projection (7 here; static 2 + 3)."""
+    """One launch set per batch: the weight streams (1-8 tokens) expand the
+    activation themselves, and an activation of at most 4096 blocks is
+    quantised in one launch, so a dynamic-scale MLP call with the gate/up K in
+    one split is 5 launches at every such T (quantise 1, gate/up 2, down 2) and
+    the static-scale pair 1 + 2; larger batches add the expansion launch of
+    each projection (7 here; static 2 + 3).  A gate/up K in several splits on
+    the 3-8 token stream adds the launch that clears its tickets."""
     import mlp_prefill_amd as m
     from tests.test_gpu_mlp import run_device_mlp
     k, i = 1024, 2048
@@ -224,3 +232,9 @@ def test_stream_launch_counts():
     assert dyn[9] == dyn[64] == 7, dyn
     assert all(sta[t] == (1, 2) for t in (1, 2, 3, 5, 8)), sta
     assert sta[9] == sta[64] == (2, 3), sta
+    k, i = 3072, 1024                              # gate/up in 2 splits at 3-8 tokens
+    wdev, _ = _weights(k, i, (964, 965, 966))
+    for t, want in ((2, 5), (5, 6)):
+        b0 = m.launch_count()
+        run_device_mlp(bf16_normal(967, (t, k)), wdev)
+        assert m.launch_count() - b0 == want, (t, m.launch_count() - b0)
