@@ -98,15 +98,13 @@ __global__ void __launch_bounds__(256) quantize_kernel(const T* __restrict__ x, 
     // eight independent loads per step: the reduction is latency-bound when
     // there are thousands of partials (max is exact in any order)
     float m = 0.f;
-    uint32_t i = threadIdx.x;
-    for (; i + 7u * 256u < npart; i += 8u * 256u) {
+    for (uint32_t i = threadIdx.x; i < npart; i += 8u * 256u) {
       float v[8];
 #pragma unroll
-      for (int k = 0; k < 8; ++k) v[k] = partials[i + k * 256u];
+      for (int k = 0; k < 8; ++k) v[k] = i + k * 256u < npart ? partials[i + k * 256u] : 0.f;
 #pragma unroll
       for (int k = 0; k < 8; ++k) m = fmaxf(m, v[k]);
     }
-    for (; i < npart; i += 256u) m = fmaxf(m, partials[i]);
     m = block_max(m, red);
     gs = global_scale_from_amax(m);
     if (blockIdx.x == 0 && threadIdx.x == 0) *gs_ptr = gs;
@@ -169,18 +167,24 @@ __global__ void __launch_bounds__(256) rms_amax_kernel(const T* __restrict__ x, 
   if (threadIdx.x == 0) partials[blockIdx.x] = m;
 }
 
-// Small tensors (decode activations: at most kSmallBlocks blocks of 16): one
-// work-group of 1024 threads takes the amax, forms the global scale and
-// quantises, in one launch instead of two; a kernel boundary costs more than
-// this work.  The max is exact in any order and the per-block routine is the
-// same, so the result equals the two-kernel path bit for bit.
+// Small tensors (decode activations: at most kSmallBlocks = 4096 blocks of
+// 16) in one launch of ceil(blocks / 1024) work-groups of 1024 threads: every
+// work-group reduces the amax of the whole tensor itself -- each thread loads
+// up to four blocks, all in flight at once (at most 128 KiB of bf16, from L2
+// after the first work-group) -- and then quantises its own 1024 blocks, the
+// one whose index matches its work-group already in registers.  No
+// work-group waits for another, and a kernel boundary costs more than the
+// repeated reduction.  The max is exact in any order and the per-block
+// routine is the same, so the result equals the two-kernel path bit for bit.
 constexpr uint32_t kSmallBlocks = kSmallQuantBlocks;
+static_assert(kSmallBlocks <= 4u * 1024u, "four blocks per thread");
+static_assert(kAmaxSlots <= 1024u, "one given partial maximum per thread");
 
 //
 // As the first launch of a whole-MLP call it also clears `nzero` words
 // (the split-K tickets and output-amax slots the later launches of the call
-// use), and it can take the amax from `given` (npart partial maxima written by
-// an earlier call's output-amax epilogue) instead of reducing x.
+// use), and it can take the amax from `given` (npart <= 1024 partial maxima
+// written by an earlier call's output-amax epilogue) instead of reducing x.
 template <typename T>
 __global__ void __launch_bounds__(1024) quantize_small_kernel(const T* __restrict__ x, uint32_t nbc,
                                                               uint32_t nblocks, int64_t ld, float* gs_ptr,
@@ -194,34 +198,53 @@ __global__ void __launch_bounds__(1024) quantize_small_kernel(const T* __restric
                                                               uint32_t nzero2 = 0,
                                                               _Float16* __restrict__ x16 = nullptr) {
   __shared__ float red[16];
-  for (uint32_t i = threadIdx.x; i < nzero; i += 1024u) zero[i] = 0u;
-  for (uint32_t i = threadIdx.x; i < nzero2; i += 1024u) zero2[i] = 0u;
+  const uint32_t tid = blockIdx.x * 1024u + threadIdx.x, nthr = gridDim.x * 1024u;
+  for (uint32_t i = tid; i < nzero; i += nthr) zero[i] = 0u;
+  for (uint32_t i = tid; i < nzero2; i += nthr) zero2[i] = 0u;
+  float v[4][16];
   float m = 0.f;
   if (given != nullptr) {
-    for (uint32_t i = threadIdx.x; i < npart; i += 1024u) m = fmaxf(m, given[i]);
+    if (threadIdx.x < npart) m = given[threadIdx.x];
   } else {
-    for (uint32_t b = threadIdx.x; b < nblocks; b += 1024u) {
-      const uint32_t row = b / nbc, cb = b - row * nbc;
-      float v[16];
-      Load16<T>::run(x + (int64_t)row * ld + (int64_t)cb * kBlock, v);
 #pragma unroll
-      for (int i = 0; i < 16; ++i) m = fmaxf(m, fabsf(v[i]));
+    for (int q = 0; q < 4; ++q) {
+      const uint32_t b = threadIdx.x + q * 1024u;
+      if (b < nblocks) {
+        const uint32_t row = b / nbc, cb = b - row * nbc;
+        Load16<T>::run(x + (int64_t)row * ld + (int64_t)cb * kBlock, v[q]);
+      } else {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) v[q][i] = 0.f;
+      }
     }
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) m = fmaxf(m, fabsf(v[q][i]));
   }
   m = block_max(m, red);
   const float gs = global_scale_from_amax(m);
-  if (threadIdx.x == 0) *gs_ptr = gs;
-  for (uint32_t b = threadIdx.x; b < nblocks; b += 1024u) {
-    const uint32_t row = b / nbc, cb = b - row * nbc;
-    float v[16];
-    Load16<T>::run(x + (int64_t)row * ld + (int64_t)cb * kBlock, v);
-    uint32_t w0, w1;
-    const uint32_t sc = quantize_block16(v, gs, w0, w1);
-    const int64_t boff = (int64_t)row * nbc + cb;
-    *reinterpret_cast<uint2*>(codes + boff * 8) = make_uint2(w0, w1);
-    scales[boff] = (uint8_t)sc;
-    store_expanded(x16, boff, w0, w1, sc);
+  if (tid == 0) *gs_ptr = gs;
+  const uint32_t b = tid;
+  if (b >= nblocks) return;
+  const uint32_t row = b / nbc, cb = b - row * nbc;
+  float w[16];
+  if (given != nullptr) {
+    Load16<T>::run(x + (int64_t)row * ld + (int64_t)cb * kBlock, w);
+  } else {
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+      if (q == (int)blockIdx.x) {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) w[i] = v[q][i];
+      }
   }
+  uint32_t w0, w1;
+  const uint32_t sc = quantize_block16(w, gs, w0, w1);
+  const int64_t boff = (int64_t)row * nbc + cb;
+  *reinterpret_cast<uint2*>(codes + boff * 8) = make_uint2(w0, w1);
+  scales[boff] = (uint8_t)sc;
+  store_expanded(x16, boff, w0, w1, sc);
 }
 
 // Work-groups of the quantiser: enough to fill the chip, few enough that the
@@ -254,7 +277,8 @@ static int quantize_launch_t(const T* x, int64_t rows, int64_t cols, int64_t ld,
   if (qgrid < 1) qgrid = 1;
   if (gs_mode == 0 && ext_partials == nullptr && nblocks <= kSmallBlocks) {
     const int s0 = launch_begin(KC_QUANTIZE, st);
-    hipLaunchKernelGGL(quantize_small_kernel<T>, dim3(1), dim3(1024), 0, st, x, nbc, nblocks, ld, gs, codes, scales,
+    hipLaunchKernelGGL(quantize_small_kernel<T>, dim3((nblocks + 1023u) / 1024u), dim3(1024), 0, st, x, nbc,
+                       nblocks, ld, gs, codes, scales,
                        (uint32_t*)nullptr, 0u, (const float*)nullptr, 0u, (uint32_t*)nullptr, 0u, x16);
     launch_end(s0, st);
   } else if (gs_mode == 0 && ext_partials == nullptr) {
@@ -381,13 +405,14 @@ int mlp_prologue_launch(const void* x, int x_dtype, int64_t rows, int64_t cols, 
   const uint32_t nbc = (uint32_t)(cols / kBlock);
   const uint32_t nblocks = (uint32_t)rows * nbc;
   const uint32_t npart = x_amax ? kAmaxSlots : 0u;
+  const uint32_t grid = nblocks > 0 ? (nblocks + 1023u) / 1024u : 1u;
   const int s0 = launch_begin(KC_QUANTIZE, st);
   if (x_dtype == 1)
-    hipLaunchKernelGGL(quantize_small_kernel<uint16_t>, dim3(1), dim3(1024), 0, st,
+    hipLaunchKernelGGL(quantize_small_kernel<uint16_t>, dim3(grid), dim3(1024), 0, st,
                        reinterpret_cast<const uint16_t*>(x), nbc, nblocks, ld, gs, codes, scales, zero, nzero, x_amax,
                        npart, zero2, nzero2);
   else
-    hipLaunchKernelGGL(quantize_small_kernel<float>, dim3(1), dim3(1024), 0, st, reinterpret_cast<const float*>(x),
+    hipLaunchKernelGGL(quantize_small_kernel<float>, dim3(grid), dim3(1024), 0, st, reinterpret_cast<const float*>(x),
                        nbc, nblocks, ld, gs, codes, scales, zero, nzero, x_amax, npart, zero2, nzero2);
   launch_end(s0, st);
   return hipGetLastError() == hipSuccess ? 0 : 7;
