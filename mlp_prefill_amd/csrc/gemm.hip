@@ -1806,7 +1806,7 @@ static uint32_t cdiv(int64_t a, int64_t b) { return (uint32_t)((a + b - 1) / b);
 
 // The weight stream takes M <= NVFP4_GV_MAXT tokens and K >= 1024 (a multiple
 // of 16; the last 1024-wide unit may be partial); a split covers BPL units (the
-// largest divisor of the unit count up to 5).  The gate/up pair needs whole
+// largest divisor of the unit count up to 5, else 2 with a shorter last split).  The gate/up pair needs whole
 // rows in one split (GLU epilogue), so there K <= 5120.
 struct GvPlan {
   int bpl;          // 0: not applicable
@@ -1823,7 +1823,12 @@ static GvPlan plan_gemv(int64_t M, int64_t K, bool dual) {
       bpl = b;
       break;
     }
-  const int64_t S = U / bpl;
+  // No divisor up to 5 (U prime, e.g. 17 units for K = 17408): two units per
+  // lane with a shorter last split beat one-unit splits (half the partial sums
+  // and twice the bytes per row and wave; measured on the 5120 x 17408 down
+  // projection at one token).
+  if (!dual && bpl == 1 && U > 2) bpl = 2;
+  const int64_t S = (U + bpl - 1) / bpl;          // the last split may hold fewer units
   if ((dual && S != 1) || S > 64) return pl;
   pl.bpl = bpl;
   pl.splits = (uint32_t)S;

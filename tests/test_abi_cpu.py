@@ -127,11 +127,18 @@ def test_whole_mlp_validation_and_workspace():
     assert call(xa=FAKE, ya=FAKE) == m.ERR_ARG                       # x_amax and y_amax alias
     assert f(None, m.BF16, 5120, None, 0, 5120, 17408, z, z, z, z, z, None, m.F32, 5120, None, None, None,
              None) == m.OK                                           # T = 0: no-op
-    # workspace: decode path [H][partials][down partial sums][tickets]; large batches: the separate calls' sum
+    # workspace: decode path [H][partials][down partial sums][tickets][gate/up partial sums];
+    # large batches: the separate calls' sum
     s = _size()
     assert f(None, m.BF16, 5120, None, 1, 5120, 17408, z, z, z, z, z, None, m.F32, 5120, None, None,
              ctypes.byref(s), None) == m.OK
-    assert s.value == 17408 * 4 + 17408 // 4 * 4 + 17 * 5120 * 4 + 5120 // 4 * 4
+    # T = 1: the down projection's K = 17408 runs in 9 splits (8 of two 1024-wide units + 1)
+    assert s.value == 17408 * 4 + 17408 // 4 * 4 + 9 * 5120 * 4 + 5120 // 4 * 4
+    # T = 5 (16x16x32 stream, splits of 8 stages of 256): down 9 splits, gate/up 3 splits
+    # with its partial sums [3][5][2 x 17408] and 1088 tickets after the 160 of the down
+    assert f(None, m.BF16, 5120, None, 5, 5120, 17408, z, z, z, z, z, None, m.F32, 5120, None, None,
+             ctypes.byref(s), None) == m.OK
+    assert s.value == 5 * 17408 * 4 + 1088 * 4 + 9 * 5 * 5120 * 4 + 5120 + 3 * 5 * 2 * 17408 * 4
     assert f(None, m.BF16, 5120, None, 1024, 5120, 17408, z, z, z, z, z, None, m.F32, 5120, None, None,
              ctypes.byref(s), None) == m.OK
     assert s.value >= m.mlp_gu_act_ws_bytes(1024, 5120, 17408) + m.mlp_down_ws_bytes(1024, 17408, 5120)

@@ -1,8 +1,10 @@
 """The small-batch weight streams against the oracle.
 
 One or two tokens (K >= 1024): every split width (1 to 5 units of 1024),
-split K with a partial reduction (K = 7168: 7 splits of 1 unit, 8192: 2 of 4,
-17408: 17 of 1), a partial last unit (K = 1152, 1536, 2560, 4608, 8704, 9984),
+split K with a partial reduction (K = 8192: 2 splits of 4 units; a prime unit
+count takes splits of 2 with a shorter last one: 7168 = 3 x 2 + 1, 11264 =
+5 x 2 + 1, 17408 = 8 x 2 + 1), a partial last unit (K = 1152, 1536, 2560,
+4608, 8704, 9984, and 13056 = 6 x 2 + a partial unit),
 ragged N (columns past N), fp32 and bf16
 outputs, the gate/up GLU with its requantisation, the quantising GLU
 epilogue, and per-token independence (token 0 of a 2-token call is
@@ -51,12 +53,13 @@ def _gemm(a, b, m, n, dtype=torch.float32):
     return c.cpu().numpy() if dtype == torch.float32 else bf16_tensor_to_f32(c)
 
 
-# (M, N, K): K/1024 = 1, 2, 3, 4, 5 (one split), 8 (2 splits of 4), 7 (7 splits of 1),
-# 17 (17 splits of 1); N multiples of 16 and ragged
+# (M, N, K): K/1024 = 1, 2, 3, 4, 5 (one split), 8 (2 splits of 4), 7, 11, 17 (splits of 2,
+# the last one of 1); N multiples of 16 and ragged
 STREAM_SHAPES = [(1, 64, 1024), (2, 48, 2048), (1, 200, 3072), (2, 128, 4096), (1, 96, 5120), (2, 100, 5120),
                  (1, 36, 8192), (2, 160, 7168), (1, 5120, 17408), (2, 332, 17408),
                  # K not a multiple of 1024: the last unit is partial (lanes past K read nothing)
-                 (1, 5120, 8704), (2, 64, 4608), (1, 48, 2560), (2, 40, 1152), (1, 96, 9984)]
+                 (1, 5120, 8704), (2, 64, 4608), (1, 48, 2560), (2, 40, 1152), (1, 96, 9984),
+                 (1, 96, 11264), (2, 48, 13056)]
 
 
 @pytest.mark.parametrize("m,n,k", STREAM_SHAPES, ids=[f"{m}x{n}x{k}" for m, n, k in STREAM_SHAPES])
