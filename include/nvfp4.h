@@ -183,8 +183,9 @@ int nvfp4_rmsnorm_quantize_act(const void *x, int x_dtype, int64_t rows, int64_t
  * stores them ([llama] "Verified", MUL_MAT).  One launch set per
  * call whatever M is ([vllm] Fix directions 1): expansion of a~ to f16
  * (exact), the contraction, and a fixed-order split-K reduction (over zero
- * rows when K is not split); with M <= 8 and K a multiple of 1024 the
- * contraction is a weight stream that expands a~ itself, so two launches.
+ * rows when K is not split); with M <= 2 and K >= 1024, or 3 <= M <= 8 and
+ * K a multiple of 256, the contraction is a weight stream that expands a~
+ * itself, so two launches.
  * Accumulation in float32 (matrix cores, or dot products of exact f16
  * products on the one/two-token stream); every product is exact.
  *   a  : [M][K] NVFP4, b : [N][K] NVFP4 (one gscale each)
@@ -221,9 +222,11 @@ int nvfp4_gemm(nvfp4_tensor a, nvfp4_tensor b, int64_t M, int64_t N, int64_t K,
  *            the f16 copy of x~ (written on the matrix-core paths, unused by
  *            the weight streams) and the partial maxima of |H|
  * Three launches per call (expansion, contraction with the SiLU*up epilogue
- * and the |H| tile maxima, requantisation); two when T <= 8 and K is a
- * multiple of 1024 (the weight stream expands x~ itself).  One launch set per
- * batch: the count never grows with T within either range.
+ * and the |H| tile maxima, requantisation); two on the weight streams, which
+ * expand x~ themselves (T <= 2 with 1024 <= K <= 5120, or 3 <= T <= 8 with K
+ * a multiple of 256), except that at 3 <= T <= 8 a K above 2048 is split and
+ * one launch clears the column tiles' arrival tickets first (three).  One
+ * launch set per batch: the count never grows with T within a range.
  */
 int nvfp4_mlp_gu_act(nvfp4_tensor x, nvfp4_tensor w_gate, nvfp4_tensor w_up,
                      int64_t T, int64_t K, int64_t I, nvfp4_tensor h_out,
@@ -241,8 +244,8 @@ int nvfp4_mlp_gu_act(nvfp4_tensor x, nvfp4_tensor w_gate, nvfp4_tensor w_up,
  *        input amax, so the next nvfp4_quantize_act (NVFP4_GS_FROM_AMAX) is
  *        one launch
  *   ws : required, as for nvfp4_gemm (f16 copy of h~, split-K partials)
- * Three launches per call (two when T <= 8 and I is a multiple of 1024, as
- * for nvfp4_gemm).
+ * Three launches per call (two on the weight streams: T <= 2 with I >= 1024,
+ * or 3 <= T <= 8 with I a multiple of 256, as for nvfp4_gemm).
  */
 int nvfp4_mlp_down(nvfp4_tensor h, nvfp4_tensor w_down, int64_t T, int64_t I, int64_t K,
                    void *y, int y_dtype, int64_t ldy, float *y_amax, void *ws, size_t *ws_bytes, void *stream);
@@ -268,15 +271,17 @@ int nvfp4_mlp_down(nvfp4_tensor h, nvfp4_tensor w_down, int64_t T, int64_t I, in
  *            alternate two buffers
  *   ws     : required (size query as usual); contents unspecified on return
  * Decode batches -- T <= 8 with both projections on the weight streams (T <=
- * 2 with K >= 1024, or 3 <= T <= 8 with K a multiple of 1024; I >= 1024, or a
- * multiple of 1024 for 3 <= T <= 8; T * K <= 65536) -- take four launches:
- * (1) quantise x in one work-group, which also clears the per-column-group
- * tickets and the y_amax slots; (2) the gate/up weight stream with the
- * SiLU*up epilogue, float32 H and its partial maxima; (3) requantisation of H;
- * (4) the down weight stream, whose K splits are added, in split order, by
- * the last-arriving wave (or work-group) of each column group after an
- * agent-scope fence and a ticket increment -- nothing waits for anything, and
- * no reduction launch follows.  Other shapes run the separate calls' kernels
+ * 2 with 1024 <= K <= 5120 and I >= 1024, or 3 <= T <= 8 with K and I
+ * multiples of 256; T * K <= 65536) -- take four launches: (1) quantise x
+ * (one to four work-groups, each reducing the amax itself), which also clears
+ * the per-column-group arrival tickets and the y_amax slots; (2) the gate/up
+ * weight stream with the SiLU*up epilogue, float32 H and its partial maxima;
+ * (3) requantisation of H; (4) the down weight stream.  In each stream whose
+ * K is split, the splits store their partial sums with device-coherent
+ * stores and, once those are acknowledged, take a ticket of their column
+ * group; the arrival that completes the group adds the partial sums in split
+ * order and runs the epilogue -- nothing waits for anything, and no
+ * reduction launch follows.  Other shapes run the separate calls' kernels
  * minus their two expansion launches -- the quantisers of x and H also write
  * the f16 operand copies the matrix-core contractions read -- so six launches
  * (quantise 2, gate/up contraction, requantisation, down contraction, split-K
@@ -299,8 +304,9 @@ int nvfp4_mlp(const void *x, int x_dtype, int64_t ld_x, const float *x_amax, int
  *   x, w_gate, w_up, K, I : as nvfp4_mlp_gu_act
  *   h_out : [T][I] NVFP4; codes and scales written, gscale read
  *   ws    : required (the f16 copy of x~)
- * Two launches per call (expansion, contraction); one when T <= 8 and K is a
- * multiple of 1024.
+ * Two launches per call (expansion, contraction); one on the weight streams
+ * (as nvfp4_mlp_gu_act), where a split K at 3 <= T <= 8 instead takes the
+ * ticket-clearing launch (two).
  */
 int nvfp4_mlp_gu_act_static(nvfp4_tensor x, nvfp4_tensor w_gate, nvfp4_tensor w_up,
                             int64_t T, int64_t K, int64_t I, nvfp4_tensor h_out,
@@ -317,7 +323,7 @@ int nvfp4_mlp_gu_act_static(nvfp4_tensor x, nvfp4_tensor w_gate, nvfp4_tensor w_
  *   K multiple of 16;  y_out : [T][K] NVFP4 (codes, scales written)
  *   ws : required, as nvfp4_mlp_down
  * Three launches per call (expansion, contraction, quantising split
- * reduction); two when T <= 8 and I is a multiple of 1024.
+ * reduction); two on the weight streams (as nvfp4_mlp_down).
  */
 int nvfp4_mlp_down_quant(nvfp4_tensor h, nvfp4_tensor w_down, int64_t T, int64_t I, int64_t K,
                          nvfp4_tensor y_out, void *ws, size_t *ws_bytes, void *stream);
