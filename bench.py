@@ -269,6 +269,8 @@ def main():
                           "1024-token ubatch)",
                 "flops_per_launch": gemm_flops, "avg_launch_ms": gemm_ms, "launches_timed": n_gemm,
                 "arith": "f16 MFMA 32x32x16, fp32 accumulate (NVFP4 operands expanded exactly)",
+                "peak_kind": "dense f16 MFMA: the instruction the exact NVFP4 contraction runs on gfx950 (frac is "
+                             "against it); the fp4 peak is quoted in frac_of_fp4_dense_peak",
                 "frac_of_fp4_dense_peak": achieved / PEAK_FP4_TFLOPS}
     log(f"dominant kernel {gemm_ms:.3f} ms -> {achieved:.1f} TFLOP/s ({100 * achieved / PEAK_F16_TFLOPS:.1f}% of f16 peak)")
 
