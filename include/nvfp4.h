@@ -131,7 +131,7 @@ enum nvfp4_epilogue {
  *             16-byte aligned; gscale is formed from it exactly as COMPUTE
  *             would (the max is exact)
  * Two kernel launches (COMPUTE) or one (GIVEN, FROM_AMAX); a COMPUTE call on
- * at most 4096 blocks of 16 (rows * cols <= 65536, e.g. decode activations)
+ * at most 8192 blocks of 16 (rows * cols <= 131072, e.g. decode activations)
  * takes the amax, the global scale and the codes in one launch.  One launch
  * set per call, never one per row.
  */
@@ -183,7 +183,7 @@ int nvfp4_rmsnorm_quantize_act(const void *x, int x_dtype, int64_t rows, int64_t
  * stores them ([llama] "Verified", MUL_MAT).  One launch set per
  * call whatever M is ([vllm] Fix directions 1): expansion of a~ to f16
  * (exact), the contraction, and a fixed-order split-K reduction (over zero
- * rows when K is not split); with M <= 2 and K >= 1024, or 3 <= M <= 8 and
+ * rows when K is not split); with M <= 2 and K >= 1024, or 3 <= M <= 16 and
  * K a multiple of 256, the contraction is a weight stream that expands a~
  * itself, so two launches.
  * Accumulation in float32 (matrix cores, or dot products of exact f16
@@ -223,8 +223,8 @@ int nvfp4_gemm(nvfp4_tensor a, nvfp4_tensor b, int64_t M, int64_t N, int64_t K,
  *            the weight streams) and the partial maxima of |H|
  * Three launches per call (expansion, contraction with the SiLU*up epilogue
  * and the |H| tile maxima, requantisation); two on the weight streams, which
- * expand x~ themselves (T <= 2 with 1024 <= K <= 5120, or 3 <= T <= 8 with K
- * a multiple of 256), except that at 3 <= T <= 8 a K above 2048 is split and
+ * expand x~ themselves (T <= 2 with 1024 <= K <= 5120, or 3 <= T <= 16 with
+ * K a multiple of 256), except that at 3 <= T <= 16 a K above 2048 is split and
  * one launch clears the column tiles' arrival tickets first (three).  One
  * launch set per batch: the count never grows with T within a range.
  */
@@ -245,7 +245,7 @@ int nvfp4_mlp_gu_act(nvfp4_tensor x, nvfp4_tensor w_gate, nvfp4_tensor w_up,
  *        one launch
  *   ws : required, as for nvfp4_gemm (f16 copy of h~, split-K partials)
  * Three launches per call (two on the weight streams: T <= 2 with I >= 1024,
- * or 3 <= T <= 8 with I a multiple of 256, as for nvfp4_gemm).
+ * or 3 <= T <= 16 with I a multiple of 256, as for nvfp4_gemm).
  */
 int nvfp4_mlp_down(nvfp4_tensor h, nvfp4_tensor w_down, int64_t T, int64_t I, int64_t K,
                    void *y, int y_dtype, int64_t ldy, float *y_amax, void *ws, size_t *ws_bytes, void *stream);
@@ -270,10 +270,10 @@ int nvfp4_mlp_down(nvfp4_tensor h, nvfp4_tensor w_down, int64_t T, int64_t I, in
  *            not the same buffer as x_amax (NVFP4_ERR_ARG): chained layers
  *            alternate two buffers
  *   ws     : required (size query as usual); contents unspecified on return
- * Decode batches -- T <= 8 with both projections on the weight streams (T <=
- * 2 with 1024 <= K <= 5120 and I >= 1024, or 3 <= T <= 8 with K and I
- * multiples of 256; T * K <= 65536) -- take four launches: (1) quantise x
- * (one to four work-groups, each reducing the amax itself), which also clears
+ * Decode batches -- T <= 16 with both projections on the weight streams (T
+ * <= 2 with 1024 <= K <= 5120 and I >= 1024, or 3 <= T <= 16 with K and I
+ * multiples of 256; T * K <= 131072) -- take four launches: (1) quantise x
+ * (one to eight work-groups, each reducing the amax itself), which also clears
  * the per-column-group arrival tickets and the y_amax slots; (2) the gate/up
  * weight stream with the SiLU*up epilogue, float32 H and its partial maxima;
  * (3) requantisation of H; (4) the down weight stream.  In each stream whose
@@ -285,7 +285,7 @@ int nvfp4_mlp_down(nvfp4_tensor h, nvfp4_tensor w_down, int64_t T, int64_t I, in
  * minus their two expansion launches -- the quantisers of x and H also write
  * the f16 operand copies the matrix-core contractions read -- so six launches
  * (quantise 2, gate/up contraction, requantisation, down contraction, split-K
- * reduction), five with x_amax or an x of at most 4096 blocks of 16.
+ * reduction), five with x_amax or an x of at most 8192 blocks of 16.
  */
 int nvfp4_mlp(const void *x, int x_dtype, int64_t ld_x, const float *x_amax, int64_t T, int64_t K, int64_t I,
               nvfp4_tensor w_gate, nvfp4_tensor w_up, nvfp4_tensor w_down, nvfp4_tensor x_q, nvfp4_tensor h_q,
@@ -305,7 +305,7 @@ int nvfp4_mlp(const void *x, int x_dtype, int64_t ld_x, const float *x_amax, int
  *   h_out : [T][I] NVFP4; codes and scales written, gscale read
  *   ws    : required (the f16 copy of x~)
  * Two launches per call (expansion, contraction); one on the weight streams
- * (as nvfp4_mlp_gu_act), where a split K at 3 <= T <= 8 instead takes the
+ * (as nvfp4_mlp_gu_act), where a split K at 3 <= T <= 16 instead takes the
  * ticket-clearing launch (two).
  */
 int nvfp4_mlp_gu_act_static(nvfp4_tensor x, nvfp4_tensor w_gate, nvfp4_tensor w_up,

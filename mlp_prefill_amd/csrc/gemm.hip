@@ -1278,14 +1278,15 @@ __global__ void __launch_bounds__(256) gemv_kernel(GemmArgs p) {
   }
 }
 
-// ---- weight stream for 3 to 8 tokens on the 16x16x32 matrix core ------------------------
+// ---- weight stream for 3 to 16 tokens on the 16x16x32 matrix core -----------------------
 // v_mfma_f32_16x16x32_f16 takes, in lane l, row l % 16 of the 16-row operand
 // A and K positions 8 * (l / 16) .. +7; the same lanes hold column l % 16 of
 // B at those K positions; lane l receives D[4 * (l / 16) + r][l % 16] in entry
-// r.  Here A holds the tokens (rows past M repeat the last token: computed,
-// never stored) and B sixteen weight rows, so one instruction takes 16 rows x
-// 32 K positions of the weights for every token at once, at the full
-// matrix-core rate (the 4x4x4 instruction runs at a fraction of it).
+// r.  Here A holds the tokens (MT = 8 rows staged for 3-8 tokens, 16 for
+// 9-16; rows past M repeat the last token: computed, never stored) and B
+// sixteen weight rows, so one instruction takes 16 rows x 32 K positions of
+// the weights for every token at once, at the full matrix-core rate (the
+// 4x4x4 instruction runs at a fraction of it).
 //
 // A wave is one work item: a column tile (16 output columns of the gate/up
 // pair, i.e. 16 gate rows and the same 16 up rows; or 32 output columns of
@@ -1327,32 +1328,42 @@ __global__ void __launch_bounds__(256) gemv_kernel(GemmArgs p) {
 #endif
 constexpr int kTlDepth = NVFP4_TL_DEPTH;
 constexpr int kTlWaves = NVFP4_TL_WAVES;
-constexpr int kTlMaxT = 8;
+constexpr int kTlMaxT = 16;
 constexpr int kTlStageK = 256;
-// Bytes of one stage in LDS: weight codes (32 rows x 8 units), weight scales
-// (32 rows x 16), token codes (8 rows x 8 units), token scales (16 slots x 16).
-constexpr int kTlBc = 0, kTlBs = 4096, kTlAc = 4608, kTlAs = 5632, kTlStage = 5888;
-constexpr int kTlDmaPerStage = 8;   // 4 + 2 weight copies, 2 token copies
+// Bytes of one stage in LDS for MT (8 or 16) token rows: weight codes (32 rows
+// x 8 units), weight scales (32 rows x 16), token codes (MT rows x 8 units),
+// token scales (16 slots x 16); and the copies per stage (4 + 2 for the
+// weights, MT/8 + 1 for the tokens).
+template <int MT>
+struct TlCfg {
+  static_assert(MT == 8 || MT == 16, "8 or 16 token rows");
+  static constexpr int Bc = 0, Bs = 4096, Ac = 4608, As = Ac + MT * 128, Stage = As + 256;
+  static constexpr int Dma = 6 + MT / 8 + 1;
+};
 
-// Wait until at most `ahead` stages' copies of this wave are in flight.
+// Wait until at most `ahead` stages' copies (DMA copies each) of this wave are
+// in flight.
+template <int DMA>
 __device__ __forceinline__ void tl_wait(int64_t ahead) {
-  static_assert(kTlDmaPerStage * (kTlDepth - 1) <= 63, "vmcnt range");
+  static_assert(DMA * (kTlDepth - 1) <= 63, "vmcnt range");
   switch (ahead) {
     case 0: asm volatile("s_waitcnt vmcnt(0)" : : : "memory"); break;
-    case 1: asm volatile("s_waitcnt vmcnt(%0)" : : "n"(kTlDmaPerStage) : "memory"); break;
-    case 2: asm volatile("s_waitcnt vmcnt(%0)" : : "n"(2 * kTlDmaPerStage) : "memory"); break;
-    case 3: asm volatile("s_waitcnt vmcnt(%0)" : : "n"(3 * kTlDmaPerStage) : "memory"); break;
-    case 4: asm volatile("s_waitcnt vmcnt(%0)" : : "n"(4 * kTlDmaPerStage) : "memory"); break;
-    case 5: asm volatile("s_waitcnt vmcnt(%0)" : : "n"(5 * kTlDmaPerStage) : "memory"); break;
-    case 6: asm volatile("s_waitcnt vmcnt(%0)" : : "n"(6 * kTlDmaPerStage) : "memory"); break;
-    default: asm volatile("s_waitcnt vmcnt(%0)" : : "n"(7 * kTlDmaPerStage) : "memory"); break;
+    case 1: asm volatile("s_waitcnt vmcnt(%0)" : : "n"(DMA) : "memory"); break;
+    case 2: asm volatile("s_waitcnt vmcnt(%0)" : : "n"(2 * DMA) : "memory"); break;
+    case 3: asm volatile("s_waitcnt vmcnt(%0)" : : "n"(3 * DMA) : "memory"); break;
+    case 4: asm volatile("s_waitcnt vmcnt(%0)" : : "n"(4 * DMA) : "memory"); break;
+    case 5: asm volatile("s_waitcnt vmcnt(%0)" : : "n"(5 * DMA) : "memory"); break;
+    case 6: asm volatile("s_waitcnt vmcnt(%0)" : : "n"(6 * DMA) : "memory"); break;
+    default: asm volatile("s_waitcnt vmcnt(%0)" : : "n"(7 * DMA) : "memory"); break;
   }
   __builtin_amdgcn_sched_barrier(0);
 }
 
-template <bool DUAL, int EPI>
+template <int MT, bool DUAL, int EPI>
 __global__ void __launch_bounds__(kTlWaves * 64) tile_kernel(GemmArgs p) {
   static_assert(kTlDepth >= 1 && kTlDepth <= 8, "ring depth");
+  using L = TlCfg<MT>;
+  constexpr int kTlBc = L::Bc, kTlBs = L::Bs, kTlAc = L::Ac, kTlAs = L::As, kTlStage = L::Stage;
   __shared__ __align__(16) uint8_t lds[kTlWaves * kTlDepth * kTlStage];
   constexpr int CW = DUAL ? 16 : 32;                      // output columns per tile
   const int lane = threadIdx.x & 63;
@@ -1400,9 +1411,15 @@ __global__ void __launch_bounds__(kTlWaves * 64) tile_kernel(GemmArgs p) {
     r = r < nrow ? r : nrow - 1;
     vs[e] = (uint32_t)(r * ks) + (uint32_t)(lane & 3) * 4u;
   }
-  const int64_t tc = (lane >> 3) < M ? (lane >> 3) : M - 1;
+  // token copy d writes token rows 8d .. 8d+7 the same way (rows past M read
+  // the last token); the scale copy fills 16 token slots
+  uint32_t va[MT / 8];
+#pragma unroll
+  for (int d = 0; d < MT / 8; ++d) {
+    const int64_t tc = (8 * d + (lane >> 3)) < M ? (8 * d + (lane >> 3)) : M - 1;
+    va[d] = (uint32_t)(tc * kb) + su * 16u;
+  }
   const int64_t tsc = (lane >> 2) < M ? (lane >> 2) : M - 1;
-  const uint32_t va = (uint32_t)(tc * kb) + su * 16u;
   const uint32_t vas = (uint32_t)(tsc * ks) + (uint32_t)(lane & 3) * 4u;
 
   const uint32_t ring = (uint32_t)w * (kTlDepth * kTlStage);   // this wave's ring (byte offset in lds)
@@ -1414,7 +1431,8 @@ __global__ void __launch_bounds__(kTlWaves * 64) tile_kernel(GemmArgs p) {
     for (int d = 0; d < 4; ++d) dma_b128((DUAL && d >= 2) ? ru : rb, vb[d], sc, b + kTlBc + d * 1024);
 #pragma unroll
     for (int e = 0; e < 2; ++e) dma_b32((DUAL && e >= 1) ? rus : rbs, vs[e], ss, b + kTlBs + e * 256);
-    dma_b128(ra, va, sc, b + kTlAc);
+#pragma unroll
+    for (int d = 0; d < MT / 8; ++d) dma_b128(ra, va[d], sc, b + kTlAc + d * 1024);
     dma_b32(ras, vas, ss, b + kTlAs);
   };
 
@@ -1429,7 +1447,7 @@ __global__ void __launch_bounds__(kTlWaves * 64) tile_kernel(GemmArgs p) {
     obs[j] = kTlBs + (uint32_t)(16 * j + t) * 16u + 4u * g;
   }
 #pragma unroll
-  for (int h = 0; h < 2; ++h) oa[h] = kTlAc + (uint32_t)((t & 7) * 8 + ((2 * g + h) ^ (t & 7))) * 16u;
+  for (int h = 0; h < 2; ++h) oa[h] = kTlAc + (uint32_t)((MT == 16 ? t : (t & 7)) * 8 + ((2 * g + h) ^ (t & 7))) * 16u;
   const uint32_t oas = kTlAs + (uint32_t)t * 16u + 4u * g;
 
 #pragma unroll
@@ -1439,7 +1457,7 @@ __global__ void __launch_bounds__(kTlWaves * 64) tile_kernel(GemmArgs p) {
   f32x4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
   for (int64_t i = 0; i < nst; ++i) {
     const int64_t left = nst - 1 - i;
-    tl_wait(left < kTlDepth - 1 ? left : kTlDepth - 1);
+    tl_wait<L::Dma>(left < kTlDepth - 1 ? left : kTlDepth - 1);
     const uint32_t buf = (uint32_t)(i % kTlDepth);
     const uint8_t* sb = lds + ring + buf * kTlStage;
     u32x4 bc[2][2], ac[2];
@@ -1576,37 +1594,38 @@ __global__ void __launch_bounds__(kTlWaves * 64) tile_kernel(GemmArgs p) {
       uint32_t last = 0;
       if (lane == 0) last = last_arrival(p.tickets + ct, p.splits) ? 1u : 0u;
       if (!__builtin_amdgcn_readfirstlane((int)last)) return;
-      // the tile's M x 32 outputs (M <= 8: at most four per lane), their
-      // partial sums added in split order as finish_output does, with sixteen
-      // splits' loads of all four in flight at a time
-      static_assert(kTlMaxT * CW <= 4 * 64, "four outputs per lane");
+      // the tile's M x 32 outputs (NQ per lane), their partial sums added in
+      // split order as finish_output does, with SB splits' loads of all NQ in
+      // flight at a time
+      constexpr int NQ = MT * CW / 64, SB = 64 / NQ;
       const int64_t plane = M * N;
-      float sum[4] = {0.f, 0.f, 0.f, 0.f};
-      int64_t idx[4];
+      float sum[NQ];
+      int64_t idx[NQ];
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
+      for (int q = 0; q < NQ; ++q) {
+        sum[q] = 0.f;
         const int o = lane + 64 * q;
         const int64_t tok = o / CW < M ? o / CW : M - 1, c = n0 + o % CW < N ? n0 + o % CW : N - 1;
         idx[q] = tok * N + c;
       }
-      for (uint32_t s0 = 0; s0 < p.splits; s0 += 16u) {
-        float l[4][16];
+      for (uint32_t s0 = 0; s0 < p.splits; s0 += SB) {
+        float l[NQ][SB];
 #pragma unroll
-        for (int q = 0; q < 4; ++q)
+        for (int q = 0; q < NQ; ++q)
 #pragma unroll
-          for (int k = 0; k < 16; ++k) {
+          for (int k = 0; k < SB; ++k) {
             const uint32_t s2 = s0 + k < p.splits ? s0 + k : p.splits - 1;
             l[q][k] = load_coherent(p.split_out + (int64_t)s2 * plane + idx[q]);
           }
 #pragma unroll
-        for (int q = 0; q < 4; ++q)
+        for (int q = 0; q < NQ; ++q)
 #pragma unroll
-          for (int k = 0; k < 16; ++k)
+          for (int k = 0; k < SB; ++k)
             if (s0 + k < p.splits) sum[q] += l[q][k];
       }
       float am = 0.f;
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
+      for (int q = 0; q < NQ; ++q) {
         const int o = lane + 64 * q;
         const int64_t tok = o / CW, c = n0 + o % CW;
         if (tok < M && c < N) am = fmaxf(am, store_output(p, tok, c, sum[q]));
@@ -1798,7 +1817,7 @@ __global__ void __launch_bounds__(256) splitk_reduce_quant_kernel(const float* _
 struct Plan {
   bool small;
   int gv_bpl;   // > 0: the one/two-token weight stream with BPL units of K per split
-  bool tl;      // the 3-8 token stream (chunks_per_split: stages of 256 per split)
+  bool tl;      // the 3-16 token stream (chunks_per_split: stages of 256 per split)
   uint32_t m_tiles, n_tiles, splits, chunks_per_split;
 };
 
@@ -1835,7 +1854,7 @@ static GvPlan plan_gemv(int64_t M, int64_t K, bool dual) {
   return pl;
 }
 
-// The 3-8 token stream: K a multiple of 256 (one stage); K is cut into
+// The 3-16 token stream: K a multiple of 256 (one stage); K is cut into
 // splits of about NVFP4_TL_SPS stages, so that thousands of waves share the
 // weights; with the gate/up pair N is a multiple of 16 (whole column tiles).
 struct TlPlan {
@@ -1935,7 +1954,10 @@ template <bool DUAL, int EPI>
 static void launch_tile(const GemmArgs& g, hipStream_t st) {
   const uint32_t items = cdiv(g.N, DUAL ? 16 : 32) * g.splits;
   const int slot = launch_begin(EPI != EPI_STORE ? KC_GEMM_GLU : KC_GEMM_STORE, st);
-  hipLaunchKernelGGL((tile_kernel<DUAL, EPI>), dim3(cdiv(items, kTlWaves)), dim3(kTlWaves * 64), 0, st, g);
+  if (g.M <= 8)
+    hipLaunchKernelGGL((tile_kernel<8, DUAL, EPI>), dim3(cdiv(items, kTlWaves)), dim3(kTlWaves * 64), 0, st, g);
+  else
+    hipLaunchKernelGGL((tile_kernel<16, DUAL, EPI>), dim3(cdiv(items, kTlWaves)), dim3(kTlWaves * 64), 0, st, g);
   launch_end(slot, st);
 }
 
@@ -2058,7 +2080,7 @@ static uint32_t glu_parts(int64_t M, int64_t N, int64_t K, int E, bool grouped) 
   return cdiv(M, 32 * NVFP4_GLU_TM) * cdiv(N, 32 * NVFP4_GLU_WN);
 }
 
-// The gate/up pair on the 3-8 token stream with K split: partial sums
+// The gate/up pair on the 3-16 token stream with K split: partial sums
 // [splits][M][2N] (gate, then up, per token) and one ticket per column tile.
 static size_t tile_dual_bytes(int64_t M, int64_t N, int64_t K) {
   const TlPlan tl = plan_tile(M, N, K, true);
@@ -2211,7 +2233,7 @@ struct MlpDecodePlan {
 
 static MlpDecodePlan plan_mlp_decode(int64_t T, int64_t K, int64_t I) {
   MlpDecodePlan d{};
-  if (T < 1 || T > 8 || T * (K / 16) > (int64_t)kSmallQuantBlocks) return d;
+  if (T < 1 || T > kTlMaxT || T * (K / 16) > (int64_t)kSmallQuantBlocks) return d;
   d.gu_gv = plan_gemv(T, K, true);
   d.gu_tl = plan_tile(T, I, K, true);
   if (d.gu_gv.bpl == 0 && !d.gu_tl.ok) return d;

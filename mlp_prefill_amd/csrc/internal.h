@@ -45,11 +45,11 @@ int quantize_scratch(void** out);
 int requant_f32_launch(const float* h, int64_t rows, int64_t cols, uint8_t* codes, uint8_t* scales,
                        float* gs, const float* partials, uint32_t npart, hipStream_t st, _Float16* h16 = nullptr);
 
-// First launch of the whole-MLP decode path: quantise x (at most 4096 blocks
-// of 16) in one work-group, with the amax reduced from x or taken from the
+// First launch of the whole-MLP decode path: quantise x (at most 8192 blocks
+// of 16) in one launch, with the amax reduced from x or taken from the
 // kAmaxSlots partial maxima `x_amax` (nullable), and clear the words
 // [zero, zero + nzero) and [zero2, zero2 + nzero2) for the launches that follow.
-constexpr uint32_t kSmallQuantBlocks = 4096;
+constexpr uint32_t kSmallQuantBlocks = 8192;
 int mlp_prologue_launch(const void* x, int x_dtype, int64_t rows, int64_t cols, int64_t ld, uint8_t* codes,
                         uint8_t* scales, float* gs, const float* x_amax, uint32_t* zero, uint32_t nzero,
                         uint32_t* zero2, uint32_t nzero2, hipStream_t st);
@@ -81,7 +81,7 @@ int store_launch(Operand a, const int32_t* rows, const int32_t* off, int E, int6
 
 // H = SiLU(A . G^T * gs_a*gs_g) * (A . U^T * gs_a*gs_u) (float32, row-major
 // [M][N], at the start of the workspace), then its NVFP4 requantisation with a
-// global scale over all M rows.  Dense or grouped as above.  On the 3-8 token
+// global scale over all M rows.  Dense or grouped as above.  On the 3-16 token
 // stream with K split, the workspace also holds the split partial sums and the
 // column tiles' tickets, cleared by a launch of their own before the
 // contraction.
@@ -95,7 +95,7 @@ int glu_launch(Operand a, const int32_t* a_rows, const int32_t* off, int E, int6
 // The same GLU output (dense, or expert-grouped when `off` is given)
 // quantised in the contraction's epilogue with the given global scale *hq_gs
 // (two launches: expansion or ticket clearing, contraction).  Workspace: the
-// f16 copy of A, then (3-8 token stream, K split) partial sums and tickets.
+// f16 copy of A, then (3-16 token stream, K split) partial sums and tickets.
 size_t glu_static_ws_bytes(int64_t M, int64_t N, int64_t K, bool grouped);
 int glu_static_launch(Operand a, const int32_t* a_rows, const int32_t* off, int E, int64_t M, Operand gt,
                       Operand up, int64_t N, int64_t K, uint8_t* hq_codes, uint8_t* hq_scales, const float* hq_gs,
@@ -108,7 +108,7 @@ int store_quant_launch(Operand a, int64_t M, Operand w, int64_t N, int64_t K, ui
                        const float* yq_gs, void* ws, hipStream_t st);
 
 // Whole MLP: quantise x, gate/up + SiLU*up + requantisation, down projection.
-// For decode batches (T <= 8 with both projections on the weight streams) four
+// For decode batches (T <= 16 with both projections on the weight streams) four
 // launches: quantise x (also clearing the split-K tickets), gate/up, requantise
 // H, and the down projection; in each contraction whose K is split the wave
 // that arrives last on a column group adds the partial sums (no reduction

@@ -6,7 +6,7 @@
 // on the device and never read back to the host.  Packing happens on the
 // device (vllm.cpp issue, "Fix directions" 3).
 //
-// Two kernels (one for tensors of at most 4096 blocks, see
+// Two kernels (one for tensors of at most 8192 blocks, see
 // quantize_small_kernel): amax_partials writes one partial maximum per work-group;
 // quantize reduces those partials again in every work-group (a few KiB from
 // L2, no atomics, no zero-initialised state), forms the global scale, and
@@ -167,17 +167,18 @@ __global__ void __launch_bounds__(256) rms_amax_kernel(const T* __restrict__ x, 
   if (threadIdx.x == 0) partials[blockIdx.x] = m;
 }
 
-// Small tensors (decode activations: at most kSmallBlocks = 4096 blocks of
+// Small tensors (decode activations: at most kSmallBlocks = 8192 blocks of
 // 16) in one launch of ceil(blocks / 1024) work-groups of 1024 threads: every
 // work-group reduces the amax of the whole tensor itself -- each thread loads
-// up to four blocks, all in flight at once (at most 128 KiB of bf16, from L2
-// after the first work-group) -- and then quantises its own 1024 blocks, the
-// one whose index matches its work-group already in registers.  No
-// work-group waits for another, and a kernel boundary costs more than the
-// repeated reduction.  The max is exact in any order and the per-block
-// routine is the same, so the result equals the two-kernel path bit for bit.
+// up to four blocks per round, all in flight at once, one round per 4096
+// blocks (at most 256 KiB of bf16, from L2 after the first work-group) -- and
+// then quantises its own 1024 blocks, the one whose index matches its
+// work-group kept in registers from its round.  No work-group waits for
+// another, and a kernel boundary costs more than the repeated reduction.  The
+// max is exact in any order and the per-block routine is the same, so the
+// result equals the two-kernel path bit for bit.
 constexpr uint32_t kSmallBlocks = kSmallQuantBlocks;
-static_assert(kSmallBlocks <= 4u * 1024u, "four blocks per thread");
+static_assert(kSmallBlocks <= 8u * 1024u, "at most eight work-groups, two rounds");
 static_assert(kAmaxSlots <= 1024u, "one given partial maximum per thread");
 
 //
@@ -201,26 +202,34 @@ __global__ void __launch_bounds__(1024) quantize_small_kernel(const T* __restric
   const uint32_t tid = blockIdx.x * 1024u + threadIdx.x, nthr = gridDim.x * 1024u;
   for (uint32_t i = tid; i < nzero; i += nthr) zero[i] = 0u;
   for (uint32_t i = tid; i < nzero2; i += nthr) zero2[i] = 0u;
-  float v[4][16];
+  float w[16];
   float m = 0.f;
   if (given != nullptr) {
     if (threadIdx.x < npart) m = given[threadIdx.x];
   } else {
+    for (uint32_t r0 = 0; r0 < nblocks; r0 += 4096u) {
+      float v[4][16];
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const uint32_t b = threadIdx.x + q * 1024u;
-      if (b < nblocks) {
-        const uint32_t row = b / nbc, cb = b - row * nbc;
-        Load16<T>::run(x + (int64_t)row * ld + (int64_t)cb * kBlock, v[q]);
-      } else {
+      for (int q = 0; q < 4; ++q) {
+        const uint32_t b = r0 + threadIdx.x + q * 1024u;
+        if (b < nblocks) {
+          const uint32_t row = b / nbc, cb = b - row * nbc;
+          Load16<T>::run(x + (int64_t)row * ld + (int64_t)cb * kBlock, v[q]);
+        } else {
 #pragma unroll
-        for (int i = 0; i < 16; ++i) v[q][i] = 0.f;
+          for (int i = 0; i < 16; ++i) v[q][i] = 0.f;
+        }
+      }
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) m = fmaxf(m, fabsf(v[q][i]));
+        if (r0 / 1024u + q == blockIdx.x) {           // this work-group's own block
+#pragma unroll
+          for (int i = 0; i < 16; ++i) w[i] = v[q][i];
+        }
       }
     }
-#pragma unroll
-    for (int q = 0; q < 4; ++q)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) m = fmaxf(m, fabsf(v[q][i]));
   }
   m = block_max(m, red);
   const float gs = global_scale_from_amax(m);
@@ -228,17 +237,7 @@ __global__ void __launch_bounds__(1024) quantize_small_kernel(const T* __restric
   const uint32_t b = tid;
   if (b >= nblocks) return;
   const uint32_t row = b / nbc, cb = b - row * nbc;
-  float w[16];
-  if (given != nullptr) {
-    Load16<T>::run(x + (int64_t)row * ld + (int64_t)cb * kBlock, w);
-  } else {
-#pragma unroll
-    for (int q = 0; q < 4; ++q)
-      if (q == (int)blockIdx.x) {
-#pragma unroll
-        for (int i = 0; i < 16; ++i) w[i] = v[q][i];
-      }
-  }
+  if (given != nullptr) Load16<T>::run(x + (int64_t)row * ld + (int64_t)cb * kBlock, w);
   uint32_t w0, w1;
   const uint32_t sc = quantize_block16(w, gs, w0, w1);
   const int64_t boff = (int64_t)row * nbc + cb;

@@ -159,20 +159,20 @@ def test_mlp_tp2_shard_shapes(t):
 
 def test_launch_count_independent_of_T():
     """One launch set per batch, never one per token: the count is the same
-    for every T of a size range -- 7 while the activation has at most 4096
-    blocks of 16 (one-launch quantiser: T <= 170 at K = 384), 8 above -- and
+    for every T of a size range -- 7 while the activation has at most 8192
+    blocks of 16 (one-launch quantiser: T <= 341 at K = 384), 8 above -- and
     never exceeds 8.  (K = I = 384 is too short for the one/two-token stream and
     not a multiple of 256, so no weight stream is involved.)"""
     import mlp_prefill_amd as m
     wdev, _ = _weights(384, 384, (1, 2, 3))
     counts = {}
-    for t in (1, 5, 64, 170, 171, 1024):
+    for t in (1, 5, 64, 341, 342, 1024):
         announce(f"launch count T={t}")
         before = m.launch_count()
         run_device_mlp(bf16_normal(9, (t, 384)), wdev)
         counts[t] = m.launch_count() - before
-    assert counts[1] == counts[5] == counts[64] == counts[170] == 7, counts     # T * 24 <= 4096 blocks
-    assert counts[171] == counts[1024] == 8, counts                           # quantise 2, gate/up 3, down 3
+    assert counts[1] == counts[5] == counts[64] == counts[341] == 7, counts     # T * 24 <= 8192 blocks
+    assert counts[342] == counts[1024] == 8, counts                           # quantise 2, gate/up 3, down 3
 
 
 @pytest.mark.parametrize("t,k,i", [(1000, 384, 1024), (1024, 5120, 17408)], ids=["T1000_K384_I1024", "T1024_K5120_I17408"])

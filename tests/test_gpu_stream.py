@@ -9,12 +9,14 @@ ragged N (columns past N), fp32 and bf16
 outputs, the gate/up GLU with its requantisation, the quantising GLU
 epilogue, and per-token independence (token 0 of a 2-token call is
 bit-identical to the 1-token call: the accumulation order does not depend on
-the batch).  Three to eight tokens (16x16x32 matrix core, K a multiple of
-256): one to seventeen K splits, even and uneven, with the split partial sums
-added by the last-arriving wave of the gate/up pair's column tiles (and by the
-reduction launch for a separate store), ragged N, the same epilogues and
-token independence.  Shapes next to those limits (K not a multiple of 256,
-9-16 tokens) take the MFMA weight stream and are checked the same way.
+the batch).  Three to sixteen tokens (16x16x32 matrix core, K a multiple of
+256; 8 token rows staged up to 8 tokens, 16 above): one to seventeen K
+splits, even and uneven, with the split partial sums added by the
+last-arriving wave of the gate/up pair's column tiles (and by the reduction
+launch for a separate store), ragged N, the same epilogues and token
+independence, also across the 8- and 16-row variants.  Shapes next to those
+limits (K not a multiple of 256, 17-32 tokens) take the 32-row MFMA weight
+stream and are checked the same way.
 """
 import numpy as np
 import pytest
@@ -137,7 +139,9 @@ def test_stream_glu_quant_epilogue(t):
 # of 32 and ragged
 TILE_SHAPES = [(3, 64, 1024), (4, 48, 2048), (5, 200, 3072), (8, 128, 4096), (5, 96, 5120), (6, 100, 5120),
                (7, 36, 8192), (8, 160, 7168), (8, 20, 6144), (5, 5120, 17408), (3, 332, 17408),
-               (3, 48, 768), (7, 40, 1280), (8, 100, 2304), (4, 36, 4352)]
+               (3, 48, 768), (7, 40, 1280), (8, 100, 2304), (4, 36, 4352),
+               # 9-16 tokens: 16 token rows staged
+               (9, 64, 1280), (12, 200, 5120), (16, 96, 2048), (16, 100, 17408), (11, 5120, 17408), (13, 36, 4352)]
 
 
 @pytest.mark.parametrize("m,n,k", TILE_SHAPES, ids=[f"{m}x{n}x{k}" for m, n, k in TILE_SHAPES])
@@ -146,9 +150,11 @@ def test_tile_stream_gemm(m, n, k):
 
 
 def test_tile_stream_token_independence():
-    """Rows 0-2 of a 5-token product equal the 3-token product bit for bit, and
-    row 0 of the 3-token product does not depend on rows 1-2 (each token is a
-    row of the matrix-core tile; rows past the batch repeat the last token)."""
+    """Rows 0-2 of a 5-token product equal the 3-token product bit for bit, row
+    0 of the 3-token product does not depend on rows 1-2, and rows 0-4 of a
+    12-token product (16 token rows staged) equal the 5-token product (8 rows
+    staged): each token is a row of the matrix-core tile, and rows past the
+    batch repeat the last token."""
     announce("tile stream token independence 5/3 x 256 x 5120")
     xb = bf16_normal(811, (5, 5120))
     wb = bf16_normal(812, (256, 5120), sigma=0.02)
@@ -161,10 +167,16 @@ def test_tile_stream_token_independence():
     y5, y3, y3b = _gemm(a5, b, 5, 256), _gemm(a3, b, 3, 256), _gemm(a3b, b, 3, 256)
     assert np.array_equal(y3.view(np.uint32), y5[:3].view(np.uint32))
     assert np.array_equal(y3[0].view(np.uint32), y3b[0].view(np.uint32))
+    # 16 token rows staged (12 tokens) against 8 (the 5-token product): the same rows
+    xb12 = np.concatenate([xb, bf16_normal(814, (7, 5120))])
+    a12 = dev_quantize(xb12, gs_mode=1, gs=gs)
+    y12 = _gemm(a12, b, 12, 256)
+    assert np.array_equal(y12[:5].view(np.uint32), y5.view(np.uint32))
 
 
 # gate/up K in 1 split (1024, 1280), 2 (3072, 4096), 3 uneven (5120), 4 (7168)
-TILE_GLU = [(3, 1024, 256), (4, 3072, 128), (5, 5120, 640), (6, 7168, 384), (8, 4096, 1024), (7, 1280, 512)]
+TILE_GLU = [(3, 1024, 256), (4, 3072, 128), (5, 5120, 640), (6, 7168, 384), (8, 4096, 1024), (7, 1280, 512),
+            (9, 1280, 256), (12, 5120, 640), (16, 2304, 384)]
 
 
 @pytest.mark.parametrize("t,k,i", TILE_GLU, ids=[f"T{t}_K{k}_I{i}" for t, k, i in TILE_GLU])
@@ -172,15 +184,14 @@ def test_tile_stream_mlp(t, k, i):
     test_stream_mlp(t, k, i)
 
 
-@pytest.mark.parametrize("t", [3, 5, 8])
+@pytest.mark.parametrize("t", [3, 5, 8, 12, 16])
 def test_tile_stream_glu_quant_epilogue(t):
     test_stream_glu_quant_epilogue(t)
 
 
-# ---- batches around the stream limits: K not a multiple of 256 (3 tokens, MFMA weight
-# stream) and 9-16 tokens (MFMA weight stream) --------------------------------------------
-MFMA_SHAPES = [(3, 48, 640), (9, 64, 1280), (12, 200, 5120), (16, 96, 2048), (16, 100, 17408), (11, 5120, 17408),
-              (13, 36, 4352)]
+# ---- batches around the stream limits: K not a multiple of 256 (3 and 12 tokens) and
+# 17-32 tokens, on the 32-row MFMA weight stream ------------------------------------------
+MFMA_SHAPES = [(3, 48, 640), (12, 40, 1152), (17, 64, 1024), (24, 100, 2048), (32, 96, 5120), (20, 256, 17408)]
 
 
 @pytest.mark.parametrize("m,n,k", MFMA_SHAPES, ids=[f"{m}x{n}x{k}" for m, n, k in MFMA_SHAPES])
@@ -188,7 +199,7 @@ def test_mfma_stream_gemm(m, n, k):
     test_stream_gemm(m, n, k)
 
 
-MFMA_GLU = [(9, 1280, 256), (12, 5120, 640), (16, 2304, 384)]
+MFMA_GLU = [(17, 1280, 256), (24, 5120, 640), (32, 2304, 384)]
 
 
 @pytest.mark.parametrize("t,k,i", MFMA_GLU, ids=[f"T{t}_K{k}_I{i}" for t, k, i in MFMA_GLU])
@@ -196,25 +207,25 @@ def test_mfma_stream_mlp(t, k, i):
     test_stream_mlp(t, k, i)
 
 
-@pytest.mark.parametrize("t", [10, 16])
+@pytest.mark.parametrize("t", [17, 32])
 def test_mfma_stream_glu_quant_epilogue(t):
     test_stream_glu_quant_epilogue(t)
 
 
 def test_stream_launch_counts():
-    """One launch set per batch: the weight streams (1-8 tokens) expand the
-    activation themselves, and an activation of at most 4096 blocks is
+    """One launch set per batch: the weight streams (1-16 tokens) expand the
+    activation themselves, and an activation of at most 8192 blocks is
     quantised in one launch, so a dynamic-scale MLP call with the gate/up K in
     one split is 5 launches at every such T (quantise 1, gate/up 2, down 2) and
     the static-scale pair 1 + 2; larger batches add the expansion launch of
     each projection (7 here; static 2 + 3).  A gate/up K in several splits on
-    the 3-8 token stream adds the launch that clears its tickets."""
+    the 3-16 token stream adds the launch that clears its tickets."""
     import mlp_prefill_amd as m
     from tests.test_gpu_mlp import run_device_mlp
     k, i = 1024, 2048
     wdev, _ = _weights(k, i, (960, 961, 962))
     dyn, sta = {}, {}
-    for t in (1, 2, 3, 5, 8, 9, 64):
+    for t in (1, 2, 3, 5, 8, 9, 16, 17, 64):
         announce(f"stream launch counts T={t}")
         xbits = bf16_normal(963, (t, k))
         b0 = m.launch_count()
@@ -231,13 +242,13 @@ def test_stream_launch_counts():
         m.nvfp4_mlp_down_quant(hq, wdev[2], yq)
         sta[t] = (b1 - b0, m.launch_count() - b1)
     torch.cuda.synchronize()
-    assert all(dyn[t] == 5 for t in (1, 2, 3, 5, 8)), dyn
-    assert dyn[9] == dyn[64] == 7, dyn
-    assert all(sta[t] == (1, 2) for t in (1, 2, 3, 5, 8)), sta
-    assert sta[9] == sta[64] == (2, 3), sta
-    k, i = 3072, 1024                              # gate/up in 2 splits at 3-8 tokens
+    assert all(dyn[t] == 5 for t in (1, 2, 3, 5, 8, 9, 16)), dyn
+    assert dyn[17] == dyn[64] == 7, dyn
+    assert all(sta[t] == (1, 2) for t in (1, 2, 3, 5, 8, 9, 16)), sta
+    assert sta[17] == sta[64] == (2, 3), sta
+    k, i = 3072, 1024                              # gate/up in 2 splits at 3-16 tokens
     wdev, _ = _weights(k, i, (964, 965, 966))
-    for t, want in ((2, 5), (5, 6)):
+    for t, want in ((2, 5), (5, 6), (12, 6)):
         b0 = m.launch_count()
         run_device_mlp(bf16_normal(967, (t, k)), wdev)
         assert m.launch_count() - b0 == want, (t, m.launch_count() - b0)
