@@ -371,7 +371,8 @@ def static_line(m, layers, x_all, steps, ub=1024):
 
 
 def decode_line(m):
-    """Decode-shaped MLP (5120/17408) at T = 1 and T = 5: weight-streaming GB/s cold and hot."""
+    """Decode-shaped MLP (5120/17408) at T = 1 and T = 5: weight-streaming GB/s cold and hot; the
+    whole-MLP call at 8, 12 and 16 tokens (cold)."""
     from synthetic import WORKLOADS, bf16_normal
     p2 = WORKLOADS["mlp_decode_5120x17408"].params
     log("extra: decode-shaped MLP T=1, T=5")
@@ -433,6 +434,24 @@ def decode_line(m):
     dec["launches_per_call"] = launches
     dec["t5_over_t1_cold"] = dec["T5"]["ms_cold"] / dec["T1"]["ms_cold"]
     dec["whole_mlp_t5_over_t1_cold"] = dec["T5"]["whole_mlp_ms_cold"] / dec["T1"]["whole_mlp_ms_cold"]
+    # medium batches on the same weights: the whole-MLP call, cold
+    med = {}
+    for tt in (8, 12, 16):
+        x = m.bf16_from_bits(bf16_normal(p2["x_seed"] + tt, (tt, K_HID)))
+        xq, hq = m.NVFP4.empty(tt, K_HID), m.NVFP4.empty(tt, lay.w[0].rows)
+        y = torch.empty((tt, K_HID), dtype=torch.float32, device="cuda")
+        ws_f = torch.empty(m.mlp_ws_bytes(tt, K_HID, lay.w[0].rows), dtype=torch.uint8, device="cuda")
+
+        def run_fused():
+            m.nvfp4_mlp(x, lay.w[0], lay.w[1], lay.w[2], xq, hq, y, ws=ws_f)
+        run_fused()
+        b0 = m.launch_count()
+        run_fused()
+        nl = m.launch_count() - b0
+        cold_f = float(np.median(time_events(run_fused, 20, scrub=lambda: scrub_buf.sum())))
+        med[f"T{tt}"] = {"whole_mlp_ms_cold": cold_f, "whole_mlp_hbm_gbs_cold": wbytes / (cold_f * 1e-3) / 1e9,
+                         "whole_mlp_launches": nl}
+    dec["medium_batches"] = med
     del lay, scrub_buf
     return dec
 
