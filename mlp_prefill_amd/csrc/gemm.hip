@@ -989,10 +989,10 @@ __global__ void __launch_bounds__(kSkWaves * 64) skinny_kernel(GemmArgs p) {
 // per instruction) streams at about half the rate of a layout where a wave
 // reads one row at a time.  So here the lanes run along K: K is cut into
 // units of 1024 elements (64 blocks of 16), a split takes BPL consecutive
-// units, and lane l takes the BPL consecutive blocks l*BPL .. l*BPL+BPL-1 of
-// it (8*BPL code bytes, BPL scale bytes).  The activation (f16, expanded
-// once per call) follows the same layout and stays in registers for the
-// whole wave.
+// units, and lane l takes block l of each of them (BPL blocks 64 apart, 8
+// code bytes and one scale byte each), so one load instruction of the wave
+// reads 512 contiguous code bytes.  The activation (f16, expanded once per
+// call) follows the same layout and stays in registers for the whole wave.
 //
 // Each block's 16 products code * x are summed by v_dot2_f32_f16 on the
 // plain code values (the converter's scale is 1, so they are exact in f16;
@@ -1062,7 +1062,9 @@ __global__ void __launch_bounds__(256) gemv_kernel(GemmArgs p) {
   if (wave >= wps * (int64_t)p.splits) return;
   const int64_t split = wave / wps;
   const int64_t n0 = (wave - split * wps) * kGvCols;
-  const int64_t e0 = split * BPL * 1024 + (int64_t)lane * BPL * 16;   // first K element of this lane
+  // block b of this lane is block 64 b + lane of the split
+  const int64_t e0 = split * BPL * 1024 + (int64_t)lane * 16;          // K element of this lane's block 0
+  constexpr int64_t EB = 1024;                                          // K elements between its blocks
   const int64_t kb = K >> 1, ks = K >> 4;
 
   struct Slot {
@@ -1087,8 +1089,8 @@ __global__ void __launch_bounds__(256) gemv_kernel(GemmArgs p) {
       for (int b = 0; b < BPL; ++b) {
         // the resources span one row: a block past K (last unit partial) reads
         // past them and gets zero, with no memory traffic
-        sl.c[r][b] = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(rc, vo_c + 8 * b, 0, 0));
-        sl.s[r][b] = __builtin_amdgcn_raw_buffer_load_b8(rs, vo_s + b, 0, 0);
+        sl.c[r][b] = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(rc, vo_c + (int32_t)(EB / 2) * b, 0, 0));
+        sl.s[r][b] = __builtin_amdgcn_raw_buffer_load_b8(rs, vo_s + (int32_t)(EB / 16) * b, 0, 0);
       }
     }
   };
@@ -1111,9 +1113,9 @@ __global__ void __launch_bounds__(256) gemv_kernel(GemmArgs p) {
   for (int t = 0; t < T; ++t)
 #pragma unroll
     for (int b = 0; b < BPL; ++b) {
-      if (t < M && e0 + 16 * b < K) {                    // blocks past K (last unit partial): zero
-        const uint2 cw = *reinterpret_cast<const uint2*>(p.a_codes + t * (K >> 1) + e0 / 2 + 8 * b);
-        const uint32_t sh = (uint32_t)p.a_scales[t * (K >> 4) + e0 / 16 + b] << 7;
+      if (t < M && e0 + EB * b < K) {                    // blocks past K (last unit partial): zero
+        const uint2 cw = *reinterpret_cast<const uint2*>(p.a_codes + t * (K >> 1) + (e0 + EB * b) / 2);
+        const uint32_t sh = (uint32_t)p.a_scales[t * (K >> 4) + (e0 + EB * b) / 16] << 7;
         const f16x2 sc = bitcast<f16x2>(sh | (sh << 16));
         xp[t][b][0] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(cw.x, 256.0f, 0) * sc;
         xp[t][b][1] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(cw.x, 256.0f, 1) * sc;
