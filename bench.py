@@ -69,8 +69,14 @@ def mlp_flops(t, k=K_HID, i=I_INT):
     return 6.0 * t * k * i
 
 
+# Weight preparation at set-up (not timed, like the weights' quantisation):
+# the tile-contiguous copy the large-batch contractions stage from.
+TILED_WEIGHTS = True
+
+
 class Layer:
-    """Quantised weights of one MLP layer on the device."""
+    """Quantised weights of one MLP layer on the device (with their
+    tile-contiguous copies unless --row-major-weights)."""
 
     def __init__(self, m, seeds, k=K_HID, i=I_INT):
         from synthetic import bf16_normal
@@ -81,6 +87,8 @@ class Layer:
             q = m.NVFP4.empty(*shp)
             m.nvfp4_quantize_act(x, q)
             del x
+            if TILED_WEIGHTS:
+                q.tile()
             self.w.append(q)
 
 
@@ -195,11 +203,15 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extra", action="store_true", help="skip the 1024-token, decode and expert-grouped lines")
     ap.add_argument("--cpu-ubatches", type=int, default=8, help="ubatches the CPU oracle runs (about 10-15 s)")
+    ap.add_argument("--row-major-weights", action="store_true",
+                    help="no tile-contiguous weight copies: the contractions stage the row-major weights")
     ap.add_argument("--decode-only", action="store_true",
                     help="print only the decode-shaped MLP line (T = 1 and T = 5) and exit")
     ap.add_argument("--moe-only", action="store_true",
                     help="print only the expert-grouped MLP line (4096 tokens, top-8 of 64 experts) and exit")
     args = ap.parse_args()
+    global TILED_WEIGHTS
+    TILED_WEIGHTS = not args.row_major_weights
     if args.gpus != 1:
         print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported (the path is built and measured "
               f"on a single MI355X)", file=sys.stderr)
@@ -307,7 +319,9 @@ def main():
         "vs_baseline": None, "dtype": "f16", "data": "synthetic",
         "config": {"workload": "mlp_long_prefill_16x1024_4layers", "tokens": T, "ubatch": UB, "layers": L,
                    "hidden": K_HID, "intermediate": I_INT, "storage": "nvfp4 (e2m1 codes, e4m3 block-16 scales, "
-                   "fp32 global scale)", "accumulate": "fp32"},
+                   "fp32 global scale)", "accumulate": "fp32",
+                   "weights": ("row-major, plus tile-contiguous copies written at set-up (untimed, like the weight "
+                               "quantisation)") if TILED_WEIGHTS else "row-major"},
         "tokens_per_s": tokens_s, "flops_per_step": flops,
         "roofline": roofline,
     }
@@ -637,6 +651,9 @@ def moe_line(m):
             mats[j].append(q)
     wg, wu, wd = (m.NVFP4.stack(v) for v in mats)
     del mats
+    if TILED_WEIGHTS:
+        for w in (wg, wu, wd):
+            w.tile()
     x = m.bf16_from_bits(bf16_normal(p["x_seed"], (t, k)))
     logits = torch.from_numpy(router_logits(p["router_seed"], t, e)).cuda()
     slots = t * top

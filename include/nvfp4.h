@@ -76,6 +76,9 @@ typedef struct nvfp4_tensor {
   uint8_t *codes;   /* packed E2M1 codes, see the layout above          */
   uint8_t *scales;  /* E4M3 block scales, one per 16 elements of a row  */
   float   *gscale;  /* device float32 global scale(s)                   */
+  const uint8_t *tiled;  /* optional (NULL): the tile-contiguous copy of
+                      a weight written by nvfp4_tile_weight, 256-byte
+                      aligned; read only for weight operands          */
 } nvfp4_tensor;
 
 enum nvfp4_status {
@@ -327,6 +330,34 @@ int nvfp4_mlp_gu_act_static(nvfp4_tensor x, nvfp4_tensor w_gate, nvfp4_tensor w_
  */
 int nvfp4_mlp_down_quant(nvfp4_tensor h, nvfp4_tensor w_down, int64_t T, int64_t I, int64_t K,
                          nvfp4_tensor y_out, void *ws, size_t *ws_bytes, void *stream);
+
+/*
+ * nvfp4_tile_weight -- the tile-contiguous copy of a weight (or expert
+ * stack) for the large-batch contractions ([llama] "What the patch does":
+ * aligned whole-tile loads feeding the matrix unit).  A permutation of the
+ * weight's codes and scales, no value changes: every contraction call gives
+ * bit-identical results with and without it.  Written once per weight (like
+ * the weight's quantisation), then passed as w.tiled to the calls; the
+ * large-batch contractions (more than 32 tokens, and the expert-grouped
+ * GEMMs) stage the weight from it, each chunk of a column tile a run of
+ * whole 1 KiB pieces instead of 64 bytes of every row.  The decode weight
+ * streams read the row-major codes and scales as before.
+ *   w        : [experts][N][K] NVFP4 (codes, scales; gscale not read)
+ *   experts  : 1 for a single weight, E for an expert stack
+ *   K        : multiple of 128;  N >= 0
+ *   tiled    : output, tiled_bytes = experts * ceil(N/128) * (K/128) * 9216
+ *              bytes, 256-byte aligned (tiled == NULL: size query).  Block
+ *              (e, g, c) -- rows 128g .. 128g+127 of expert e, K elements
+ *              128c .. 128c+127 -- starts at byte ((e*G + g)*(K/128) + c) *
+ *              9216, G = ceil(N/128): 8192 bytes of codes, the 16-byte unit
+ *              u (0..3) of local row r at unit r*4 + (u ^ ((r/4) % 4)), then
+ *              local row r's 8 scale bytes at 8192 + 8r.  Rows past N are 0.
+ * One launch.  The copy must be rewritten when the weight changes; a call
+ * reads it only when its weight operand's tiled pointer is not NULL (with the
+ * gate/up pair, both).
+ */
+int nvfp4_tile_weight(nvfp4_tensor w, int64_t experts, int64_t N, int64_t K, uint8_t *tiled, size_t *tiled_bytes,
+                      void *stream);
 
 /*
  * nvfp4_grouped_gemm -- expert-grouped NVFP4 GEMM in one launch per GEMM

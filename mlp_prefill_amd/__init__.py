@@ -27,7 +27,7 @@ _i64 = ctypes.c_int64
 
 
 class nvfp4_tensor(ctypes.Structure):
-    _fields_ = [("codes", _vp), ("scales", _vp), ("gscale", _vp)]
+    _fields_ = [("codes", _vp), ("scales", _vp), ("gscale", _vp), ("tiled", _vp)]
 
 
 OK, ERR_NULL, ERR_SHAPE, ERR_ALIGN, ERR_WORKSPACE, ERR_ARG, ERR_DEVICE, ERR_LAUNCH = range(8)
@@ -62,6 +62,7 @@ _sig = {
                         ctypes.POINTER(ctypes.c_size_t), _vp],
     "nvfp4_moe_combine": [_vp, ctypes.c_int, _i64, _vp, _vp, _i64, ctypes.c_int, _i64, _vp, ctypes.c_int, _i64,
                           _vp],
+    "nvfp4_tile_weight": [nvfp4_tensor, _i64, _i64, _i64, _vp, ctypes.POINTER(ctypes.c_size_t), _vp],
 }
 for _name, _args in _sig.items():
     _f = getattr(_lib, _name)
@@ -126,6 +127,7 @@ class NVFP4:
     gscale: torch.Tensor    # float32 [1] or [experts]
     rows: int
     cols: int
+    tiled: torch.Tensor = None   # uint8: tile-contiguous copy of a weight (nvfp4_tile_weight), or None
 
     @staticmethod
     def empty(rows, cols, device="cuda", experts=None):
@@ -142,11 +144,17 @@ class NVFP4:
                      torch.cat([m.gscale for m in mats]), mats[0].rows, mats[0].cols)
 
     def c(self):
-        return nvfp4_tensor(self.codes.data_ptr(), self.scales.data_ptr(), self.gscale.data_ptr())
+        return nvfp4_tensor(self.codes.data_ptr(), self.scales.data_ptr(), self.gscale.data_ptr(),
+                            self.tiled.data_ptr() if self.tiled is not None else 0)
+
+    def tile(self, stream=None):
+        """Write (or rewrite) this weight's tile-contiguous copy; returns self."""
+        nvfp4_tile_weight(self, stream=stream)
+        return self
 
 
 def _null_tensor():
-    return nvfp4_tensor(0, 0, 0)
+    return nvfp4_tensor(0, 0, 0, 0)
 
 
 def _dtype_code(t):
@@ -441,6 +449,25 @@ def nvfp4_moe_combine(y_slots, slot_of, weights, y, stream=None):
 
 
 # ---- convenience: host <-> device NVFP4 (test and setup plumbing) -------------------
+def tile_weight_bytes(n, k, experts=1):
+    need = ctypes.c_size_t(0)
+    _check(_lib.nvfp4_tile_weight(_null_tensor(), experts, n, k, None, ctypes.byref(need), None), "nvfp4_tile_weight")
+    return need.value
+
+
+def nvfp4_tile_weight(w, stream=None):
+    """Tile-contiguous copy of weight `w` (or an expert stack) into w.tiled,
+    allocated here when absent; the large-batch contractions then stage the
+    weight from it (bit-identical results)."""
+    experts = w.codes.shape[0] if w.codes.dim() == 3 else 1
+    need = tile_weight_bytes(w.rows, w.cols, experts)
+    if w.tiled is None or w.tiled.numel() < need:
+        w.tiled = torch.empty(max(need, 1), dtype=torch.uint8, device=w.codes.device)
+    have = ctypes.c_size_t(w.tiled.numel())
+    _check(_lib.nvfp4_tile_weight(w.c(), experts, w.rows, w.cols, _ptr(w.tiled), ctypes.byref(have), _stream(stream)),
+           "nvfp4_tile_weight")
+
+
 def to_device(q_codes, q_scales, gs, rows, cols, device="cuda"):
     """NVFP4 from host arrays (numpy uint8 codes/scales, float32 gs)."""
     return NVFP4(torch.from_numpy(q_codes).to(device), torch.from_numpy(q_scales).to(device),

@@ -85,6 +85,10 @@ struct GemmArgs {
   // too): max |stored output| of each group folded into slot group % kAmaxSlots.
   uint32_t* tickets;
   float* amax_slots;
+  // Optional tile-contiguous copies of the weights (gate / up) that the
+  // large-batch kernels stage from instead of the row-major codes and scales.
+  const uint8_t* b_tiled;
+  const uint8_t* u_tiled;
 };
 
 // Partial sums shared between the work-groups of one launch go through the
@@ -159,6 +163,53 @@ __global__ void __launch_bounds__(256) expand_kernel(const uint8_t* __restrict__
   }
 }
 
+// ---- tile-contiguous weight copy ----------------------------------------------------
+// One work-group per block (e, g, c): 128 rows x 128 K of a weight [E][N][K].
+// Its 512 code units (16 bytes, 32 codes) go where the large-batch kernels'
+// staging puts them in LDS -- unit u of row r at r * 4 + (u ^ ((r / 4) % 4)) --
+// and its 128 rows of 8 scale bytes follow in row order, so that staging a
+// chunk of a column tile is a run of whole 1 KiB pieces.  Rows past N are
+// zero.  A permutation of the weight's bytes: no value changes.
+__global__ void __launch_bounds__(256) tile_weight_kernel(const uint8_t* __restrict__ codes,
+                                                          const uint8_t* __restrict__ scales, int64_t N, int64_t K,
+                                                          int64_t G, uint8_t* __restrict__ out) {
+  const int64_t Cn = K / kTileK;
+  const int64_t blk = blockIdx.x;
+  const int64_t c = blk % Cn, eg = blk / Cn, g = eg % G, e = eg / G;
+  const int64_t kb = K / 2, ks = K / 16;
+  uint8_t* dst = out + blk * kTileBlock;
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int q = (int)threadIdx.x + 256 * j;
+    const int r = q >> 2, u = (q & 3) ^ ((r >> 2) & 3);
+    const int64_t n = g * kTileRows + r;
+    uint4 v = make_uint4(0u, 0u, 0u, 0u);
+    if (n < N) v = *reinterpret_cast<const uint4*>(codes + (e * N + n) * kb + c * 64 + u * 16);
+    *reinterpret_cast<uint4*>(dst + q * 16) = v;
+  }
+  if (threadIdx.x < kTileRows) {
+    const int64_t n = g * kTileRows + threadIdx.x;
+    uint2 v = make_uint2(0u, 0u);
+    if (n < N) v = *reinterpret_cast<const uint2*>(scales + (e * N + n) * ks + c * 8);
+    *reinterpret_cast<uint2*>(dst + 8192 + threadIdx.x * 8) = v;
+  }
+}
+
+size_t tile_weight_bytes(int64_t E, int64_t N, int64_t K) {
+  return (size_t)(E * ((N + kTileRows - 1) / kTileRows) * (K / kTileK) * kTileBlock);
+}
+
+int tile_weight_launch(const uint8_t* codes, const uint8_t* scales, int64_t E, int64_t N, int64_t K, uint8_t* out,
+                       hipStream_t st) {
+  const int64_t G = (N + kTileRows - 1) / kTileRows;
+  const int64_t blocks = E * G * (K / kTileK);
+  if (blocks <= 0) return 0;
+  const int slot = launch_begin(KC_EXPAND, st);
+  hipLaunchKernelGGL(tile_weight_kernel, dim3((uint32_t)blocks), dim3(256), 0, st, codes, scales, N, K, G, out);
+  launch_end(slot, st);
+  return hipGetLastError() == hipSuccess ? 0 : 7;
+}
+
 // ---- packed weight fragments --------------------------------------------------------
 struct Frag {
   u32x4 c0, c1;  // 32 code bytes: 64 elements
@@ -227,6 +278,7 @@ struct Ctx {
   // first row and this split's first chunk) and each lane's byte offset of
   // every staged unit; a chunk adds a scalar offset.
   i32x4 ra, rb, ru, rsb, rsu;
+  uint32_t wstep, sstep;         // bytes between consecutive chunks of the weight codes / scales
   uint32_t a_off[C::SA];
   uint32_t b_off[C::SB];
   uint32_t s_off[C::SD];
@@ -300,7 +352,7 @@ template <int WN, int TM, int TN, bool DUAL>
 __device__ __forceinline__ void stage_dma(const Ctx<WN, TM, TN, DUAL>& x, uint32_t la, uint32_t lb, uint32_t ls,
                                           int64_t chunk) {
   using C = Cfg<WN, TM, TN, DUAL>;
-  const uint32_t ca = (uint32_t)chunk * 256u, cb = (uint32_t)chunk * 64u, cs = (uint32_t)chunk * 8u;
+  const uint32_t ca = (uint32_t)chunk * 256u, cb = (uint32_t)chunk * x.wstep, cs = (uint32_t)chunk * x.sstep;
 #pragma unroll
   for (int u = 0; u < C::SA; ++u) dma_b128(x.ra, x.a_off[u], ca, la + u * C::NT * 16);
 #pragma unroll
@@ -525,6 +577,7 @@ __global__ void __launch_bounds__(WN * 64, MINWG) gemm_kernel(GemmArgs p) {
   using C = Cfg<WN, TM, TN, DUAL>;
   constexpr int BM = C::BM;
   constexpr int BN = C::BN;
+  static_assert(BN % kTileRows == 0 && C::NB * 4 % 512 == 0, "whole 128-row groups of the tiled weights per tile");
   __shared__ float red[WN];
   __shared__ f16x8 lds_a[NS][C::LDS_A];
   __shared__ u32x4 lds_b[NS][C::LDS_B];
@@ -611,18 +664,39 @@ __global__ void __launch_bounds__(WN * 64, MINWG) gemm_kernel(GemmArgs p) {
 
   // ---- staging sources (rows past the end are clamped; never stored) ----------
   Ctx<WN, TM, TN, DUAL> x;
+  // uniform: the weights come from their tile-contiguous copies (both of the pair)
+  const bool tiled = p.b_tiled != nullptr && (!DUAL || p.u_tiled != nullptr);
   {
     const int64_t a_rows = (m_end < m0 + BM ? m_end : m0 + BM) - m0;
-    const int64_t b_rows = (p.N < n0 + BN ? p.N : n0 + BN) - n0;
     x.ra = buf_desc(p.a + m0 * K + c_begin * 128, a_rows * K * 2 - c_begin * 256);
-    x.rb = buf_desc(p.b_codes + wstride_c + n0 * kb + c_begin * 64, b_rows * kb - c_begin * 64);
-    x.rsb = buf_desc(p.b_scales + wstride_s + n0 * ks + c_begin * 8, b_rows * ks - c_begin * 8);
-    if constexpr (DUAL) {
-      x.ru = buf_desc(p.u_codes + wstride_c + n0 * kb + c_begin * 64, b_rows * kb - c_begin * 64);
-      x.rsu = buf_desc(p.u_scales + wstride_s + n0 * ks + c_begin * 8, b_rows * ks - c_begin * 8);
+    if (tiled) {
+      // blocks (e, g, c): this tile's first group g0 = n0 / 128, from chunk c_begin on
+      const int64_t G = (p.N + kTileRows - 1) / kTileRows, Cn = K / kTileK;
+      const int64_t first = ((GROUPED ? (int64_t)e * G : 0) + n0 / kTileRows) * Cn + c_begin;
+      const int64_t bytes = ((G - n0 / kTileRows) * Cn - c_begin) * kTileBlock;
+      x.rb = buf_desc(p.b_tiled + first * kTileBlock, bytes);
+      x.rsb = buf_desc(p.b_tiled + first * kTileBlock + 8192, bytes - 8192);
+      if constexpr (DUAL) {
+        x.ru = buf_desc(p.u_tiled + first * kTileBlock, bytes);
+        x.rsu = buf_desc(p.u_tiled + first * kTileBlock + 8192, bytes - 8192);
+      } else {
+        x.ru = x.rb;
+        x.rsu = x.rsb;
+      }
+      x.wstep = x.sstep = (uint32_t)kTileBlock;
     } else {
-      x.ru = x.rb;
-      x.rsu = x.rsb;
+      const int64_t b_rows = (p.N < n0 + BN ? p.N : n0 + BN) - n0;
+      x.rb = buf_desc(p.b_codes + wstride_c + n0 * kb + c_begin * 64, b_rows * kb - c_begin * 64);
+      x.rsb = buf_desc(p.b_scales + wstride_s + n0 * ks + c_begin * 8, b_rows * ks - c_begin * 8);
+      if constexpr (DUAL) {
+        x.ru = buf_desc(p.u_codes + wstride_c + n0 * kb + c_begin * 64, b_rows * kb - c_begin * 64);
+        x.rsu = buf_desc(p.u_scales + wstride_s + n0 * ks + c_begin * 8, b_rows * ks - c_begin * 8);
+      } else {
+        x.ru = x.rb;
+        x.rsu = x.rsb;
+      }
+      x.wstep = 64u;
+      x.sstep = 8u;
     }
   }
 #pragma unroll
@@ -638,16 +712,26 @@ __global__ void __launch_bounds__(WN * 64, MINWG) gemm_kernel(GemmArgs p) {
     if (n > p.N - 1) n = p.N - 1;
     return n - n0;
   };
+  // tiled: row rho of the tile (gate rows first with the pair) is row rho % 128
+  // of group min(g0 + (rho mod BN) / 128, G - 1); a block holds the LDS order of
+  // its 128 rows, so LDS unit (dword) q of a group is byte 16 q (8192 + 4 q)
+  const int64_t tgrp_last = tiled ? (p.N + kTileRows - 1) / kTileRows - 1 - n0 / kTileRows : 0;
+  auto tgrp = [&](int rho) -> int64_t {          // group of tile row rho, relative to g0, clamped
+    const int64_t g = ((DUAL && rho >= BN) ? rho - BN : rho) / kTileRows;
+    return (g < tgrp_last ? g : tgrp_last) * (K / kTileK) * kTileBlock;
+  };
 #pragma unroll
   for (int u = 0; u < C::SB; ++u) {
     const int pu = u * C::NT + threadIdx.x;      // LDS unit: row pu/4, slot pu%4
     const int row = pu >> 2, slot = pu & 3;
-    x.b_off[u] = (uint32_t)(wrow(row) * kb + ((slot ^ ((row >> 2) & 3)) << 4));
+    x.b_off[u] = tiled ? (uint32_t)(tgrp(row) + (int64_t)(pu & 511) * 16)
+                       : (uint32_t)(wrow(row) * kb + ((slot ^ ((row >> 2) & 3)) << 4));
   }
 #pragma unroll
   for (int u = 0; u < C::SD; ++u) {
     const int pu = u * C::NT + threadIdx.x;      // LDS dword: row pu/2, half pu%2
-    x.s_off[u] = (uint32_t)(wrow(pu >> 1) * ks + ((pu & 1) << 2));
+    x.s_off[u] = tiled ? (uint32_t)(tgrp(pu >> 1) + (int64_t)(pu & 255) * 4)
+                       : (uint32_t)(wrow(pu >> 1) * ks + ((pu & 1) << 2));
   }
 #pragma unroll
   for (int i = 0; i < TM; ++i) x.lds_row[i] = (i * 32 + r32) * 16;
@@ -2021,6 +2105,7 @@ static GemmArgs base_args(const _Float16* a16, const float* a_gs, Operand b, int
   g.b_codes = b.codes;
   g.b_scales = b.scales;
   g.b_gs = b.gscale;
+  g.b_tiled = b.tiled;
   g.M = M;
   g.N = N;
   g.K = K;
@@ -2122,6 +2207,7 @@ int glu_launch(Operand a, const int32_t* a_rows, const int32_t* off, int E, int6
   g.u_codes = up.codes;
   g.u_scales = up.scales;
   g.u_gs = up.gscale;
+  g.u_tiled = up.tiled;
   g.h = h;
   g.partials = partials;
   g.off = off;
@@ -2165,6 +2251,7 @@ int glu_static_launch(Operand a, const int32_t* a_rows, const int32_t* off, int 
   g.u_codes = up.codes;
   g.u_scales = up.scales;
   g.u_gs = up.gscale;
+  g.u_tiled = up.tiled;
   g.q_codes = hq_codes;
   g.q_scales = hq_scales;
   g.q_gs = hq_gs;
@@ -2307,6 +2394,7 @@ int mlp_launch(const void* x, int x_dtype, int64_t ld_x, int64_t T, int64_t K, i
   g.u_codes = wu.codes;
   g.u_scales = wu.scales;
   g.u_gs = wu.gscale;
+  g.u_tiled = wu.tiled;
   g.h = h;
   g.partials = partials;
   if (d.gu_gv.bpl > 0) {

@@ -65,7 +65,18 @@ struct Operand {
   const uint8_t* codes;
   const uint8_t* scales;
   const float* gscale;
+  const uint8_t* tiled;   // optional tile-contiguous copy of a weight (tile_weight_launch), else nullptr
 };
+
+// Tile-contiguous copy of a weight [experts][N][K] for the large-batch
+// contractions: blocks of 128 rows x 128 K (kTileBlock bytes: the 8 KiB of
+// codes in the order the contraction stages them in LDS, then the 1 KiB of
+// scales), block (e, g, c) at ((e * G + g) * K/128 + c) * kTileBlock with
+// G = ceil(N / 128); rows past N are zero.
+constexpr int64_t kTileRows = 128, kTileK = 128, kTileBlock = 9216;
+size_t tile_weight_bytes(int64_t E, int64_t N, int64_t K);
+int tile_weight_launch(const uint8_t* codes, const uint8_t* scales, int64_t E, int64_t N, int64_t K, uint8_t* out,
+                       hipStream_t st);
 
 // Store-epilogue contraction C[M][N] = A . W^T * gs_a * gs_w (float32 or bf16),
 // dense (off == nullptr) or expert-grouped (slot s reads activation row

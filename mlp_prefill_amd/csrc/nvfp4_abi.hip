@@ -80,10 +80,11 @@ bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p
 int check_tensor(const nvfp4_tensor& t) {
   if (!t.codes || !t.scales || !t.gscale) return NVFP4_ERR_NULL;
   if (!aligned(t.codes, 16) || !aligned(t.scales, 16) || !aligned(t.gscale, 4)) return NVFP4_ERR_ALIGN;
+  if (t.tiled && !aligned(t.tiled, 256)) return NVFP4_ERR_ALIGN;
   return NVFP4_OK;
 }
 
-Operand op(const nvfp4_tensor& t) { return Operand{t.codes, t.scales, t.gscale}; }
+Operand op(const nvfp4_tensor& t) { return Operand{t.codes, t.scales, t.gscale, t.tiled}; }
 
 // Workspace bookkeeping: returns NVFP4_OK and sets *is_query when the call is
 // a size query; NVFP4_ERR_WORKSPACE when the given workspace is too small.
@@ -380,6 +381,21 @@ int nvfp4_moe_combine(const void* y_slots, int slots_dtype, int64_t ld_slots, co
   if ((rc = check_device()) != NVFP4_OK) return rc;
   return nvfp4::combine_launch(y_slots, slots_dtype == NVFP4_BF16, ld_slots, slot_of, weights, T, k, N, y,
                                y_dtype == NVFP4_BF16, ldy, reinterpret_cast<hipStream_t>(stream));
+}
+
+int nvfp4_tile_weight(nvfp4_tensor w, int64_t experts, int64_t N, int64_t K, uint8_t* tiled,
+                      size_t* tiled_bytes, void* stream) {
+  if (experts < 1 || experts > 4096) return NVFP4_ERR_ARG;
+  if (N < 0 || K <= 0 || K % 128 != 0) return NVFP4_ERR_SHAPE;
+  bool query;
+  const size_t need = nvfp4::tile_weight_bytes(experts, N, K);
+  int rc = workspace(tiled, tiled_bytes, need, &query);
+  if (rc != NVFP4_OK || query) return rc;
+  if (N == 0) return NVFP4_OK;
+  if (!w.codes || !w.scales) return NVFP4_ERR_NULL;
+  if (!aligned(w.codes, 16) || !aligned(w.scales, 16)) return NVFP4_ERR_ALIGN;
+  if ((rc = check_device()) != NVFP4_OK) return rc;
+  return nvfp4::tile_weight_launch(w.codes, w.scales, experts, N, K, tiled, reinterpret_cast<hipStream_t>(stream));
 }
 
 int nvfp4_grouped_gemm(nvfp4_tensor a, const int32_t* a_rows, const int32_t* group_offsets, int E, int64_t M,

@@ -191,6 +191,41 @@ def test_gemm_and_down_validation():
     assert d(_t(), _t(), 4, 128, 64, None, m.F32, 64, None, *ws) == m.ERR_NULL
 
 
+def test_tile_weight_validation_and_size():
+    tw = m.lib.nvfp4_tile_weight
+    s = _size()
+    # 128-row groups x 128-K chunks x 9216 bytes (8 KiB codes + 1 KiB scales)
+    assert tw(nvfp4_tensor(0, 0, 0), 1, 17408, 5120, None, ctypes.byref(s), None) == m.OK
+    assert s.value == 136 * 40 * 9216
+    assert tw(nvfp4_tensor(0, 0, 0), 64, 2048, 4096, None, ctypes.byref(s), None) == m.OK
+    assert s.value == 64 * 16 * 32 * 9216
+    assert tw(nvfp4_tensor(0, 0, 0), 1, 200, 256, None, ctypes.byref(s), None) == m.OK
+    assert s.value == 2 * 2 * 9216                                   # the last group of 128 rows is partial
+    assert m.tile_weight_bytes(5120, 17408) == 40 * 136 * 9216
+    big = ctypes.c_size_t(1 << 30)
+    assert tw(_t(), 1, 64, 100, FAKE, ctypes.byref(big), None) == m.ERR_SHAPE    # K % 128
+    assert tw(_t(), 1, -1, 128, FAKE, ctypes.byref(big), None) == m.ERR_SHAPE
+    assert tw(_t(), 0, 64, 128, FAKE, ctypes.byref(big), None) == m.ERR_ARG      # experts
+    assert tw(_t(), 1, 64, 128, FAKE + 16, ctypes.byref(big), None) == m.ERR_ALIGN
+    assert tw(_t(c=0), 1, 64, 128, FAKE, ctypes.byref(big), None) == m.ERR_NULL
+    assert tw(_t(s=FAKE + 4), 1, 64, 128, FAKE, ctypes.byref(big), None) == m.ERR_ALIGN
+    small = ctypes.c_size_t(9215)
+    assert tw(_t(), 1, 64, 128, FAKE, ctypes.byref(small), None) == m.ERR_WORKSPACE
+    assert tw(_t(), 1, 0, 128, None, None, None) == m.OK                          # empty: no-op
+    # a weight operand's tiled copy must be 256-byte aligned
+    ws = (FAKE, ctypes.byref(big), None)
+    wt = nvfp4_tensor(FAKE, FAKE, FAKE, FAKE + 64)
+    assert m.lib.nvfp4_gemm(_t(), wt, 4, 8, 128, FAKE, m.F32, 8, None, *ws) == m.ERR_ALIGN
+
+
+@no_gpu
+def test_tile_weight_without_device():
+    big = ctypes.c_size_t(1 << 30)
+    before = m.lib.nvfp4_launch_count()
+    assert m.lib.nvfp4_tile_weight(_t(), 1, 64, 128, FAKE, ctypes.byref(big), None) == m.ERR_DEVICE
+    assert m.lib.nvfp4_launch_count() == before
+
+
 def test_gu_act_validation_and_workspace():
     f = m.lib.nvfp4_mlp_gu_act
     z = nvfp4_tensor(0, 0, 0)
