@@ -530,9 +530,13 @@ __device__ __forceinline__ void xchunk(Ctx<WN, TM, TN, DUAL>& x, const Lds& lc, 
 #ifndef NVFP4_MIN_WG_PER_CU
 #define NVFP4_MIN_WG_PER_CU 2
 #endif
-// Work-groups the split-K plan of the store epilogue aims for.
+// Work-groups the split-K plan of the store epilogue aims for: about two
+// rounds of the 512 resident work-groups.  The 1024-token down projection
+// (320 tiles) then takes 4 splits; with tiled weights 4 measured faster than
+// 3 (10.47 -> 10.21 ms of down projection per long-prefill step, same box)
+// and 5 or 6 slower.
 #ifndef NVFP4_SPLIT_TARGET
-#define NVFP4_SPLIT_TARGET 768
+#define NVFP4_SPLIT_TARGET 1000
 #endif
 // Waves per work-group of the large-batch kernels (side by side in N).
 #ifndef NVFP4_GLU_WN

@@ -177,9 +177,9 @@ def test_gemm_and_down_validation():
     s = _size()
     assert g(nvfp4_tensor(0, 0, 0), nvfp4_tensor(0, 0, 0), 1024, 5120, 17408, None, m.F32, 5120, None, None,
              ctypes.byref(s), None) == m.OK
-    # f16 activation copy + float32 partials of the 3 K splits: 1024 tokens in
-    # 64 x 256 tiles make 16 x 20 = 320 work-groups, split 3 ways to 960
-    assert s.value == 1024 * 17408 * 2 + 3 * 1024 * 5120 * 4
+    # f16 activation copy + float32 partials of the 4 K splits: 1024 tokens in
+    # 64 x 256 tiles make 16 x 20 = 320 work-groups, split 4 ways to 1280
+    assert s.value == 1024 * 17408 * 2 + 4 * 1024 * 5120 * 4
     assert g(nvfp4_tensor(0, 0, 0), nvfp4_tensor(0, 0, 0), 4096, 4096, 4096, None, m.F32, 4096, None, None,
              ctypes.byref(s), None) == m.OK
     assert s.value == 4096 * 4096 * 2 + 4096 * 4096 * 4   # 64 x 16 = 1024 tiles: one split

@@ -81,7 +81,7 @@ GEMMS = [(96, 200, 1024), (64, 512, 8192), (1024, 5120, 17408)]
 @pytest.mark.parametrize("mm,n,k", GEMMS, ids=[f"{mm}x{n}x{k}" for mm, n, k in GEMMS])
 def test_gemm_tiled_bit_identical(mm, n, k):
     """Dense store contraction: unsplit, split K (64 x 512 x 8192) and the
-    1024-token down-projection shape (3 splits); float32 and bf16 outputs."""
+    1024-token down-projection shape (4 splits); float32 and bf16 outputs."""
     import mlp_prefill_amd as m
     announce(f"gemm tiled vs row-major {mm}x{n}x{k}")
     a = dev_quantize(bf16_normal(920, (mm, k)))
