@@ -1472,12 +1472,18 @@ __global__ void __launch_bounds__(kTlWaves * 64) tile_kernel(GemmArgs p) {
   // Buffer resources based at the tile's first weight row (rows past N read
   // row N-1: valid memory, never stored) and at the first token.
   const int64_t nrow = (N - n0) < (DUAL ? 16 : 32) ? (N - n0) : (DUAL ? 16 : 32);
-  const i32x4 rb = buf_desc(p.b_codes + n0 * kb, nrow * kb);
-  const i32x4 rbs = buf_desc(p.b_scales + n0 * ks, nrow * ks);
+  // With the tile-contiguous copies the resources cover this tile's 128-row
+  // group g (rows 128g .. 128g+127, all chunks): its 16 or 32 rows of one
+  // 128-K chunk are 1 or 2 KiB of consecutive code units there (rows past N
+  // are zero in the copy).
+  const bool tiled = p.b_tiled != nullptr && (!DUAL || p.u_tiled != nullptr);   // uniform
+  const int64_t tgroup = (n0 / kTileRows) * (K / kTileK) * kTileBlock, tbytes = (K / kTileK) * kTileBlock;
+  const i32x4 rb = tiled ? buf_desc(p.b_tiled + tgroup, tbytes) : buf_desc(p.b_codes + n0 * kb, nrow * kb);
+  const i32x4 rbs = tiled ? rb : buf_desc(p.b_scales + n0 * ks, nrow * ks);
   i32x4 ru = rb, rus = rbs;
   if constexpr (DUAL) {
-    ru = buf_desc(p.u_codes + n0 * kb, nrow * kb);
-    rus = buf_desc(p.u_scales + n0 * ks, nrow * ks);
+    ru = tiled ? buf_desc(p.u_tiled + tgroup, tbytes) : buf_desc(p.u_codes + n0 * kb, nrow * kb);
+    rus = tiled ? ru : buf_desc(p.u_scales + n0 * ks, nrow * ks);
   }
   const i32x4 ra = buf_desc(p.a_codes, M * kb);
   const i32x4 ras = buf_desc(p.a_scales, M * ks);
@@ -1487,20 +1493,33 @@ __global__ void __launch_bounds__(kTlWaves * 64) tile_kernel(GemmArgs p) {
   // tile (with the gate/up pair, copies 2 and 3 hold the up rows), swizzled
   // unit l % 8, i.e. source unit (l % 8) ^ (l / 8).  Scale copy e writes row
   // 16e + l/4 (the up rows for e = 1 with the pair), 4-byte piece l % 4.
+  //
+  // Tiled: code copy d takes 1 KiB (16 rows x 4 units, already in the staged
+  // order) of chunk half d % 2 of the stage, rows 16 (d / 2) .. (the up rows
+  // for d >= 2 with the pair) into stage bytes (d % 2) * 2048 + (d / 2) * 1024;
+  // scale copy e takes 16 rows x 8 bytes of both chunk halves of one matrix
+  // (lanes 0-31 the first, 32-63 the second) into e * 256, or with one weight
+  // all 32 rows of chunk half e.
   const uint32_t su = (uint32_t)((lane & 7) ^ (lane >> 3));
-  uint32_t vb[4], vs[2];
+  const int64_t lr0 = n0 % kTileRows;               // the tile's first row within its group
+  uint32_t vb[4], vs[2], db[4];
 #pragma unroll
   for (int d = 0; d < 4; ++d) {
     int64_t r = DUAL ? 8 * (d & 1) + (lane >> 3) : 8 * d + (lane >> 3);
     r = r < nrow ? r : nrow - 1;
-    vb[d] = (uint32_t)(r * kb) + su * 16u;
+    vb[d] = tiled ? (uint32_t)((d & 1) * kTileBlock + (lr0 + (DUAL ? 0 : 16 * (d >> 1))) * 64 + lane * 16)
+                  : (uint32_t)(r * kb) + su * 16u;
+    db[d] = tiled ? (uint32_t)((d & 1) * 2048 + (d >> 1) * 1024) : (uint32_t)(d * 1024);
   }
 #pragma unroll
   for (int e = 0; e < 2; ++e) {
     int64_t r = DUAL ? (lane >> 2) : 16 * e + (lane >> 2);
     r = r < nrow ? r : nrow - 1;
-    vs[e] = (uint32_t)(r * ks) + (uint32_t)(lane & 3) * 4u;
+    vs[e] = tiled ? (DUAL ? (uint32_t)(8192 + (lane >> 5) * kTileBlock + lr0 * 8 + (lane & 31) * 4)
+                          : (uint32_t)(8192 + e * kTileBlock + lr0 * 8 + lane * 4))
+                  : (uint32_t)(r * ks) + (uint32_t)(lane & 3) * 4u;
   }
+  const uint32_t sc_step = tiled ? (uint32_t)(2 * kTileBlock) : 128u, ss_step = tiled ? (uint32_t)(2 * kTileBlock) : 16u;
   // token copy d writes token rows 8d .. 8d+7 the same way (rows past M read
   // the last token); the scale copy fills 16 token slots
   uint32_t va[MT / 8];
@@ -1515,12 +1534,13 @@ __global__ void __launch_bounds__(kTlWaves * 64) tile_kernel(GemmArgs p) {
   const uint32_t ring = (uint32_t)w * (kTlDepth * kTlStage);   // this wave's ring (byte offset in lds)
   const uint32_t ring_addr = lds_addr(lds) + ring;
   auto issue = [&](int64_t stg, uint32_t buf) {
-    const uint32_t sc = (uint32_t)stg * 128u, ss = (uint32_t)stg * 16u;
+    const uint32_t sw = (uint32_t)stg * sc_step, sws = (uint32_t)stg * ss_step;   // weight codes / scales
+    const uint32_t sc = (uint32_t)stg * 128u, ss = (uint32_t)stg * 16u;           // tokens
     const uint32_t b = ring_addr + buf * kTlStage;
 #pragma unroll
-    for (int d = 0; d < 4; ++d) dma_b128((DUAL && d >= 2) ? ru : rb, vb[d], sc, b + kTlBc + d * 1024);
+    for (int d = 0; d < 4; ++d) dma_b128((DUAL && d >= 2) ? ru : rb, vb[d], sw, b + kTlBc + db[d]);
 #pragma unroll
-    for (int e = 0; e < 2; ++e) dma_b32((DUAL && e >= 1) ? rus : rbs, vs[e], ss, b + kTlBs + e * 256);
+    for (int e = 0; e < 2; ++e) dma_b32((DUAL && e >= 1) ? rus : rbs, vs[e], sws, b + kTlBs + e * 256);
 #pragma unroll
     for (int d = 0; d < MT / 8; ++d) dma_b128(ra, va[d], sc, b + kTlAc + d * 1024);
     dma_b32(ras, vas, ss, b + kTlAs);
@@ -1528,13 +1548,20 @@ __global__ void __launch_bounds__(kTlWaves * 64) tile_kernel(GemmArgs p) {
 
   // Fragment offsets of this lane within a stage: row t of each 16-row tile
   // (t = l % 16), quarter g = l / 16 (units 2g and 2g+1, scale piece g).
+  // Tiled: quarter g is chunk half g / 2, units 2 (g % 2) and 2 (g % 2) + 1 of
+  // its 64-byte row piece, stored at unit ^ ((row / 4) % 4); scale piece g % 2
+  // of the row's 8 bytes of that half.
   const int t = lane & 15, g = lane >> 4;
   uint32_t ob[2][2], obs[2], oa[2];
 #pragma unroll
   for (int j = 0; j < 2; ++j) {
 #pragma unroll
-    for (int h = 0; h < 2; ++h) ob[j][h] = kTlBc + (uint32_t)((16 * j + t) * 8 + ((2 * g + h) ^ (t & 7))) * 16u;
-    obs[j] = kTlBs + (uint32_t)(16 * j + t) * 16u + 4u * g;
+    for (int h = 0; h < 2; ++h)
+      ob[j][h] = tiled ? kTlBc + (uint32_t)((g >> 1) * 2048 + (16 * j + t) * 64 + ((2 * (g & 1) + h) ^ ((t >> 2) & 3)) * 16)
+                       : kTlBc + (uint32_t)((16 * j + t) * 8 + ((2 * g + h) ^ (t & 7))) * 16u;
+    obs[j] = tiled ? (DUAL ? kTlBs + (uint32_t)((2 * j + (g >> 1)) * 128 + t * 8 + 4 * (g & 1))
+                           : kTlBs + (uint32_t)((g >> 1) * 256 + (16 * j + t) * 8 + 4 * (g & 1)))
+                   : kTlBs + (uint32_t)(16 * j + t) * 16u + 4u * g;
   }
 #pragma unroll
   for (int h = 0; h < 2; ++h) oa[h] = kTlAc + (uint32_t)((MT == 16 ? t : (t & 7)) * 8 + ((2 * g + h) ^ (t & 7))) * 16u;

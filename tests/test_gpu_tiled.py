@@ -75,13 +75,17 @@ def _same(a, b, what):
     assert torch.equal(a, b), f"{what}: outputs differ with the tiled weights"
 
 
-GEMMS = [(96, 200, 1024), (64, 512, 8192), (1024, 5120, 17408)]
+# large batches (unsplit, split K, the 1024-token down projection) and the
+# 3-16 token stream (ragged N, 8 and 16 staged token rows, split K)
+GEMMS = [(96, 200, 1024), (64, 512, 8192), (1024, 5120, 17408), (5, 100, 4352), (12, 200, 5120), (16, 96, 17408),
+         (3, 5120, 17408)]
 
 
 @pytest.mark.parametrize("mm,n,k", GEMMS, ids=[f"{mm}x{n}x{k}" for mm, n, k in GEMMS])
 def test_gemm_tiled_bit_identical(mm, n, k):
-    """Dense store contraction: unsplit, split K (64 x 512 x 8192) and the
-    1024-token down-projection shape (4 splits); float32 and bf16 outputs."""
+    """Dense store contraction: unsplit, split K (64 x 512 x 8192), the
+    1024-token down-projection shape (4 splits), and the 3-16 token stream;
+    float32 and bf16 outputs."""
     import mlp_prefill_amd as m
     announce(f"gemm tiled vs row-major {mm}x{n}x{k}")
     a = dev_quantize(bf16_normal(920, (mm, k)))
@@ -104,7 +108,8 @@ def _nvfp4_same(x, y, what):
         _same(getattr(x, f), getattr(y, f), f"{what} {f}")
 
 
-MLPS = [(64, 256, 384), (300, 512, 640), (1024, 5120, 17408), (1, 5120, 17408), (5, 5120, 17408)]
+MLPS = [(64, 256, 384), (300, 512, 640), (1024, 5120, 17408), (1, 5120, 17408), (5, 5120, 17408),
+        (8, 3072, 1024), (12, 5120, 640), (16, 2304, 384), (3, 1024, 256)]
 
 
 @pytest.mark.parametrize("t,k,i", MLPS, ids=[f"T{t}_K{k}_I{i}" for t, k, i in MLPS])
@@ -138,9 +143,10 @@ def test_mlp_tiled_bit_identical(t, k, i):
     _same(ya, yb, "y (whole-MLP call)")
 
 
-def test_static_pair_tiled_bit_identical():
+@pytest.mark.parametrize("t", [5, 64])
+def test_static_pair_tiled_bit_identical(t):
     import mlp_prefill_amd as m
-    t, k, i = 64, 256, 384
+    k, i = 256, 384
     announce(f"static-scale pair tiled vs row-major T={t} K={k} I={i}")
     wdev, _ = _weights(k, i, (940, 941, 942))
     wt = [_tiled(w) for w in wdev]
