@@ -15,10 +15,12 @@ stack eager and replayed from a HIP graph, the expert-grouped MLP, the
 roofline of the dominant kernel and the CPU oracle timed on a bounded sample.
 """
 import argparse
+import dataclasses
 import json
 import os
 import sys
 import time
+import types
 
 import numpy as np
 import torch
@@ -515,6 +517,12 @@ def extra_lines(m):
                            "tflops": mlp_flops(p3["T"]) / (ms * 1e-3) / 1e12,
                            "tokens_per_s": p3["T"] / (ms * 1e-3),
                            "frac_f16_peak": mlp_flops(p3["T"]) / (ms * 1e-3) / 1e12 / PEAK_F16_TFLOPS}
+    if TILED_WEIGHTS:
+        # the same call on the row-major weights alone (no tile-contiguous copies)
+        rm = [dataclasses.replace(w, tiled=None) for w in lay.w]
+        lay_rm = types.SimpleNamespace(w=rm)
+        ms_rm = float(np.median(time_events(lambda: run(x, lay_rm, y), 20)))
+        out["prefill_1024"]["row_major_weights"] = {"ms": ms_rm, "tflops": mlp_flops(p3["T"]) / (ms_rm * 1e-3) / 1e12}
     del lay, run, x, y
     out["decode"] = decode_line(m)
     # the tensor-parallel (tp = 2) shard on one GPU: intermediate 8704

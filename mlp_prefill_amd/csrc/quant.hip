@@ -248,7 +248,10 @@ __global__ void __launch_bounds__(1024) quantize_small_kernel(const T* __restric
 
 // Work-groups of the quantiser: enough to fill the chip, few enough that the
 // per-work-group re-reduction of the partial maxima stays cheap.
-constexpr uint32_t kQuantGrid = 2048;
+#ifndef NVFP4_QUANT_GRID
+#define NVFP4_QUANT_GRID 2048
+#endif
+constexpr uint32_t kQuantGrid = NVFP4_QUANT_GRID;
 
 static uint32_t amax_grid(uint32_t nblocks) {
   uint32_t g = (nblocks + 1023u) / 1024u;   // ~4 blocks of 16 per thread
