@@ -644,8 +644,9 @@ def decode_stack_line(m, layers):
 
 def moe_line(m):
     """Expert-grouped MoE layer on the device: 4096 tokens routed top-8 over 64
-    experts (hidden 4096, expert width 2048): route, quantise, grouped gate/up +
-    SiLU*up + requantise, grouped down, combine."""
+    experts (hidden 4096, expert width 2048): route, the expert MLP in one call
+    (quantise, grouped gate/up + SiLU*up + requantise, grouped down), combine;
+    also timed with the separate quantise and grouped-GEMM calls."""
     from synthetic import WORKLOADS, bf16_normal, expert_seeds, router_logits
     p = WORKLOADS["moe_4096_top8_of_64"].params
     t, e, top, k, i = p["T"], p["E"], p["topk"], p["K"], p["I"]
@@ -678,8 +679,14 @@ def moe_line(m):
     ws_g = torch.empty(max(m.grouped_ws_bytes(slots, i, k, e, m.EPI_SILU_MUL_REQUANT), 256), dtype=torch.uint8,
                        device="cuda")
     ws_d = torch.empty(max(m.grouped_ws_bytes(slots, k, i, e, m.EPI_STORE), 256), dtype=torch.uint8, device="cuda")
+    ws_m = torch.empty(m.moe_mlp_ws_bytes(t, k, i, e, slots), dtype=torch.uint8, device="cuda")
 
     def layer():
+        m.nvfp4_moe_route(logits, top, offs, rows, slot_of, cw, ws=ws_r)
+        m.nvfp4_moe_mlp(x, rows, offs, wg, wu, wd, xq, hq, ys, ws=ws_m)
+        m.nvfp4_moe_combine(ys, slot_of, cw, y)
+
+    def layer_separate():
         m.nvfp4_moe_route(logits, top, offs, rows, slot_of, cw, ws=ws_r)
         m.nvfp4_quantize_act(x, xq, ws=ws_q)
         m.nvfp4_grouped_gemm(xq, rows, offs, wg, wu, out_q=hq, epilogue=m.EPI_SILU_MUL_REQUANT, m=slots, ws=ws_g)
@@ -690,7 +697,10 @@ def moe_line(m):
     layer()
     launches = m.launch_count() - before
     ms = float(np.median(time_events(layer, 10)))
-    parts = {}
+    before = m.launch_count()
+    layer_separate()
+    parts = {"separate_calls_launches": m.launch_count() - before,
+             "separate_calls_ms": float(np.median(time_events(layer_separate, 10)))}
     for name, kc in (("route", m.KC_ROUTE), ("combine", m.KC_COMBINE)):
         m.nvfp4_timing_begin(kc, 64)
         for _ in range(5):
@@ -727,8 +737,8 @@ def moe_line(m):
     return {"workload": "moe_4096_top8_of_64", "ms": ms, "tflops": tf, "frac_f16_peak": tf / PEAK_F16_TFLOPS,
             "tokens_per_s": t / (ms * 1e-3), "slots": slots, "launches_per_call": launches, **parts,
             "combine_gbs": comb_bytes / (parts["combine_ms"] * 1e-3) / 1e9,
-            "note": "ms covers routing, quantisation, both grouped GEMMs and the combine; TFLOP/s counts the "
-                    "6*slots*K*I of the expert MLPs"}
+            "note": "ms covers routing, the expert MLP call (quantisation, both grouped GEMMs) and the combine; "
+                    "TFLOP/s counts the 6*slots*K*I of the expert MLPs"}
 
 
 if __name__ == "__main__":

@@ -332,6 +332,37 @@ int nvfp4_mlp_down_quant(nvfp4_tensor h, nvfp4_tensor w_down, int64_t T, int64_t
                          nvfp4_tensor y_out, void *ws, size_t *ws_bytes, void *stream);
 
 /*
+ * nvfp4_moe_mlp -- the expert MLP over routed slots in one call ([llama]
+ * "Verified", MUL_MAT_ID; [dsv4] P8 item 5): x~ = NVFP4(x) with its global
+ * scale computed on the device; for every slot s of expert e (slots
+ * [group_offsets[e], group_offsets[e+1])) the gate/up pair of expert e on
+ * token row a_rows[s], SiLU(gate) * up requantised into h_q with one global
+ * scale over all M slots, and the down projection of expert e into row s of
+ * y_slots, scaled by gscale_h * w_down.gscale[e].  The values are those of
+ * nvfp4_quantize_act, then nvfp4_grouped_gemm with NVFP4_EPI_SILU_MUL_REQUANT
+ * and with NVFP4_EPI_STORE (bit-identical); the quantiser and the
+ * requantisation also write the f16 operand copies the contractions stage
+ * (the gate/up gathers its slots' rows from the token copy), so no launch
+ * expands or gathers an operand: six launches in all (five when x has at
+ * most 8192 blocks of 16: one quantiser launch).
+ *   x             : [T][K] float32 or bf16 (x_dtype), row stride ld_x
+ *   a_rows        : [M] token row of each slot (values < T); group_offsets
+ *                   [E+1] as nvfp4_grouped_gemm (group_offsets[E] == M)
+ *   w_gate, w_up  : [E][I][K] expert stacks;  w_down : [E][K][I]
+ *   K, I          : multiples of 128;  T * K * 2 < 2^31
+ *   x_q           : [T][K] NVFP4 (codes, scales, gscale written)
+ *   h_q           : [M][I] NVFP4 (codes, scales, gscale written)
+ *   y_slots       : [M][K] float32 or bf16 (y_dtype), row stride ld_y
+ *   ws            : required (size query with ws == NULL)
+ * T == 0 or M == 0: a no-op.  Routing (nvfp4_moe_route) and the weighted
+ * combine (nvfp4_moe_combine) are their own calls.
+ */
+int nvfp4_moe_mlp(const void *x, int x_dtype, int64_t ld_x, int64_t T, int64_t K, int64_t I, int E,
+                  const int32_t *a_rows, const int32_t *group_offsets, int64_t M, nvfp4_tensor w_gate,
+                  nvfp4_tensor w_up, nvfp4_tensor w_down, nvfp4_tensor x_q, nvfp4_tensor h_q, void *y_slots,
+                  int y_dtype, int64_t ld_y, void *ws, size_t *ws_bytes, void *stream);
+
+/*
  * nvfp4_tile_weight -- the tile-contiguous copy of a weight (or expert
  * stack) for the large-batch contractions ([llama] "What the patch does":
  * aligned whole-tile loads feeding the matrix unit).  A permutation of the

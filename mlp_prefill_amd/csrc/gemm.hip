@@ -89,6 +89,10 @@ struct GemmArgs {
   // large-batch kernels stage from instead of the row-major codes and scales.
   const uint8_t* b_tiled;
   const uint8_t* u_tiled;
+  // Expert-grouped gather (nullable): slot s stages activation row a_gather[s]
+  // of the f16 copy at `a` ([a_gather_rows][K]) instead of row s.
+  const int32_t* a_gather;
+  int64_t a_gather_rows;
 };
 
 // Partial sums shared between the work-groups of one launch go through the
@@ -710,6 +714,19 @@ __global__ void __launch_bounds__(WN * 64, MINWG) gemm_kernel(GemmArgs p) {
     int64_t m = m0 + row;
     if (m > m_end - 1) m = m_end - 1;
     x.a_off[u] = (uint32_t)(((m - m0) * K + ((slot ^ (row & 15)) << 3)) * 2);
+  }
+  if constexpr (GROUPED) {
+    if (p.a_gather != nullptr) {   // uniform: stage the slots' rows of the token copy directly
+      x.ra = buf_desc(p.a + c_begin * 128, p.a_gather_rows * K * 2 - c_begin * 256);
+#pragma unroll
+      for (int u = 0; u < C::SA; ++u) {
+        const int pu = u * C::NT + threadIdx.x;
+        const int row = pu >> 4, slot = pu & 15;
+        int64_t m = m0 + row;
+        if (m > m_end - 1) m = m_end - 1;
+        x.a_off[u] = (uint32_t)(((int64_t)p.a_gather[m] * K + ((slot ^ (row & 15)) << 3)) * 2);
+      }
+    }
   }
   auto wrow = [&](int rho) -> int64_t {          // row of this tile's gate (or up) matrix, clamped
     int64_t n = n0 + ((DUAL && rho >= BN) ? rho - BN : rho);
@@ -2158,7 +2175,7 @@ int store_launch(Operand a, const int32_t* rows, const int32_t* off, int E, int6
   float* part = reinterpret_cast<float*>(reinterpret_cast<char*>(ws) + align256((size_t)M * K * 2));
   const Plan pl = plan_store(M, N, K, E, grouped);
   // the weight streams expand the activation themselves; a given copy needs no expansion
-  if (a16_given != nullptr && !grouped) a16 = const_cast<_Float16*>(a16_given);
+  if (a16_given != nullptr && (!grouped || rows == nullptr)) a16 = const_cast<_Float16*>(a16_given);
   else if (grouped || (pl.gv_bpl == 0 && !pl.tl)) launch_expand(a.codes, a.scales, rows, M, K, a16, st);
   GemmArgs g = base_args(a16, a.gscale, w, M, N, K);
   g.a_codes = a.codes;
@@ -2217,22 +2234,27 @@ static void tile_dual_setup(GemmArgs& g, const TlPlan& tl, char* w, hipStream_t 
   launch_clear(g.tickets, cdiv(g.N, 16), KC_GEMM_GLU, st);
 }
 
-size_t glu_ws_bytes(int64_t M, int64_t N, int64_t K, int E, bool grouped) {
-  return align256((size_t)M * N * 4) + align256((size_t)M * K * 2) + align256((size_t)glu_parts(M, N, K, E, grouped) * 4) +
-         (grouped ? 0 : tile_dual_bytes(M, N, K));
+size_t glu_ws_bytes(int64_t M, int64_t N, int64_t K, int E, bool grouped, bool gather) {
+  return align256((size_t)M * N * 4) + (gather ? 0 : align256((size_t)M * K * 2)) +
+         align256((size_t)glu_parts(M, N, K, E, grouped) * 4) + (grouped ? 0 : tile_dual_bytes(M, N, K));
 }
 
 int glu_launch(Operand a, const int32_t* a_rows, const int32_t* off, int E, int64_t M, Operand gt, Operand up,
                int64_t N, int64_t K, uint8_t* hq_codes, uint8_t* hq_scales, float* hq_gs, void* ws,
-               hipStream_t st, const _Float16* a16_given, _Float16* hq16) {
+               hipStream_t st, const _Float16* a16_given, _Float16* hq16, int64_t gather_rows) {
   const bool grouped = off != nullptr;
+  const bool gather = grouped && a16_given != nullptr;   // slot rows staged from the token copy via a_rows
   float* h = reinterpret_cast<float*>(ws);
   _Float16* a16 = reinterpret_cast<_Float16*>(reinterpret_cast<char*>(ws) + align256((size_t)M * N * 4));
-  float* partials = reinterpret_cast<float*>(reinterpret_cast<char*>(a16) + align256((size_t)M * K * 2));
+  float* partials = reinterpret_cast<float*>(reinterpret_cast<char*>(a16) + (gather ? 0 : align256((size_t)M * K * 2)));
   const bool stream = !grouped && (plan_gemv(M, K, true).bpl > 0 || plan_tile(M, N, K, true).ok);
-  if (a16_given != nullptr && !grouped) a16 = const_cast<_Float16*>(a16_given);
+  if (a16_given != nullptr) a16 = const_cast<_Float16*>(a16_given);
   else if (!stream) launch_expand(a.codes, a.scales, a_rows, M, K, a16, st);   // the streams expand x~ themselves
   GemmArgs g = base_args(a16, a.gscale, gt, M, N, K);
+  if (gather) {
+    g.a_gather = a_rows;
+    g.a_gather_rows = gather_rows;
+  }
   g.a_codes = a.codes;
   g.a_scales = a.scales;
   g.u_codes = up.codes;
@@ -2363,6 +2385,30 @@ static MlpDecodePlan plan_mlp_decode(int64_t T, int64_t K, int64_t I) {
   d.gu_groups = d.gu_tl.ok && d.gu_tl.splits > 1 ? cdiv(I, 16) : 0;
   d.ok = true;
   return d;
+}
+
+size_t moe_mlp_ws_bytes(int64_t T, int64_t K, int64_t I, int E, int64_t M) {
+  return align256(quantize_ws_bytes(T, K, 0)) + align256((size_t)T * K * 2) + align256(glu_ws_bytes(M, I, K, E, true, true)) +
+         align256(store_ws_bytes(M, K, I, E, true));
+}
+
+int moe_mlp_launch(const void* x, int x_dtype, int64_t ld_x, int64_t T, int64_t K, int64_t I, int E,
+                   const int32_t* a_rows, const int32_t* off, int64_t M, Operand wg, Operand wu, Operand wd,
+                   uint8_t* xq_codes, uint8_t* xq_scales, float* xq_gs, uint8_t* hq_codes, uint8_t* hq_scales,
+                   float* hq_gs, void* y, int y_bf16, int64_t ldy, void* ws, hipStream_t st) {
+  char* w = reinterpret_cast<char*>(ws);
+  const size_t q_bytes = align256(quantize_ws_bytes(T, K, 0));
+  _Float16* x16 = reinterpret_cast<_Float16*>(w + q_bytes);
+  char* wg_ws = w + q_bytes + align256((size_t)T * K * 2);
+  char* wd_ws = wg_ws + align256(glu_ws_bytes(M, I, K, E, true, true));
+  _Float16* h16 = reinterpret_cast<_Float16*>(wd_ws);   // the down projection's f16 slot
+  int rc = quantize_launch(x, x_dtype, T, K, ld_x, xq_codes, xq_scales, xq_gs, 0, w, st, x16);
+  if (rc) return rc;
+  const Operand xq{xq_codes, xq_scales, xq_gs, nullptr};
+  if ((rc = glu_launch(xq, a_rows, off, E, M, wg, wu, I, K, hq_codes, hq_scales, hq_gs, wg_ws, st, x16, h16, T)))
+    return rc;
+  const Operand hq{hq_codes, hq_scales, hq_gs, nullptr};
+  return store_launch(hq, nullptr, off, E, M, wd, K, I, y, y_bf16, ldy, nullptr, wd_ws, st, h16);
 }
 
 size_t mlp_ws_bytes(int64_t T, int64_t K, int64_t I) {

@@ -96,12 +96,15 @@ int store_launch(Operand a, const int32_t* rows, const int32_t* off, int E, int6
 // stream with K split, the workspace also holds the split partial sums and the
 // column tiles' tickets, cleared by a launch of their own before the
 // contraction.
-size_t glu_ws_bytes(int64_t M, int64_t N, int64_t K, int E, bool grouped);
-// a16 (nullable): as for store_launch; hq16 (nullable): the requantisation
-// also writes the f16 copy of H~ there (for the down projection).
+size_t glu_ws_bytes(int64_t M, int64_t N, int64_t K, int E, bool grouped, bool gather = false);
+// a16 (nullable): as for store_launch -- except expert-grouped, where it is
+// the f16 copy of the whole activation [gather_rows][K] and slot s stages row
+// a_rows[s] of it (no expansion launch, no f16 slot in the workspace:
+// glu_ws_bytes(..., gather = true)); hq16 (nullable): the requantisation also
+// writes the f16 copy of H~ there (for the down projection).
 int glu_launch(Operand a, const int32_t* a_rows, const int32_t* off, int E, int64_t M, Operand gt, Operand up,
                int64_t N, int64_t K, uint8_t* hq_codes, uint8_t* hq_scales, float* hq_gs, void* ws,
-               hipStream_t st, const _Float16* a16 = nullptr, _Float16* hq16 = nullptr);
+               hipStream_t st, const _Float16* a16 = nullptr, _Float16* hq16 = nullptr, int64_t gather_rows = 0);
 
 // The same GLU output (dense, or expert-grouped when `off` is given)
 // quantised in the contraction's epilogue with the given global scale *hq_gs
@@ -131,6 +134,18 @@ int mlp_launch(const void* x, int x_dtype, int64_t ld_x, int64_t T, int64_t K, i
                Operand wd, uint8_t* xq_codes, uint8_t* xq_scales, float* xq_gs, uint8_t* hq_codes, uint8_t* hq_scales,
                float* hq_gs, void* y, int y_bf16, int64_t ldy, const float* x_amax, float* y_amax, void* ws,
                hipStream_t st);
+
+// Expert MLP over routed slots: quantise x [T][K] (also writing its f16 copy),
+// expert-grouped gate/up + SiLU*up staging each slot's row of that copy,
+// requantisation over all M slots (also writing the f16 copy of H~), and the
+// expert-grouped down projection into y_slots [M][K] -- six launches (five
+// with the one-launch quantiser), none of them an expansion.  Workspace: [quantiser partials][x f16][gate/up
+// workspace without its f16 slot][down workspace, H~ f16 in its f16 slot].
+size_t moe_mlp_ws_bytes(int64_t T, int64_t K, int64_t I, int E, int64_t M);
+int moe_mlp_launch(const void* x, int x_dtype, int64_t ld_x, int64_t T, int64_t K, int64_t I, int E,
+                   const int32_t* a_rows, const int32_t* off, int64_t M, Operand wg, Operand wu, Operand wd,
+                   uint8_t* xq_codes, uint8_t* xq_scales, float* xq_gs, uint8_t* hq_codes, uint8_t* hq_scales,
+                   float* hq_gs, void* y, int y_bf16, int64_t ldy, void* ws, hipStream_t st);
 
 // ---- expert routing and combine ----------------------------------------------
 size_t route_ws_bytes(int64_t T, int E, int k);

@@ -349,6 +349,35 @@ int nvfp4_mlp(const void* x, int x_dtype, int64_t ld_x, const float* x_amax, int
                            ws, reinterpret_cast<hipStream_t>(stream));
 }
 
+int nvfp4_moe_mlp(const void* x, int x_dtype, int64_t ld_x, int64_t T, int64_t K, int64_t I, int E,
+                  const int32_t* a_rows, const int32_t* group_offsets, int64_t M, nvfp4_tensor w_gate,
+                  nvfp4_tensor w_up, nvfp4_tensor w_down, nvfp4_tensor x_q, nvfp4_tensor h_q, void* y_slots,
+                  int y_dtype, int64_t ld_y, void* ws, size_t* ws_bytes, void* stream) {
+  if (!dtype_ok(x_dtype) || !dtype_ok(y_dtype)) return NVFP4_ERR_ARG;
+  if (E < 1 || E > 4096) return NVFP4_ERR_ARG;
+  if (T < 0 || M < 0 || K <= 0 || I <= 0 || K % 128 != 0 || I % 128 != 0 || ld_x < K || ld_y < K)
+    return NVFP4_ERR_SHAPE;
+  if (M * (I / 16) >= ((int64_t)1 << 31) || M * (K / 16) >= ((int64_t)1 << 31) ||
+      T * (K / 16) >= ((int64_t)1 << 31) || T * K * 2 >= ((int64_t)1 << 31))
+    return NVFP4_ERR_SHAPE;
+  bool query;
+  int rc = workspace(ws, ws_bytes, T > 0 && M > 0 ? nvfp4::moe_mlp_ws_bytes(T, K, I, E, M) : 0, &query);
+  if (rc != NVFP4_OK || query) return rc;
+  if (T == 0 || M == 0) return NVFP4_OK;
+  if (!x || !y_slots || !a_rows || !group_offsets) return NVFP4_ERR_NULL;
+  if ((rc = check_tensor(w_gate)) != NVFP4_OK || (rc = check_tensor(w_up)) != NVFP4_OK ||
+      (rc = check_tensor(w_down)) != NVFP4_OK || (rc = check_tensor(x_q)) != NVFP4_OK ||
+      (rc = check_tensor(h_q)) != NVFP4_OK)
+    return rc;
+  if (!aligned(x, 16) || (ld_x * elem_size(x_dtype)) % 16 != 0 || !aligned(y_slots, 16) ||
+      (ld_y * elem_size(y_dtype)) % 16 != 0 || !aligned(a_rows, 4) || !aligned(group_offsets, 4))
+    return NVFP4_ERR_ALIGN;
+  if ((rc = check_device()) != NVFP4_OK) return rc;
+  return nvfp4::moe_mlp_launch(x, x_dtype, ld_x, T, K, I, E, a_rows, group_offsets, M, op(w_gate), op(w_up),
+                               op(w_down), x_q.codes, x_q.scales, x_q.gscale, h_q.codes, h_q.scales, h_q.gscale,
+                               y_slots, y_dtype == NVFP4_BF16, ld_y, ws, reinterpret_cast<hipStream_t>(stream));
+}
+
 int nvfp4_moe_route(const float* logits, int64_t T, int E, int k, int64_t ld, int32_t* group_offsets,
                     int32_t* a_rows, int32_t* slot_of, float* weights, void* ws, size_t* ws_bytes, void* stream) {
   if (E < 1 || E > nvfp4::kMaxExperts || k < 1 || k > nvfp4::kMaxTopK || k > E) return NVFP4_ERR_ARG;

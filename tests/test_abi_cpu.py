@@ -226,6 +226,48 @@ def test_tile_weight_without_device():
     assert m.lib.nvfp4_launch_count() == before
 
 
+def test_moe_mlp_validation_and_workspace():
+    f = m.lib.nvfp4_moe_mlp
+    big = ctypes.c_size_t(1 << 34)
+    t3 = (_t(), _t(), _t(), _t(), _t())
+
+    def call(x=FAKE, xd=m.BF16, ldx=256, t=96, k=256, i=384, e=8, rows=FAKE, offs=FAKE, mm=192, y=FAKE, yd=m.F32,
+             ldy=256, ws=FAKE, sz=None, tens=t3):
+        return f(x, xd, ldx, t, k, i, e, rows, offs, mm, *tens, y, yd, ldy, ws, ctypes.byref(sz or big), None)
+
+    assert call(xd=7) == m.ERR_ARG
+    assert call(yd=7) == m.ERR_ARG
+    assert call(e=0) == m.ERR_ARG
+    assert call(k=200, ldx=200, ldy=200) == m.ERR_SHAPE          # K % 128
+    assert call(i=200) == m.ERR_SHAPE                            # I % 128
+    assert call(ldx=128) == m.ERR_SHAPE                          # ld_x < K
+    assert call(ldy=128) == m.ERR_SHAPE
+    assert call(t=1 << 22, k=1024, ldx=1024, ldy=1024) == m.ERR_SHAPE   # T * K * 2 >= 2^31
+    assert call(rows=None) == m.ERR_NULL
+    assert call(y=None) == m.ERR_NULL
+    assert call(rows=FAKE + 2) == m.ERR_ALIGN
+    assert call(y=FAKE + 8) == m.ERR_ALIGN
+    assert call(tens=(_t(), _t(s=FAKE + 4), _t(), _t(), _t())) == m.ERR_ALIGN
+    assert call(sz=ctypes.c_size_t(256)) == m.ERR_WORKSPACE
+    assert f(None, m.BF16, 256, 0, 256, 384, 8, None, None, 0, *t3, None, m.F32, 256, None, None, None) == m.OK
+    s = _size()
+    assert f(None, m.BF16, 4096, 4096, 4096, 2048, 64, None, None, 32768, *(nvfp4_tensor(0, 0, 0),) * 5, None, m.BF16,
+             4096, None, ctypes.byref(s), None) == m.OK
+    # x f16 copy + float32 H + f16 H~ + the down projection's partial sums: no gathered activation copy
+    assert s.value >= 4096 * 4096 * 2 + 32768 * 2048 * 4 + 32768 * 2048 * 2
+    assert s.value < 4096 * 4096 * 2 + 32768 * 2048 * 4 + 32768 * 2048 * 2 + 32768 * 4096 * 4 + (1 << 24)
+    assert m.moe_mlp_ws_bytes(4096, 4096, 2048, 64, 32768) == s.value
+
+
+@no_gpu
+def test_moe_mlp_without_device():
+    big = ctypes.c_size_t(1 << 34)
+    before = m.lib.nvfp4_launch_count()
+    assert m.lib.nvfp4_moe_mlp(FAKE, m.BF16, 256, 96, 256, 384, 8, FAKE, FAKE, 192, _t(), _t(), _t(), _t(), _t(),
+                               FAKE, m.F32, 256, FAKE, ctypes.byref(big), None) == m.ERR_DEVICE
+    assert m.lib.nvfp4_launch_count() == before
+
+
 def test_gu_act_validation_and_workspace():
     f = m.lib.nvfp4_mlp_gu_act
     z = nvfp4_tensor(0, 0, 0)
