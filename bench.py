@@ -509,21 +509,32 @@ def extra_lines(m):
     lay = Layer(m, (p3["wg_seed"], p3["wu_seed"], p3["wd_seed"]))
     x = m.bf16_from_bits(bf16_normal(p3["x_seed"], (p3["T"], K_HID),
                                      outliers=outlier_channels(p3["outlier_seed"], K_HID)))
-    run = MlpRunner(m, p3["T"])
+    whole = WholeRunner(m, p3["T"])
     y = torch.empty((p3["T"], K_HID), dtype=torch.float32, device="cuda")
-    t = time_events(lambda: run(x, lay, y), 20)
-    ms = float(np.median(t))
+    before = m.launch_count()
+    whole(x, lay, y, 0, False)
+    launches = m.launch_count() - before
+    ms = float(np.median(time_events(lambda: whole(x, lay, y, 0, False), 20)))
     out["prefill_1024"] = {"workload": "mlp_prefill_1024x5120x17408", "ms": ms,
                            "tflops": mlp_flops(p3["T"]) / (ms * 1e-3) / 1e12,
                            "tokens_per_s": p3["T"] / (ms * 1e-3),
-                           "frac_f16_peak": mlp_flops(p3["T"]) / (ms * 1e-3) / 1e12 / PEAK_F16_TFLOPS}
+                           "frac_f16_peak": mlp_flops(p3["T"]) / (ms * 1e-3) / 1e12 / PEAK_F16_TFLOPS,
+                           "launches": launches, "call": "nvfp4_mlp (whole MLP; global scales computed on the device)"}
+    # the separate calls (quantise, gate/up + requantise, down), and the
+    # whole-MLP call on the row-major weights alone (no tile-contiguous copies)
+    run = MlpRunner(m, p3["T"])
+    before = m.launch_count()
+    run(x, lay, y)
+    launches_sep = m.launch_count() - before
+    ms_sep = float(np.median(time_events(lambda: run(x, lay, y), 20)))
+    out["prefill_1024"]["separate_calls"] = {"ms": ms_sep, "tflops": mlp_flops(p3["T"]) / (ms_sep * 1e-3) / 1e12,
+                                             "launches": launches_sep}
     if TILED_WEIGHTS:
-        # the same call on the row-major weights alone (no tile-contiguous copies)
         rm = [dataclasses.replace(w, tiled=None) for w in lay.w]
         lay_rm = types.SimpleNamespace(w=rm)
-        ms_rm = float(np.median(time_events(lambda: run(x, lay_rm, y), 20)))
+        ms_rm = float(np.median(time_events(lambda: whole(x, lay_rm, y, 0, False), 20)))
         out["prefill_1024"]["row_major_weights"] = {"ms": ms_rm, "tflops": mlp_flops(p3["T"]) / (ms_rm * 1e-3) / 1e12}
-    del lay, run, x, y
+    del lay, run, whole, x, y
     out["decode"] = decode_line(m)
     # the tensor-parallel (tp = 2) shard on one GPU: intermediate 8704
     log("extra: tp=2 shard MLP (5120 -> 2 x 8704 -> 5120), T = 1024 and T = 1")

@@ -78,7 +78,9 @@ def _same(a, b, what):
 # large batches (unsplit, split K, the 1024-token down projection) and the
 # 3-16 token stream (ragged N, 8 and 16 staged token rows, split K)
 GEMMS = [(96, 200, 1024), (64, 512, 8192), (1024, 5120, 17408), (5, 100, 4352), (12, 200, 5120), (16, 96, 17408),
-         (3, 5120, 17408)]
+         (3, 5120, 17408),
+         # a 256-wide store tile whose second 128-row group does not exist (clamped, never stored)
+         (96, 100, 1024)]
 
 
 @pytest.mark.parametrize("mm,n,k", GEMMS, ids=[f"{mm}x{n}x{k}" for mm, n, k in GEMMS])
