@@ -487,6 +487,12 @@ __device__ __forceinline__ void xstep(Ctx<WN, TM, TN, DUAL>& x, const Lds& lc, c
   constexpr int NMFMA = TM * TN * (DUAL ? 2 : 1);
   constexpr int NVALU = TN * (DUAL ? 2 : 1) * 9;
   constexpr int NDS = TM + (S == 6 ? 3 * TN * (DUAL ? 2 : 1) : 0);
+  // Gate/up: the wave issues steps 0-5 at raised priority and returns to the
+  // normal one before the chunk barrier, so the SIMD's arbiter favours a wave
+  // in its MFMA steps over one arriving at (or leaving) the barrier (gate/up
+  // 311 -> 305 us on one box; the store kernel measured slower with it).
+  if constexpr (DUAL && S == 0) __builtin_amdgcn_s_setprio(1);
+  if constexpr (DUAL && S == 6) __builtin_amdgcn_s_setprio(0);
   if constexpr (S == 6) {
     asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" : : : "memory");
     __builtin_amdgcn_sched_barrier(0);
@@ -777,10 +783,17 @@ __global__ void __launch_bounds__(WN * 64, MINWG) gemm_kernel(GemmArgs p) {
     const Lds l0{lds_a[0], lds_b[0], lds_s[0]}, l1{lds_a[1], lds_b[1], lds_s[1]};
     BPack<TN, DUAL> f0, f1;
     BExp<TN, DUAL> e0, e1;
+    // both buffers' copies in flight before the first wait (chunk 0 landed:
+    // at most chunk 1's copies still outstanding)
+    constexpr int PER0 = C::SA + C::SB + C::SD;
     stage_dma(x, la(0), lb(0), ls(0), 0);
-    asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" : : : "memory");
+    if (nch > 1) {
+      stage_dma(x, la(1), lb(1), ls(1), 1);
+      asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" : : "n"(PER0) : "memory");
+    } else {
+      asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" : : : "memory");
+    }
     __builtin_amdgcn_sched_barrier(0);
-    if (nch > 1) stage_dma(x, la(1), lb(1), ls(1), 1);
     read_b<WN, TM, TN, DUAL>(l0, f0);
     read_a<0, 0>(x, l0);
     read_a<1, 1>(x, l0);
