@@ -487,11 +487,12 @@ __device__ __forceinline__ void xstep(Ctx<WN, TM, TN, DUAL>& x, const Lds& lc, c
   constexpr int NMFMA = TM * TN * (DUAL ? 2 : 1);
   constexpr int NVALU = TN * (DUAL ? 2 : 1) * 9;
   constexpr int NDS = TM + (S == 6 ? 3 * TN * (DUAL ? 2 : 1) : 0);
-  // Gate/up: the wave issues steps 0-5 at raised priority and returns to the
+  // Gate/up: the wave issues steps 2-5 at raised priority and returns to the
   // normal one before the chunk barrier, so the SIMD's arbiter favours a wave
-  // in its MFMA steps over one arriving at (or leaving) the barrier (gate/up
-  // 311 -> 305 us on one box; the store kernel measured slower with it).
-  if constexpr (DUAL && S == 0) __builtin_amdgcn_s_setprio(1);
+  // in the middle of its MFMA steps over one leaving or arriving at the
+  // barrier (same box: gate/up 310.8 -> 308.5 us; steps 0-5 305.4 against
+  // 311.0 on another; the store kernel measured slower with it).
+  if constexpr (DUAL && S == 2) __builtin_amdgcn_s_setprio(1);
   if constexpr (DUAL && S == 6) __builtin_amdgcn_s_setprio(0);
   if constexpr (S == 6) {
     asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" : : : "memory");
