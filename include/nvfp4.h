@@ -375,7 +375,8 @@ int nvfp4_moe_mlp(const void *x, int x_dtype, int64_t ld_x, int64_t T, int64_t K
  * streams read the row-major codes and scales as before.
  *   w        : [experts][N][K] NVFP4 (codes, scales; gscale not read)
  *   experts  : 1 for a single weight, E for an expert stack
- *   K        : multiple of 128;  N >= 0
+ *   K        : multiple of 128;  N >= 0;  one expert's copy below 2 GiB
+ *              (ceil(N/128) * (K/128) * 9216 < 2^31)
  *   tiled    : output, tiled_bytes = experts * ceil(N/128) * (K/128) * 9216
  *              bytes, 256-byte aligned (tiled == NULL: size query).  Block
  *              (e, g, c) -- rows 128g .. 128g+127 of expert e, K elements

@@ -451,7 +451,6 @@ def nvfp4_moe_combine(y_slots, slot_of, weights, y, stream=None):
            "nvfp4_moe_combine")
 
 
-# ---- convenience: host <-> device NVFP4 (test and setup plumbing) -------------------
 def moe_mlp_ws_bytes(t, k, i, e, m):
     size = ctypes.c_size_t(0)
     _check(_lib.nvfp4_moe_mlp(_vp(0), BF16, k, t, k, i, e, _vp(0), _vp(0), m, _null_tensor(), _null_tensor(),
@@ -496,6 +495,7 @@ def nvfp4_tile_weight(w, stream=None):
            "nvfp4_tile_weight")
 
 
+# ---- convenience: host <-> device NVFP4 (test and setup plumbing) -------------------
 def to_device(q_codes, q_scales, gs, rows, cols, device="cuda"):
     """NVFP4 from host arrays (numpy uint8 codes/scales, float32 gs)."""
     return NVFP4(torch.from_numpy(q_codes).to(device), torch.from_numpy(q_scales).to(device),

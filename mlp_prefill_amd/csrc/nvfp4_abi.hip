@@ -416,6 +416,8 @@ int nvfp4_tile_weight(nvfp4_tensor w, int64_t experts, int64_t N, int64_t K, uin
                       size_t* tiled_bytes, void* stream) {
   if (experts < 1 || experts > 4096) return NVFP4_ERR_ARG;
   if (N < 0 || K <= 0 || K % 128 != 0) return NVFP4_ERR_SHAPE;
+  // the contractions address one expert's copy with 32-bit offsets
+  if (nvfp4::tile_weight_bytes(1, N, K) >= ((size_t)1 << 31)) return NVFP4_ERR_SHAPE;
   bool query;
   const size_t need = nvfp4::tile_weight_bytes(experts, N, K);
   int rc = workspace(tiled, tiled_bytes, need, &query);

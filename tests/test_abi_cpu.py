@@ -206,6 +206,7 @@ def test_tile_weight_validation_and_size():
     assert tw(_t(), 1, 64, 100, FAKE, ctypes.byref(big), None) == m.ERR_SHAPE    # K % 128
     assert tw(_t(), 1, -1, 128, FAKE, ctypes.byref(big), None) == m.ERR_SHAPE
     assert tw(_t(), 0, 64, 128, FAKE, ctypes.byref(big), None) == m.ERR_ARG      # experts
+    assert tw(_t(), 1, 65536, 65536, FAKE, ctypes.byref(big), None) == m.ERR_SHAPE   # one expert's copy >= 2 GiB
     assert tw(_t(), 1, 64, 128, FAKE + 16, ctypes.byref(big), None) == m.ERR_ALIGN
     assert tw(_t(c=0), 1, 64, 128, FAKE, ctypes.byref(big), None) == m.ERR_NULL
     assert tw(_t(s=FAKE + 4), 1, 64, 128, FAKE, ctypes.byref(big), None) == m.ERR_ALIGN
