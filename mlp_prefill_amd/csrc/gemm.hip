@@ -44,6 +44,7 @@
 // requantisation kernel forms the global scale of H on the device.
 #include "device_common.h"
 #include "internal.h"
+#include <atomic>
 
 namespace nvfp4 {
 
@@ -587,31 +588,50 @@ constexpr uint32_t kGroupGm = 8;   // m tiles per super-tile of the expert-group
 #define NVFP4_DENSE_GROUP_M 4
 #endif
 
-template <int WN, int TM, int TN, bool DUAL, bool GROUPED, int EPI, int NS, int MINWG>
-__global__ void __launch_bounds__(WN * 64, MINWG) gemm_kernel(GemmArgs p) {
-  using C = Cfg<WN, TM, TN, DUAL>;
-  constexpr int BM = C::BM;
-  constexpr int BN = C::BN;
-  static_assert(BN % kTileRows == 0 && C::NB * 4 % 512 == 0, "whole 128-row groups of the tiled weights per tile");
-  __shared__ float red[WN];
-  __shared__ f16x8 lds_a[NS][C::LDS_A];
-  __shared__ u32x4 lds_b[NS][C::LDS_B];
-  __shared__ uint2 lds_s[NS][C::NB];
-  const int lane = threadIdx.x & 63;
-  const int wn = threadIdx.x >> 6;
-  const int r32 = lane & 31, hh = lane >> 5;
+// Work-groups of the dense large-batch kernels are persistent: work-group b
+// takes the tiles v = b, b + grid, b + 2 grid, ... of the launch's tile order
+// (grid = the work-groups the chip holds at once), and with the two-buffer
+// pipeline and a register epilogue it issues the copies of its next tile's
+// first two chunks before it writes the current tile's outputs, so that their
+// latency hides behind the epilogue instead of following a new work-group's
+// start.  Every tile's arithmetic and its order are those it has on a
+// work-group of its own.  Measured on the 1024-token gate/up (4.25 tiles per
+// work-group): 300-303 against 307 us.  The expert-grouped kernels keep one
+// work-group per tile: with 18 tiles per work-group the work-groups of an XCD
+// drift apart over the fixed stride, its tiles in flight spread out, and the
+// 64-expert layer measured 1.93 against 1.89-1.90 ms.  0: one work-group per
+// tile everywhere.
+#ifndef NVFP4_PERSIST
+#define NVFP4_PERSIST 1
+#endif
+#ifndef NVFP4_PERSIST_GROUPED
+#define NVFP4_PERSIST_GROUPED 0
+#endif
 
-  // ---- tile: K splits slowest, then super-tiles of kGm m tiles x all n tiles
-  // (m fastest inside), so that the work-groups resident on one XCD work on
-  // one K range and share both activation rows and weight columns in its L2
-  // (for expert groups the gathered activations of all experts do not fit
-  // the MALL); kGm = 0: m fastest, then n
-  const uint32_t t = xcd_remap(blockIdx.x, gridDim.x);
-  uint32_t mt, split, n_tile;
+// A tile of the launch: K split, first row and row end (the expert's end for
+// expert groups; m0 < 0: a tile past the last expert, no work), first column,
+// expert.
+struct TileLoc {
+  int64_t m0, m_end, n0;
+  uint32_t split;
+  int e;
+};
+
+// Tile order: K splits slowest, then super-tiles of kGm m tiles x all n tiles
+// (m fastest inside), so that the work-groups resident on one XCD work on one
+// K range and share both activation rows and weight columns in its L2 (for
+// expert groups the gathered activations of all experts do not fit the
+// MALL); kGm = 0: m fastest, then n.  Virtual tile v is dealt to the XCD that
+// runs work-group v % 8 (xcd_remap).
+template <int BM, int BN, bool GROUPED>
+__device__ __forceinline__ TileLoc locate_tile(const GemmArgs& p, uint32_t v, uint32_t vtotal) {
+  TileLoc L;
+  const uint32_t t = xcd_remap(v, vtotal);
+  uint32_t mt, n_tile;
   constexpr uint32_t kGm = GROUPED ? kGroupGm : (uint32_t)NVFP4_DENSE_GROUP_M;
   const uint32_t per_split = p.m_tiles * p.n_tiles;
-  split = t / per_split;
-  const uint32_t u = t - split * per_split;
+  L.split = t / per_split;
+  const uint32_t u = t - L.split * per_split;
   if (kGm > 0) {
     const uint32_t span = kGm * p.n_tiles;
     const uint32_t sup = u / span, r = u - sup * span;
@@ -622,8 +642,8 @@ __global__ void __launch_bounds__(WN * 64, MINWG) gemm_kernel(GemmArgs p) {
     mt = u % p.m_tiles;
     n_tile = u / p.m_tiles;
   }
-  int64_t m0, m_end;
-  int e = 0;
+  L.n0 = (int64_t)n_tile * BN;
+  L.e = 0;
   if constexpr (GROUPED) {
     // (expert, tile within the expert) from the device-resident offsets;
     // tiles past the last expert have no work.  The lanes of each wave take
@@ -632,8 +652,8 @@ __global__ void __launch_bounds__(WN * 64, MINWG) gemm_kernel(GemmArgs p) {
     // sum, and the first expert whose running count passes the tile wins.
     const int lane = threadIdx.x & 63;
     uint32_t cum = 0;
-    m0 = -1;
-    m_end = 0;
+    L.m0 = -1;
+    L.m_end = 0;
     for (int g0 = 0; g0 < p.E; g0 += 64) {
       const int xe = g0 + lane;
       const int32_t s0 = xe < p.E ? p.off[xe] : 0;
@@ -642,98 +662,101 @@ __global__ void __launch_bounds__(WN * 64, MINWG) gemm_kernel(GemmArgs p) {
       uint32_t incl = nt;
 #pragma unroll
       for (int d = 1; d < 64; d <<= 1) {
-        const uint32_t v = __shfl_up(incl, d, 64);
-        if (lane >= d) incl += v;
+        const uint32_t w = __shfl_up(incl, d, 64);
+        if (lane >= d) incl += w;
       }
       const uint32_t group = (uint32_t)__builtin_amdgcn_readfirstlane(__shfl(incl, 63, 64));
       if (mt < cum + group) {                      // wave-uniform
         const uint64_t hit = __ballot(cum + incl > mt);
         const int l = __builtin_amdgcn_readfirstlane(__ffsll((unsigned long long)hit) - 1);
-        e = g0 + l;
+        L.e = g0 + l;
         const uint32_t before = (uint32_t)__builtin_amdgcn_readfirstlane(__shfl(incl - nt, l, 64));
-        m0 = (int64_t)__builtin_amdgcn_readfirstlane(__shfl(s0, l, 64)) + (int64_t)(mt - cum - before) * BM;
-        m_end = (int64_t)__builtin_amdgcn_readfirstlane(__shfl(s1, l, 64));
+        L.m0 = (int64_t)__builtin_amdgcn_readfirstlane(__shfl(s0, l, 64)) + (int64_t)(mt - cum - before) * BM;
+        L.m_end = (int64_t)__builtin_amdgcn_readfirstlane(__shfl(s1, l, 64));
         break;
       }
       cum += group;
     }
-    if (m0 < 0) {
-      if constexpr (EPI == EPI_GLU) {
-        if (threadIdx.x == 0) p.partials[blockIdx.x] = 0.f;
-      }
-      return;
-    }
   } else {
-    m0 = (int64_t)mt * BM;
-    m_end = p.M;
+    L.m0 = (int64_t)mt * BM;
+    L.m_end = p.M;
   }
-  const int64_t n0 = (int64_t)n_tile * BN;
+  return L;
+}
+
+// Staging sources of one tile (from chunk c_begin of its K split), in two
+// parts: the buffer descriptors (wave-uniform; rebuilt wherever a tile's
+// copies are issued, so that no descriptor is carried around the tile loop,
+// which would move it out of the scalar registers the copies need), and each
+// lane's byte offset of every unit it copies.  Rows past the end are clamped
+// (staged, never stored).
+template <int WN, int TM, int TN, bool DUAL, bool GROUPED>
+__device__ __forceinline__ void tile_desc(Ctx<WN, TM, TN, DUAL>& x, const GemmArgs& p, const TileLoc& L,
+                                          int64_t c_begin) {
+  using C = Cfg<WN, TM, TN, DUAL>;
+  constexpr int BM = C::BM;
+  constexpr int BN = C::BN;
+  const int64_t m0 = L.m0, m_end = L.m_end, n0 = L.n0;
   const int64_t K = p.K;
   const int64_t kb = K >> 1, ks = K >> 4;
-  const int64_t nchunks_total = K >> 7;
-  const int64_t c_begin = (int64_t)split * p.chunks_per_split;
-  int64_t nch = nchunks_total - c_begin;
-  if (nch > (int64_t)p.chunks_per_split) nch = p.chunks_per_split;
-  const int64_t wstride_c = GROUPED ? (int64_t)e * p.N * kb : 0;
-  const int64_t wstride_s = GROUPED ? (int64_t)e * p.N * ks : 0;
-
-  // ---- staging sources (rows past the end are clamped; never stored) ----------
-  Ctx<WN, TM, TN, DUAL> x;
+  const int64_t wstride_c = GROUPED ? (int64_t)L.e * p.N * kb : 0;
+  const int64_t wstride_s = GROUPED ? (int64_t)L.e * p.N * ks : 0;
   // uniform: the weights come from their tile-contiguous copies (both of the pair)
   const bool tiled = p.b_tiled != nullptr && (!DUAL || p.u_tiled != nullptr);
-  {
-    const int64_t a_rows = (m_end < m0 + BM ? m_end : m0 + BM) - m0;
-    x.ra = buf_desc(p.a + m0 * K + c_begin * 128, a_rows * K * 2 - c_begin * 256);
-    if (tiled) {
-      // blocks (e, g, c): this tile's first group g0 = n0 / 128, from chunk c_begin on
-      const int64_t G = (p.N + kTileRows - 1) / kTileRows, Cn = K / kTileK;
-      const int64_t first = ((GROUPED ? (int64_t)e * G : 0) + n0 / kTileRows) * Cn + c_begin;
-      const int64_t bytes = ((G - n0 / kTileRows) * Cn - c_begin) * kTileBlock;
-      x.rb = buf_desc(p.b_tiled + first * kTileBlock, bytes);
-      x.rsb = buf_desc(p.b_tiled + first * kTileBlock + 8192, bytes - 8192);
-      if constexpr (DUAL) {
-        x.ru = buf_desc(p.u_tiled + first * kTileBlock, bytes);
-        x.rsu = buf_desc(p.u_tiled + first * kTileBlock + 8192, bytes - 8192);
-      } else {
-        x.ru = x.rb;
-        x.rsu = x.rsb;
-      }
-      x.wstep = x.sstep = (uint32_t)kTileBlock;
-    } else {
-      const int64_t b_rows = (p.N < n0 + BN ? p.N : n0 + BN) - n0;
-      x.rb = buf_desc(p.b_codes + wstride_c + n0 * kb + c_begin * 64, b_rows * kb - c_begin * 64);
-      x.rsb = buf_desc(p.b_scales + wstride_s + n0 * ks + c_begin * 8, b_rows * ks - c_begin * 8);
-      if constexpr (DUAL) {
-        x.ru = buf_desc(p.u_codes + wstride_c + n0 * kb + c_begin * 64, b_rows * kb - c_begin * 64);
-        x.rsu = buf_desc(p.u_scales + wstride_s + n0 * ks + c_begin * 8, b_rows * ks - c_begin * 8);
-      } else {
-        x.ru = x.rb;
-        x.rsu = x.rsb;
-      }
-      x.wstep = 64u;
-      x.sstep = 8u;
-    }
+  const int64_t a_rows = (m_end < m0 + BM ? m_end : m0 + BM) - m0;
+  x.ra = buf_desc(p.a + m0 * K + c_begin * 128, a_rows * K * 2 - c_begin * 256);
+  if constexpr (GROUPED) {
+    if (p.a_gather != nullptr)   // uniform: the slots' rows are staged from the token copy directly
+      x.ra = buf_desc(p.a + c_begin * 128, p.a_gather_rows * K * 2 - c_begin * 256);
   }
+  if (tiled) {
+    // blocks (e, g, c): this tile's first group g0 = n0 / 128, from chunk c_begin on
+    const int64_t G = (p.N + kTileRows - 1) / kTileRows, Cn = K / kTileK;
+    const int64_t first = ((GROUPED ? (int64_t)L.e * G : 0) + n0 / kTileRows) * Cn + c_begin;
+    const int64_t bytes = ((G - n0 / kTileRows) * Cn - c_begin) * kTileBlock;
+    x.rb = buf_desc(p.b_tiled + first * kTileBlock, bytes);
+    x.rsb = buf_desc(p.b_tiled + first * kTileBlock + 8192, bytes - 8192);
+    if constexpr (DUAL) {
+      x.ru = buf_desc(p.u_tiled + first * kTileBlock, bytes);
+      x.rsu = buf_desc(p.u_tiled + first * kTileBlock + 8192, bytes - 8192);
+    } else {
+      x.ru = x.rb;
+      x.rsu = x.rsb;
+    }
+    x.wstep = x.sstep = (uint32_t)kTileBlock;
+  } else {
+    const int64_t b_rows = (p.N < n0 + BN ? p.N : n0 + BN) - n0;
+    x.rb = buf_desc(p.b_codes + wstride_c + n0 * kb + c_begin * 64, b_rows * kb - c_begin * 64);
+    x.rsb = buf_desc(p.b_scales + wstride_s + n0 * ks + c_begin * 8, b_rows * ks - c_begin * 8);
+    if constexpr (DUAL) {
+      x.ru = buf_desc(p.u_codes + wstride_c + n0 * kb + c_begin * 64, b_rows * kb - c_begin * 64);
+      x.rsu = buf_desc(p.u_scales + wstride_s + n0 * ks + c_begin * 8, b_rows * ks - c_begin * 8);
+    } else {
+      x.ru = x.rb;
+      x.rsu = x.rsb;
+    }
+    x.wstep = 64u;
+    x.sstep = 8u;
+  }
+}
+
+template <int WN, int TM, int TN, bool DUAL, bool GROUPED>
+__device__ __forceinline__ void tile_offsets(Ctx<WN, TM, TN, DUAL>& x, const GemmArgs& p, const TileLoc& L) {
+  using C = Cfg<WN, TM, TN, DUAL>;
+  constexpr int BN = C::BN;
+  const int64_t m0 = L.m0, m_end = L.m_end, n0 = L.n0;
+  const int64_t K = p.K;
+  const int64_t kb = K >> 1, ks = K >> 4;
+  const bool tiled = p.b_tiled != nullptr && (!DUAL || p.u_tiled != nullptr);
+  const bool gather = GROUPED && p.a_gather != nullptr;   // uniform
 #pragma unroll
   for (int u = 0; u < C::SA; ++u) {
     const int pu = u * C::NT + threadIdx.x;
     const int row = pu >> 4, slot = pu & 15;
     int64_t m = m0 + row;
     if (m > m_end - 1) m = m_end - 1;
-    x.a_off[u] = (uint32_t)(((m - m0) * K + ((slot ^ (row & 15)) << 3)) * 2);
-  }
-  if constexpr (GROUPED) {
-    if (p.a_gather != nullptr) {   // uniform: stage the slots' rows of the token copy directly
-      x.ra = buf_desc(p.a + c_begin * 128, p.a_gather_rows * K * 2 - c_begin * 256);
-#pragma unroll
-      for (int u = 0; u < C::SA; ++u) {
-        const int pu = u * C::NT + threadIdx.x;
-        const int row = pu >> 4, slot = pu & 15;
-        int64_t m = m0 + row;
-        if (m > m_end - 1) m = m_end - 1;
-        x.a_off[u] = (uint32_t)(((int64_t)p.a_gather[m] * K + ((slot ^ (row & 15)) << 3)) * 2);
-      }
-    }
+    const int64_t src = gather ? (int64_t)p.a_gather[m] : m - m0;
+    x.a_off[u] = (uint32_t)((src * K + ((slot ^ (row & 15)) << 3)) * 2);
   }
   auto wrow = [&](int rho) -> int64_t {          // row of this tile's gate (or up) matrix, clamped
     int64_t n = n0 + ((DUAL && rho >= BN) ? rho - BN : rho);
@@ -761,6 +784,32 @@ __global__ void __launch_bounds__(WN * 64, MINWG) gemm_kernel(GemmArgs p) {
     x.s_off[u] = tiled ? (uint32_t)(tgrp(pu >> 1) + (int64_t)(pu & 255) * 4)
                        : (uint32_t)(wrow(pu >> 1) * ks + ((pu & 1) << 2));
   }
+}
+
+template <int WN, int TM, int TN, bool DUAL, bool GROUPED, int EPI, int NS, int MINWG>
+__global__ void __launch_bounds__(WN * 64, MINWG) gemm_kernel(GemmArgs p) {
+  using C = Cfg<WN, TM, TN, DUAL>;
+  constexpr int BM = C::BM;
+  constexpr int BN = C::BN;
+  static_assert(BN % kTileRows == 0 && C::NB * 4 % 512 == 0, "whole 128-row groups of the tiled weights per tile");
+  __shared__ float red[WN];
+  __shared__ f16x8 lds_a[NS][C::LDS_A];
+  __shared__ u32x4 lds_b[NS][C::LDS_B];
+  __shared__ uint2 lds_s[NS][C::NB];
+  const int lane = threadIdx.x & 63;
+  const int wn = threadIdx.x >> 6;
+  const int r32 = lane & 31, hh = lane >> 5;
+  // the next tile's first copies go out before this tile's epilogue (two
+  // buffers, and an epilogue that does not use them)
+  constexpr bool kAhead = NS == 2 && EPI != EPI_GLUQ;
+  const uint32_t vtotal = p.m_tiles * p.n_tiles * p.splits;
+  const int64_t nchunks_total = p.K >> 7;
+  auto chunks_of = [&](uint32_t split) -> int64_t {   // chunks of a K split
+    const int64_t n = nchunks_total - (int64_t)split * p.chunks_per_split;
+    return n < (int64_t)p.chunks_per_split ? n : (int64_t)p.chunks_per_split;
+  };
+
+  Ctx<WN, TM, TN, DUAL> x;
 #pragma unroll
   for (int i = 0; i < TM; ++i) x.lds_row[i] = (i * 32 + r32) * 16;
   x.lds_swz = r32 & 15;
@@ -773,140 +822,197 @@ __global__ void __launch_bounds__(WN * 64, MINWG) gemm_kernel(GemmArgs p) {
         x.acc[i][j][r] = 0.f;
         if constexpr (DUAL) x.accu[i][j][r] = 0.f;
       }
-
-  // ---- main loop ------------------------------------------------------------------
   const uint32_t wb = (uint32_t)__builtin_amdgcn_readfirstlane(threadIdx.x >> 6) * 64u;
   auto la = [&](int st) { return lds_addr(lds_a[st]) + wb * 16u; };
   auto lb = [&](int st) { return lds_addr(lds_b[st]) + wb * 16u; };
   auto ls = [&](int st) { return lds_addr(lds_s[st]) + wb * 4u; };
-  if constexpr (NS == 2) {
-    // Two buffers, pipelined across chunk boundaries (xstep above).
-    const Lds l0{lds_a[0], lds_b[0], lds_s[0]}, l1{lds_a[1], lds_b[1], lds_s[1]};
-    BPack<TN, DUAL> f0, f1;
-    BExp<TN, DUAL> e0, e1;
-    // both buffers' copies in flight before the first wait (chunk 0 landed:
-    // at most chunk 1's copies still outstanding)
-    constexpr int PER0 = C::SA + C::SB + C::SD;
-    stage_dma(x, la(0), lb(0), ls(0), 0);
-    if (nch > 1) {
-      stage_dma(x, la(1), lb(1), ls(1), 1);
-      asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" : : "n"(PER0) : "memory");
-    } else {
-      asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" : : : "memory");
-    }
-    __builtin_amdgcn_sched_barrier(0);
-    read_b<WN, TM, TN, DUAL>(l0, f0);
-    read_a<0, 0>(x, l0);
-    read_a<1, 1>(x, l0);
-    expand_b<TN, DUAL, 0>(f0, e0);
-    // Chunk pairs in one loop body (no exit between them, so the
-    // accumulators keep their registers across the back edge), then the odd
-    // last chunk.
-    int64_t c = 0;
-    for (; c + 1 < nch; c += 2) {
-      xchunk(x, l0, l1, f0, f1, e0, e1, c + 2 < nch, c + 2, la(0), lb(0), ls(0));
-      xchunk(x, l1, l0, f1, f0, e0, e1, c + 3 < nch, c + 3, la(1), lb(1), ls(1));
-    }
-    if (c < nch) xchunk(x, l0, l1, f0, f1, e0, e1, false, c + 2, la(0), lb(0), ls(0));
-  } else {
-    // NS-buffer ring: the copies of chunks c+1 .. c+NS-2 stay in flight while
-    // chunk c is consumed; the buffer of chunk c-1 is refilled with chunk
-    // c+NS-1 right after the barrier that ends its last reads.
-    static_assert(NS >= 3 && NS <= 4, "ring of 3 or 4 buffers");
-    constexpr int PER = C::SA + C::SB + C::SD;      // copies per wave per chunk
-    static_assert((NS - 2) * PER <= 63, "vmcnt range");
-#pragma unroll
-    for (int st = 0; st < NS - 1; ++st)
-      if (st < nch) stage_dma(x, la(st), lb(st), ls(st), st);
-    int sc = 0;                                      // buffer of chunk c
-    for (int64_t c = 0; c < nch; ++c) {
-      const int64_t later = (nch - 1 - c) < (NS - 2) ? (nch - 1 - c) : (NS - 2);
-      ring_wait<PER, NS - 2>(later);
-      const int sf = sc == 0 ? NS - 1 : sc - 1;      // buffer of chunk c-1
-      if (c + NS - 1 < nch) stage_dma(x, la(sf), lb(sf), ls(sf), c + NS - 1);
-      run_chunk(x, Lds{lds_a[sc], lds_b[sc], lds_s[sc]});
-      sc = sc == NS - 1 ? 0 : sc + 1;
-    }
-  }
+  constexpr int PER0 = C::SA + C::SB + C::SD;      // copies per wave per chunk
 
-  // ---- epilogue ---------------------------------------------------------------------
-  if constexpr (EPI == EPI_GLUQ) {
-    // SiLU(gate) * up of the whole tile goes to LDS (the stage buffers are
-    // free once every wave is past the main loop), then each thread quantises
-    // whole 16-column blocks of it with the given global scale.  Columns are
-    // XOR-swizzled in units of four floats by the row, so the two row halves
-    // of an MFMA fragment store to different banks.
-    static_assert(DUAL, "quantising GLU epilogue: gate/up pair");
-    static_assert(BM * C::BN * 4 <= (int)sizeof(lds_b), "GLU tile must fit the stage buffers");
-    float* tile = reinterpret_cast<float*>(&lds_b[0][0]);
-    const float alpha = p.a_gs[0] * p.b_gs[GROUPED ? e : 0];
-    const float alpha_u = p.a_gs[0] * p.u_gs[GROUPED ? e : 0];
-    __syncthreads();
+  TileLoc cur = locate_tile<BM, BN, GROUPED>(p, blockIdx.x, vtotal);
+  bool staged = false;                             // cur's first copies already issued
+  for (uint32_t v = blockIdx.x; v < vtotal; v += gridDim.x) {
+    const uint32_t vn = v + gridDim.x;
+    if (cur.m0 < 0) {                              // (uniform) a tile past the last expert
+      if constexpr (EPI == EPI_GLU) {
+        if (threadIdx.x == 0) p.partials[v] = 0.f;
+      }
+      if (vn < vtotal) cur = locate_tile<BM, BN, GROUPED>(p, vn, vtotal);
+      continue;
+    }
+    const int64_t m0 = cur.m0, m_end = cur.m_end, n0 = cur.n0;
+    const uint32_t split = cur.split;
+    const int e = cur.e;
+    const int64_t nch = chunks_of(split);
+    tile_desc<WN, TM, TN, DUAL, GROUPED>(x, p, cur, (int64_t)split * p.chunks_per_split);
+    if (!staged) {
+      // every wave is past its last reads of the stage buffers (earlier tile)
+      asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" : : : "memory");
+      __builtin_amdgcn_sched_barrier(0);
+      tile_offsets<WN, TM, TN, DUAL, GROUPED>(x, p, cur);
+    }
+
+    // ---- main loop ----------------------------------------------------------------
+    if constexpr (NS == 2) {
+      // Two buffers, pipelined across chunk boundaries (xstep above).
+      const Lds l0{lds_a[0], lds_b[0], lds_s[0]}, l1{lds_a[1], lds_b[1], lds_s[1]};
+      BPack<TN, DUAL> f0, f1;
+      BExp<TN, DUAL> e0, e1;
+      // both buffers' copies in flight before the first wait (chunk 0 landed:
+      // at most chunk 1's copies still outstanding); copies issued ahead of the
+      // previous tile's epilogue wait for everything that epilogue stored too
+      if (!staged) {
+        stage_dma(x, la(0), lb(0), ls(0), 0);
+        if (nch > 1) {
+          stage_dma(x, la(1), lb(1), ls(1), 1);
+          asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" : : "n"(PER0) : "memory");
+        } else {
+          asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" : : : "memory");
+        }
+      } else {
+        asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" : : : "memory");
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      read_b<WN, TM, TN, DUAL>(l0, f0);
+      read_a<0, 0>(x, l0);
+      read_a<1, 1>(x, l0);
+      expand_b<TN, DUAL, 0>(f0, e0);
+      // Chunk pairs in one loop body (no exit between them, so the
+      // accumulators keep their registers across the back edge), then the odd
+      // last chunk.
+      int64_t c = 0;
+      for (; c + 1 < nch; c += 2) {
+        xchunk(x, l0, l1, f0, f1, e0, e1, c + 2 < nch, c + 2, la(0), lb(0), ls(0));
+        xchunk(x, l1, l0, f1, f0, e0, e1, c + 3 < nch, c + 3, la(1), lb(1), ls(1));
+      }
+      if (c < nch) xchunk(x, l0, l1, f0, f1, e0, e1, false, c + 2, la(0), lb(0), ls(0));
+    } else {
+      // NS-buffer ring: the copies of chunks c+1 .. c+NS-2 stay in flight while
+      // chunk c is consumed; the buffer of chunk c-1 is refilled with chunk
+      // c+NS-1 right after the barrier that ends its last reads.
+      static_assert(NS >= 3 && NS <= 4, "ring of 3 or 4 buffers");
+      constexpr int PER = PER0;
+      static_assert((NS - 2) * PER <= 63, "vmcnt range");
 #pragma unroll
-    for (int i = 0; i < TM; ++i)
-#pragma unroll
-      for (int j = 0; j < TN; ++j) {
-        const int col = (wn * TN + j) * 32 + r32;
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int row = i * 32 + 8 * (r >> 2) + 4 * hh + (r & 3);
-          tile[row * C::BN + (col ^ ((row & 7) << 2))] = silu_mul(x.acc[i][j][r] * alpha, x.accu[i][j][r] * alpha_u);
+      for (int st = 0; st < NS - 1; ++st)
+        if (st < nch) stage_dma(x, la(st), lb(st), ls(st), st);
+      int sc = 0;                                      // buffer of chunk c
+      for (int64_t c = 0; c < nch; ++c) {
+        const int64_t later = (nch - 1 - c) < (NS - 2) ? (nch - 1 - c) : (NS - 2);
+        ring_wait<PER, NS - 2>(later);
+        const int sf = sc == 0 ? NS - 1 : sc - 1;      // buffer of chunk c-1
+        if (c + NS - 1 < nch) stage_dma(x, la(sf), lb(sf), ls(sf), c + NS - 1);
+        run_chunk(x, Lds{lds_a[sc], lds_b[sc], lds_s[sc]});
+        sc = sc == NS - 1 ? 0 : sc + 1;
+      }
+    }
+
+    // ---- the next tile's first copies -------------------------------------------------
+    staged = false;
+    if (vn < vtotal) {
+      cur = locate_tile<BM, BN, GROUPED>(p, vn, vtotal);
+      if constexpr (kAhead) {
+        if (cur.m0 >= 0) {
+          // every wave is past its reads of both buffers (the last chunk's
+          // reads of the other buffer fetch data that is never used)
+          asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" : : : "memory");
+          __builtin_amdgcn_sched_barrier(0);
+          tile_desc<WN, TM, TN, DUAL, GROUPED>(x, p, cur, (int64_t)cur.split * p.chunks_per_split);
+          tile_offsets<WN, TM, TN, DUAL, GROUPED>(x, p, cur);
+          stage_dma(x, la(0), lb(0), ls(0), 0);
+          if (chunks_of(cur.split) > 1) stage_dma(x, la(1), lb(1), ls(1), 1);
+          staged = true;
         }
       }
-    __syncthreads();
-    const float gs = p.q_gs[0];
-    constexpr int NBC = C::BN / 16;
-    for (int q = threadIdx.x; q < BM * NBC; q += C::NT) {
-      const int row = q / NBC, cb = q - row * NBC;
-      const int64_t grow = m0 + row, gcol = n0 + cb * 16;
-      if (grow >= m_end || gcol >= p.N) continue;
-      float v[16];
-#pragma unroll
-      for (int g4 = 0; g4 < 4; ++g4) {
-        const float4 t4 = *reinterpret_cast<const float4*>(tile + row * C::BN + ((cb * 16 + 4 * g4) ^ ((row & 7) << 2)));
-        v[4 * g4] = t4.x; v[4 * g4 + 1] = t4.y; v[4 * g4 + 2] = t4.z; v[4 * g4 + 3] = t4.w;
-      }
-      uint32_t w0, w1;
-      const uint32_t sc = quantize_block16(v, gs, w0, w1);
-      *reinterpret_cast<uint2*>(p.q_codes + grow * (p.N / 2) + gcol / 2) = make_uint2(w0, w1);
-      p.q_scales[grow * (p.N / 16) + gcol / 16] = (uint8_t)sc;
     }
-    return;
-  }
-  const float alpha = p.a_gs[0] * p.b_gs[GROUPED ? e : 0];
-  float alpha_u = 0.f;
-  if constexpr (DUAL) alpha_u = p.a_gs[0] * p.u_gs[GROUPED ? e : 0];
-  float hmax = 0.f;
+
+    // ---- epilogue ---------------------------------------------------------------------
+    if constexpr (EPI == EPI_GLUQ) {
+      // SiLU(gate) * up of the whole tile goes to LDS (the stage buffers are
+      // free once every wave is past the main loop), then each thread quantises
+      // whole 16-column blocks of it with the given global scale.  Columns are
+      // XOR-swizzled in units of four floats by the row, so the two row halves
+      // of an MFMA fragment store to different banks.
+      static_assert(DUAL, "quantising GLU epilogue: gate/up pair");
+      static_assert(BM * C::BN * 4 <= (int)sizeof(lds_b), "GLU tile must fit the stage buffers");
+      float* tile = reinterpret_cast<float*>(&lds_b[0][0]);
+      const float alpha = p.a_gs[0] * p.b_gs[GROUPED ? e : 0];
+      const float alpha_u = p.a_gs[0] * p.u_gs[GROUPED ? e : 0];
+      __syncthreads();
 #pragma unroll
-  for (int i = 0; i < TM; ++i)
+      for (int i = 0; i < TM; ++i)
 #pragma unroll
-    for (int j = 0; j < TN; ++j) {
-      const int64_t col = n0 + (wn * TN + j) * 32 + r32;
+        for (int j = 0; j < TN; ++j) {
+          const int col = (wn * TN + j) * 32 + r32;
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int64_t row = m0 + i * 32 + 8 * (r >> 2) + 4 * hh + (r & 3);
-        if (row < m_end && col < p.N) {
-          if constexpr (EPI == EPI_GLU) {
-            const float hv = silu_mul(x.acc[i][j][r] * alpha, x.accu[DUAL ? i : 0][DUAL ? j : 0][r] * alpha_u);
-            p.h[row * p.N + col] = hv;
-            hmax = fmaxf(hmax, fabsf(hv));
-          } else {
-            if (p.splits > 1 || p.force_split) {
-              p.split_out[((int64_t)split * p.M + row) * p.N + col] = x.acc[i][j][r];
-            } else {
-              const float v = x.acc[i][j][r] * alpha;
-              if (p.c_bf16)
-                reinterpret_cast<uint16_t*>(p.c)[row * p.ldc + col] = (uint16_t)f32_to_bf16_bits(v);
-              else
-                reinterpret_cast<float*>(p.c)[row * p.ldc + col] = v;
+          for (int r = 0; r < 16; ++r) {
+            const int row = i * 32 + 8 * (r >> 2) + 4 * hh + (r & 3);
+            tile[row * C::BN + (col ^ ((row & 7) << 2))] = silu_mul(x.acc[i][j][r] * alpha, x.accu[i][j][r] * alpha_u);
+          }
+        }
+      __syncthreads();
+      const float gs = p.q_gs[0];
+      constexpr int NBC = C::BN / 16;
+      for (int q = threadIdx.x; q < BM * NBC; q += C::NT) {
+        const int row = q / NBC, cb = q - row * NBC;
+        const int64_t grow = m0 + row, gcol = n0 + cb * 16;
+        if (grow >= m_end || gcol >= p.N) continue;
+        float vv[16];
+#pragma unroll
+        for (int g4 = 0; g4 < 4; ++g4) {
+          const float4 t4 = *reinterpret_cast<const float4*>(tile + row * C::BN + ((cb * 16 + 4 * g4) ^ ((row & 7) << 2)));
+          vv[4 * g4] = t4.x; vv[4 * g4 + 1] = t4.y; vv[4 * g4 + 2] = t4.z; vv[4 * g4 + 3] = t4.w;
+        }
+        uint32_t w0, w1;
+        const uint32_t sc = quantize_block16(vv, gs, w0, w1);
+        *reinterpret_cast<uint2*>(p.q_codes + grow * (p.N / 2) + gcol / 2) = make_uint2(w0, w1);
+        p.q_scales[grow * (p.N / 16) + gcol / 16] = (uint8_t)sc;
+      }
+    } else {
+      const float alpha = p.a_gs[0] * p.b_gs[GROUPED ? e : 0];
+      float alpha_u = 0.f;
+      if constexpr (DUAL) alpha_u = p.a_gs[0] * p.u_gs[GROUPED ? e : 0];
+      float hmax = 0.f;
+#pragma unroll
+      for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int j = 0; j < TN; ++j) {
+          const int64_t col = n0 + (wn * TN + j) * 32 + r32;
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int64_t row = m0 + i * 32 + 8 * (r >> 2) + 4 * hh + (r & 3);
+            if (row < m_end && col < p.N) {
+              if constexpr (EPI == EPI_GLU) {
+                const float hv = silu_mul(x.acc[i][j][r] * alpha, x.accu[DUAL ? i : 0][DUAL ? j : 0][r] * alpha_u);
+                p.h[row * p.N + col] = hv;
+                hmax = fmaxf(hmax, fabsf(hv));
+              } else {
+                if (p.splits > 1 || p.force_split) {
+                  p.split_out[((int64_t)split * p.M + row) * p.N + col] = x.acc[i][j][r];
+                } else {
+                  const float vo = x.acc[i][j][r] * alpha;
+                  if (p.c_bf16)
+                    reinterpret_cast<uint16_t*>(p.c)[row * p.ldc + col] = (uint16_t)f32_to_bf16_bits(vo);
+                  else
+                    reinterpret_cast<float*>(p.c)[row * p.ldc + col] = vo;
+                }
+              }
             }
           }
         }
+      if constexpr (EPI == EPI_GLU) {
+        hmax = block_max(hmax, red);
+        if (threadIdx.x == 0) p.partials[v] = hmax;
       }
     }
-  if constexpr (EPI == EPI_GLU) {
-    hmax = block_max(hmax, red);
-    if (threadIdx.x == 0) p.partials[blockIdx.x] = hmax;
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+      for (int j = 0; j < TN; ++j)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          x.acc[i][j][r] = 0.f;
+          if constexpr (DUAL) x.accu[i][j][r] = 0.f;
+        }
   }
 }
 
@@ -2118,9 +2224,36 @@ static void launch_clear(uint32_t* p, uint32_t n, int kc, hipStream_t st) {
   launch_end(slot, st);
 }
 
+// Compute units of the current device, read once per device.
+static uint32_t cu_count() {
+  static std::atomic<int> cache[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) {
+    (void)hipGetLastError();
+    return 256;
+  }
+  int n = cache[dev].load(std::memory_order_relaxed);
+  if (n <= 0) {
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) {
+      (void)hipGetLastError();
+      n = 256;
+    }
+    cache[dev].store(n, std::memory_order_relaxed);
+  }
+  return (uint32_t)n;
+}
+
 template <int WN, int TM, int TN, bool DUAL, bool GROUPED, int EPI>
 static void launch_cfg(const GemmArgs& g, hipStream_t st) {
-  const uint32_t grid = g.m_tiles * g.n_tiles * g.splits;
+  const uint32_t tiles = g.m_tiles * g.n_tiles * g.splits;
+  constexpr int MW0 = EPI != EPI_STORE ? NVFP4_GLU_MINWG : NVFP4_STORE_MINWG;
+  uint32_t grid = tiles;
+  if (NVFP4_PERSIST && (!GROUPED || NVFP4_PERSIST_GROUPED)) {
+    // the work-groups the chip holds at once, a multiple of the 8 XCDs
+    uint32_t resident = cu_count() * (uint32_t)MW0;
+    if (resident > 8u) resident -= resident % 8u;
+    if (grid > resident) grid = resident;
+  }
   const int slot = launch_begin(EPI != EPI_STORE ? KC_GEMM_GLU : KC_GEMM_STORE, st);
   constexpr int NS = EPI != EPI_STORE ? NVFP4_GLU_STAGES : NVFP4_STORE_STAGES;
   constexpr int MW = EPI != EPI_STORE ? NVFP4_GLU_MINWG : NVFP4_STORE_MINWG;
