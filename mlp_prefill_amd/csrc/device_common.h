@@ -146,16 +146,138 @@ __device__ __forceinline__ uint32_t e2m1_code(float x, const float T[7]) {
   return ((__float_as_uint(x) >> 31) << 3) | idx;
 }
 
+// ---- the same decisions in float32 ------------------------------------------
+// For a global scale in [2^-90, 2^100] every decision threshold above is a
+// product P * gs of a float32 P with at most 7 significant bits (6 * mid for
+// the block scale, mid * dec(S) for the element codes) and gs: at most 31
+// significant bits, with no underflow or overflow, so t = RN32(P * gs) and its
+// rounding error fma(P, gs, -t) (exact: the error of a product is a float32
+// when nothing underflows) decide every comparison exactly.
+constexpr float kGsFastMin = 0x1p-90f;
+constexpr float kGsFastMax = 0x1p100f;
+
+__host__ __device__ __forceinline__ bool gs_fast(float gs) { return gs >= kGsFastMin && gs <= kGsFastMax; }
+
+// Value of an E4M3 code 0..0x7E as a float32 (exact).
+__host__ __device__ __forceinline__ float e4m3_valuef(uint32_t c) {
+  if (c < 8) return (float)c * 0x1p-9f;
+  uint32_t bits = (((c >> 3) + 120u) << 23) | ((c & 7u) << 20);   // (1 + m/8) 2^(E-7)
+  float f;
+  __builtin_memcpy(&f, &bits, 4);
+  return f;
+}
+
+// Sign of a - P * g in exact arithmetic (a >= 0; P * g in the range above).
+__host__ __device__ __forceinline__ int cmp_exact(float a, float P, float g) {
+  const float t = P * g;
+  if (a != t) return a > t ? 1 : -1;
+  const float err = fmaf(P, g, -t);            // P g - t
+  return err < 0.f ? 1 : (err > 0.f ? -1 : 0);
+}
+
+// E4M3 block scale code, as e4m3_block_scale, with inv6 = 1 / (6 gs) (any
+// float32 within a relative 2^-21 of it): the code nearest to amax_b * inv6
+// is at most one code from the exact answer (E4M3 codes lie at least a
+// relative 2^-4 apart), and the two midpoints around it settle which.
+__host__ __device__ __forceinline__ uint32_t e4m3_block_scale_f32(float amax_b, float gs, float inv6) {
+  const float q = amax_b * inv6;
+  uint32_t c;
+  if (!(q < 448.f)) {
+    c = 0x7E;
+  } else if (q < 0x1p-6f) {
+    c = (uint32_t)rintf(q * 512.f);              // subnormal codes 0..8
+  } else {
+    const int E = ilogbf(q);                     // q in [2^E, 2^(E+1)), E in -6..8
+    const int m = (int)rintf(ldexpf(q, 3 - E));  // 8..16; 16 carries into the next binade
+    c = (uint32_t)((E + 7) * 8 + m - 8);
+  }
+  if (c < 0x7E) {                                // between c and c+1: the even code on a tie
+    const int s = cmp_exact(amax_b, 6.f * (0.5f * (e4m3_valuef(c) + e4m3_valuef(c + 1))), gs);
+    if (s > 0 || (s == 0 && (c & 1u))) return c + 1;
+  }
+  if (c > 0) {                                   // between c-1 and c
+    const int s = cmp_exact(amax_b, 6.f * (0.5f * (e4m3_valuef(c - 1) + e4m3_valuef(c))), gs);
+    if (s < 0 || (s == 0 && (c & 1u))) return c - 1;
+  }
+  return c;
+}
+
+// E2M1 thresholds as e2m1_thresholds for the block scale value d = dec(S):
+// T[i] is t = RN32(mid_i * d * gs), moved one float32 up when t is at or
+// below the exact threshold (even i) or below it (odd i).
+__host__ __device__ __forceinline__ void e2m1_thresholds_f32(float d, float gs, float T[7]) {
+  const float mids[7] = {0.25f, 0.75f, 1.25f, 1.75f, 2.5f, 3.5f, 5.0f};
+#pragma unroll
+  for (int i = 0; i < 7; ++i) {
+    const float P = mids[i] * d;                 // exact: at most 7 significant bits
+    const float t = P * gs;
+    const float err = fmaf(P, gs, -t);           // exact threshold minus t
+    const bool bump = (i & 1) ? (err > 0.f) : (err >= 0.f);
+    uint32_t u;
+    __builtin_memcpy(&u, &t, 4);
+    u += bump ? 1u : 0u;
+    float f;
+    __builtin_memcpy(&f, &u, 4);
+    T[i] = d == 0.f ? __builtin_huge_valf() : f;
+  }
+}
+
+// Byte J of the two code words from below and from above: elements 2J, 2J+1
+// (low nibble first) and 8 + 2J, 9 + 2J.
+template <int J>
+__device__ __forceinline__ void cvt8_fp4(const float v[16], float lo, float hi, uint32_t& l0, uint32_t& h0,
+                                         uint32_t& l1, uint32_t& h1) {
+  l0 = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(l0, v[2 * J] * lo, v[2 * J + 1] * lo, 1.0f, J);
+  h0 = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(h0, v[2 * J] * hi, v[2 * J + 1] * hi, 1.0f, J);
+  l1 = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(l1, v[8 + 2 * J] * lo, v[9 + 2 * J] * lo, 1.0f, J);
+  h1 = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(h1, v[8 + 2 * J] * hi, v[9 + 2 * J] * hi, 1.0f, J);
+}
+
+// Element codes of a block with block scale value d > 0 from the hardware
+// E2M1 conversion (round to nearest, ties to even, saturating at magnitude 6,
+// sign kept) of x * inv from below and from above: inv is within a relative
+// 2^-22 of 1 / (d gs) (reciprocal of the rounded product), so x * lo and
+// x * hi (lo, hi = inv (1 -/+ 2^-19)) bracket the exact quotient x / (d gs)
+// strictly.  Rounding is monotone, so where both give the same code that code
+// is the exact one; an exact tie always lies strictly inside the bracket and
+// gives two codes.  Returns whether all sixteen codes agree (w0, w1: the
+// codes from below).
+__device__ __forceinline__ bool e2m1_codes_bracketed(const float v[16], float d, float gs, uint32_t& w0,
+                                                     uint32_t& w1) {
+  const float inv = __builtin_amdgcn_rcpf(d * gs);
+  const float lo = inv * (1.0f - 0x1p-19f), hi = inv * (1.0f + 0x1p-19f);
+  uint32_t l0 = 0, l1 = 0, h0 = 0, h1 = 0;
+  cvt8_fp4<0>(v, lo, hi, l0, h0, l1, h1);
+  cvt8_fp4<1>(v, lo, hi, l0, h0, l1, h1);
+  cvt8_fp4<2>(v, lo, hi, l0, h0, l1, h1);
+  cvt8_fp4<3>(v, lo, hi, l0, h0, l1, h1);
+  w0 = l0;
+  w1 = l1;
+  return l0 == h0 && l1 == h1;
+}
+
 // One 16-element block with global scale gs -> its E4M3 scale code (the
 // return value) and its sixteen E2M1 codes packed low nibble first (w0:
-// elements 0..7, w1: elements 8..15).  Both roundings are decided exactly.
+// elements 0..7, w1: elements 8..15).  Both roundings are decided exactly:
+// in float32 for a global scale in [2^-90, 2^100] (every one the amax of a
+// float32 tensor up to 2^111 gives), the element codes by the bracketed
+// hardware conversion where it is conclusive, else by the thresholds; in
+// float64 for other global scales.
 __device__ __forceinline__ uint32_t quantize_block16(const float v[16], float gs, uint32_t& w0, uint32_t& w1) {
   float amax_b = 0.f;
 #pragma unroll
   for (int i = 0; i < 16; ++i) amax_b = fmaxf(amax_b, fabsf(v[i]));
-  const uint32_t s = e4m3_block_scale(amax_b, gs);
+  uint32_t s;
   float thr[7];
-  e2m1_thresholds(e4m3_value(s) * (double)gs, thr);
+  if (gs_fast(gs)) {                             // uniform: one global scale per call
+    s = e4m3_block_scale_f32(amax_b, gs, 1.0f / (6.0f * gs));
+    const float d = e4m3_valuef(s);
+    if (d > 0.f && e2m1_codes_bracketed(v, d, gs, w0, w1)) return s;
+    e2m1_thresholds_f32(d, gs, thr);
+  } else {
+    s = e4m3_block_scale(amax_b, gs);
+    e2m1_thresholds(e4m3_value(s) * (double)gs, thr);
+  }
   w0 = 0;
   w1 = 0;
 #pragma unroll
