@@ -53,6 +53,13 @@ __device__ __forceinline__ float wave_sum(float v) {
   return v;
 }
 
+// Wave sum of unsigned integers (exact in any order).
+__device__ __forceinline__ uint32_t wave_sum_u32(uint32_t v) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, kWave);
+  return v;
+}
+
 // Block-wide max; `lds` holds at least blockDim.x / 64 floats.  All threads
 // get the result.
 __device__ __forceinline__ float block_max(float v, float* lds) {

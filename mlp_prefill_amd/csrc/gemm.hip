@@ -622,38 +622,56 @@ struct TileLoc {
 // K range and share both activation rows and weight columns in its L2 (for
 // expert groups the gathered activations of all experts do not fit the
 // MALL); kGm = 0: m fastest, then n.  Virtual tile v is dealt to the XCD that
-// runs work-group v % 8 (xcd_remap).
+// runs work-group v % 8 (xcd_remap).  Expert groups: the launch covers a
+// static bound on the m tiles, but only the experts' own m tiles (their row
+// counts rounded up to BM, read from the device-resident offsets) enter the
+// order, so that every XCD gets an equal share of the tiles that have work;
+// virtual tiles past them have none (m0 < 0).
 template <int BM, int BN, bool GROUPED>
 __device__ __forceinline__ TileLoc locate_tile(const GemmArgs& p, uint32_t v, uint32_t vtotal) {
   TileLoc L;
+  L.e = 0;
+  L.m0 = -1;
+  L.m_end = 0;
+  L.split = 0;
+  L.n0 = 0;
+  uint32_t m_tiles = p.m_tiles;
+  const int lane = threadIdx.x & 63;
+  if constexpr (GROUPED) {
+    // the experts' m tiles: the lanes of each wave take 64 experts at a time
+    uint32_t real = 0;
+    for (int g0 = 0; g0 < p.E; g0 += 64) {
+      const int xe = g0 + lane;
+      const int32_t s0 = xe < p.E ? p.off[xe] : 0;
+      const int32_t s1 = xe < p.E ? p.off[xe + 1] : 0;
+      real += (uint32_t)__builtin_amdgcn_readfirstlane((int)wave_sum_u32((uint32_t)((s1 - s0 + BM - 1) / BM)));
+    }
+    m_tiles = real < p.m_tiles ? real : p.m_tiles;
+    vtotal = m_tiles * p.n_tiles * p.splits;
+    if (v >= vtotal) return L;
+  }
   const uint32_t t = xcd_remap(v, vtotal);
   uint32_t mt, n_tile;
   constexpr uint32_t kGm = GROUPED ? kGroupGm : (uint32_t)NVFP4_DENSE_GROUP_M;
-  const uint32_t per_split = p.m_tiles * p.n_tiles;
+  const uint32_t per_split = m_tiles * p.n_tiles;
   L.split = t / per_split;
   const uint32_t u = t - L.split * per_split;
   if (kGm > 0) {
     const uint32_t span = kGm * p.n_tiles;
     const uint32_t sup = u / span, r = u - sup * span;
-    const uint32_t gm = (sup + 1) * kGm <= p.m_tiles ? kGm : p.m_tiles - sup * kGm;
+    const uint32_t gm = (sup + 1) * kGm <= m_tiles ? kGm : m_tiles - sup * kGm;
     mt = sup * kGm + r % gm;
     n_tile = r / gm;
   } else {
-    mt = u % p.m_tiles;
-    n_tile = u / p.m_tiles;
+    mt = u % m_tiles;
+    n_tile = u / m_tiles;
   }
   L.n0 = (int64_t)n_tile * BN;
-  L.e = 0;
   if constexpr (GROUPED) {
-    // (expert, tile within the expert) from the device-resident offsets;
-    // tiles past the last expert have no work.  The lanes of each wave take
-    // 64 experts at a time (one pair of loads each instead of a chain of
-    // dependent loads), add up the experts' tile counts with a wave prefix
-    // sum, and the first expert whose running count passes the tile wins.
-    const int lane = threadIdx.x & 63;
+    // (expert, tile within the expert): the lanes add up the experts' tile
+    // counts with a wave prefix sum, and the first expert whose running count
+    // passes the tile wins
     uint32_t cum = 0;
-    L.m0 = -1;
-    L.m_end = 0;
     for (int g0 = 0; g0 < p.E; g0 += 64) {
       const int xe = g0 + lane;
       const int32_t s0 = xe < p.E ? p.off[xe] : 0;
