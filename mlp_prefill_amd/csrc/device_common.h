@@ -317,10 +317,10 @@ __device__ __forceinline__ f16x8 expand8(uint32_t codes, uint32_t s) {
   return r;
 }
 
-// float32 -> bf16 bits, round to nearest even (finite inputs).
+// float32 -> bf16 bits, round to nearest even (finite inputs): the hardware
+// conversion (v_cvt_pk_bf16_f32, round to nearest even).
 __device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
-  const uint32_t u = __float_as_uint(f);
-  return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+  return __builtin_bit_cast(uint16_t, (__bf16)f);
 }
 
 // SiLU(g) * u in float32, SiLU(g) = g / (1 + e^-g), with the hardware

@@ -45,6 +45,7 @@
 #include "device_common.h"
 #include "internal.h"
 #include <atomic>
+#include <type_traits>
 
 namespace nvfp4 {
 
@@ -986,37 +987,70 @@ __global__ void __launch_bounds__(WN * 64, MINWG) gemm_kernel(GemmArgs p) {
         p.q_scales[grow * (p.N / 16) + gcol / 16] = (uint8_t)sc;
       }
     } else {
+      // Register epilogue.  Output (row, col) of this lane: row = urow + 4 hh,
+      // col = ucol + r32 with urow, ucol the same for the whole wave, so each
+      // store is a wave-uniform address (scalar arithmetic) plus this lane's
+      // fixed offset; tiles inside the matrix skip the bounds checks.
       const float alpha = p.a_gs[0] * p.b_gs[GROUPED ? e : 0];
       float alpha_u = 0.f;
       if constexpr (DUAL) alpha_u = p.a_gs[0] * p.u_gs[GROUPED ? e : 0];
       float hmax = 0.f;
+      const int wnu = __builtin_amdgcn_readfirstlane(wn);
+      const bool full = m0 + BM <= m_end && n0 + BN <= p.N;   // uniform
+      // KIND 0: SiLU(gate) * up, float32 H; 1: split-K partial sums; 2: float32
+      // output * alpha; 3: bf16 output * alpha
+      auto emit = [&](auto kind, auto check) {
+        constexpr int KIND = decltype(kind)::value;
+        constexpr bool CHECK = decltype(check)::value;
+        constexpr int ESZ = KIND == 3 ? 2 : 4;
+        char* out;
+        int64_t ld;
+        if constexpr (KIND == 0) {
+          out = reinterpret_cast<char*>(p.h);
+          ld = p.N;
+        } else if constexpr (KIND == 1) {
+          out = reinterpret_cast<char*>(p.split_out + (int64_t)split * p.M * p.N);
+          ld = p.N;
+        } else {
+          out = reinterpret_cast<char*>(p.c);
+          ld = p.ldc;
+        }
+        const uint32_t lane_off = (uint32_t)(((int64_t)(4 * hh) * ld + r32) * ESZ);
 #pragma unroll
-      for (int i = 0; i < TM; ++i)
+        for (int i = 0; i < TM; ++i)
 #pragma unroll
-        for (int j = 0; j < TN; ++j) {
-          const int64_t col = n0 + (wn * TN + j) * 32 + r32;
+          for (int j = 0; j < TN; ++j) {
+            const int64_t ucol = n0 + (int64_t)(wnu * TN + j) * 32;
 #pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int64_t row = m0 + i * 32 + 8 * (r >> 2) + 4 * hh + (r & 3);
-            if (row < m_end && col < p.N) {
-              if constexpr (EPI == EPI_GLU) {
-                const float hv = silu_mul(x.acc[i][j][r] * alpha, x.accu[DUAL ? i : 0][DUAL ? j : 0][r] * alpha_u);
-                p.h[row * p.N + col] = hv;
-                hmax = fmaxf(hmax, fabsf(hv));
+            for (int r = 0; r < 16; ++r) {
+              const int64_t urow = m0 + i * 32 + 8 * (r >> 2) + (r & 3);
+              float val;
+              if constexpr (KIND == 0) {
+                val = silu_mul(x.acc[i][j][r] * alpha, x.accu[DUAL ? i : 0][DUAL ? j : 0][r] * alpha_u);
+                if (!CHECK || (urow + 4 * hh < m_end && ucol + r32 < p.N)) hmax = fmaxf(hmax, fabsf(val));
+              } else if constexpr (KIND == 1) {
+                val = x.acc[i][j][r];
               } else {
-                if (p.splits > 1 || p.force_split) {
-                  p.split_out[((int64_t)split * p.M + row) * p.N + col] = x.acc[i][j][r];
-                } else {
-                  const float vo = x.acc[i][j][r] * alpha;
-                  if (p.c_bf16)
-                    reinterpret_cast<uint16_t*>(p.c)[row * p.ldc + col] = (uint16_t)f32_to_bf16_bits(vo);
-                  else
-                    reinterpret_cast<float*>(p.c)[row * p.ldc + col] = vo;
-                }
+                val = x.acc[i][j][r] * alpha;
+              }
+              if (!CHECK || (urow + 4 * hh < m_end && ucol + r32 < p.N)) {
+                char* a = out + (urow * ld + ucol) * ESZ + lane_off;
+                if constexpr (KIND == 3)
+                  *reinterpret_cast<uint16_t*>(a) = (uint16_t)f32_to_bf16_bits(val);
+                else
+                  *reinterpret_cast<float*>(a) = val;
               }
             }
           }
-        }
+      };
+      auto emit_kind = [&](auto kind) {
+        if (full) emit(kind, std::false_type{});
+        else emit(kind, std::true_type{});
+      };
+      if constexpr (EPI == EPI_GLU) emit_kind(std::integral_constant<int, 0>{});
+      else if (p.splits > 1 || p.force_split) emit_kind(std::integral_constant<int, 1>{});
+      else if (p.c_bf16) emit_kind(std::integral_constant<int, 3>{});
+      else emit_kind(std::integral_constant<int, 2>{});
       if constexpr (EPI == EPI_GLU) {
         hmax = block_max(hmax, red);
         if (threadIdx.x == 0) p.partials[v] = hmax;
