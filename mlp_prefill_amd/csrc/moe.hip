@@ -115,7 +115,8 @@ __global__ void __launch_bounds__(kRouteWg) route_topk_kernel(const float* __res
 
 // The same results with more parallelism, for E <= kWaveTopkMaxE: one
 // work-group (8 waves) per 64-token routing block; each token gets 8 lanes
-// of a wave, each lane holding up to 16 of its logits (expert 8i + lane%8).
+// of a wave, each lane holding PER of its logits (expert 8i + lane%8; PER = 8
+// for up to 64 experts, 16 for up to 128).
 // k rounds each pick the largest logit not yet chosen, ties to the lower
 // expert id (an arg-max within the 8 lanes), which is the order the insertion
 // above produces.  The block's choices go through LDS to the rank and count
@@ -123,7 +124,7 @@ __global__ void __launch_bounds__(kRouteWg) route_topk_kernel(const float* __res
 constexpr int kWaveTopkMaxE = 128;
 constexpr int kWaveTopkWaves = 8;
 constexpr int kTokLanes = 8;
-constexpr int kPerLane = kWaveTopkMaxE / kTokLanes;
+constexpr int kPerLane = kWaveTopkMaxE / kTokLanes;   // logits per lane: 16 for up to 128 experts, 8 up to 64
 
 __device__ __forceinline__ void argmax_merge(float& v, int& i, float ov, int oi) {
   // (v, i) = the better of two candidates: the larger logit, ties to the
@@ -135,6 +136,7 @@ __device__ __forceinline__ void argmax_merge(float& v, int& i, float ov, int oi)
   i = take ? oi : i;
 }
 
+template <int PER>
 __global__ void __launch_bounds__(kWaveTopkWaves * 64) route_topk_wave_kernel(
     const float* __restrict__ logits, int64_t T, int E, int k, int64_t ld, int32_t* __restrict__ ids,
     float* __restrict__ weights, int32_t* __restrict__ rank, int32_t* __restrict__ hist) {
@@ -148,11 +150,11 @@ __global__ void __launch_bounds__(kWaveTopkWaves * 64) route_topk_wave_kernel(
   const int tb = wv * (64 / kTokLanes) + (lane >> 3);   // token within the block
   const int64_t tt = t0 + tb;
   const bool tvalid = tt < T;
-  float v[kPerLane];
-  bool free_[kPerLane];
+  float v[PER];
+  bool free_[PER];
   const float* row = logits + (tvalid ? tt : 0) * ld;
 #pragma unroll
-  for (int i = 0; i < kPerLane; ++i) {
+  for (int i = 0; i < PER; ++i) {
     const int e = sub + kTokLanes * i;
     free_[i] = tvalid && e < E;
     v[i] = free_[i] ? row[e] : 0.f;
@@ -167,7 +169,7 @@ __global__ void __launch_bounds__(kWaveTopkWaves * 64) route_topk_wave_kernel(
       float bv = -__builtin_huge_valf();
       int bi = INT_MAX;
 #pragma unroll
-      for (int i = 0; i < kPerLane; ++i)
+      for (int i = 0; i < PER; ++i)
         argmax_merge(bv, bi, free_[i] ? v[i] : -__builtin_huge_valf(), free_[i] ? sub + kTokLanes * i : INT_MAX);
 #pragma unroll
       for (int off = kTokLanes / 2; off >= 1; off >>= 1) {
@@ -178,7 +180,7 @@ __global__ void __launch_bounds__(kWaveTopkWaves * 64) route_topk_wave_kernel(
       val[j] = bv;
       id[j] = bi;
 #pragma unroll
-      for (int i = 0; i < kPerLane; ++i) free_[i] = free_[i] & (sub + kTokLanes * i != bi);
+      for (int i = 0; i < PER; ++i) free_[i] = free_[i] & (sub + kTokLanes * i != bi);
     }
   }
   if (tvalid && sub == 0) {
@@ -353,8 +355,12 @@ int route_launch(const float* logits, int64_t T, int E, int k, int64_t ld, int32
   int32_t* hist = reinterpret_cast<int32_t*>(reinterpret_cast<char*>(ws) + 2 * a256((size_t)T * k * 4));
   int slot = launch_begin(KC_ROUTE, st);
   if (E <= kWaveTopkMaxE) {
-    hipLaunchKernelGGL(route_topk_wave_kernel, dim3((uint32_t)nb), dim3(kWaveTopkWaves * 64), 0, st, logits, T, E,
-                       k, ld, ids, weights, rank, hist);
+    if (E <= kWaveTopkMaxE / 2)
+      hipLaunchKernelGGL((route_topk_wave_kernel<kPerLane / 2>), dim3((uint32_t)nb), dim3(kWaveTopkWaves * 64), 0, st,
+                         logits, T, E, k, ld, ids, weights, rank, hist);
+    else
+      hipLaunchKernelGGL((route_topk_wave_kernel<kPerLane>), dim3((uint32_t)nb), dim3(kWaveTopkWaves * 64), 0, st,
+                         logits, T, E, k, ld, ids, weights, rank, hist);
   } else {
     const uint32_t g1 = (uint32_t)((T + kRouteWg - 1) / kRouteWg);
     hipLaunchKernelGGL(route_topk_kernel, dim3(g1), dim3(kRouteWg), 0, st, logits, T, E, k, ld, ids, weights, rank,
