@@ -1318,8 +1318,16 @@ __device__ __forceinline__ float wave_sum_dpp(float v) {
   return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 63));
 }
 
-template <int T, int BPL, bool DUAL, int EPI>
-__global__ void __launch_bounds__(256) gemv_kernel(GemmArgs p) {
+// WGK (store epilogue, at most kGvWgkSplits K splits): the work-group is one
+// column group's K splits, wave w taking split w, and the splits' partial
+// sums are added through LDS, in split order, by the work-group's first wave
+// (the arithmetic of the reduction kernels): one barrier instead of partial
+// sums stored to and read back from memory across work-groups.
+constexpr int kGvWgkSplits = 12;
+
+template <int T, int BPL, bool DUAL, int EPI, bool WGK = false>
+__global__ void __launch_bounds__(WGK ? 64 * kGvWgkSplits : 256) gemv_kernel(GemmArgs p) {
+  static_assert(!WGK || (!DUAL && EPI == EPI_STORE), "split-K in one work-group: store epilogue");
   constexpr int PER = BPL * (DUAL ? 2 : 1);
   constexpr int RP0 = (8 / PER) > 0 ? (8 / PER) : 1;
   constexpr int RP = RP0 < kGvCols ? RP0 : kGvCols;       // columns per group
@@ -1328,15 +1336,17 @@ __global__ void __launch_bounds__(256) gemv_kernel(GemmArgs p) {
   constexpr int D = NVFP4_GV_DEPTH < G ? NVFP4_GV_DEPTH : G;
   static_assert(kGvCols % RP == 0, "groups must tile the wave's columns");
   __shared__ float hq[EPI == EPI_GLUQ && kGvCols < 16 ? T * 4 * kGvCols : 1];
+  __shared__ float wgk[WGK ? kGvWgkSplits * T * kGvCols : 1];
   const int lane = threadIdx.x & 63;
   const int wi = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int64_t wave = (int64_t)blockIdx.x * 4 + wi;
   const int64_t N = p.N, K = p.K, M = p.M;
   const int64_t wps = (N + kGvCols - 1) / kGvCols;       // waves per split
+  // WGK: one work-group per column group, one wave per split (no wave past the end)
+  const int64_t wave = WGK ? (int64_t)wi * wps + blockIdx.x : (int64_t)blockIdx.x * 4 + wi;
   // Only the store epilogue can have waves past the end (the gate/up pair
   // has N % 128 == 0 and one split, so its work-groups are full); the
   // quantising epilogue's barrier below is never skipped by any wave.
-  if (wave >= wps * (int64_t)p.splits) return;
+  if (!WGK && wave >= wps * (int64_t)p.splits) return;
   const int64_t split = wave / wps;
   const int64_t n0 = (wave - split * wps) * kGvCols;
   // block b of this lane is block 64 b + lane of the split
@@ -1509,6 +1519,28 @@ __global__ void __launch_bounds__(256) gemv_kernel(GemmArgs p) {
         const uint32_t sc = quantize_block16(b16, p.q_gs[0], w0, w1);
         *reinterpret_cast<uint2*>(p.q_codes + t * (N / 2) + c0 / 2) = make_uint2(w0, w1);
         p.q_scales[t * (N / 16) + c0 / 16] = (uint8_t)sc;
+      }
+    }
+  } else if constexpr (WGK) {
+    // each split's sums to LDS, then the first wave adds them in split order
+    // (lane = token * kGvCols + column) and stores the outputs
+    if (active) {
+#pragma unroll
+      for (int c = 0; c < kGvCols; ++c) wgk[(wi * T + lane) * kGvCols + c] = v[c];
+    }
+    __syncthreads();
+    if (wi == 0) {
+      const int64_t t = lane / kGvCols, c = lane % kGvCols;
+      float am = 0.f;
+      if (t < M && t < T && n0 + c < N) {
+        float acc = 0.f;
+        for (uint32_t sp = 0; sp < p.splits; ++sp) acc += wgk[(sp * T + t) * kGvCols + c];
+        am = store_output(p, t, n0 + c, acc);
+      }
+      if (p.amax_slots != nullptr) {
+        am = wave_max(am);
+        if (lane == 0)
+          atomicMax(reinterpret_cast<unsigned int*>(p.amax_slots + (n0 / kGvCols) % kAmaxSlots), __float_as_uint(am));
       }
     }
   } else {
@@ -2232,25 +2264,36 @@ static void launch_skinny(const GemmArgs& g, hipStream_t st) {
   launch_end(slot, st);
 }
 
-template <int T, bool DUAL, int EPI>
-static void launch_gemv_t(const GemmArgs& g, int bpl, uint32_t grid, hipStream_t st) {
+template <int T, bool DUAL, int EPI, bool WGK = false>
+static void launch_gemv_t(const GemmArgs& g, int bpl, uint32_t grid, uint32_t block, hipStream_t st) {
   switch (bpl) {
-    case 1: hipLaunchKernelGGL((gemv_kernel<T, 1, DUAL, EPI>), dim3(grid), dim3(256), 0, st, g); break;
-    case 2: hipLaunchKernelGGL((gemv_kernel<T, 2, DUAL, EPI>), dim3(grid), dim3(256), 0, st, g); break;
-    case 3: hipLaunchKernelGGL((gemv_kernel<T, 3, DUAL, EPI>), dim3(grid), dim3(256), 0, st, g); break;
-    case 4: hipLaunchKernelGGL((gemv_kernel<T, 4, DUAL, EPI>), dim3(grid), dim3(256), 0, st, g); break;
-    default: hipLaunchKernelGGL((gemv_kernel<T, 5, DUAL, EPI>), dim3(grid), dim3(256), 0, st, g); break;
+    case 1: hipLaunchKernelGGL((gemv_kernel<T, 1, DUAL, EPI, WGK>), dim3(grid), dim3(block), 0, st, g); break;
+    case 2: hipLaunchKernelGGL((gemv_kernel<T, 2, DUAL, EPI, WGK>), dim3(grid), dim3(block), 0, st, g); break;
+    case 3: hipLaunchKernelGGL((gemv_kernel<T, 3, DUAL, EPI, WGK>), dim3(grid), dim3(block), 0, st, g); break;
+    case 4: hipLaunchKernelGGL((gemv_kernel<T, 4, DUAL, EPI, WGK>), dim3(grid), dim3(block), 0, st, g); break;
+    default: hipLaunchKernelGGL((gemv_kernel<T, 5, DUAL, EPI, WGK>), dim3(grid), dim3(block), 0, st, g); break;
   }
 }
 
-// g.splits holds the K splits; one wave per 16 output columns per split.
+// g.splits holds the K splits; one wave per kGvCols output columns per
+// split.  The store epilogue with its split-K finished in the kernel (tickets
+// given) takes one work-group per column group, its splits added in LDS.
 template <bool DUAL, int EPI>
 static void launch_gemv(const GemmArgs& g, int bpl, hipStream_t st) {
+  const int slot = launch_begin(EPI != EPI_STORE ? KC_GEMM_GLU : KC_GEMM_STORE, st);
+  if constexpr (!DUAL && EPI == EPI_STORE) {
+    if (g.tickets != nullptr && g.splits > 1 && g.splits <= (uint32_t)kGvWgkSplits) {
+      const uint32_t grid = cdiv(g.N, kGvCols), block = 64u * g.splits;
+      if (g.M <= 1) launch_gemv_t<1, false, EPI_STORE, true>(g, bpl, grid, block, st);
+      else launch_gemv_t<NVFP4_GV_MAXT, false, EPI_STORE, true>(g, bpl, grid, block, st);
+      launch_end(slot, st);
+      return;
+    }
+  }
   const uint32_t waves = cdiv(g.N, kGvCols) * g.splits;
   const uint32_t grid = cdiv(waves, 4);
-  const int slot = launch_begin(EPI != EPI_STORE ? KC_GEMM_GLU : KC_GEMM_STORE, st);
-  if (g.M <= 1) launch_gemv_t<1, DUAL, EPI>(g, bpl, grid, st);
-  else launch_gemv_t<NVFP4_GV_MAXT, DUAL, EPI>(g, bpl, grid, st);
+  if (g.M <= 1) launch_gemv_t<1, DUAL, EPI>(g, bpl, grid, 256, st);
+  else launch_gemv_t<NVFP4_GV_MAXT, DUAL, EPI>(g, bpl, grid, 256, st);
   launch_end(slot, st);
 }
 
