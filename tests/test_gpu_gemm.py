@@ -48,7 +48,10 @@ def test_gemm_16x256x512_workload():
 
 
 SHAPES = [(1, 64, 128), (5, 320, 384), (31, 128, 256), (33, 512, 256), (200, 384, 640), (130, 1000, 1024),
-          (64, 8, 128), (7, 100, 256), (32, 1000, 384), (3, 40, 1152), (2, 96, 8192)]
+          (64, 8, 128), (7, 100, 256), (32, 1000, 384), (3, 40, 1152), (2, 96, 8192),
+          # 27 x 19 = 513 tiles of 64 x 256, ragged in both: one more than the 512 persistent
+          # work-groups, so work-group 0 takes a second tile after the epilogue of its first
+          (1700, 4800, 256)]
 
 
 @pytest.mark.parametrize("m,n,k", SHAPES, ids=[f"{m}x{n}x{k}" for m, n, k in SHAPES])

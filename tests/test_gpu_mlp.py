@@ -93,7 +93,8 @@ def check_mlp(xbits, wdev, wref, label):
     return e2e
 
 
-SMALL = [(1, 256, 384), (37, 256, 384), (64, 512, 256), (129, 384, 640)]
+# the last: 27 x 19 = 513 gate/up tiles of 64 x 128 (one more than the 512 persistent work-groups)
+SMALL = [(1, 256, 384), (37, 256, 384), (64, 512, 256), (129, 384, 640), (1700, 256, 2432)]
 
 
 @pytest.mark.parametrize("t,k,i", SMALL, ids=[f"T{t}_K{k}_I{i}" for t, k, i in SMALL])
