@@ -560,11 +560,16 @@ def extra_lines(m):
     whole(x, lay, y, 0, False)
     launches = m.launch_count() - before
     ms = float(np.median(time_events(lambda: whole(x, lay, y, 0, False), 20)))
+    # ten calls between one pair of events: the per-call time without the host's
+    # launch latency in front of each call (the one-call figure above includes it)
+    ms_b2b = float(np.median(time_events(lambda: [whole(x, lay, y, 0, False) for _ in range(10)], 5))) / 10
     out["prefill_1024"] = {"workload": "mlp_prefill_1024x5120x17408", "ms": ms,
                            "tflops": mlp_flops(p3["T"]) / (ms * 1e-3) / 1e12,
                            "tokens_per_s": p3["T"] / (ms * 1e-3),
                            "frac_f16_peak": mlp_flops(p3["T"]) / (ms * 1e-3) / 1e12 / PEAK_F16_TFLOPS,
-                           "launches": launches, "call": "nvfp4_mlp (whole MLP; global scales computed on the device)"}
+                           "launches": launches, "call": "nvfp4_mlp (whole MLP; global scales computed on the device)",
+                           "back_to_back": {"ms_per_call": ms_b2b,
+                                            "tflops": mlp_flops(p3["T"]) / (ms_b2b * 1e-3) / 1e12}}
     # the separate calls (quantise, gate/up + requantise, down), and the
     # whole-MLP call on the row-major weights alone (no tile-contiguous copies)
     run = MlpRunner(m, p3["T"])
