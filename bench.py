@@ -781,7 +781,16 @@ def moe_line(m):
     ws_gs = torch.empty(max(m.grouped_ws_bytes(slots, i, k, e, m.EPI_SILU_MUL_QUANT_GIVEN), 256), dtype=torch.uint8,
                         device="cuda")
 
+    ws_ms = torch.empty(m.moe_mlp_ws_bytes(t, k, i, e, slots, static=True), dtype=torch.uint8, device="cuda")
+
     def layer_static():
+        # one call: quantise x with its given scale (and its f16 copy), gate/up
+        # quantising H~ in its epilogue (and H~'s f16 copy), down, reduction
+        m.nvfp4_moe_route(logits, top, offs, rows, slot_of, cw, ws=ws_r)
+        m.nvfp4_moe_mlp_static(x, rows, offs, wg, wu, wd, xq_s, hq_s, ys, ws=ws_ms)
+        m.nvfp4_moe_combine(ys, slot_of, cw, y)
+
+    def layer_static_separate():
         m.nvfp4_moe_route(logits, top, offs, rows, slot_of, cw, ws=ws_r)
         m.nvfp4_quantize_act(x, xq_s, gs_mode=m.GS_GIVEN, ws=ws_q)
         m.nvfp4_grouped_gemm(xq_s, rows, offs, wg, wu, out_q=hq_s, epilogue=m.EPI_SILU_MUL_QUANT_GIVEN, m=slots,
@@ -795,6 +804,10 @@ def moe_line(m):
     ms_s = float(np.median(time_events(layer_static, 10)))
     parts["static_gs_ms"] = ms_s
     parts["static_gs_launches_per_call"] = launches_s
+    before = m.launch_count()
+    layer_static_separate()
+    parts["static_gs_separate_calls_launches"] = m.launch_count() - before
+    parts["static_gs_separate_calls_ms"] = float(np.median(time_events(layer_static_separate, 10)))
     flops = mlp_flops(slots, k, i)
     parts["static_gs_tflops"] = flops / (ms_s * 1e-3) / 1e12
     tf = flops / (ms * 1e-3) / 1e12

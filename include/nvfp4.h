@@ -363,6 +363,26 @@ int nvfp4_moe_mlp(const void *x, int x_dtype, int64_t ld_x, int64_t T, int64_t K
                   int y_dtype, int64_t ld_y, void *ws, size_t *ws_bytes, void *stream);
 
 /*
+ * nvfp4_moe_mlp_static -- the expert MLP over routed slots in one call with
+ * static global scales ([dsv4] P0, fix 1: scales from a warm-up pass; P8
+ * item 1: the GLU output quantised in the producer's epilogue): as
+ * nvfp4_moe_mlp, but *x_q.gscale and *h_q.gscale are READ on the device (the
+ * scales x~ and H~ are quantised with) instead of computed, and the gate/up
+ * pair quantises SiLU(gate) * up in its epilogue (no float32 H, no
+ * requantisation launch).  The values are those of nvfp4_quantize_act with
+ * NVFP4_GS_GIVEN, then nvfp4_grouped_gemm with NVFP4_EPI_SILU_MUL_QUANT_GIVEN
+ * and with NVFP4_EPI_STORE (bit-identical); the quantiser writes the f16 copy
+ * of x that the gate/up stages its slots' rows from, and the gate/up's
+ * epilogue writes the f16 copy of H~ that the down projection stages: four
+ * launches, none of them an expansion.  Arguments and limits as
+ * nvfp4_moe_mlp; x_q and h_q: codes and scales written, gscale read.
+ */
+int nvfp4_moe_mlp_static(const void *x, int x_dtype, int64_t ld_x, int64_t T, int64_t K, int64_t I, int E,
+                         const int32_t *a_rows, const int32_t *group_offsets, int64_t M, nvfp4_tensor w_gate,
+                         nvfp4_tensor w_up, nvfp4_tensor w_down, nvfp4_tensor x_q, nvfp4_tensor h_q, void *y_slots,
+                         int y_dtype, int64_t ld_y, void *ws, size_t *ws_bytes, void *stream);
+
+/*
  * nvfp4_tile_weight -- the tile-contiguous copy of a weight (or expert
  * stack) for the large-batch contractions ([llama] "What the patch does":
  * aligned whole-tile loads feeding the matrix unit).  A permutation of the

@@ -66,6 +66,9 @@ _sig = {
     "nvfp4_moe_mlp": [_vp, ctypes.c_int, _i64, _i64, _i64, _i64, ctypes.c_int, _vp, _vp, _i64, nvfp4_tensor,
                       nvfp4_tensor, nvfp4_tensor, nvfp4_tensor, nvfp4_tensor, _vp, ctypes.c_int, _i64, _vp,
                       ctypes.POINTER(ctypes.c_size_t), _vp],
+    "nvfp4_moe_mlp_static": [_vp, ctypes.c_int, _i64, _i64, _i64, _i64, ctypes.c_int, _vp, _vp, _i64, nvfp4_tensor,
+                             nvfp4_tensor, nvfp4_tensor, nvfp4_tensor, nvfp4_tensor, _vp, ctypes.c_int, _i64, _vp,
+                             ctypes.POINTER(ctypes.c_size_t), _vp],
 }
 for _name, _args in _sig.items():
     _f = getattr(_lib, _name)
@@ -451,11 +454,12 @@ def nvfp4_moe_combine(y_slots, slot_of, weights, y, stream=None):
            "nvfp4_moe_combine")
 
 
-def moe_mlp_ws_bytes(t, k, i, e, m):
+def moe_mlp_ws_bytes(t, k, i, e, m, static=False):
     size = ctypes.c_size_t(0)
-    _check(_lib.nvfp4_moe_mlp(_vp(0), BF16, k, t, k, i, e, _vp(0), _vp(0), m, _null_tensor(), _null_tensor(),
-                              _null_tensor(), _null_tensor(), _null_tensor(), _vp(0), F32, k, _vp(0),
-                              ctypes.byref(size), _vp(0)), "workspace query")
+    fn = _lib.nvfp4_moe_mlp_static if static else _lib.nvfp4_moe_mlp
+    _check(fn(_vp(0), BF16, k, t, k, i, e, _vp(0), _vp(0), m, _null_tensor(), _null_tensor(),
+              _null_tensor(), _null_tensor(), _null_tensor(), _vp(0), F32, k, _vp(0),
+              ctypes.byref(size), _vp(0)), "workspace query")
     return size.value
 
 
@@ -473,6 +477,25 @@ def nvfp4_moe_mlp(x, a_rows, group_offsets, w_gate, w_up, w_down, x_q, h_q, y_sl
                               w_gate.c(), w_up.c(), w_down.c(), x_q.c(), h_q.c(), _ptr(y_slots),
                               _dtype_code(y_slots), y_slots.stride(0), _ptr(ws), ctypes.byref(sz), _stream(stream)),
            "nvfp4_moe_mlp")
+    return ws
+
+
+def nvfp4_moe_mlp_static(x, a_rows, group_offsets, w_gate, w_up, w_down, x_q, h_q, y_slots, ws=None, stream=None):
+    """The expert MLP over routed slots in one call with the given global
+    scales x_q.gscale and h_q.gscale; see include/nvfp4.h."""
+    t, k = x.shape
+    m = y_slots.shape[0]
+    e = w_gate.gscale.numel()
+    i = w_gate.rows
+    need = moe_mlp_ws_bytes(t, k, i, e, m, static=True)
+    if need:
+        ws = _scratch(need, ws, x.device, stream)
+    sz = ctypes.c_size_t(ws.numel() if ws is not None else 0)
+    _check(_lib.nvfp4_moe_mlp_static(_ptr(x), _dtype_code(x), x.stride(0), t, k, i, e, _ptr(a_rows),
+                                     _ptr(group_offsets), m, w_gate.c(), w_up.c(), w_down.c(), x_q.c(), h_q.c(),
+                                     _ptr(y_slots), _dtype_code(y_slots), y_slots.stride(0), _ptr(ws),
+                                     ctypes.byref(sz), _stream(stream)),
+           "nvfp4_moe_mlp_static")
     return ws
 
 

@@ -80,6 +80,7 @@ struct GemmArgs {
   uint8_t* q_codes;       // EPI_GLUQ output [M][N] NVFP4 and its given global scale
   uint8_t* q_scales;
   const float* q_gs;
+  _Float16* q16;          // EPI_GLUQ (nullable): the f16 copy of the quantised output, code * scale
   // Split-K finished inside the weight streams (store epilogue, split_out
   // written): one ticket per column group, cleared by an earlier launch; the
   // wave (or work-group) of a group that arrives last adds the group's partial
@@ -985,6 +986,11 @@ __global__ void __launch_bounds__(WN * 64, MINWG) gemm_kernel(GemmArgs p) {
         const uint32_t sc = quantize_block16(vv, gs, w0, w1);
         *reinterpret_cast<uint2*>(p.q_codes + grow * (p.N / 2) + gcol / 2) = make_uint2(w0, w1);
         p.q_scales[grow * (p.N / 16) + gcol / 16] = (uint8_t)sc;
+        if (p.q16 != nullptr) {
+          f16x8* o = reinterpret_cast<f16x8*>(p.q16 + grow * p.N + gcol);
+          o[0] = expand8(w0, sc);
+          o[1] = expand8(w1, sc);
+        }
       }
     } else {
       // Register epilogue.  Output (row, col) of this lane: row = urow + 4 hh,
@@ -2530,17 +2536,24 @@ int glu_launch(Operand a, const int32_t* a_rows, const int32_t* off, int E, int6
   return requant_f32_launch(h, M, N, hq_codes, hq_scales, hq_gs, partials, glu_parts(M, N, K, E, grouped), st, hq16);
 }
 
-size_t glu_static_ws_bytes(int64_t M, int64_t N, int64_t K, bool grouped) {
-  return align256((size_t)M * K * 2) + (grouped ? 0 : tile_dual_bytes(M, N, K));
+size_t glu_static_ws_bytes(int64_t M, int64_t N, int64_t K, bool grouped, bool gather) {
+  return (gather ? 0 : align256((size_t)M * K * 2)) + (grouped ? 0 : tile_dual_bytes(M, N, K));
 }
 
 int glu_static_launch(Operand a, const int32_t* a_rows, const int32_t* off, int E, int64_t M, Operand gt,
                       Operand up, int64_t N, int64_t K, uint8_t* hq_codes, uint8_t* hq_scales, const float* hq_gs,
-                      void* ws, hipStream_t st) {
+                      void* ws, hipStream_t st, const _Float16* a16_given, _Float16* hq16, int64_t gather_rows) {
+  const bool gather = off != nullptr && a16_given != nullptr;   // slot rows staged from the token copy via a_rows
   _Float16* a16 = reinterpret_cast<_Float16*>(ws);
   const bool stream = !off && (plan_gemv(M, K, true).bpl > 0 || plan_tile(M, N, K, true).ok);
-  if (!stream) launch_expand(a.codes, a.scales, a_rows, M, K, a16, st);   // the streams expand x~ themselves
+  if (a16_given != nullptr) a16 = const_cast<_Float16*>(a16_given);
+  else if (!stream) launch_expand(a.codes, a.scales, a_rows, M, K, a16, st);   // the streams expand x~ themselves
   GemmArgs g = base_args(a16, a.gscale, gt, M, N, K);
+  if (gather) {
+    g.a_gather = a_rows;
+    g.a_gather_rows = gather_rows;
+  }
+  g.q16 = off != nullptr ? hq16 : nullptr;   // written by the expert-grouped contraction's epilogue
   g.a_codes = a.codes;
   g.a_scales = a.scales;
   g.u_codes = up.codes;
@@ -2560,7 +2573,7 @@ int glu_static_launch(Operand a, const int32_t* a_rows, const int32_t* off, int 
   } else if (const GvPlan gv = plan_gemv(M, K, true); gv.bpl > 0) {
     launch_gemv<true, EPI_GLUQ>(g, gv.bpl, st);
   } else if (const TlPlan tl = plan_tile(M, N, K, true); tl.ok) {
-    tile_dual_setup(g, tl, reinterpret_cast<char*>(ws) + align256((size_t)M * K * 2), st);
+    tile_dual_setup(g, tl, reinterpret_cast<char*>(ws) + (a16_given != nullptr ? 0 : align256((size_t)M * K * 2)), st);
     launch_tile<true, EPI_GLUQ>(g, st);
   } else if (M <= 32) {
     g.m_tiles = 1;
@@ -2650,6 +2663,30 @@ int moe_mlp_launch(const void* x, int x_dtype, int64_t ld_x, int64_t T, int64_t 
   if ((rc = glu_launch(xq, a_rows, off, E, M, wg, wu, I, K, hq_codes, hq_scales, hq_gs, wg_ws, st, x16, h16, T)))
     return rc;
   const Operand hq{hq_codes, hq_scales, hq_gs, nullptr};
+  return store_launch(hq, nullptr, off, E, M, wd, K, I, y, y_bf16, ldy, nullptr, wd_ws, st, h16);
+}
+
+size_t moe_mlp_static_ws_bytes(int64_t T, int64_t K, int64_t I, int E, int64_t M) {
+  return align256((size_t)T * K * 2) + align256(glu_static_ws_bytes(M, I, K, true, true)) +
+         align256(store_ws_bytes(M, K, I, E, true));
+}
+
+int moe_mlp_static_launch(const void* x, int x_dtype, int64_t ld_x, int64_t T, int64_t K, int64_t I, int E,
+                          const int32_t* a_rows, const int32_t* off, int64_t M, Operand wg, Operand wu, Operand wd,
+                          uint8_t* xq_codes, uint8_t* xq_scales, float* xq_gs, uint8_t* hq_codes, uint8_t* hq_scales,
+                          const float* hq_gs, void* y, int y_bf16, int64_t ldy, void* ws, hipStream_t st) {
+  char* w = reinterpret_cast<char*>(ws);
+  _Float16* x16 = reinterpret_cast<_Float16*>(w);
+  char* wg_ws = w + align256((size_t)T * K * 2);
+  char* wd_ws = wg_ws + align256(glu_static_ws_bytes(M, I, K, true, true));
+  _Float16* h16 = reinterpret_cast<_Float16*>(wd_ws);   // the down projection's f16 slot
+  int rc = quantize_launch(x, x_dtype, T, K, ld_x, xq_codes, xq_scales, xq_gs, 1, nullptr, st, x16);
+  if (rc) return rc;
+  const Operand xq{xq_codes, xq_scales, xq_gs, nullptr};
+  if ((rc = glu_static_launch(xq, a_rows, off, E, M, wg, wu, I, K, hq_codes, hq_scales, hq_gs, wg_ws, st, x16, h16,
+                              T)))
+    return rc;
+  const Operand hq{hq_codes, hq_scales, const_cast<float*>(hq_gs), nullptr};
   return store_launch(hq, nullptr, off, E, M, wd, K, I, y, y_bf16, ldy, nullptr, wd_ws, st, h16);
 }
 

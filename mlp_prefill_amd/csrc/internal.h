@@ -110,10 +110,14 @@ int glu_launch(Operand a, const int32_t* a_rows, const int32_t* off, int E, int6
 // quantised in the contraction's epilogue with the given global scale *hq_gs
 // (two launches: expansion or ticket clearing, contraction).  Workspace: the
 // f16 copy of A, then (3-16 token stream, K split) partial sums and tickets.
-size_t glu_static_ws_bytes(int64_t M, int64_t N, int64_t K, bool grouped);
+// With a16 given (expert groups: the token copy, a_rows the slots' token rows,
+// gather_rows its rows) no expansion runs and the workspace holds no f16 copy
+// of A; hq16 (expert groups, nullable) receives the f16 copy of H~.
+size_t glu_static_ws_bytes(int64_t M, int64_t N, int64_t K, bool grouped, bool gather = false);
 int glu_static_launch(Operand a, const int32_t* a_rows, const int32_t* off, int E, int64_t M, Operand gt,
                       Operand up, int64_t N, int64_t K, uint8_t* hq_codes, uint8_t* hq_scales, const float* hq_gs,
-                      void* ws, hipStream_t st);
+                      void* ws, hipStream_t st, const _Float16* a16 = nullptr, _Float16* hq16 = nullptr,
+                      int64_t gather_rows = 0);
 
 // C = A . W^T * gs_a * gs_w quantised to NVFP4 with the given global scale
 // *yq_gs by the (always launched) fixed-order split reduction.  Workspace as
@@ -146,6 +150,18 @@ int moe_mlp_launch(const void* x, int x_dtype, int64_t ld_x, int64_t T, int64_t 
                    const int32_t* a_rows, const int32_t* off, int64_t M, Operand wg, Operand wu, Operand wd,
                    uint8_t* xq_codes, uint8_t* xq_scales, float* xq_gs, uint8_t* hq_codes, uint8_t* hq_scales,
                    float* hq_gs, void* y, int y_bf16, int64_t ldy, void* ws, hipStream_t st);
+
+// The same with given global scales (x~ with *xq_gs, H~ with *hq_gs): quantise
+// x with its scale (also writing its f16 copy), expert-grouped gate/up with
+// the quantising epilogue staging each slot's row of that copy (also writing
+// the f16 copy of H~), expert-grouped down projection on that copy, split
+// reduction -- four launches, none of them an expansion.  Workspace: [x f16]
+// [gate/up workspace][down workspace, H~ f16 in its f16 slot].
+size_t moe_mlp_static_ws_bytes(int64_t T, int64_t K, int64_t I, int E, int64_t M);
+int moe_mlp_static_launch(const void* x, int x_dtype, int64_t ld_x, int64_t T, int64_t K, int64_t I, int E,
+                          const int32_t* a_rows, const int32_t* off, int64_t M, Operand wg, Operand wu, Operand wd,
+                          uint8_t* xq_codes, uint8_t* xq_scales, float* xq_gs, uint8_t* hq_codes, uint8_t* hq_scales,
+                          const float* hq_gs, void* y, int y_bf16, int64_t ldy, void* ws, hipStream_t st);
 
 // ---- expert routing and combine ----------------------------------------------
 size_t route_ws_bytes(int64_t T, int E, int k);

@@ -349,10 +349,14 @@ int nvfp4_mlp(const void* x, int x_dtype, int64_t ld_x, const float* x_amax, int
                            ws, reinterpret_cast<hipStream_t>(stream));
 }
 
-int nvfp4_moe_mlp(const void* x, int x_dtype, int64_t ld_x, int64_t T, int64_t K, int64_t I, int E,
-                  const int32_t* a_rows, const int32_t* group_offsets, int64_t M, nvfp4_tensor w_gate,
-                  nvfp4_tensor w_up, nvfp4_tensor w_down, nvfp4_tensor x_q, nvfp4_tensor h_q, void* y_slots,
-                  int y_dtype, int64_t ld_y, void* ws, size_t* ws_bytes, void* stream) {
+// Shared by the two one-call expert MLPs: argument checks and the workspace
+// query; NVFP4_OK with *go set when the launch should run.
+static int moe_mlp_checks(const void* x, int x_dtype, int64_t ld_x, int64_t T, int64_t K, int64_t I, int E,
+                          const int32_t* a_rows, const int32_t* group_offsets, int64_t M, const nvfp4_tensor& w_gate,
+                          const nvfp4_tensor& w_up, const nvfp4_tensor& w_down, const nvfp4_tensor& x_q,
+                          const nvfp4_tensor& h_q, void* y_slots, int y_dtype, int64_t ld_y, void* ws,
+                          size_t* ws_bytes, size_t need, bool* go) {
+  *go = false;
   if (!dtype_ok(x_dtype) || !dtype_ok(y_dtype)) return NVFP4_ERR_ARG;
   if (E < 1 || E > 4096) return NVFP4_ERR_ARG;
   if (T < 0 || M < 0 || K <= 0 || I <= 0 || K % 128 != 0 || I % 128 != 0 || ld_x < K || ld_y < K)
@@ -361,7 +365,7 @@ int nvfp4_moe_mlp(const void* x, int x_dtype, int64_t ld_x, int64_t T, int64_t K
       T * (K / 16) >= ((int64_t)1 << 31) || T * K * 2 >= ((int64_t)1 << 31))
     return NVFP4_ERR_SHAPE;
   bool query;
-  int rc = workspace(ws, ws_bytes, T > 0 && M > 0 ? nvfp4::moe_mlp_ws_bytes(T, K, I, E, M) : 0, &query);
+  int rc = workspace(ws, ws_bytes, T > 0 && M > 0 ? need : 0, &query);
   if (rc != NVFP4_OK || query) return rc;
   if (T == 0 || M == 0) return NVFP4_OK;
   if (!x || !y_slots || !a_rows || !group_offsets) return NVFP4_ERR_NULL;
@@ -373,9 +377,37 @@ int nvfp4_moe_mlp(const void* x, int x_dtype, int64_t ld_x, int64_t T, int64_t K
       (ld_y * elem_size(y_dtype)) % 16 != 0 || !aligned(a_rows, 4) || !aligned(group_offsets, 4))
     return NVFP4_ERR_ALIGN;
   if ((rc = check_device()) != NVFP4_OK) return rc;
+  *go = true;
+  return NVFP4_OK;
+}
+
+int nvfp4_moe_mlp(const void* x, int x_dtype, int64_t ld_x, int64_t T, int64_t K, int64_t I, int E,
+                  const int32_t* a_rows, const int32_t* group_offsets, int64_t M, nvfp4_tensor w_gate,
+                  nvfp4_tensor w_up, nvfp4_tensor w_down, nvfp4_tensor x_q, nvfp4_tensor h_q, void* y_slots,
+                  int y_dtype, int64_t ld_y, void* ws, size_t* ws_bytes, void* stream) {
+  bool go;
+  const size_t need = T > 0 && M > 0 && K > 0 && I > 0 ? nvfp4::moe_mlp_ws_bytes(T, K, I, E, M) : 0;
+  int rc = moe_mlp_checks(x, x_dtype, ld_x, T, K, I, E, a_rows, group_offsets, M, w_gate, w_up, w_down, x_q, h_q,
+                          y_slots, y_dtype, ld_y, ws, ws_bytes, need, &go);
+  if (rc != NVFP4_OK || !go) return rc;
   return nvfp4::moe_mlp_launch(x, x_dtype, ld_x, T, K, I, E, a_rows, group_offsets, M, op(w_gate), op(w_up),
                                op(w_down), x_q.codes, x_q.scales, x_q.gscale, h_q.codes, h_q.scales, h_q.gscale,
                                y_slots, y_dtype == NVFP4_BF16, ld_y, ws, reinterpret_cast<hipStream_t>(stream));
+}
+
+int nvfp4_moe_mlp_static(const void* x, int x_dtype, int64_t ld_x, int64_t T, int64_t K, int64_t I, int E,
+                         const int32_t* a_rows, const int32_t* group_offsets, int64_t M, nvfp4_tensor w_gate,
+                         nvfp4_tensor w_up, nvfp4_tensor w_down, nvfp4_tensor x_q, nvfp4_tensor h_q, void* y_slots,
+                         int y_dtype, int64_t ld_y, void* ws, size_t* ws_bytes, void* stream) {
+  bool go;
+  const size_t need = T > 0 && M > 0 && K > 0 && I > 0 ? nvfp4::moe_mlp_static_ws_bytes(T, K, I, E, M) : 0;
+  int rc = moe_mlp_checks(x, x_dtype, ld_x, T, K, I, E, a_rows, group_offsets, M, w_gate, w_up, w_down, x_q, h_q,
+                          y_slots, y_dtype, ld_y, ws, ws_bytes, need, &go);
+  if (rc != NVFP4_OK || !go) return rc;
+  return nvfp4::moe_mlp_static_launch(x, x_dtype, ld_x, T, K, I, E, a_rows, group_offsets, M, op(w_gate),
+                                      op(w_up), op(w_down), x_q.codes, x_q.scales, x_q.gscale, h_q.codes,
+                                      h_q.scales, h_q.gscale, y_slots, y_dtype == NVFP4_BF16, ld_y, ws,
+                                      reinterpret_cast<hipStream_t>(stream));
 }
 
 int nvfp4_moe_route(const float* logits, int64_t T, int E, int k, int64_t ld, int32_t* group_offsets,

@@ -227,8 +227,10 @@ def test_tile_weight_without_device():
     assert m.lib.nvfp4_launch_count() == before
 
 
-def test_moe_mlp_validation_and_workspace():
-    f = m.lib.nvfp4_moe_mlp
+@pytest.mark.parametrize("name", ["nvfp4_moe_mlp", "nvfp4_moe_mlp_static"])
+def test_moe_mlp_validation_and_workspace(name):
+    f = getattr(m.lib, name)
+    static = name.endswith("static")
     big = ctypes.c_size_t(1 << 34)
     t3 = (_t(), _t(), _t(), _t(), _t())
 
@@ -254,18 +256,21 @@ def test_moe_mlp_validation_and_workspace():
     s = _size()
     assert f(None, m.BF16, 4096, 4096, 4096, 2048, 64, None, None, 32768, *(nvfp4_tensor(0, 0, 0),) * 5, None, m.BF16,
              4096, None, ctypes.byref(s), None) == m.OK
-    # x f16 copy + float32 H + f16 H~ + the down projection's partial sums: no gathered activation copy
-    assert s.value >= 4096 * 4096 * 2 + 32768 * 2048 * 4 + 32768 * 2048 * 2
-    assert s.value < 4096 * 4096 * 2 + 32768 * 2048 * 4 + 32768 * 2048 * 2 + 32768 * 4096 * 4 + (1 << 24)
-    assert m.moe_mlp_ws_bytes(4096, 4096, 2048, 64, 32768) == s.value
+    # x f16 copy + float32 H (not with static scales: the gate/up quantises H itself) + f16 H~ + the down
+    # projection's partial sums: no gathered activation copy
+    h32 = 0 if static else 32768 * 2048 * 4
+    assert s.value >= 4096 * 4096 * 2 + h32 + 32768 * 2048 * 2
+    assert s.value < 4096 * 4096 * 2 + h32 + 32768 * 2048 * 2 + 32768 * 4096 * 4 + (1 << 24)
+    assert m.moe_mlp_ws_bytes(4096, 4096, 2048, 64, 32768, static=static) == s.value
 
 
 @no_gpu
-def test_moe_mlp_without_device():
+@pytest.mark.parametrize("name", ["nvfp4_moe_mlp", "nvfp4_moe_mlp_static"])
+def test_moe_mlp_without_device(name):
     big = ctypes.c_size_t(1 << 34)
     before = m.lib.nvfp4_launch_count()
-    assert m.lib.nvfp4_moe_mlp(FAKE, m.BF16, 256, 96, 256, 384, 8, FAKE, FAKE, 192, _t(), _t(), _t(), _t(), _t(),
-                               FAKE, m.F32, 256, FAKE, ctypes.byref(big), None) == m.ERR_DEVICE
+    assert getattr(m.lib, name)(FAKE, m.BF16, 256, 96, 256, 384, 8, FAKE, FAKE, 192, _t(), _t(), _t(), _t(), _t(),
+                                FAKE, m.F32, 256, FAKE, ctypes.byref(big), None) == m.ERR_DEVICE
     assert m.lib.nvfp4_launch_count() == before
 
 
